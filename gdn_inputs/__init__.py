@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs for the gated-delta-rule (GDN) prepare / decode /
+prefill workloads.
+
+This module is shared by the GPU path's tests and benchmark and by the CPU
+oracle's tests.  It holds *no* arithmetic of the method itself: it only draws
+random numbers, rounds them to their storage format (so that both sides see
+exactly the same values) and lays them out.  Every array is returned as
+float32 (or int32 / uint8 for indices and flags); the values of an array whose
+storage dtype is bf16 or f16 are exactly representable in that dtype.
+
+Shapes follow the GDN layer's layout (vllm.cpp qwen3_5.cpp, GDN state-cache
+layout checks; ferrum-kernels cpu.rs, linear_attention_prepare_varlen_f32):
+
+* ``x``        [T, Cc] mixed q|k|v projection rows, Cc = 2*Hk*Dk + Hv*Dv
+* ``w``        [Cc, K] depthwise conv taps, tap j multiplies token t-(K-1)+j
+* ``a``, ``b`` [T, Hv] raw gate projections
+* ``A_log``, ``dt_bias`` [Hv]
+* ``conv_pool`` [S, Cc, K-1] raw-input history per slot, oldest column first
+* ``ssm_pool``  [S, Hv, Dv, Dk] recurrent state per slot
+* ``cu``       [N+1] int32 sequence offsets, ``slots`` [N] int32, ``has_init`` [N] uint8
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+DTYPES = ("f32", "bf16", "f16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    Hk: int
+    Hv: int
+    Dk: int
+    Dv: int
+    K: int
+
+    @property
+    def Cc(self) -> int:
+        return 2 * self.Hk * self.Dk + self.Hv * self.Dv
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """One synthetic workload.
+
+    mode is "decode" (one token per row, state pools indexed by ``slots``) or
+    "prefill" (varlen sequences given by ``seqlens``).
+    """
+    name: str
+    mode: str
+    dims: Dims
+    seqlens: Sequence[int] = ()      # prefill: token count per sequence
+    batch: int = 0                   # decode: rows
+    num_slots: int = 1
+    act_dtype: str = "bf16"          # raw activations, conv weight, conv pool
+    state_dtype: str = "f32"         # ssm pool
+    qkv_dtype: str = "bf16"          # prepare outputs / prefill inputs
+    init_state_std: float = 0.0      # 0 => zero initial state (has_init = 0)
+    conv_state_std: float = 0.0      # 0 => zero conv history
+    conv_weight_std: float = 0.5
+    chunk: int = 64
+    seed: int = 0
+    null_rows: int = 0               # decode: rows whose slot is -1
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seqlens)) if self.mode == "prefill" else self.batch
+
+    @property
+    def N(self) -> int:
+        return len(self.seqlens) if self.mode == "prefill" else self.batch
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dims.Dk)
+
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float values to the storage dtype (round-to-nearest-even) and
+    return them as float32.  Used only to define input values."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x32
+    if dtype == "f16":
+        return x32.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        bits = x32.view(np.uint32).astype(np.uint64)
+        lsb = (bits >> 16) & 1
+        bits = (bits + 0x7FFF + lsb) & 0xFFFF0000
+        return bits.astype(np.uint32).view(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    # float32 draws keep the multi-GiB pools affordable
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    return round_to_dtype(v, dtype)
+
+
+def varlen_lengths(n: int, lo: int, hi: int, seed: int) -> List[int]:
+    """Sequence lengths ~ U[lo, hi] (inclusive), seeded."""
+    rng = np.random.default_rng(seed)
+    return [int(v) for v in rng.integers(lo, hi + 1, size=n)]
+
+
+def make_inputs(cfg: Config, slot_seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw every input of ``cfg`` from numpy's PCG64 seeded with cfg.seed."""
+    d = cfg.dims
+    rng = np.random.default_rng(cfg.seed)
+    T, N, S = cfg.T, cfg.N, cfg.num_slots
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = _normal(rng, (T, d.Cc), 1.0, cfg.act_dtype)
+    out["w"] = _normal(rng, (d.Cc, d.K), cfg.conv_weight_std, cfg.act_dtype)
+    out["a"] = _normal(rng, (T, d.Hv), 1.0, cfg.act_dtype)
+    out["b"] = _normal(rng, (T, d.Hv), 1.0, cfg.act_dtype)
+    out["A_log"] = rng.uniform(0.0, math.log(16.0), size=d.Hv).astype(np.float32)
+    out["dt_bias"] = rng.uniform(-1.0, 1.0, size=d.Hv).astype(np.float32)
+    if cfg.conv_state_std > 0:
+        out["conv_pool"] = _normal(rng, (S, d.Cc, d.K - 1), cfg.conv_state_std, cfg.act_dtype)
+    else:
+        out["conv_pool"] = np.zeros((S, d.Cc, d.K - 1), np.float32)
+    if cfg.init_state_std > 0:
+        out["ssm_pool"] = _normal(rng, (S, d.Hv, d.Dv, d.Dk), cfg.init_state_std, cfg.state_dtype)
+    else:
+        out["ssm_pool"] = np.zeros((S, d.Hv, d.Dv, d.Dk), np.float32)
+    srng = np.random.default_rng(cfg.seed + 7 if slot_seed is None else slot_seed)
+    if cfg.mode == "decode":
+        slots = srng.permutation(S)[:N].astype(np.int32)
+        if cfg.null_rows:
+            where = srng.choice(N, size=cfg.null_rows, replace=False)
+            slots[where] = -1
+        out["slots"] = slots
+        out["cu"] = np.arange(N + 1, dtype=np.int32)
+        out["has_init"] = np.ones(N, np.uint8)
+    else:
+        out["cu"] = np.concatenate([[0], np.cumsum(cfg.seqlens)]).astype(np.int32)
+        out["slots"] = srng.permutation(S)[:N].astype(np.int32)
+        flag = 1 if (cfg.init_state_std > 0 or cfg.conv_state_std > 0) else 0
+        out["has_init"] = np.full(N, flag, np.uint8)
+    return out
+
+
+def decode_slot_sets(cfg: Config, count: int, seed: int) -> np.ndarray:
+    """``count`` independent draws of the decode slot subset (distinct slots
+    within each draw), so that repeated timed calls touch different slots."""
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(cfg.num_slots)[: cfg.batch] for _ in range(count)]).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads.
+# ---------------------------------------------------------------------------
+QWEN_DIMS = Dims(Hk=16, Hv=32, Dk=128, Dv=128, K=4)
+
+
+def tiny() -> Config:
+    """1 sequence of 8 tokens, Hk=1, Hv=2, Dk=Dv=16, K=4, f32 throughout."""
+    return Config(name="tiny_f32_T8", mode="prefill", dims=Dims(1, 2, 16, 16, 4), seqlens=(8,),
+                  num_slots=1, act_dtype="f32", state_dtype="f32", qkv_dtype="f32", seed=1001)
+
+
+def tiny_decode() -> Config:
+    """The tiny workload's shapes as a decode batch of 8 rows."""
+    return Config(name="tiny_f32_decode", mode="decode", dims=Dims(1, 2, 16, 16, 4), batch=8,
+                  num_slots=16, act_dtype="f32", state_dtype="f32", qkv_dtype="f32",
+                  init_state_std=0.05, conv_state_std=1.0, seed=1001)
+
+
+def decode_batch(state_dtype: str = "f32") -> Config:
+    """256 rows x 1 token, Hk=16, Hv=32, Dk=Dv=128, K=4; bf16 activations;
+    512-slot state pool ~N(0, 0.05); bf16 conv pool [512, Cc, 3]."""
+    return Config(name="decode_b256_hk16_hv32_d128", mode="decode", dims=QWEN_DIMS, batch=256,
+                  num_slots=512, act_dtype="bf16", state_dtype=state_dtype, qkv_dtype="bf16",
+                  init_state_std=0.05, conv_state_std=1.0, seed=1002)
+
+
+def prefill_single(qkv_dtype: str = "bf16") -> Config:
+    """1 sequence of 4096 tokens, Hk=16, Hv=32, Dk=Dv=128, K=4; bf16 raw
+    activations; f32 state from zero; chunk 64."""
+    return Config(name="prefill_T4096_hk16_hv32_d128", mode="prefill", dims=QWEN_DIMS, seqlens=(4096,),
+                  num_slots=1, act_dtype="bf16", state_dtype="f32", qkv_dtype=qkv_dtype, seed=1003)
+
+
+def prefill_varlen() -> Config:
+    """16 sequences, lengths ~U[128, 8192] (seeded), bf16 activations, bf16
+    state cache with nonzero initial states ~N(0, 0.05)."""
+    return Config(name="varlen_16seq_hk16_hv32_d128", mode="prefill", dims=QWEN_DIMS,
+                  seqlens=tuple(varlen_lengths(16, 128, 8192, 2004)), num_slots=32, act_dtype="bf16",
+                  state_dtype="bf16", qkv_dtype="bf16", init_state_std=0.05, conv_state_std=1.0, seed=1004)
+
+
+def prefill_long(tokens: int = 32768) -> Config:
+    """1 sequence of 32768 tokens, Hk=16, Hv=48, Dk=Dv=128, K=4; bf16
+    activations; f16 state from zero."""
+    return Config(name=f"long_T{tokens}_hk16_hv48_d128", mode="prefill", dims=Dims(16, 48, 128, 128, 4),
+                  seqlens=(tokens,), num_slots=1, act_dtype="bf16", state_dtype="f16", qkv_dtype="bf16",
+                  seed=1005)
+
+
+def named_configs() -> Dict[str, Config]:
+    cs = [tiny(), decode_batch(), prefill_single(), prefill_varlen(), prefill_long()]
+    return {c.name: c for c in cs}
