@@ -1,0 +1,190 @@
+"""Python binding of the GDN prepare / decode / prefill library (libgdn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gdn.h``.  PyTorch supplies
+device memory and the current HIP stream.  If the library is not built, the
+first call raises; there is no fallback path.
+
+Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`,
+:func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+_STATUS = {0: "ok", 1: "invalid argument", 2: "shape mismatch", 3: "bad slot index", 4: "unsupported dtype",
+           5: "workspace too small", 6: "device error"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed ({_STATUS.get(status, status)}): {message}")
+        self.status = status
+        self.message = message
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
+                ("conv_kernel", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    Hk: int
+    Hv: int
+    Dk: int
+    Dv: int
+    K: int
+
+    @property
+    def Cc(self) -> int:
+        return 2 * self.Hk * self.Dk + self.Hv * self.Dv
+
+    def c(self) -> _Dims:
+        return _Dims(self.Hk, self.Hv, self.Dk, self.Dv, self.K)
+
+
+_lib = None
+EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_prefill_varlen", "gdn_prefill_workspace_size",
+           "gdn_status_string", "gdn_last_error", "gdn_version")
+
+
+def load_library():
+    """Load libgdn.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libgdn.so is not built ({LIB_PATH}); run __graft_entry__.build() or "
+                           "python gated_delta_rule_prepare_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(_Dims)
+    lib.gdn_prepare.argtypes = [D, i32, i64, P, P, P, i64, P, i64, P, i64, i32, P, P, P, P, i32, P, P, P, i32,
+                                P, P, P, i32, P, P, P]
+    lib.gdn_decode.argtypes = [D, i32, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, P, P, f32, P, P]
+    lib.gdn_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32, i32,
+                                       i32, P, P, sz, P]
+    lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
+    lib.gdn_prefill_workspace_size.restype = sz
+    for fn in ("gdn_prepare", "gdn_decode", "gdn_prefill_varlen"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise GdnError(fn, status, _lib.gdn_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _host_i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _hptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def gdn_prepare(dims: Dims, cu_seqlens, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias, conv_state_pool,
+                q_out, k_out, v_out, g_out, beta_out, slot_idx=None, has_initial_state=None,
+                apply_qk_l2norm: bool = True, cu_seqlens_host=None, slot_idx_host=None, stream=None) -> None:
+    """Varlen prepare step; writes q/k/v/g/beta and updates the conv pool in place.
+
+    ``cu_seqlens`` and ``slot_idx`` are int32 device tensors; their host copies
+    are taken from ``*_host`` if given, else copied from the device tensors.
+    """
+    lib = load_library()
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    st = lib.gdn_prepare(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(mixed_qkv),
+                         mixed_qkv.stride(0), _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0),
+                         _dtype_code(mixed_qkv), _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias),
+                         _ptr(conv_state_pool), conv_state_pool.shape[0] if conv_state_pool is not None else 0,
+                         _hptr(sl_h), _ptr(slot_idx), _ptr(has_initial_state), int(apply_qk_l2norm),
+                         _ptr(q_out), _ptr(k_out), _ptr(v_out), _dtype_code(q_out), _ptr(g_out), _ptr(beta_out),
+                         _stream(stream))
+    _check("gdn_prepare", st)
+
+
+def gdn_decode(dims: Dims, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias, conv_state_pool, ssm_state_pool,
+               slot_idx, out, scale: float, slot_idx_host=None, validate: bool = True, stream=None) -> None:
+    """Fused decode step for ``mixed_qkv.shape[0]`` rows; pools updated in place.
+
+    With ``validate`` the slot indices are checked on the host (a host copy is
+    made from ``slot_idx`` unless ``slot_idx_host`` is given)."""
+    lib = load_library()
+    sl_h = None
+    if validate:
+        sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    st = lib.gdn_decode(ctypes.byref(dims.c()), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
+                        _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0), _dtype_code(mixed_qkv),
+                        _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_pool),
+                        _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
+                        _ptr(slot_idx), _hptr(sl_h), float(scale), _ptr(out), _stream(stream))
+    _check("gdn_decode", st)
+
+
+def gdn_prefill_workspace_size(dims: Dims, num_seqs: int, total_tokens: int, chunk_size: int = 64) -> int:
+    lib = load_library()
+    return int(lib.gdn_prefill_workspace_size(ctypes.byref(dims.c()), num_seqs, total_tokens, chunk_size))
+
+
+def gdn_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool, out, scale: float,
+                       slot_idx=None, has_initial_state=None, use_qk_l2norm: bool = False, chunk_size: int = 64,
+                       workspace=None, cu_seqlens_host=None, slot_idx_host=None, stream=None) -> None:
+    """Chunked varlen prefill; the pool slot of each sequence is its initial
+    and final state.  ``workspace`` (a uint8 device tensor) is allocated here
+    with torch if not given."""
+    lib = load_library()
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    need = gdn_prefill_workspace_size(dims, n, T, chunk_size)
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_prefill_varlen(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(ssm_state_pool),
+                                _dtype_code(ssm_state_pool), ssm_state_pool.shape[0], _hptr(sl_h), _ptr(slot_idx),
+                                _ptr(has_initial_state), float(scale), int(use_qk_l2norm), int(chunk_size),
+                                _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("gdn_prefill_varlen", st)

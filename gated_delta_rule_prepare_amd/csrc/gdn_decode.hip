@@ -1,0 +1,199 @@
+// gdn_decode.hip -- fused single-token GDN step against slot-indexed pools.
+//
+// One workgroup (4 waves) per (batch row, key head kh).  It owns the
+// r = Hv/Hk value heads kh*r .. kh*r+r-1 that share q and k, i.e. R = r*Dv
+// state rows of Dk elements, which sit contiguously in the slot's pool entry.
+//
+// Phase A (prepare, vllm.cpp cpu_ops.cpp CausalConv1dUpdateKernel and
+// GdnPackedDecodeKernel): the 2*Dk + R channels of this key head are
+// convolved against the slot's conv history, which is shifted left and
+// appended with the raw input in place; SiLU; q and k are L2-normalised;
+// g and beta per value head.  The first batch of state rows is already in
+// flight while this runs, since the state loads do not depend on it.
+//
+// Phase B (the recurrence, vllm.cpp cpu_ops.cpp GdnHeadTokenStep): state rows
+// stream through registers.  A lane holds 16 bytes of a row (Dk/lanes-per-row
+// columns); a wave load covers 1 KiB of consecutive rows.  Per row the two
+// dot products S.k and S.q are formed in one pass and summed across the
+// lanes of the row; then, with d = exp(g):
+//   u = d (S.k);  delta = beta (v - u);  o = d (S.q) + delta (k.q);
+//   S' = d S + delta k
+// which is the token step written so that the row is read once and written
+// once.  Value rows are independent, so rows need no synchronisation.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kLoads = 8;  // 16-byte state loads in flight per lane
+
+template <typename ActT, typename StT, int DK>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
+  constexpr int SV = Elem<StT>::kVec;       // state elements per lane load
+  constexpr int LPR = DK / SV;              // lanes per state row
+  static_assert(LPR >= 1 && LPR <= 64, "lanes per row");
+  constexpr int RPL = 64 / LPR;             // rows per wave load
+  constexpr int ROWS_PER_ITER = kDecWaves * kLoads * RPL;
+
+  extern __shared__ float smem[];
+  const int kh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int r = p.Hv / p.Hk;
+  const int Dv = p.Dv;
+  const int R = r * Dv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  ActT* __restrict__ out = static_cast<ActT*>(p.out) + ((int64_t)b * p.Hv + (int64_t)kh * r) * Dv;
+  const int slot = p.slots[b];
+  if (slot < 0 || slot >= p.num_slots) {  // inert row: zero output, pools untouched
+    for (int i = tid; i < R; i += kDecThreads) Elem<ActT>::store(out + i, 0.0f);
+    return;
+  }
+  StT* __restrict__ S = static_cast<StT*>(p.ssm_pool) + ((int64_t)slot * p.Hv + (int64_t)kh * r) * Dv * DK;
+
+  const int sub = lane / LPR;          // row within this wave's load
+  const int col = (lane % LPR) * SV;   // first state column of this lane
+  auto row_of = [&](int it, int u) { return it * ROWS_PER_ITER + (u * kDecWaves + wave) * RPL + sub; };
+
+  // issue the first batch of state loads before the prepare work
+  uint4 raw[kLoads];
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int row = row_of(0, u);
+    if (row < R) raw[u] = *reinterpret_cast<const uint4*>(S + (int64_t)row * DK + col);
+  }
+
+  // ---- phase A: conv update + SiLU for the 2*DK + R channels of this key head
+  float* s_y = smem;                      // [2*DK + R]
+  float* s_decay = smem + 2 * DK + R;     // [r]
+  float* s_beta = s_decay + r;            // [r]
+  float* s_red = s_beta + r;              // [4]: 1/|q|, 1/|k|, k.q
+  const int K = p.K;
+  const ActT* __restrict__ x = static_cast<const ActT*>(p.x) + (int64_t)b * p.x_stride;
+  const ActT* __restrict__ w = static_cast<const ActT*>(p.w);
+  ActT* __restrict__ hist = static_cast<ActT*>(p.conv_pool);
+  const int key_dim = p.Hk * DK;
+  for (int ch = tid; ch < 2 * DK + R; ch += kDecThreads) {
+    const int cg = ch < DK ? kh * DK + ch
+                 : ch < 2 * DK ? key_dim + kh * DK + (ch - DK)
+                               : 2 * key_dim + kh * R + (ch - 2 * DK);
+    const float xv = Elem<ActT>::load(x + cg);
+    float acc = Elem<ActT>::load(w + (int64_t)cg * K + (K - 1)) * xv;
+    if (K > 1) {
+      ActT* h = hist + ((int64_t)slot * p.Cc + cg) * (K - 1);
+      float old[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < K - 1) {
+          old[j] = Elem<ActT>::load(h + j);
+          acc += Elem<ActT>::load(w + (int64_t)cg * K + j) * old[j];
+        }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j < K - 2) Elem<ActT>::store(h + j, old[j + 1]);
+      Elem<ActT>::store(h + (K - 2), xv);
+    }
+    s_y[ch] = silu_f(acc);
+  }
+  __syncthreads();
+  if (wave < 3) {
+    // wave 0: |q|^2, wave 1: |k|^2, wave 2: k.q (raw values)
+    float acc = 0.0f;
+    for (int d = lane; d < DK; d += 64) {
+      const float qd = s_y[d], kd = s_y[DK + d];
+      acc += wave == 0 ? qd * qd : (wave == 1 ? kd * kd : kd * qd);
+    }
+    acc = group_sum<64>(acc);
+    if (lane == 0) s_red[wave] = acc;
+  } else {
+    for (int j = lane; j < r; j += 64) {
+      const int h = kh * r + j;
+      const float a = Elem<ActT>::load(static_cast<const ActT*>(p.a) + (int64_t)b * p.a_stride + h);
+      const float bb = Elem<ActT>::load(static_cast<const ActT*>(p.b) + (int64_t)b * p.b_stride + h);
+      s_decay[j] = expf(-expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]));
+      s_beta[j] = sigmoid_f(bb);
+    }
+  }
+  __syncthreads();
+  const float q_inv = 1.0f / sqrtf(s_red[0] + 1e-6f);
+  const float k_inv = 1.0f / sqrtf(s_red[1] + 1e-6f);
+  const float kq = s_red[2] * q_inv * k_inv * p.scale;  // k_hat . (scale q_hat)
+  float kv[SV], qv[SV];
+#pragma unroll
+  for (int i = 0; i < SV; ++i) {
+    kv[i] = s_y[DK + col + i] * k_inv;
+    qv[i] = s_y[col + i] * q_inv * p.scale;
+  }
+
+  // ---- phase B: stream the R state rows
+  const int iters = (R + ROWS_PER_ITER - 1) / ROWS_PER_ITER;
+  for (int it = 0; it < iters; ++it) {
+    if (it > 0) {
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int row = row_of(it, u);
+        if (row < R) raw[u] = *reinterpret_cast<const uint4*>(S + (int64_t)row * DK + col);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int row = row_of(it, u);
+      if (row >= R) continue;  // uniform across the row's lanes
+      float st[SV];
+      Elem<StT>::unpack(raw[u], st);
+      float p1 = 0.0f, p2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        p1 += st[i] * kv[i];
+        p2 += st[i] * qv[i];
+      }
+      p1 = group_sum<LPR>(p1);
+      p2 = group_sum<LPR>(p2);
+      const int hl = row / Dv;
+      const float d = s_decay[hl];
+      const float delta = s_beta[hl] * (s_y[2 * DK + row] - d * p1);
+      const float o = d * p2 + delta * kq;
+#pragma unroll
+      for (int i = 0; i < SV; ++i) st[i] = d * st[i] + delta * kv[i];
+      *reinterpret_cast<uint4*>(S + (int64_t)row * DK + col) = Elem<StT>::pack(st);
+      if ((lane % LPR) == 0) Elem<ActT>::store(out + row, o);
+    }
+  }
+}
+
+template <typename ActT, typename StT>
+hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
+  const int r = p.Hv / p.Hk;
+  const size_t smem = (size_t)(2 * p.Dk + r * p.Dv + 2 * r + 4) * sizeof(float);
+  dim3 grid(p.Hk, p.B);
+  switch (p.Dk) {
+    case 16: decode_kernel<ActT, StT, 16><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 32: decode_kernel<ActT, StT, 32><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 64: decode_kernel<ActT, StT, 64><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 128: decode_kernel<ActT, StT, 128><<<grid, kDecThreads, smem, stream>>>(p); break;
+    default: decode_kernel<ActT, StT, 256><<<grid, kDecThreads, smem, stream>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename ActT>
+hipError_t launch_state(const DecodeParams& p, hipStream_t stream) {
+  switch (p.state) {
+    case GDN_F32: return launch_dk<ActT, float>(p, stream);
+    case GDN_BF16: return launch_dk<ActT, bf16>(p, stream);
+    default: return launch_dk<ActT, f16>(p, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  return p.act == GDN_F32 ? launch_state<float>(p, stream) : launch_state<bf16>(p, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,96 @@
+// gdn_internal.h -- parameter blocks and launcher entry points between the
+// host-side C ABI (gdn_api.cpp) and the HIP kernels.  Everything here has
+// already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+struct PrepareParams {
+  int Hk, Hv, Dk, Dv, K;
+  int Cc;
+  int N;
+  int64_t T;
+  const int32_t* cu;      // device [N+1]
+  const void* x;          // [T, x_stride] act
+  int64_t x_stride;
+  const void* a;          // [T, a_stride] act
+  int64_t a_stride;
+  const void* b;          // [T, b_stride] act
+  int64_t b_stride;
+  const void* w;          // [Cc, K] act
+  const float* A_log;     // [Hv]
+  const float* dt_bias;   // [Hv]
+  void* conv_pool;        // [S, Cc, K-1] act
+  int num_slots;
+  const int32_t* slots;   // device [N] or null (slot = s)
+  const uint8_t* has_init;  // device [N] or null (all 1)
+  int l2norm;
+  void* q;                // [T, Hk, Dk] qkv
+  void* k;                // [T, Hk, Dk] qkv
+  void* v;                // [T, Hv, Dv] qkv
+  float* g;               // [T, Hv]
+  float* beta;            // [T, Hv]
+  gdn_dtype act, qkv;
+};
+
+struct DecodeParams {
+  int Hk, Hv, Dk, Dv, K;
+  int Cc;
+  int B;
+  const void* x;
+  int64_t x_stride;
+  const void* a;
+  int64_t a_stride;
+  const void* b;
+  int64_t b_stride;
+  const void* w;
+  const float* A_log;
+  const float* dt_bias;
+  void* conv_pool;        // [S, Cc, K-1] act
+  void* ssm_pool;         // [S, Hv, Dv, Dk] state
+  int num_slots;
+  const int32_t* slots;   // device [B]
+  float scale;
+  void* out;              // [B, Hv, Dv] act
+  gdn_dtype act, state;
+};
+
+struct PrefillParams {
+  int Hk, Hv, Dk, Dv;
+  int N;
+  int64_t T;
+  const int32_t* cu;      // device [N+1]
+  const void* q;          // [T, Hk, Dk] qkv
+  const void* k;
+  const void* v;          // [T, Hv, Dv] qkv
+  const float* g;         // [T, Hv]
+  const float* beta;      // [T, Hv]
+  void* ssm_pool;         // [S, Hv, Dv, Dk] state
+  int num_slots;
+  const int32_t* slots;   // device [N] or null
+  const uint8_t* has_init;  // device [N] or null
+  float scale;
+  int l2norm;
+  int chunk;
+  void* out;              // [T, Hv, Dv] qkv
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t num_chunks;     // sum over sequences of ceil(L / chunk)
+  int max_chunks_per_seq;
+  gdn_dtype qkv, state;
+};
+
+// Each launcher enqueues its kernels on `stream` and returns the HIP status
+// of the launch.
+hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
+
+}  // namespace gdn

@@ -1,0 +1,237 @@
+// gdn_prepare.hip -- varlen prepare step of the GDN layer on gfx950.
+//
+// Kernel 1 (conv): one wave owns a block of 64*V consecutive channels
+// (V = 16 bytes of input per lane) and a strip of tokens.  It walks its
+// tokens in order keeping the last K-1 raw inputs of each channel in
+// registers (a sliding window), so every input element is read from HBM once
+// (plus K-1 halo rows per strip).  Per token it forms the causal depthwise
+// conv + SiLU, L2-normalises q and k heads with a cross-lane sum over the
+// lanes of one head (a head of Dk channels is Dk/V aligned lanes), and
+// stores q/k/v.  Strips may cross sequence boundaries: the window is
+// reloaded from the slot's conv history (or zeros) where a sequence starts.
+// Conv semantics: vllm.cpp cpu_ops.cpp, CausalConv1dFwdKernel; split and
+// norm: GdnPostConvKernel, L2NormKernel.
+//
+// Kernel 2 (finish): the per-(token, value head) gates g and beta
+// (vllm.cpp cpu_ops.cpp, GdnGBetaKernel) and the write-back of each
+// sequence's last K-1 raw inputs into its conv history row.  It runs after
+// kernel 1 on the same stream, so every read of an old history row happens
+// before that row is overwritten.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kConvWaves = 4;   // waves per workgroup (one channel block each)
+constexpr int kStrip = 32;      // tokens per wave
+constexpr int kAhead = 8;       // token rows loaded before they are used
+
+// Largest s in [0, N) with cu[s] <= t, found by the whole wave (t is
+// wave-uniform and cu[0] = 0 <= t).  Each round splits the candidate range
+// into 64 pieces and keeps the one the ballot points at.
+__device__ int find_sequence(const int32_t* cu, int N, int64_t t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = N;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool le = idx < hi && cu[idx] <= t;
+    const int cnt = __popcll(__ballot(le));
+    lo += (cnt - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
+template <typename ActT, typename QkvT, int K>
+__global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PrepareParams p) {
+  constexpr int V = Elem<ActT>::kVec;
+  constexpr int H = K > 1 ? K - 1 : 1;  // history length (storage for K = 1 unused)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c0 = (blockIdx.x * kConvWaves + wave) * 64 * V;
+  if (c0 >= p.Cc) return;  // wave-uniform; the kernel uses no block barrier
+  const int c = c0 + lane * V;
+  const bool active = c < p.Cc;  // Cc is a multiple of 16, so lanes are all-in or all-out
+  const int64_t t0 = (int64_t)blockIdx.y * kStrip;
+  const int64_t t1 = min(p.T, t0 + kStrip);
+
+  const ActT* __restrict__ x = static_cast<const ActT*>(p.x);
+  const ActT* __restrict__ w = static_cast<const ActT*>(p.w);
+  const ActT* __restrict__ hist = static_cast<const ActT*>(p.conv_pool);
+  const int key_dim = p.Hk * p.Dk;
+  const int region = c < key_dim ? 0 : (c < 2 * key_dim ? 1 : 2);
+  const int head_lanes = p.Dk / V;  // lanes sharing one q or k head
+
+  // taps: wt[j][i] multiplies the input K-1-j tokens back, channel c+i
+  float wt[K][V];
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+#pragma unroll
+    for (int j = 0; j < K; ++j) wt[j][i] = active ? Elem<ActT>::load(w + (int64_t)(c + i) * K + j) : 0.0f;
+
+  // win[j][i]: raw input j+1 tokens back
+  float win[H][V];
+  int s = find_sequence(p.cu, p.N, t0);
+  int64_t seq_start = p.cu[s];
+  int64_t seq_end = p.cu[s + 1];
+
+  // history value d tokens before the start of sequence s (1 <= d <= K-1)
+  auto hist_at = [&](int seq, int d, int i) -> float {
+    const bool has = p.has_init == nullptr || p.has_init[seq] != 0;
+    if (!has || !active) return 0.0f;
+    const int slot = p.slots ? p.slots[seq] : seq;
+    return Elem<ActT>::load(hist + ((int64_t)slot * p.Cc + c + i) * (K - 1) + (K - 1 - d));
+  };
+  if constexpr (K > 1) {
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      const int64_t tp = t0 - 1 - j;
+      if (tp >= seq_start) {
+        if (active) load_vec<ActT>(x + tp * p.x_stride + c, win[j]);
+        else
+#pragma unroll
+          for (int i = 0; i < V; ++i) win[j][i] = 0.0f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) win[j][i] = hist_at(s, (int)(seq_start - tp), i);
+      }
+    }
+  }
+
+  QkvT* __restrict__ out_base;
+  int64_t out_row;
+  int out_col;
+  if (region == 0) {
+    out_base = static_cast<QkvT*>(p.q); out_row = key_dim; out_col = c;
+  } else if (region == 1) {
+    out_base = static_cast<QkvT*>(p.k); out_row = key_dim; out_col = c - key_dim;
+  } else {
+    out_base = static_cast<QkvT*>(p.v); out_row = (int64_t)p.Hv * p.Dv; out_col = c - 2 * key_dim;
+  }
+
+  for (int64_t tb = t0; tb < t1; tb += kAhead) {
+    float xv[kAhead][V];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t t = tb + u;
+      if (t < t1 && active) load_vec<ActT>(x + t * p.x_stride + c, xv[u]);
+      else
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[u][i] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t t = tb + u;
+      if (t >= t1) break;  // wave-uniform
+      if (t == seq_end) {  // a new sequence starts here: reload its history
+        ++s;
+        seq_start = t;
+        seq_end = p.cu[s + 1];
+        if constexpr (K > 1) {
+#pragma unroll
+          for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+            for (int i = 0; i < V; ++i) win[j][i] = hist_at(s, j + 1, i);
+        }
+      }
+      float y[V];
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float acc = wt[K - 1][i] * xv[u][i];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) acc += wt[K - 2 - j][i] * win[j][i];
+        y[i] = silu_f(acc);
+        ss += y[i] * y[i];
+      }
+      if (p.l2norm) {
+        for (int off = head_lanes >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (region < 2) {
+          const float inv = 1.0f / sqrtf(ss + 1e-6f);
+#pragma unroll
+          for (int i = 0; i < V; ++i) y[i] *= inv;
+        }
+      }
+      if (active) store_n<QkvT, V>(out_base + t * out_row + out_col, y);
+      if constexpr (K > 1) {
+#pragma unroll
+        for (int j = K - 2; j > 0; --j)
+#pragma unroll
+          for (int i = 0; i < V; ++i) win[j][i] = win[j - 1][i];
+#pragma unroll
+        for (int i = 0; i < V; ++i) win[0][i] = xv[u][i];
+      }
+    }
+  }
+}
+
+template <typename ActT, int K>
+__global__ __launch_bounds__(256) void prepare_finish_kernel(PrepareParams p, int gate_blocks) {
+  if ((int)blockIdx.x < gate_blocks) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= p.T * p.Hv) return;
+    const int64_t t = i / p.Hv;
+    const int h = (int)(i % p.Hv);
+    const float a = Elem<ActT>::load(static_cast<const ActT*>(p.a) + t * p.a_stride + h);
+    const float b = Elem<ActT>::load(static_cast<const ActT*>(p.b) + t * p.b_stride + h);
+    p.g[i] = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
+    p.beta[i] = sigmoid_f(b);
+    return;
+  }
+  if constexpr (K > 1) {
+    const int64_t i = (int64_t)(blockIdx.x - gate_blocks) * 256 + threadIdx.x;
+    if (i >= (int64_t)p.N * p.Cc) return;
+    const int s = (int)(i / p.Cc);
+    const int c = (int)(i % p.Cc);
+    const int64_t start = p.cu[s];
+    const int64_t len = p.cu[s + 1] - start;
+    const int slot = p.slots ? p.slots[s] : s;
+    const bool has = p.has_init == nullptr || p.has_init[s] != 0;
+    ActT* row = static_cast<ActT*>(p.conv_pool) + ((int64_t)slot * p.Cc + c) * (K - 1);
+    const ActT* x = static_cast<const ActT*>(p.x);
+    float old[K - 1];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) old[j] = Elem<ActT>::load(row + j);
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      const int64_t tp = len - (K - 1) + j;  // position of the input history column j holds
+      const float val = tp >= 0 ? Elem<ActT>::load(x + (start + tp) * p.x_stride + c)
+                                : (has ? old[(K - 1) + tp] : 0.0f);
+      Elem<ActT>::store(row + j, val);
+    }
+  }
+}
+
+template <typename ActT, typename QkvT, int K>
+hipError_t launch_typed(const PrepareParams& p, hipStream_t stream) {
+  constexpr int V = Elem<ActT>::kVec;
+  const int chans_per_block = kConvWaves * 64 * V;
+  dim3 grid((p.Cc + chans_per_block - 1) / chans_per_block, (unsigned)((p.T + kStrip - 1) / kStrip));
+  prepare_conv_kernel<ActT, QkvT, K><<<grid, kConvWaves * 64, 0, stream>>>(p);
+  const int gate_blocks = (int)((p.T * p.Hv + 255) / 256);
+  const int hist_blocks = K > 1 ? (int)(((int64_t)p.N * p.Cc + 255) / 256) : 0;
+  prepare_finish_kernel<ActT, K><<<gate_blocks + hist_blocks, 256, 0, stream>>>(p, gate_blocks);
+  return hipGetLastError();
+}
+
+template <typename ActT, typename QkvT>
+hipError_t launch_k(const PrepareParams& p, hipStream_t stream) {
+  switch (p.K) {
+    case 1: return launch_typed<ActT, QkvT, 1>(p, stream);
+    case 2: return launch_typed<ActT, QkvT, 2>(p, stream);
+    case 3: return launch_typed<ActT, QkvT, 3>(p, stream);
+    default: return launch_typed<ActT, QkvT, 4>(p, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream) {
+  if (p.act == GDN_F32)
+    return p.qkv == GDN_F32 ? launch_k<float, float>(p, stream) : launch_k<float, bf16>(p, stream);
+  return p.qkv == GDN_F32 ? launch_k<bf16, float>(p, stream) : launch_k<bf16, bf16>(p, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,213 @@
+/*
+ * gdn.h -- C ABI of the gated-delta-rule (GDN) prepare / decode / prefill
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the GDN linear-attention layer of the
+ * Qwen3-Next / Qwen3.5 family, as the following pages define them:
+ *   [P1] vllm.cpp src/vt/cpu/cpu_ops.cpp
+ *   [P2] vllm.cpp src/vllm/model_executor/models/qwen3_5.cpp
+ *   [P3] ferrum-kernels 0.8.0 src/ferrum_kernels/backend/cpu.rs
+ * (cited below by page and function).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Dimensions: Hk key heads, Hv value heads (Hv a multiple of Hk; value head h
+ *   reads key/query head h / (Hv/Hk)), head dims Dk and Dv, conv kernel K.
+ *   Cc = 2*Hk*Dk + Hv*Dv conv channels, laid out q | k | v, each head-major
+ *   ([P1] GdnConvSplitKernel; [P3] linear_attention_prepare_varlen_f32).
+ *   Supported: Dk, Dv in {16, 32, 64, 128, 256}; 1 <= K <= 4.
+ * Pointers: "device" pointers must be device memory visible to the stream;
+ *   "host" pointers are read synchronously before the call returns.  Device
+ *   tensors are dense row-major, 16-byte aligned, except where a row stride
+ *   (in elements) is passed; such rows must start on 16-byte boundaries.
+ * Ownership: the caller owns every buffer.  The library allocates nothing;
+ *   scratch memory is passed in as a workspace whose size a query returns.
+ *   Weights (conv weight, A_log, dt_bias) are read in place every call.
+ * Streams: `stream` is a hipStream_t (NULL = the null stream).  All device
+ *   work is enqueued on it; no call synchronises the host.
+ * Errors: every argument is checked on the host before any device work is
+ *   enqueued; a failing check returns a non-zero gdn_status, enqueues
+ *   nothing and records a message retrievable with gdn_last_error() on the
+ *   calling thread.  GDN_ERR_DEVICE reports a failed kernel launch.
+ * State pools: the conv history pool is [num_slots, Cc, K-1] in the
+ *   activation dtype (column j holds the j-th oldest of the last K-1 raw
+ *   inputs); the recurrent state pool is [num_slots, Hv, Dv, Dk] (Dk
+ *   contiguous) in f32, bf16 or f16 ([P2] ValidateGdnStateCacheLayout,
+ *   ResolveMambaSsmCacheDType).  A call reads a slot's state at its storage
+ *   dtype, computes in f32 and stores it back rounded (round to nearest
+ *   even) once at the end of the call ([P2] GatherStateF32 /
+ *   ScatterStateF32).  Slot indices are int32; a live slot is in
+ *   [0, num_slots) and appears at most once per call; -1 marks an inert row
+ *   in decode only ([P2] ValidateGdnStateIndices).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_dtype {
+  GDN_F32 = 0,
+  GDN_BF16 = 1,
+  GDN_F16 = 2
+} gdn_dtype;
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1, /* null pointer, misaligned pointer, bad flag */
+  GDN_ERR_SHAPE = 2,            /* dims, offsets or strides inconsistent     */
+  GDN_ERR_INDEX = 3,            /* slot index out of range or duplicated     */
+  GDN_ERR_DTYPE = 4,            /* unsupported dtype combination             */
+  GDN_ERR_WORKSPACE = 5,        /* workspace missing or too small            */
+  GDN_ERR_DEVICE = 6            /* HIP reported an error                     */
+} gdn_status;
+
+typedef struct gdn_dims {
+  int32_t num_k_heads; /* Hk */
+  int32_t num_v_heads; /* Hv, a multiple of Hk */
+  int32_t head_k_dim;  /* Dk */
+  int32_t head_v_dim;  /* Dv */
+  int32_t conv_kernel; /* K */
+} gdn_dims;
+
+/*
+ * gdn_prepare -- varlen prepare step (conv + SiLU, split, L2 norm, gates).
+ *
+ * Defined by [P1] CausalConv1dFwdKernel, GdnPostConvKernel, L2NormKernel,
+ * GdnGBetaKernel and [P3] linear_attention_prepare_varlen_f32.
+ * For every sequence s (tokens cu[s] .. cu[s+1]-1, each sequence non-empty),
+ * channel c and token t:
+ *   y[t,c] = silu( sum_j w[c,j] * x_s(t-(K-1)+j) ),
+ * where x_s(p) is mixed_qkv[p, c] inside the sequence and, before its start,
+ * the conv history row of the sequence's slot (when has_initial_state[s] is
+ * non-zero) or zero.  Then q = y[:, q block], k = y[:, k block], v = y[:, v
+ * block]; when apply_qk_l2norm is non-zero, q and k are scaled per (token,
+ * key head) by 1/sqrt(sum of squares + 1e-6).  Per (token, value head):
+ *   g    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *   beta = sigmoid(b[t,h]).
+ * Finally the history row of each sequence's slot is replaced by the
+ * sequence's last K-1 raw inputs (a sequence shorter than K-1 keeps the
+ * tail of the old history in front of them).
+ *
+ * Arguments:
+ *   dims                  layer dimensions (see above).
+ *   num_seqs, total_tokens N >= 1 sequences, T = cu[N] tokens (N = T = 0 is a no-op).
+ *   cu_seqlens_host       host int32 [N+1], cu[0] = 0, strictly increasing, cu[N] = T.
+ *   cu_seqlens_dev        device copy of the same offsets.
+ *   mixed_qkv             device [T, mixed_row_stride] in act_dtype; the first Cc columns are used.
+ *   a_raw, b_raw          device [T, row stride] in act_dtype; the first Hv columns are used.
+ *   act_dtype             GDN_F32 or GDN_BF16; also the dtype of conv_weight and of the history pool.
+ *   conv_weight           device [Cc, K] in act_dtype.
+ *   A_log, dt_bias        device f32 [Hv].
+ *   conv_state_pool       device [num_slots, Cc, K-1] in act_dtype, read and written in place
+ *                         (may be NULL when K = 1).
+ *   slot_idx_host/_dev    int32 [N] slot of each sequence; both NULL means slot s for sequence s.
+ *   has_initial_state_dev device uint8 [N], or NULL for "every sequence continues its slot".
+ *   q_out, k_out          device [T, Hk, Dk] in qkv_dtype (GDN_F32 or GDN_BF16).
+ *   v_out                 device [T, Hv, Dv] in qkv_dtype.
+ *   g_out, beta_out       device f32 [T, Hv].
+ */
+gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                       const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                       const void* mixed_qkv, int64_t mixed_row_stride, const void* a_raw,
+                       int64_t a_row_stride, const void* b_raw, int64_t b_row_stride,
+                       gdn_dtype act_dtype, const void* conv_weight, const float* A_log,
+                       const float* dt_bias, void* conv_state_pool, int32_t num_slots,
+                       const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                       const uint8_t* has_initial_state_dev, int32_t apply_qk_l2norm,
+                       void* q_out, void* k_out, void* v_out, gdn_dtype qkv_dtype,
+                       float* g_out, float* beta_out, void* stream);
+
+/*
+ * gdn_decode -- fused single-token step for a batch of rows against the
+ * slot-indexed pools: the prepare step of one token (conv against the slot's
+ * history, which is then shifted left by one and appended with the raw
+ * input; SiLU; q/k L2 norm, always applied; gates) followed by one step of
+ * the gated delta rule per value head h with key head kh = h/(Hv/Hk):
+ *   S <- exp(g) S;  u = S k;  delta = beta (v - u);  S <- S + delta k^T;
+ *   o = S (scale q)
+ * on the [Dv, Dk] state of the row's slot, in place.
+ *
+ * Defined by [P1] CausalConv1dUpdateKernel, GdnPackedDecodeKernel,
+ * GdnDecodeKernel, GdnHeadTokenStep and [P3]
+ * linear_attention_decode_prepare_f32, recurrent_gated_delta_rule_batch_f32.
+ * A row whose slot is -1 gets a zero output and touches neither pool
+ * ([P1] GdnDecodeKernel, CausalConv1dUpdateKernel).
+ *
+ * Arguments:
+ *   batch                 B >= 0 rows (B = 0 is a no-op).
+ *   mixed_qkv, a_raw, b_raw, act_dtype, conv_weight, A_log, dt_bias: as gdn_prepare, with B rows.
+ *   conv_state_pool       device [num_slots, Cc, K-1] in act_dtype, in place.
+ *   ssm_state_pool        device [num_slots, Hv, Dv, Dk] in state_dtype, in place.
+ *   slot_idx_dev          device int32 [B]; -1 = inert row.
+ *   slot_idx_host         host copy for validation (range, -1 only negative, no duplicate live slot),
+ *                         or NULL to skip it; the kernel then treats any slot outside
+ *                         [0, num_slots) as inert, and duplicated live slots race.
+ *   scale                 query scale (1/sqrt(Dk) in the Qwen3-Next layer).
+ *   out                   device [B, Hv, Dv] in act_dtype.
+ */
+gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
+                      int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
+                      const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
+                      const void* conv_weight, const float* A_log, const float* dt_bias,
+                      void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
+                      int32_t num_slots, const int32_t* slot_idx_dev,
+                      const int32_t* slot_idx_host, float scale, void* out, void* stream);
+
+/*
+ * gdn_prefill_varlen -- the gated delta rule over whole sequences, computed
+ * in chunks of chunk_size tokens with the WY / UT-transform form, equal to
+ * the token-by-token recurrence of gdn_decode up to rounding order ([P1]
+ * GdnPrefillKernel; [P3] recurrent_gated_delta_rule_varlen_f32).  Sequence s
+ * starts from its slot's state (or from zero when has_initial_state[s] is
+ * 0) and its final state is written back to the same slot.
+ *
+ * Arguments:
+ *   num_seqs, total_tokens, cu_seqlens_host/_dev: as gdn_prepare.
+ *   q, k                  device [T, Hk, Dk] in qkv_dtype (GDN_F32 or GDN_BF16).
+ *   v                     device [T, Hv, Dv] in qkv_dtype.
+ *   g, beta               device f32 [T, Hv] (log decay and write strength).
+ *   ssm_state_pool        device [num_slots, Hv, Dv, Dk] in state_dtype, in place.
+ *   slot_idx_host/_dev    int32 [N] (both NULL: slot s); -1 is refused.
+ *   has_initial_state_dev device uint8 [N] or NULL (= all 1).
+ *   scale                 query scale.
+ *   use_qk_l2norm         non-zero: L2-normalise q and k here (eps 1e-6), for callers whose
+ *                         prepare step did not.
+ *   chunk_size            0 (= 64) or 64.
+ *   out                   device [T, Hv, Dv] in qkv_dtype.
+ *   workspace             device scratch of at least gdn_prefill_workspace_size() bytes,
+ *                         256-byte aligned; its contents need not be initialised.
+ */
+gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                              const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                              const void* q, const void* k, const void* v, gdn_dtype qkv_dtype,
+                              const float* g, const float* beta, void* ssm_state_pool,
+                              gdn_dtype state_dtype, int32_t num_slots,
+                              const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                              const uint8_t* has_initial_state_dev, float scale,
+                              int32_t use_qk_l2norm, int32_t chunk_size, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_prefill_varlen needs for at most num_seqs sequences and
+ * total_tokens tokens (0 if the arguments are invalid). */
+size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                  int32_t chunk_size);
+
+/* Static English name of a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

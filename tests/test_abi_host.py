@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/gdn.h declares, and refuses bad arguments with the
+right status before any device work (every call below fails its checks, so
+the fake device addresses are never touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_prepare_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+OK, INVALID, SHAPE, INDEX, DTYPE, WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 0x100000  # 16-byte aligned stand-in for a device address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gdn_prepare", "gdn_decode", "gdn_prefill_varlen", "gdn_prefill_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(gdn.EXPORTS) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(3) == b"bad slot index"
+    assert lib.gdn_version() >= 100
+
+
+def _dims(Hk=2, Hv=4, Dk=128, Dv=128, K=4):
+    return ctypes.byref(gdn._Dims(Hk, Hv, Dk, Dv, K))
+
+
+def _arr(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prepare(lib, dims=None, N=2, T=10, cu=(0, 4, 10), stride=None, act=1, qkv=1, slots=(0, 1), num_slots=4,
+             x=FAKE, l2=1, ptr_q=FAKE):
+    cu_a, cu_p = _arr(cu)
+    sl_a, sl_p = _arr(slots) if slots is not None else (None, None)
+    d = dims if dims is not None else _dims()
+    cc = 2 * 2 * 128 + 4 * 128
+    return lib.gdn_prepare(d, N, T, cu_p, FAKE, x, cc if stride is None else stride, FAKE, 4, FAKE, 4, act, FAKE,
+                           FAKE, FAKE, FAKE, num_slots, sl_p, FAKE if slots is not None else None, None, l2, ptr_q,
+                           FAKE, FAKE, qkv, FAKE, FAKE, None)
+
+
+def _err(lib):
+    return lib.gdn_last_error().decode()
+
+
+def test_prepare_rejects_bad_arguments(lib):
+    assert lib.gdn_prepare(None, 1, 1, None, None, None, 0, None, 0, None, 0, 0, None, None, None, None, 0, None,
+                           None, None, 1, None, None, None, 0, None, None, None) == INVALID
+    assert _prepare(lib, dims=_dims(Hk=0)) == SHAPE
+    assert _prepare(lib, dims=_dims(Hk=3, Hv=4)) == SHAPE and "multiple" in _err(lib)
+    assert _prepare(lib, dims=_dims(Dk=48)) == SHAPE
+    assert _prepare(lib, dims=_dims(K=5)) == SHAPE
+    assert _prepare(lib, cu=(1, 4, 10)) == SHAPE and "start at 0" in _err(lib)
+    assert _prepare(lib, cu=(0, 4, 9)) == SHAPE
+    assert _prepare(lib, cu=(0, 0, 10)) == SHAPE and "empty" in _err(lib)
+    assert _prepare(lib, cu=(0, 6, 4), T=4) == SHAPE
+    assert _prepare(lib, N=1, T=0, cu=(0, 0)) == SHAPE
+    assert _prepare(lib, act=2) == DTYPE
+    assert _prepare(lib, qkv=2) == DTYPE
+    assert _prepare(lib, stride=100) == SHAPE
+    assert _prepare(lib, x=FAKE + 4) == INVALID and "aligned" in _err(lib)
+    assert _prepare(lib, x=None) == INVALID
+    assert _prepare(lib, ptr_q=None) == INVALID
+    assert _prepare(lib, slots=(0, 0)) == INDEX and "more than one" in _err(lib)
+    assert _prepare(lib, slots=(0, 4)) == INDEX and "out of range" in _err(lib)
+    assert _prepare(lib, slots=(0, -1)) == INDEX
+    assert _prepare(lib, slots=None, num_slots=1) == INDEX
+    assert _prepare(lib, l2=2) == INVALID
+
+
+def test_prepare_empty_batch_is_a_no_op(lib):
+    assert _prepare(lib, N=0, T=0, cu=(0,)) == OK
+
+
+def _decode(lib, dims=None, B=3, slots=(2, -1, 0), num_slots=4, act=1, state=0, ssm=FAKE, validate=True,
+            scale=0.125):
+    sl_a, sl_p = _arr(slots)
+    d = dims if dims is not None else _dims()
+    cc = 2 * 2 * 128 + 4 * 128
+    return lib.gdn_decode(d, B, FAKE, cc, FAKE, 4, FAKE, 4, act, FAKE, FAKE, FAKE, FAKE, ssm, state, num_slots,
+                          FAKE, sl_p if validate else None, ctypes.c_float(scale), FAKE, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, dims=_dims(Hv=6, Hk=4)) == SHAPE
+    assert _decode(lib, slots=(2, -2, 0)) == INDEX and "only -1" in _err(lib)
+    assert _decode(lib, slots=(2, 2, 0)) == INDEX
+    assert _decode(lib, slots=(2, 4, 0)) == INDEX
+    assert _decode(lib, act=2) == DTYPE
+    assert _decode(lib, state=3) == DTYPE
+    assert _decode(lib, ssm=None) == INVALID
+    assert _decode(lib, ssm=FAKE + 8) == INVALID
+    assert _decode(lib, num_slots=0) == SHAPE
+    assert _decode(lib, B=-1) == SHAPE
+    assert _decode(lib, scale=float("nan")) == INVALID
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert _decode(lib, B=0) == OK
+
+
+def _prefill(lib, dims=None, N=2, T=10, cu=(0, 4, 10), qkv=1, state=0, slots=(1, 0), num_slots=2, chunk=64,
+             ws=None, ws_bytes=0, q=FAKE):
+    cu_a, cu_p = _arr(cu)
+    sl_a, sl_p = _arr(slots) if slots is not None else (None, None)
+    d = dims if dims is not None else _dims()
+    return lib.gdn_prefill_varlen(d, N, T, cu_p, FAKE, q, FAKE, FAKE, qkv, FAKE, FAKE, FAKE, state, num_slots,
+                                  sl_p, FAKE if slots is not None else None, None, ctypes.c_float(0.125), 0, chunk,
+                                  FAKE, ws, ws_bytes, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _prefill(lib, cu=(0, 10, 10)) == SHAPE
+    assert _prefill(lib, slots=(1, -1)) == INDEX
+    assert _prefill(lib, slots=(1, 1)) == INDEX
+    assert _prefill(lib, slots=None, num_slots=1) == INDEX
+    assert _prefill(lib, qkv=2) == DTYPE
+    assert _prefill(lib, state=5) == DTYPE
+    assert _prefill(lib, chunk=32) == INVALID
+    assert _prefill(lib, q=None) == INVALID
+    need = lib.gdn_prefill_workspace_size(_dims(), 2, 10, 64)
+    if need > 0:
+        assert _prefill(lib, ws=None) == WORKSPACE
+        assert _prefill(lib, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_prefill_empty_is_a_no_op(lib):
+    assert _prefill(lib, N=0, T=0, cu=(0,), slots=None) == OK
+
+
+def test_workspace_size_query(lib):
+    assert lib.gdn_prefill_workspace_size(_dims(), 2, 100, 32) == 0  # unsupported chunk
+    assert lib.gdn_prefill_workspace_size(_dims(Hk=3), 2, 100, 64) == 0  # invalid dims
+    a = lib.gdn_prefill_workspace_size(_dims(), 2, 100, 64)
+    b = lib.gdn_prefill_workspace_size(_dims(), 2, 1000, 0)
+    assert b >= a

@@ -1,0 +1,366 @@
+"""Parity of the HIP path (called through the C ABI) with the f64 oracle.
+
+Tolerances: f32 results allclose(atol=1e-4, rtol=1e-4); bf16 results max-abs
+2e-2; f16 results max-abs 2e-3.  Both sides read the same seeded inputs; the
+recurrence tests feed both sides the q/k/v/g/beta the oracle's prepare step
+produced (rounded to the dtype the library stores them in), so a one-ulp
+difference in a rounding decision between the two prepare steps cannot leak
+into the recurrence comparison.  Full-size workloads are checked on sampled
+key-head groups: heads are independent, so the oracle runs the slice of the
+problem that belongs to the sampled key head and its value heads.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gdn_inputs import Config, Dims, make_inputs, named_configs, prefill_long, prefill_single, prefill_varlen, \
+    decode_batch, tiny, tiny_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _runner():
+    from tests import gpu_runner
+    return gpu_runner
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_close(got, want, dtype, what):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    mx = float(err.max()) if err.size else 0.0
+    if dtype == "f32":
+        ok = np.all(err <= 1e-4 + 1e-4 * np.abs(want))
+        bad = float((err - 1e-4 * np.abs(want)).max()) if err.size else 0.0
+        assert ok, f"{what}: f32 mismatch, max abs err {mx:.3e}, worst excess {bad:.3e}"
+    else:
+        lim = 2e-2 if dtype == "bf16" else 2e-3
+        assert mx <= lim, f"{what}: {dtype} max abs err {mx:.3e} > {lim}"
+    return mx
+
+
+def slice_key_head(d: Dims, kh: int):
+    """Channel indices and value-head range of key head kh."""
+    r = d.Hv // d.Hk
+    q = np.arange(kh * d.Dk, (kh + 1) * d.Dk)
+    k = d.Hk * d.Dk + q
+    v = 2 * d.Hk * d.Dk + np.arange(kh * r * d.Dv, (kh + 1) * r * d.Dv)
+    return np.concatenate([q, k, v]), slice(kh * r, (kh + 1) * r), Dims(1, r, d.Dk, d.Dv, d.K)
+
+
+def sliced_inputs(d: Dims, inp, kh: int):
+    ch, hs, sd = slice_key_head(d, kh)
+    out = dict(inp)
+    out["x"] = inp["x"][:, ch]
+    out["w"] = inp["w"][ch]
+    out["conv_pool"] = inp["conv_pool"][:, ch]
+    out["a"] = inp["a"][:, hs]
+    out["b"] = inp["b"][:, hs]
+    out["A_log"] = inp["A_log"][hs]
+    out["dt_bias"] = inp["dt_bias"][hs]
+    out["ssm_pool"] = inp["ssm_pool"][:, hs]
+    return out, ch, hs, sd
+
+
+# ---------------------------------------------------------------------------
+# prepare
+# ---------------------------------------------------------------------------
+PREP_CASES = [
+    ("tiny_f32", tiny()),
+    ("varlen_bf16_to_bf16", Config("p1", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(1, 2, 3, 31, 32, 33, 100),
+                                   num_slots=9, act_dtype="bf16", qkv_dtype="bf16", init_state_std=0.05,
+                                   conv_state_std=1.0, seed=11)),
+    ("varlen_bf16_to_f32", Config("p2", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(5, 77, 1),
+                                  num_slots=4, act_dtype="bf16", qkv_dtype="f32", conv_state_std=1.0,
+                                  init_state_std=0.05, seed=12)),
+    ("d16_dv32_f32", Config("p3", "prefill", Dims(1, 2, 16, 32, 4), seqlens=(40, 3), num_slots=2, act_dtype="f32",
+                            qkv_dtype="f32", conv_state_std=1.0, init_state_std=0.1, seed=13)),
+    ("d64_dv16_k3_bf16", Config("p4", "prefill", Dims(2, 2, 64, 16, 3), seqlens=(2, 50), num_slots=3,
+                                act_dtype="bf16", qkv_dtype="bf16", conv_state_std=1.0, init_state_std=0.1,
+                                seed=14)),
+    ("d256_dv64_k2_bf16", Config("p5", "prefill", Dims(4, 4, 256, 64, 2), seqlens=(70,), num_slots=1,
+                                 act_dtype="bf16", qkv_dtype="bf16", seed=15)),
+    ("d32_k1_f32", Config("p6", "prefill", Dims(2, 4, 32, 32, 1), seqlens=(9, 9), num_slots=2, act_dtype="f32",
+                          qkv_dtype="f32", seed=16)),
+    ("f32_act_to_bf16", Config("p7", "prefill", Dims(2, 4, 64, 64, 4), seqlens=(33, 1, 2), num_slots=5,
+                               act_dtype="f32", qkv_dtype="bf16", conv_state_std=1.0, init_state_std=0.1,
+                               seed=17)),
+]
+
+
+def _check_prepare(d, inp, cfg, got, want, label):
+    for key in ("q", "k", "v"):
+        assert_close(got[key], want[key], cfg.qkv_dtype, f"{label} {key}")
+    assert_close(got["g"], want["g"], "f32", f"{label} g")
+    assert_close(got["beta"], want["beta"], "f32", f"{label} beta")
+    np.testing.assert_array_equal(got["conv_pool"], want["conv_pool"], err_msg=f"{label} conv history")
+
+
+@pytest.mark.parametrize("name,cfg", PREP_CASES, ids=[c[0] for c in PREP_CASES])
+@pytest.mark.parametrize("l2norm", [True, False], ids=["l2", "nol2"])
+def test_prepare_parity(name, cfg, l2norm):
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    _say(f"[prepare] {name} l2norm={l2norm} T={cfg.T} N={cfg.N}")
+    got = R.prepare(d, inp, cfg.act_dtype, cfg.qkv_dtype, l2norm)
+    want = oracle.prepare(d, inp["cu"], inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                          inp["conv_pool"], inp["slots"], inp["has_init"], l2norm, cfg.qkv_dtype)
+    _check_prepare(d, inp, cfg, got, want, name)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["prefill_single", "varlen", "long"])
+def test_prepare_full_size_sampled_heads(which):
+    cfg = {"prefill_single": prefill_single(), "varlen": prefill_varlen(), "long": prefill_long()}[which]
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    _say(f"[prepare full] {cfg.name} T={cfg.T}")
+    got = R.prepare(d, inp, cfg.act_dtype, cfg.qkv_dtype, True)
+    for kh in (0, d.Hk - 1):
+        sub, ch, hs, sd = sliced_inputs(d, inp, kh)
+        want = oracle.prepare(sd, inp["cu"], sub["x"], sub["w"], sub["a"], sub["b"], sub["A_log"],
+                              sub["dt_bias"], sub["conv_pool"], inp["slots"], inp["has_init"], True, cfg.qkv_dtype)
+        assert_close(got["q"][:, kh:kh + 1], want["q"], cfg.qkv_dtype, f"{which} q kh={kh}")
+        assert_close(got["k"][:, kh:kh + 1], want["k"], cfg.qkv_dtype, f"{which} k kh={kh}")
+        assert_close(got["v"][:, hs], want["v"], cfg.qkv_dtype, f"{which} v kh={kh}")
+        assert_close(got["g"][:, hs], want["g"], "f32", f"{which} g")
+        assert_close(got["beta"][:, hs], want["beta"], "f32", f"{which} beta")
+        np.testing.assert_array_equal(got["conv_pool"][:, ch], want["conv_pool"])
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+DEC_CASES = [
+    ("tiny_f32", tiny_decode(), "f32"),
+    ("bf16_state_f32_nulls", Config("d1", "decode", Dims(2, 4, 128, 128, 4), batch=12, num_slots=20,
+                                    act_dtype="bf16", init_state_std=0.05, conv_state_std=1.0, seed=21,
+                                    null_rows=3), "f32"),
+    ("bf16_state_bf16", Config("d2", "decode", Dims(2, 4, 128, 128, 4), batch=9, num_slots=9, act_dtype="bf16",
+                               state_dtype="bf16", init_state_std=0.05, conv_state_std=1.0, seed=22), "bf16"),
+    ("bf16_state_f16", Config("d3", "decode", Dims(2, 4, 128, 128, 4), batch=9, num_slots=30, act_dtype="bf16",
+                              state_dtype="f16", init_state_std=0.05, conv_state_std=1.0, seed=23), "f16"),
+    ("d256_dv128_r4", Config("d4", "decode", Dims(1, 4, 256, 128, 4), batch=5, num_slots=7, act_dtype="bf16",
+                             init_state_std=0.05, conv_state_std=1.0, seed=24), "f32"),
+    ("d32_dv64_k2_f32", Config("d5", "decode", Dims(2, 2, 32, 64, 2), batch=6, num_slots=6, act_dtype="f32",
+                               state_dtype="f16", init_state_std=0.05, conv_state_std=1.0, seed=25), "f16"),
+    ("d64_dv16_k1", Config("d6", "decode", Dims(4, 8, 64, 16, 1), batch=7, num_slots=8, act_dtype="bf16",
+                           state_dtype="bf16", init_state_std=0.05, seed=26, null_rows=1), "bf16"),
+    ("d16_k3_f32", Config("d7", "decode", Dims(1, 1, 16, 16, 3), batch=4, num_slots=4, act_dtype="f32",
+                          init_state_std=0.1, conv_state_std=1.0, seed=27), "f32"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,sdt", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_parity(name, cfg, sdt):
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    _say(f"[decode] {name} B={cfg.batch}")
+    out, cp, sp = R.decode(d, inp, cfg.act_dtype, sdt, cfg.scale)
+    o_ref, c_ref, s_ref = oracle.decode(d, inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                                        inp["conv_pool"], inp["ssm_pool"], inp["slots"], cfg.scale, sdt,
+                                        cfg.act_dtype)
+    assert_close(out, o_ref, cfg.act_dtype, f"{name} out")
+    assert_close(sp, s_ref, sdt, f"{name} state")
+    np.testing.assert_array_equal(cp, c_ref)
+    nulls = inp["slots"] < 0
+    assert np.all(out[nulls] == 0)
+
+
+def test_decode_two_steps_carry_state():
+    cfg = Config("d8", "decode", Dims(2, 4, 128, 128, 4), batch=6, num_slots=10, act_dtype="bf16",
+                 init_state_std=0.05, conv_state_std=1.0, seed=28)
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    inp2 = make_inputs(dataclasses.replace(cfg, seed=29))
+    _say("[decode] two steps")
+    o1, cp, sp = R.decode(d, inp, "bf16", "f32", cfg.scale)
+    o2, cp, sp = R.decode(d, {**inp2, "slots": inp["slots"]}, "bf16", "f32", cfg.scale, conv_pool=cp, ssm_pool=sp)
+    r1, c1, s1 = oracle.decode(d, inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                               inp["conv_pool"], inp["ssm_pool"], inp["slots"], cfg.scale, "f32", "bf16")
+    r2, c2, s2 = oracle.decode(d, inp2["x"], inp2["w"], inp2["a"], inp2["b"], inp2["A_log"], inp2["dt_bias"], c1, s1,
+                               inp["slots"], cfg.scale, "f32", "bf16")
+    assert_close(o2, r2, "bf16", "second step out")
+    assert_close(sp, s2, "f32", "second step state")
+    np.testing.assert_array_equal(cp, c2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_decode_full_size(sdt):
+    cfg = decode_batch(sdt)
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    _say(f"[decode full] {cfg.name} state={sdt}")
+    out, cp, sp = R.decode(d, inp, "bf16", sdt, cfg.scale)
+    o_ref, c_ref, s_ref = oracle.decode(d, inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                                        inp["conv_pool"], inp["ssm_pool"], inp["slots"], cfg.scale, sdt, "bf16")
+    assert_close(out, o_ref, "bf16", "out")
+    assert_close(sp, s_ref, sdt, "state pool")
+    np.testing.assert_array_equal(cp, c_ref)
+
+
+def test_tiny_as_eight_decode_steps_equals_prefill():
+    """The tiny workload (T=8, f32) run as 8 single-token decode calls on one
+    slot equals the oracle's 8-token prefill."""
+    cfg = tiny()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    R = _runner()
+    _say("[decode] tiny as 8 steps")
+    cp, sp = inp["conv_pool"], inp["ssm_pool"]
+    outs = []
+    for t in range(cfg.T):
+        row = dict(x=inp["x"][t:t + 1], a=inp["a"][t:t + 1], b=inp["b"][t:t + 1], w=inp["w"], A_log=inp["A_log"],
+                   dt_bias=inp["dt_bias"], slots=np.array([0], np.int32))
+        o, cp, sp = R.decode(d, row, "f32", "f32", cfg.scale, conv_pool=cp, ssm_pool=sp)
+        outs.append(o[0])
+    pre = oracle.prepare(d, inp["cu"], inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                         inp["conv_pool"], inp["slots"], inp["has_init"], True, "f32")
+    o_ref, s_ref = oracle.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"],
+                                  inp["ssm_pool"], inp["slots"], inp["has_init"], cfg.scale)
+    assert_close(np.stack(outs), o_ref, "f32", "outputs")
+    assert_close(sp, s_ref, "f32", "final state")
+    np.testing.assert_array_equal(cp, pre["conv_pool"])
+
+
+# ---------------------------------------------------------------------------
+# prefill (recurrence); inputs from the oracle's prepare
+# ---------------------------------------------------------------------------
+def _oracle_prepared(cfg, inp, l2norm=True):
+    d = cfg.dims
+    return oracle.prepare(d, inp["cu"], inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                          inp["conv_pool"], inp["slots"], inp["has_init"], l2norm, cfg.qkv_dtype)
+
+
+PF_LENS = (1, 63, 64, 65, 130, 257)
+PF_CASES = []
+for qkv in ("f32", "bf16"):
+    for sdt in ("f32", "bf16", "f16"):
+        PF_CASES.append((f"ragged_qkv{qkv}_state{sdt}",
+                         Config(f"pf_{qkv}_{sdt}", "prefill", Dims(2, 4, 128, 128, 4), seqlens=PF_LENS, num_slots=8,
+                                act_dtype="bf16", qkv_dtype=qkv, state_dtype=sdt, init_state_std=0.05,
+                                conv_state_std=1.0, seed=31)))
+PF_CASES += [
+    ("d16", Config("pf_d16", "prefill", Dims(1, 2, 16, 16, 4), seqlens=(8, 100), num_slots=2, act_dtype="f32",
+                   qkv_dtype="f32", init_state_std=0.1, seed=32)),
+    ("d64_dv32", Config("pf_d64", "prefill", Dims(2, 2, 64, 32, 4), seqlens=(70, 3, 129), num_slots=5,
+                        act_dtype="bf16", qkv_dtype="bf16", init_state_std=0.1, conv_state_std=1.0, seed=33)),
+    ("d256_dv128", Config("pf_d256", "prefill", Dims(1, 2, 256, 128, 4), seqlens=(90,), num_slots=1,
+                          act_dtype="bf16", qkv_dtype="f32", seed=34)),
+    ("d32_dv256_r4", Config("pf_d32", "prefill", Dims(1, 4, 32, 256, 4), seqlens=(65, 2), num_slots=2,
+                            act_dtype="bf16", qkv_dtype="bf16", state_dtype="bf16", init_state_std=0.1, seed=35)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", PF_CASES, ids=[c[0] for c in PF_CASES])
+def test_prefill_parity(name, cfg):
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    has = inp["has_init"].copy()
+    has[::2] = 0  # mix continuing and fresh sequences
+    pre = _oracle_prepared(cfg, {**inp, "has_init": has})
+    _say(f"[prefill] {name} T={cfg.T}")
+    out, sp = R.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
+                        inp["slots"], has, cfg.qkv_dtype, cfg.state_dtype, cfg.scale)
+    o_ref, s_ref = oracle.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
+                                  inp["slots"], has, cfg.scale, False, cfg.state_dtype, cfg.qkv_dtype)
+    assert_close(out, o_ref, cfg.qkv_dtype, f"{name} out")
+    assert_close(sp, s_ref, cfg.state_dtype, f"{name} state")
+
+
+def test_prefill_l2norm_inside():
+    cfg = Config("pf_l2", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(20, 90), num_slots=2, act_dtype="bf16",
+                 qkv_dtype="f32", init_state_std=0.05, seed=36)
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    pre = _oracle_prepared(cfg, inp, l2norm=False)
+    _say("[prefill] l2norm inside")
+    out, sp = R.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
+                        inp["slots"], inp["has_init"], "f32", "f32", cfg.scale, l2norm=True)
+    o_ref, s_ref = oracle.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
+                                  inp["slots"], inp["has_init"], cfg.scale, True, "f32", "f32")
+    assert_close(out, o_ref, "f32", "out")
+    assert_close(sp, s_ref, "f32", "state")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["prefill_single", "varlen"])
+def test_prefill_full_size_sampled_heads(which):
+    cfg = {"prefill_single": prefill_single(), "varlen": prefill_varlen()}[which]
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    pre = _oracle_prepared(cfg, inp)
+    _say(f"[prefill full] {cfg.name} T={cfg.T}")
+    out, sp = R.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
+                        inp["slots"], inp["has_init"], cfg.qkv_dtype, cfg.state_dtype, cfg.scale)
+    r = d.Hv // d.Hk
+    for kh in (0, d.Hk // 2):
+        hs = slice(kh * r, (kh + 1) * r)
+        sd = Dims(1, r, d.Dk, d.Dv, d.K)
+        o_ref, s_ref = oracle.prefill(sd, inp["cu"], pre["q"][:, kh:kh + 1], pre["k"][:, kh:kh + 1], pre["v"][:, hs],
+                                      pre["g"][:, hs], pre["beta"][:, hs], inp["ssm_pool"][:, hs], inp["slots"],
+                                      inp["has_init"], cfg.scale, False, cfg.state_dtype, cfg.qkv_dtype)
+        assert_close(out[:, hs], o_ref, cfg.qkv_dtype, f"{which} out kh={kh}")
+        assert_close(sp[:, hs], s_ref, cfg.state_dtype, f"{which} state kh={kh}")
+
+
+@pytest.mark.slow
+def test_long_prefill_one_call_equals_eight_calls():
+    """T=32768, Hv=48, f16 state: one call vs 8 chained 4096-token calls
+    (prepare + prefill each, conv history and state carried), each checked
+    against the oracle on a sampled key head."""
+    cfg = prefill_long()
+    d = cfg.dims
+    R = _runner()
+    inp = make_inputs(cfg)
+    kh = 5
+    sub, ch, hs, sd = sliced_inputs(d, inp, kh)
+    _say("[long] one call")
+    pre1 = R.prepare(d, inp, "bf16", "bf16")
+    out1, sp1 = R.prefill(d, inp["cu"], pre1["q"], pre1["k"], pre1["v"], pre1["g"], pre1["beta"], inp["ssm_pool"],
+                          inp["slots"], inp["has_init"], "bf16", "f16", cfg.scale)
+    _say("[long] eight calls")
+    cp, sp = inp["conv_pool"], inp["ssm_pool"]
+    outs = []
+    for i in range(8):
+        t0, t1 = 4096 * i, 4096 * (i + 1)
+        part = dict(inp, x=inp["x"][t0:t1], a=inp["a"][t0:t1], b=inp["b"][t0:t1], cu=np.array([0, 4096], np.int32),
+                    has_init=np.array([1 if i else 0], np.uint8))
+        pre = R.prepare(d, part, "bf16", "bf16", conv_pool=cp)
+        cp = pre["conv_pool"]
+        o, sp = R.prefill(d, part["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], sp, inp["slots"],
+                          part["has_init"], "bf16", "f16", cfg.scale)
+        outs.append(o)
+    out8 = np.concatenate(outs)
+    # one call vs eight calls: the state is rounded to f16 at 7 more call boundaries
+    assert_close(sp, sp1, "f16", "final state, 8 calls vs 1 call")
+    assert_close(out8, out1, "bf16", "outputs, 8 calls vs 1 call")
+    # both against the oracle on one key head, chaining the same way
+    ocp, osp = sub["conv_pool"], sub["ssm_pool"]
+    for i in range(8):
+        t0, t1 = 4096 * i, 4096 * (i + 1)
+        has = np.array([1 if i else 0], np.uint8)
+        pre = oracle.prepare(sd, [0, 4096], sub["x"][t0:t1], sub["w"], sub["a"][t0:t1], sub["b"][t0:t1],
+                             sub["A_log"], sub["dt_bias"], ocp, inp["slots"], has, True, "bf16")
+        ocp = pre["conv_pool"]
+        o_ref, osp = oracle.prefill(sd, [0, 4096], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], osp,
+                                    inp["slots"], has, cfg.scale, False, "f16", "bf16")
+        assert_close(outs[i][:, hs], o_ref, "bf16", f"chunk {i} out (chained prepare, bf16 q/k/v)")
+    assert_close(sp[:, hs], osp, "f16", "final state vs oracle (8 calls)")
