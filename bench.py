@@ -1,0 +1,279 @@
+"""Throughput benchmark of the GDN hot path on one MI355X.
+
+One step is one pass of the whole path over synthetic inputs of the layer's
+shapes (Hk=16, Hv=32, Dk=Dv=128, K=4):
+  * decode:  gdn_decode over 256 rows (one token each) against a 512-slot
+             f32 state pool and a bf16 conv-history pool; the slot subset is
+             re-drawn for every step so repeated steps do not hit the same
+             rows in the last-level cache;
+  * prefill: gdn_prepare + gdn_prefill_varlen over one 4096-token sequence,
+             bf16 activations and q/k/v, f32 state from zero, chunk 64.
+value = (256 + 4096) tokens / step time.  Per-kernel times come from HIP
+events recorded on the stream the kernels run on.  A bounded sample of the
+same work is also run through the f64 CPU oracle on the host cores
+(cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 64 lanes x 2 flop x 2.4 GHz, packed FP32 not used
+FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "GDN prefill tokens/s + decode tokens/s; % of HBM/MFMA roofline, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def decode_bytes(B, Hk, Hv, Dk, Dv, K, state_bytes=4, act_bytes=2):
+    """Algorithmic HBM bytes of one gdn_decode call: every operand once."""
+    Cc = 2 * Hk * Dk + Hv * Dv
+    return (2 * B * Hv * Dv * Dk * state_bytes       # state read + write
+            + 2 * B * Cc * (K - 1) * act_bytes       # conv history read + write
+            + B * Cc * act_bytes                     # raw projections
+            + 2 * B * Hv * act_bytes                 # a, b
+            + B * Hv * Dv * act_bytes                # out
+            + B * 4                                  # slot indices
+            + Cc * K * act_bytes + 2 * Hv * 4)       # conv weight, A_log, dt_bias
+
+
+def prefill_bytes(T, Hk, Hv, Dk, Dv, qkv_bytes=2, state_bytes=4, has_init=False):
+    """Algorithmic HBM bytes of one gdn_prefill_varlen call (one sequence)."""
+    return (T * (2 * Hk * Dk + Hv * Dv) * qkv_bytes  # q, k, v
+            + 2 * T * Hv * 4                         # g, beta
+            + T * Hv * Dv * qkv_bytes                # out
+            + (2 if has_init else 1) * Hv * Dv * Dk * state_bytes)
+
+
+def prefill_seq_flops(T, Hv, Dk, Dv):
+    """Flops of the token-by-token recurrence: per token and value head, the
+    decay, both dot products and the rank-1 update on Dv x Dk entries."""
+    return 7.0 * T * Hv * Dv * Dk
+
+
+def prepare_bytes(T, Hk, Hv, Dk, Dv, K, act_bytes=2, qkv_bytes=2):
+    Cc = 2 * Hk * Dk + Hv * Dv
+    return T * Cc * act_bytes + T * Cc * qkv_bytes + 2 * T * Hv * act_bytes + 2 * T * Hv * 4 + Cc * K * act_bytes
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_prepare_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha(*sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(dec, pre, threads):
+    """The f64 oracle on a bounded sample of the same workload: all 256 decode
+    rows and the first 2048 tokens of the prefill sequence (all heads)."""
+    import oracle
+    d_cfg, d_inp = dec
+    p_cfg, p_inp = pre
+    d = d_cfg.dims
+    nrow = 256
+    rows = np.arange(nrow)
+    slots = d_inp["slots"][rows]
+    conv = d_inp["conv_pool"][slots]
+    ssm = d_inp["ssm_pool"][slots]
+    t0 = time.perf_counter()
+    oracle.decode(d, d_inp["x"][rows], d_inp["w"], d_inp["a"][rows], d_inp["b"][rows], d_inp["A_log"],
+                  d_inp["dt_bias"], conv, ssm, np.arange(nrow, dtype=np.int32), d_cfg.scale, "f32", "bf16",
+                  nthreads=threads)
+    t_dec = (time.perf_counter() - t0) / nrow
+    ntok = 2048
+    cu = np.array([0, ntok], np.int32)
+    t0 = time.perf_counter()
+    prep = oracle.prepare(d, cu, p_inp["x"][:ntok], p_inp["w"], p_inp["a"][:ntok], p_inp["b"][:ntok],
+                          p_inp["A_log"], p_inp["dt_bias"], p_inp["conv_pool"], p_inp["slots"], p_inp["has_init"],
+                          True, "bf16", nthreads=threads)
+    oracle.prefill(d, cu, prep["q"], prep["k"], prep["v"], prep["g"], prep["beta"], p_inp["ssm_pool"],
+                   p_inp["slots"], p_inp["has_init"], p_cfg.scale, False, "f32", "bf16", nthreads=threads)
+    t_pre = (time.perf_counter() - t0) / ntok
+    step = d_cfg.batch * t_dec + p_cfg.T * t_pre
+    return {"value": (d_cfg.batch + p_cfg.T) / step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrow} decode rows + first {ntok} prefill tokens (all heads), f64 oracle; "
+                      f"scaled to the step's 256 decode + 4096 prefill tokens",
+            "decode_tokens_per_s": 1.0 / t_dec, "prefill_tokens_per_s": 1.0 / t_pre}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer shards "
+              "without communication by batch or by key-head group; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_launch": src.numel() * 4,
+                          "copy_probe_bytes_written_per_launch": dst.numel() * 4}), flush=True)
+        return
+
+    import gated_delta_rule_prepare_amd as gdn
+    from gdn_inputs import decode_batch, decode_slot_sets, make_inputs, prefill_single
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    bf, f32 = torch.bfloat16, torch.float32
+
+    # ---- decode inputs
+    dcfg = decode_batch("f32")
+    dinp = make_inputs(dcfg)
+    d = dcfg.dims
+    gd = gdn.Dims(d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    B = dcfg.batch
+    t = lambda a, dt=f32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    dx, dw, da, db = t(dinp["x"], bf), t(dinp["w"], bf), t(dinp["a"], bf), t(dinp["b"], bf)
+    dA, ddt = t(dinp["A_log"]), t(dinp["dt_bias"])
+    dconv = t(dinp["conv_pool"], bf)
+    dssm = t(dinp["ssm_pool"])
+    nsets = args.warmup + args.steps
+    slot_sets_h = decode_slot_sets(dcfg, nsets, seed=4242)
+    slot_sets = torch.from_numpy(slot_sets_h).to(dev)
+    dout = torch.empty(B, d.Hv, d.Dv, device=dev, dtype=bf)
+
+    # ---- prefill inputs
+    pcfg = prefill_single("bf16")
+    pinp = make_inputs(pcfg)
+    T = pcfg.T
+    px, pw, pa, pb = t(pinp["x"], bf), t(pinp["w"], bf), t(pinp["a"], bf), t(pinp["b"], bf)
+    pA, pdt = t(pinp["A_log"]), t(pinp["dt_bias"])
+    pconv = t(pinp["conv_pool"], bf)
+    pssm = t(pinp["ssm_pool"])
+    cu_h = pinp["cu"]
+    cu = torch.from_numpy(cu_h).to(dev)
+    sl_h = pinp["slots"]
+    sl = torch.from_numpy(sl_h).to(dev)
+    hi = torch.from_numpy(pinp["has_init"]).to(dev)
+    q = torch.empty(T, d.Hk, d.Dk, device=dev, dtype=bf)
+    k = torch.empty_like(q)
+    v = torch.empty(T, d.Hv, d.Dv, device=dev, dtype=bf)
+    g = torch.empty(T, d.Hv, device=dev)
+    beta = torch.empty_like(g)
+    pout = torch.empty(T, d.Hv, d.Dv, device=dev, dtype=bf)
+    ws_bytes = gdn.gdn_prefill_workspace_size(gd, 1, T, 64)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream()
+    nev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nev)]
+
+    def step(i, rec=None):
+        if rec is not None:
+            rec[0].record(stream)
+        gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i], dout, dcfg.scale,
+                       slot_idx_host=slot_sets_h[i], stream=stream)
+        if rec is not None:
+            rec[1].record(stream)
+        gdn.gdn_prepare(gd, cu, px, pa, pb, pw, pA, pdt, pconv, q, k, v, g, beta, slot_idx=sl, has_initial_state=hi,
+                        cu_seqlens_host=cu_h, slot_idx_host=sl_h, stream=stream)
+        if rec is not None:
+            rec[2].record(stream)
+        gdn.gdn_prefill_varlen(gd, cu, q, k, v, g, beta, pssm, pout, pcfg.scale, slot_idx=sl, has_initial_state=hi,
+                               workspace=ws, cu_seqlens_host=cu_h, slot_idx_host=sl_h, stream=stream)
+        if rec is not None:
+            rec[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pre_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    dec_b = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    dec_gbs = dec_b / (dec_ms * 1e-3) / 1e9
+    pre_b = prefill_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv)
+    pre_flops = prefill_seq_flops(T, d.Hv, d.Dk, d.Dv)
+    prep_b = prepare_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    kernels = {
+        "decode": {"avg_ms": dec_ms, "tokens_per_s": B / (dec_ms * 1e-3),
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_launch": dec_b,
+                                "traffic": measured_traffic("decode_kernel", ["gdn_decode.hip", "gdn_device.h"])}},
+        "prepare": {"avg_ms": prep_ms, "tokens_per_s": T / (prep_ms * 1e-3),
+                    "roofline": {"bound": "hbm", "achieved": prep_b / (prep_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": prep_b / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "bytes_per_launch": prep_b}},
+        "prefill": {"avg_ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3),
+                    "roofline": {"bound": "alu", "achieved": pre_flops / (pre_ms * 1e-3) / 1e12,
+                                 "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": pre_flops / (pre_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                                 "flops_per_launch": pre_flops, "hbm_GBps": pre_b / (pre_ms * 1e-3) / 1e9}},
+    }
+    dominant = max(("decode", "prefill"), key=lambda n: kernels[n]["avg_ms"])
+    rl = dict(kernels[dominant]["roofline"])
+    rl["kernel"] = dominant
+    rl.setdefault("traffic", None)
+    rl = {k2: rl[k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")}
+
+    line = {
+        "metric": METRIC, "value": (B + T) / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "GDN step: decode 256 rows (512-slot f32 state pool) + prefill of one 4096-token "
+                               "sequence; Hk=16 Hv=32 Dk=Dv=128 K=4; bf16 activations",
+                   "decode_rows": B, "prefill_tokens": T, "chunk": 64, "state_dtype": "f32",
+                   "activation_dtype": "bf16"},
+        "decode_tokens_per_s": kernels["decode"]["tokens_per_s"],
+        "prefill_tokens_per_s": T / ((prep_ms + pre_ms) * 1e-3),
+        "roofline": rl,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        line["cpu_baseline"] = cpu_baseline((dcfg, dinp), (pcfg, pinp), threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
