@@ -14,24 +14,37 @@
 //   S_C     = gamma_C S0 + Delta^T diag(exp(G_C - G_j)) K
 // which follows from unrolling S_i = exp(g_i) S_{i-1} + delta_i k_i^T.
 //
+// Matrix products run on the f16 16x16x32 MFMA.  An f32 operand x enters as
+// two f16 halves hi = f16(x), lo = f16(x - hi), and a product of two such
+// operands as hi*hi + hi*lo + lo*hi (f32 accumulation): about 22 significant
+// bits, where bf16 q/k/v need no split at all (every bf16 value of the
+// normalised q/k range is exact in f16).  The small inverse T uses the f32
+// 16x16x4 MFMA.  The running sums G are formed in double precision and every
+// decay factor is exp of a difference taken in double.
+//
 // Kernels (all on the caller's stream):
 //  1. chunk_table_kernel: chunk ids -> (sequence, first token); chunks never
 //     cross sequences and a sequence's last chunk may be short.
 //  2. chunk_prep_kernel, one workgroup per (chunk, value head), no state
-//     dependence: K K^T and Q K^T on MFMA, the unit-triangular inverse T in
-//     LDS (16x16 diagonal blocks by substitution, then block products), W and
-//     U on MFMA.  Writes W, U, P, gamma and exp(G_C - G_j) to the workspace.
-//     The running sums G are formed in double precision and every decay
-//     factor is exp of a difference taken in double, so long chunks of
-//     strong decay keep full f32 accuracy.
+//     dependence: K K^T and Q K^T with operands read straight from memory,
+//     T = (I + A)^-1 (16x16 diagonal blocks by substitution in registers,
+//     off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ on MFMA), then W and U
+//     against K^T / V^T staged in LDS.  Writes W and P (f16 hi/lo), U,
+//     gamma, exp(G_C - G_j) and the q/k row scales to the workspace.
 //  3. chunk_scan_kernel, one workgroup (4 waves) per (sequence, value head,
-//     block of 16 value rows): walks the sequence's chunks in order with the
-//     16 x Dk state block held in registers in the MFMA B-operand layout,
-//     and forms Delta, O and the next state on MFMA (f32 16x16x4).  Value rows
-//     of the state are independent, so row blocks never communicate.
+//     block of 16 value rows), placed so that the row blocks and value heads
+//     of one key head share an XCD's L2: walks the sequence's chunks in order with the
+//     16 x Dk state block in registers; each wave owns 16 tokens of Delta and
+//     O and a quarter of the state's column tiles, which are exchanged
+//     through LDS once per chunk.  The next chunk's operands are loaded while
+//     the current chunk computes.  Value rows of the state are independent,
+//     so row blocks never communicate.
 //
-// A token-sequential kernel (one wave per sequence, value head and 16 value
-// rows, state rows in registers) serves head dims above 128.
+// Shapes the chunked kernels do not cover (Dk != Dv, or head dims 16 or
+// 256) run a token-sequential kernel: one wave per sequence, value head and
+// 16 value rows, with the state rows in registers.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -39,33 +52,87 @@ namespace gdn {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f16(const h8& a, const h8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 to_h8(const float* x) {
+  h8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
+  return r;
+}
+// x ~= hi + lo, both f16
+__device__ __forceinline__ void split8(const float* x, h8& hi, h8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 h = (_Float16)x[i];
+    hi[i] = h;
+    lo[i] = (_Float16)(x[i] - (float)h);
+  }
+}
+__device__ __forceinline__ h8 ld_h8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
+__device__ __forceinline__ h8 zero_h8() {
+  h8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)0.0f;
+  return r;
+}
+
+// Eight consecutive input elements in their storage form (one 16-byte word
+// for bf16, two for f32).
+template <typename T>
+struct Raw8 {
+  static constexpr int kWords = (int)sizeof(T) / 2;
+  uint4 w[kWords];
+  __device__ __forceinline__ void load(const T* p) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) Elem<T>::unpack(w[i], o + i * Elem<T>::kVec);
+  }
+};
 
 constexpr int kChunk = 64;
+constexpr int KTS = kChunk + 8;  // row stride (halves) of transposed [column][token] tiles
 
 // ---------------------------------------------------------------------------
 // Workspace layout.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Per (chunk, value head) block, byte offsets (D = head dim):
+//   W hi [64][D] f16, W lo [64][D] f16, P hi [64][64] f16, P lo [64][64] f16,
+//   U [64][D] f32, gamma [64], exp(G_C - G_j) [64], k row scale [64], q row scale [64] f32
+__host__ __device__ constexpr int64_t blk_w_hi(int) { return 0; }
+__host__ __device__ constexpr int64_t blk_w_lo(int D) { return (int64_t)kChunk * D * 2; }
+__host__ __device__ constexpr int64_t blk_p_hi(int D) { return (int64_t)kChunk * D * 4; }
+__host__ __device__ constexpr int64_t blk_p_lo(int D) { return blk_p_hi(D) + kChunk * kChunk * 2; }
+__host__ __device__ constexpr int64_t blk_u(int D) { return blk_p_hi(D) + kChunk * kChunk * 4; }
+__host__ __device__ constexpr int64_t blk_vec(int D) { return blk_u(D) + (int64_t)kChunk * D * 4; }
+__host__ __device__ constexpr int64_t blk_bytes(int D) { return blk_vec(D) + 4 * kChunk * 4; }
+
 struct ChunkWs {
   int32_t* seq_chunk_off;  // [N+1] first chunk id of each sequence
   int32_t* chunk_seq;      // [NC]
   int32_t* chunk_start;    // [NC] first token (global index)
-  float* blocks;           // [NC, Hv, block_floats]
-  int64_t block_floats;    // 64*Dk (W) + 64*Dv (U) + 64*64 (P) + 64 (gamma) + 64 (exp(G_C - G_j))
+  char* blocks;            // [NC, Hv] blocks of blk_bytes(D)
 };
-
-__host__ __device__ inline int64_t block_floats(int Dk, int Dv) {
-  return (int64_t)kChunk * (Dk + Dv + kChunk) + 2 * kChunk;
-}
 
 inline int64_t max_chunks(int N, int64_t T) { return T / kChunk + N; }
 
-ChunkWs carve(void* base, int Dk, int Dv, int N, int64_t T) {
+ChunkWs carve(void* base, int N, int64_t T) {
   char* p = static_cast<char*>(base);
   ChunkWs w;
   const int64_t nc = max_chunks(N, T);
@@ -75,124 +142,226 @@ ChunkWs carve(void* base, int Dk, int Dv, int N, int64_t T) {
   p += align256((size_t)nc * 4);
   w.chunk_start = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)nc * 4);
-  w.blocks = reinterpret_cast<float*>(p);
-  w.block_floats = block_floats(Dk, Dv);
+  w.blocks = p;
   return w;
 }
 
-bool chunked_dims(int Dk, int Dv) { return Dk == Dv && Dk >= 16 && Dk <= 128; }
+bool chunked_dims(int Dk, int Dv) { return Dk == Dv && (Dk == 32 || Dk == 64 || Dk == 128); }
 
 // ---------------------------------------------------------------------------
 // 1. chunk table
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int N, ChunkWs ws) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int per = (N + 1023) / 1024;
-  const int s0 = min(N, tid * per), s1 = min(N, s0 + per);
+__global__ __launch_bounds__(64) void chunk_table_kernel(const int32_t* cu, int N, ChunkWs ws) {
+  // one wave: lane l takes sequences [l*per, (l+1)*per), an exclusive scan of
+  // their chunk counts gives each lane its first chunk id
+  const int lane = threadIdx.x;
+  const int per = (N + 63) / 64;
+  const int s0 = min(N, lane * per), s1 = min(N, s0 + per);
   int local = 0;
   for (int s = s0; s < s1; ++s) local += (cu[s + 1] - cu[s] + kChunk - 1) / kChunk;
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
   }
-  int c = part[tid] - local;
+  int c = incl - local;
   for (int s = s0; s < s1; ++s) {
     ws.seq_chunk_off[s] = c;
-    for (int t = cu[s]; t < cu[s + 1]; t += kChunk) {
+    const int a = cu[s], e = cu[s + 1];  // read once: the stores below may alias cu as far as the compiler knows
+    for (int t = a; t < e; t += kChunk) {
       ws.chunk_seq[c] = s;
       ws.chunk_start[c] = t;
       ++c;
     }
   }
-  if (tid == 1023) ws.seq_chunk_off[N] = part[1023];
+  if (lane == 63) ws.seq_chunk_off[N] = incl;
 }
 
-// Copy rows [0, n) of a [*, D] slice (row stride `gstride` elements) into LDS
-// as f32 with row stride `ls`; rows n..63 become zero.
+// Transposed staging of a [64 tokens][D] tile into LDS as [D][KTS] f16 (hi
+// and, for f32 inputs, lo).  Lane l of a wave takes tokens 2(l%32), 2(l%32)+1
+// of one 8-column segment, so each 32-lane half writes 32 consecutive words.
 template <typename T, int D>
-__device__ __forceinline__ void stage_rows(float* lds, int ls, const T* __restrict__ src, int64_t gstride, int n) {
-  constexpr int V = Elem<T>::kVec < D ? Elem<T>::kVec : D;
-  constexpr int PER_ROW = D / V;
-  for (int idx = threadIdx.x; idx < kChunk * PER_ROW; idx += blockDim.x) {
-    const int r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-    float v[V];
-    if (r < n) {
-      load_n<T, V>(src + (int64_t)r * gstride + c, v);
-    } else {
+struct TransposedTile {
+  static constexpr bool kSplit = std::is_same<T, float>::value;
+  static constexpr int kSegs = D / 8;
+  static constexpr int kPasses = (kSegs + 7) / 8;
+  Raw8<T> r0[kPasses], r1[kPasses];
+  // Loads are unconditional (rows past the chunk end re-read row n-1, and
+  // segments past D re-read segment 0) so that no load sits under a branch;
+  // store() zeroes what lies outside the tile.
+  __device__ __forceinline__ void load(const T* src, int64_t stride, int n) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = 2 * (lane & 31), seg0 = wave * 2 + (lane >> 5);
+    const int ta = min(t, n - 1), tb = min(t + 1, n - 1);
 #pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = 0.0f;
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int seg = seg0 + 8 * ps < kSegs ? seg0 + 8 * ps : 0;
+      r0[ps].load(src + (int64_t)ta * stride + seg * 8);
+      r1[ps].load(src + (int64_t)tb * stride + seg * 8);
     }
+  }
+  // row scales (l2 norm) are per token; null means 1
+  __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, const float* rowscale, int n) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = 2 * (lane & 31), seg0 = wave * 2 + (lane >> 5);
+    float s0 = rowscale ? rowscale[t] : 1.0f, s1 = rowscale ? rowscale[t + 1] : 1.0f;
+    if (t >= n) s0 = 0.0f;
+    if (t + 1 >= n) s1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < V; ++i) lds[r * ls + c + i] = v[i];
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int seg = seg0 + 8 * ps;
+      if (seg >= kSegs) continue;
+      float x0[8], x1[8];
+      r0[ps].get(x0);
+      r1[ps].get(x1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float a = x0[i] * s0, b = x1[i] * s1;
+        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+        const uint32_t wh = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+        *reinterpret_cast<uint32_t*>(hi + (seg * 8 + i) * KTS + t) = wh;
+        if constexpr (kSplit) {
+          const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
+          const uint32_t wl = (uint32_t)__builtin_bit_cast(uint16_t, la) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+          *reinterpret_cast<uint32_t*>(lo + (seg * 8 + i) * KTS + t) = wl;
+        }
+      }
+    }
   }
-}
-
-// L2-normalise `rows` rows of an LDS matrix (eps 1e-6 inside the root), one
-// wave per row at a time.
-template <int D>
-__device__ __forceinline__ void l2norm_rows(float* lds, int ls, int rows) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int r = wave; r < rows; r += nw) {
-    float ss = 0.0f;
-    for (int c = lane; c < D; c += 64) ss += lds[r * ls + c] * lds[r * ls + c];
-    ss = group_sum<64>(ss);
-    const float inv = 1.0f / sqrtf(ss + 1e-6f);
-    for (int c = lane; c < D; c += 64) lds[r * ls + c] *= inv;
-  }
-}
+};
 
 // ---------------------------------------------------------------------------
 // 2. per-chunk work
 // ---------------------------------------------------------------------------
+// Wave w owns token block I = w: it loads the K rows of blocks 0..w and the Q
+// rows of block w as MFMA fragments straight from memory, and forms the
+// transposed tiles (K_J K_w^T) and (K_J Q_w^T), so that each lane ends up with
+// four consecutive columns of a row of A and P.
+__device__ __forceinline__ void store_h4(_Float16* p, const float* v) {
+  _Float16 h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[i];
+  uint2 w;
+  w.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+  w.y = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+// f16 hi/lo of four consecutive values
+__device__ __forceinline__ void store_h4_split(_Float16* hi, _Float16* lo, const float* v) {
+  float h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (float)(_Float16)v[i];
+    l[i] = v[i] - h[i];
+  }
+  store_h4(hi, h);
+  store_h4(lo, l);
+}
+
 template <typename QkvT, int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
-  constexpr int LS = D + 4;        // LDS row stride of K / Q / V
-  constexpr int TS = kChunk + 4;   // LDS row stride of A / T
-  __shared__ float Ks[kChunk * LS];
-  __shared__ float Xs[kChunk * LS];  // Q, later V
-  __shared__ float As[kChunk * TS];
-  __shared__ float Ts[kChunk * TS];
-  __shared__ float Tmp[3 * 256];
+  constexpr bool SPLIT = std::is_same<QkvT, float>::value;
+  constexpr int NKS = D / 32;      // 32-wide k steps over the head dim
+  constexpr int NCT = D / 16;      // 16-column tiles of W (and of U)
+  constexpr int TS = kChunk + 4;   // f32 row stride of A and T
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[D * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 VTh[D * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 KTl[SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 VTl[SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) float As[kChunk * TS];
+  __shared__ __attribute__((aligned(16))) float Ts[kChunk * TS];
+  __shared__ float Ms[4 * 16 * 17];
   __shared__ double Gs[kChunk];
-  __shared__ float bs[kChunk], gs[kChunk];
+  __shared__ float bs[kChunk], bg[kChunk], kn[kChunk];
 
   const int cid = blockIdx.x, h = blockIdx.y;
-  const int r_heads = p.Hv / p.Hk, kh = h / r_heads;
+  const int kh = h / (p.Hv / p.Hk);
   const int seq = ws.chunk_seq[cid];
   const int64_t t0 = ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  float* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * ws.block_floats;
-  float* Wg = blk;
-  float* Ug = blk + kChunk * D;
-  float* Pg = blk + 2 * kChunk * D;
-  float* gam_g = Pg + kChunk * kChunk;
+  char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D);
+  _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
+  _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
+  _Float16* Ph = reinterpret_cast<_Float16*>(blk + blk_p_hi(D));
+  _Float16* Pl = reinterpret_cast<_Float16*>(blk + blk_p_lo(D));
+  float* Ug = reinterpret_cast<float*>(blk + blk_u(D));
+  float* gam_g = reinterpret_cast<float*>(blk + blk_vec(D));
   float* dc_g = gam_g + kChunk;
+  float* kn_g = dc_g + kChunk;
+  float* qn_g = kn_g + kChunk;
 
+  const int64_t qk_stride = (int64_t)p.Hk * D, v_stride = (int64_t)p.Hv * D;
   const QkvT* kp = static_cast<const QkvT*>(p.k) + (t0 * p.Hk + kh) * D;
   const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
-  stage_rows<QkvT, D>(Ks, LS, kp, (int64_t)p.Hk * D, n);
-  stage_rows<QkvT, D>(Xs, LS, qp, (int64_t)p.Hk * D, n);
-  for (int i = tid; i < kChunk * TS; i += 256) As[i] = 0.0f;
-  float gval = 0.0f;
-  if (tid < kChunk) {
-    // a decay factor exp(g) below e^-200 is exactly zero in f32; the clamp
-    // keeps the running sums finite when g = -inf
-    gval = tid < n ? fmaxf(p.g[(t0 + tid) * p.Hv + h], -200.0f) : 0.0f;
-    bs[tid] = tid < n ? p.beta[(t0 + tid) * p.Hv + h] : 0.0f;
+  const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
+
+  // all loads first: K^T / V^T tiles, this wave's K and Q row fragments, the gates
+  TransposedTile<QkvT, D> ktile, vtile;
+  ktile.load(kp, qk_stride, n);
+  vtile.load(vp, v_stride, n);
+  Raw8<QkvT> kf[4][NKS], qf[NKS];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    if (J > wave) break;
+    const int rr = min(16 * J + li, n - 1);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
   }
-  __syncthreads();
-  if (p.l2norm) {
-    l2norm_rows<D>(Ks, LS, kChunk);
-    l2norm_rows<D>(Xs, LS, kChunk);
+  {
+    const int rr = min(16 * wave + li, n - 1);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
+  }
+  const int gt = min(lane, n - 1);
+  // a decay factor exp(g) below e^-200 is exactly zero in f32; the clamp
+  // keeps the running sums finite when g = -inf
+  const float graw = fmaxf(p.g[(t0 + gt) * p.Hv + h], -200.0f);
+  const float braw = p.beta[(t0 + gt) * p.Hv + h];
+
+  // row scales of this wave's block: 1/sqrt(|row|^2 + 1e-6) with the L2 norm, else 1; zero past the end
+  const int row = 16 * wave + li;
+  float ksc, qsc;
+  {
+    float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      float xq[8];
+      qf[s].get(xq);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq += xq[i] * xq[i];
+    }
+    // K rows of this block are kf[wave]
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J != wave) continue;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        float xk[8];
+        kf[J][s].get(xk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sk += xk[i] * xk[i];
+      }
+    }
+    sk += __shfl_xor(sk, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    const bool valid = row < n;
+    ksc = valid ? (p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
+    qsc = valid ? (p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.0f;
+    if (lg == 0) {
+      kn[row] = ksc;
+      kn_g[row] = ksc;
+      qn_g[row] = qsc;
+    }
   }
   if (wave == 0) {
-    double G = (double)gval;
+    const bool valid = lane < n;
+    double G = valid ? (double)graw : 0.0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(G, off, 64);
@@ -201,95 +370,173 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     Gs[lane] = G;
     const double Glast = __shfl(G, 63, 64);
     const float gam = expf((float)G);
-    gs[lane] = gam;
+    const float bt = valid ? braw : 0.0f;
+    bs[lane] = bt;
+    bg[lane] = bt * gam;
     gam_g[lane] = gam;
     dc_g[lane] = expf((float)(Glast - G));
   }
   __syncthreads();
+  ktile.store(KTh, KTl, kn, n);
+  vtile.store(VTh, VTl, nullptr, n);
 
-  // K K^T (masked into A) and Q K^T (masked into P): lower-triangular 16x16 tiles
-  for (int idx = wave; idx < 20; idx += 4) {
-    const bool qk = idx >= 10;
-    const int t = qk ? idx - 10 : idx;
-    const int I = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    const int J = t - I * (I + 1) / 2;
-    const float* Arow = (qk ? Xs : Ks) + (16 * I + li) * LS + lg;
-    const float* Brow = Ks + (16 * J + li) * LS + lg;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // (K_J K_w^T) and (K_J Q_w^T): lane holds row i = 16w + li, columns j = 16J + 4lg + r
+  {
+    const int i = row;
+    const double Gi = Gs[i];
+    const float bi = bs[i];
 #pragma unroll
-    for (int s = 0; s < D / 4; ++s) acc = mfma16x16x4(Arow[4 * s], Brow[4 * s], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * lg + r, j = 16 * J + li;
-      const float dec = j <= i ? expf((float)(Gs[i] - Gs[j])) : 0.0f;
-      if (!qk) {
-        As[i * TS + j] = j < i ? bs[i] * dec * acc[r] : 0.0f;
-      } else {
-        Pg[i * kChunk + j] = j <= i ? p.scale * dec * acc[r] : 0.0f;
+    for (int J = 0; J < 4; ++J) {
+      if (J > wave) {
+        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, z);
+        continue;
       }
+      const float sj = kn[16 * J + li];  // scale of the K row this lane feeds as operand A
+      f32x4 akk = {0.0f, 0.0f, 0.0f, 0.0f}, aqk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        float a[8], bk[8], bq[8];
+        kf[J][s].get(a);
+#pragma unroll
+        for (int J2 = 0; J2 < 4; ++J2)
+          if (J2 == wave) kf[J2][s].get(bk);
+        qf[s].get(bq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] *= sj;
+          bk[e] *= ksc;
+          bq[e] *= qsc;
+        }
+        if constexpr (SPLIT) {
+          h8 ah, al, kh8, kl8, qh8, ql8;
+          split8(a, ah, al);
+          split8(bk, kh8, kl8);
+          split8(bq, qh8, ql8);
+          akk = mfma_f16(ah, kh8, akk);
+          akk = mfma_f16(ah, kl8, akk);
+          akk = mfma_f16(al, kh8, akk);
+          aqk = mfma_f16(ah, qh8, aqk);
+          aqk = mfma_f16(ah, ql8, aqk);
+          aqk = mfma_f16(al, qh8, aqk);
+        } else {
+          const h8 ah = to_h8(a);
+          akk = mfma_f16(ah, to_h8(bk), akk);
+          aqk = mfma_f16(ah, to_h8(bq), aqk);
+        }
+      }
+      float av[4], pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * lg + r;
+        const float dec = j <= i ? expf((float)(Gi - Gs[j])) : 0.0f;
+        av[r] = j < i ? bi * dec * akk[r] : 0.0f;
+        pv[r] = j <= i ? p.scale * dec * aqk[r] : 0.0f;
+      }
+      *reinterpret_cast<float4*>(As + i * TS + 16 * J + 4 * lg) = make_float4(av[0], av[1], av[2], av[3]);
+      store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, pv);
     }
   }
   __syncthreads();
-  // Q is no longer needed: bring in this value head's V
-  const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
-  stage_rows<QkvT, D>(Xs, LS, vp, (int64_t)p.Hv * D, n);
 
-  // T = (I + A)^-1, diagonal 16x16 blocks by forward substitution (column per lane)
-  if (wave == 0) {
-    const int B = lg, j = li;
+  // T = (I + A)^-1.  Diagonal block w by wave w: lane li solves column li.
+  {
+    const int B0 = 16 * wave, j = li;
     float tc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        const float4 v = *reinterpret_cast<const float4*>(As + (B0 + i) * TS + B0 + 4 * m4);
+        arow[4 * m4] = v.x; arow[4 * m4 + 1] = v.y; arow[4 * m4 + 2] = v.z; arow[4 * m4 + 3] = v.w;
+      }
       float acc = 0.0f;
 #pragma unroll
-      for (int m = 0; m < i; ++m)
-        if (m >= j) acc += As[(16 * B + i) * TS + 16 * B + m] * tc[m];
+      for (int m = 0; m < i; ++m) acc += arow[m] * tc[m];  // tc[m] = 0 for m < j
       tc[i] = i < j ? 0.0f : (i == j ? 1.0f : -acc);
     }
+    if (lg == 0)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Ts[(16 * B + i) * TS + 16 * B + j] = tc[i];
+      for (int i = 0; i < 16; ++i) Ts[(B0 + i) * TS + B0 + j] = tc[i];
   }
   __syncthreads();
-  // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, by distance I-J
+  // off-diagonal blocks, by distance: wave I computes T_{I, I-dist}
   for (int dist = 1; dist < 4; ++dist) {
-    const int npairs = 4 - dist;
-    for (int e = tid; e < npairs * 256; e += 256) {
-      const int J = e >> 8, I = J + dist, a = (e >> 4) & 15, b = e & 15;
-      float acc = 0.0f;
+    const int I = wave, J = wave - dist;
+    if (J >= 0) {
+      f32x4 M = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int K = J; K < I; ++K)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc += As[(16 * I + a) * TS + 16 * K + c] * Ts[(16 * K + c) * TS + 16 * J + b];
-      Tmp[e] = acc;
+        for (int s = 0; s < 4; ++s)
+          M = mfma_f32(As[(16 * I + li) * TS + 16 * K + 4 * s + lg], Ts[(16 * K + 4 * s + lg) * TS + 16 * J + li], M);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ms[wave * 272 + (4 * lg + r) * 17 + li] = M[r];
     }
     __syncthreads();
-    for (int e = tid; e < npairs * 256; e += 256) {
-      const int J = e >> 8, I = J + dist, a = (e >> 4) & 15, b = e & 15;
-      float acc = 0.0f;
+    if (J >= 0) {
+      f32x4 X = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 16; ++c) acc += Ts[(16 * I + a) * TS + 16 * I + c] * Tmp[(J << 8) + c * 16 + b];
-      Ts[(16 * I + a) * TS + 16 * J + b] = -acc;
+      for (int s = 0; s < 4; ++s)
+        X = mfma_f32(Ts[(16 * I + li) * TS + 16 * I + 4 * s + lg], Ms[wave * 272 + (4 * s + lg) * 17 + li], X);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * lg + r) * TS + 16 * J + li] = -X[r];
     }
     __syncthreads();
   }
 
-  // W = T diag(beta gamma) K and U = T diag(beta) V; column tiles spread over waves
-  for (int ct = wave; ct < 2 * (D / 16); ct += 4) {
-    const bool isK = ct < D / 16;
-    const int col0 = 16 * (isK ? ct : ct - D / 16);
-    const float* X = isK ? Ks : Xs;
-    float* out = isK ? Wg : Ug;
+  // W^T = K^T (T diag(beta gamma))^T and U^T = V^T (T diag(beta))^T, so each lane
+  // gets four consecutive columns of a row of W / U.  Column tiles over the waves.
+  constexpr int NT = (2 * NCT + 3) / 4;  // tiles per wave
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int J = 0; J <= I; ++J)
+  for (int I = 0; I < 4; ++I) {
+    const int i = 16 * I + li;
+    f32x4 acc[NT];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int k = 16 * J + 4 * s + lg;
-          const float sc = isK ? bs[k] * gs[k] : bs[k];
-          acc = mfma16x16x4(Ts[(16 * I + li) * TS + k], sc * X[k * LS + col0 + li], acc);
-        }
+    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(16 * I + 4 * lg + r) * D + col0 + li] = acc[r];
+    for (int s = 0; s <= I / 2; ++s) {
+      float tw[8], tu[8];
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const float4 v = *reinterpret_cast<const float4*>(Ts + i * TS + 32 * s + 8 * lg + 4 * e4);
+        tu[4 * e4] = v.x; tu[4 * e4 + 1] = v.y; tu[4 * e4 + 2] = v.z; tu[4 * e4 + 3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tk = 32 * s + 8 * lg + e;
+        const float tv = tk <= i ? tu[e] : 0.0f;
+        tw[e] = tv * bg[tk];
+        tu[e] = tv * bs[tk];
+      }
+      h8 twh, twl, tuh, tul;
+      split8(tw, twh, twl);
+      split8(tu, tuh, tul);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const int ct = wave + 4 * m;
+        if (ct >= 2 * NCT) break;
+        const bool isW = ct < NCT;
+        const int col0 = 16 * (isW ? ct : ct - NCT);
+        const h8 xh = ld_h8((isW ? KTh : VTh) + (col0 + li) * KTS + 32 * s + 8 * lg);
+        acc[m] = mfma_f16(xh, isW ? twh : tuh, acc[m]);
+        acc[m] = mfma_f16(xh, isW ? twl : tul, acc[m]);
+        if constexpr (SPLIT)
+          acc[m] = mfma_f16(ld_h8((isW ? KTl : VTl) + (col0 + li) * KTS + 32 * s + 8 * lg), isW ? twh : tuh, acc[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int ct = wave + 4 * m;
+      if (ct >= 2 * NCT) break;
+      const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+      if (ct < NCT) {
+        const int col = 16 * ct + 4 * lg;
+        store_h4_split(Wh + i * D + col, Wl + i * D + col, v);
+      } else {
+        const int col = 16 * (ct - NCT) + 4 * lg;
+        *reinterpret_cast<float4*>(Ug + i * D + col) = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
   }
 }
@@ -297,135 +544,257 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
 // ---------------------------------------------------------------------------
 // 3. sequential pass over chunks
 // ---------------------------------------------------------------------------
-// State fragment: lane (li = lane%16, lg = lane/16) holds S[e0 + li][col(lg, j)]
-// for j < D/4 with col(lg, j) = 16*(j/4) + 4*lg + j%4, which is at once the
-// B operand of the W S0^T and Q S0^T products (k index = col) and the output
-// layout of the S^T update tiles.
-__device__ __forceinline__ int frag_col(int lg, int j) { return 16 * (j >> 2) + 4 * lg + (j & 3); }
-
+// Register fragments: lane (li = lane%16, lg = lane/16) holds, for each
+// 32-wide k step s, the 8 columns 32s + 8lg .. 32s + 8lg + 7 of row li of an
+// operand (rows of W, Q, P; the state row e0 + li).
 template <typename QkvT, typename StT, int D>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillParams p, ChunkWs ws) {
-  constexpr int NJ = D / 4;
-  constexpr int LS = D + 4;
-  constexpr int NCT = D / 16;  // 16-column tiles of the state
-  __shared__ float Ks[kChunk * LS];
-  __shared__ float Qs[kChunk * LS];
-  __shared__ float Ds[kChunk * 17];
-  __shared__ float Ss[16 * LS];
-  __shared__ float gam_s[kChunk], dc_s[kChunk];
+  constexpr bool SPLIT = std::is_same<QkvT, float>::value;
+  constexpr int NKS = D / 32;
+  constexpr int NCT = D / 16;
+  constexpr int SS = D + 4;  // f32 row stride of the state exchange
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[D * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 KTl[SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 DTh[16 * KTS];  // Delta^T [e][token]
+  __shared__ __attribute__((aligned(16))) _Float16 DTl[16 * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 ETh[16 * KTS];  // (exp(G_C - G_j) Delta)^T
+  __shared__ __attribute__((aligned(16))) _Float16 ETl[16 * KTS];
+  __shared__ __attribute__((aligned(16))) float Ss[2][16 * SS];
+  // per-chunk vectors, double-buffered by chunk parity: gamma, exp(G_C - G_j), k and q row scales
+  __shared__ float gam_s[2][kChunk], dc_s[2][kChunk], kn_s[2][kChunk], qn_s[2][kChunk];
 
-  const int e0 = 16 * blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int r_heads = p.Hv / p.Hk, kh = h / r_heads;
+  // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
+  // row blocks of one head, and the value heads of one key head, run on the
+  // same XCD and share its L2 (they read the same W, P, K and Q blocks).
+  const int nwg = (D / 16) * p.Hv * p.N;
+  const int per_xcd = (int)gridDim.x / 8;
+  const int logical = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  if (logical >= nwg) return;
+  const int e0 = 16 * (logical % (D / 16));
+  const int h = (logical / (D / 16)) % p.Hv;
+  const int s_idx = logical / ((D / 16) * p.Hv);
+  const int kh = h / (p.Hv / p.Hk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  const int slot = p.slots ? p.slots[s] : s;
-  const bool has = p.has_init == nullptr || p.has_init[s] != 0;
-  const int64_t seq_end = p.cu[s + 1];
+  const int slot = p.slots ? p.slots[s_idx] : s_idx;
+  const bool has = p.has_init == nullptr || p.has_init[s_idx] != 0;
+  const int64_t seq_end = p.cu[s_idx + 1];
+  const int64_t qk_stride = (int64_t)p.Hk * D;
   StT* Sg = static_cast<StT*>(p.ssm_pool) + (((int64_t)slot * p.Hv + h) * D + e0 + li) * D;
-
-  float Sf[NJ];
-#pragma unroll
-  for (int q = 0; q < NCT; ++q) {
-    float v[4];
-    if (has) {
-      load_n<StT, 4>(Sg + 16 * q + 4 * lg, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Sf[4 * q + i] = v[i];
-  }
-
   const QkvT* kbase = static_cast<const QkvT*>(p.k) + (int64_t)kh * D;
   const QkvT* qbase = static_cast<const QkvT*>(p.q) + (int64_t)kh * D;
   QkvT* obase = static_cast<QkvT*>(p.out) + (int64_t)h * D + e0 + li;
-  const int c_begin = ws.seq_chunk_off[s], c_end = ws.seq_chunk_off[s + 1];
-  for (int cid = c_begin; cid < c_end; ++cid) {
-    const int64_t t0 = ws.chunk_start[cid];
-    const int n = (int)min((int64_t)kChunk, seq_end - t0);
-    const float* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * ws.block_floats;
-    const float* Wg = blk;
-    const float* Ug = blk + kChunk * D;
-    const float* Pg = blk + 2 * kChunk * D;
-    const float* gam_g = Pg + kChunk * kChunk;
-    const float* dc_g = gam_g + kChunk;
+  const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
 
-    stage_rows<QkvT, D>(Ks, LS, kbase + t0 * p.Hk * D, (int64_t)p.Hk * D, n);
-    stage_rows<QkvT, D>(Qs, LS, qbase + t0 * p.Hk * D, (int64_t)p.Hk * D, n);
-    if (tid < kChunk) {
-      gam_s[tid] = gam_g[tid];
-      dc_s[tid] = dc_g[tid];
+  // state fragment
+  float Sf[8 * NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    if (has) {
+      load_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf + 8 * s);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Sf[8 * s + i] = 0.0f;
     }
-    // this wave's operands from the workspace
+  }
+  if (wave == 0)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Ss[0][li * SS + 32 * s + 8 * lg + i] = Sf[8 * s + i];
+  int cur = 0;
+
+  // operands of the chunk about to be computed; every load below is
+  // unconditional (the last chunk prefetches itself again) so that no load
+  // sits under a branch
+  TransposedTile<QkvT, D> ktile;
+  h8 Wfh[NKS], Wfl[NKS], Pfh[2], Pfl[2];
+  Raw8<QkvT> Qr[NKS];
+  float Uv[4], gd0, gd1, gd2, gd3;
+  const int64_t seq_start = p.cu[s_idx];
+  auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D); };
+  auto tok0 = [&](int cid) { return seq_start + (int64_t)kChunk * (cid - c_begin); };
+  auto ntok = [&](int cid) { return (int)min((int64_t)kChunk, seq_end - tok0(cid)); };
+  auto load_k = [&](int cid) {
+    ktile.load(kbase + tok0(cid) * qk_stride, qk_stride, ntok(cid));
+    const float* v = reinterpret_cast<const float*>(blk_of(cid) + blk_vec(D));
+    gd0 = v[lane];
+    gd1 = v[kChunk + lane];
+    gd2 = v[2 * kChunk + lane];
+    gd3 = v[3 * kChunk + lane];
+  };
+  auto put_vectors = [&](int b) {  // after load_k's values have arrived
+    if (wave == 0) {
+      gam_s[b][lane] = gd0;
+      dc_s[b][lane] = gd1;
+      kn_s[b][lane] = gd2;
+      qn_s[b][lane] = gd3;
+    }
+  };
+  auto load_wu = [&](int cid) {
+    const char* b = blk_of(cid);
     const int row = 16 * wave + li;
-    float Wf[NJ];
 #pragma unroll
-    for (int q = 0; q < NCT; ++q) {
-      const float4 w4 = *reinterpret_cast<const float4*>(Wg + row * D + 16 * q + 4 * lg);
-      Wf[4 * q] = w4.x; Wf[4 * q + 1] = w4.y; Wf[4 * q + 2] = w4.z; Wf[4 * q + 3] = w4.w;
+    for (int s = 0; s < NKS; ++s) {
+      Wfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_hi(D)) + row * D + 32 * s + 8 * lg);
+      Wfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_lo(D)) + row * D + 32 * s + 8 * lg);
     }
-    float Uv[4];
+    const float* ug = reinterpret_cast<const float*>(b + blk_u(D));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Uv[r] = Ug[(16 * wave + 4 * lg + r) * D + e0 + li];
+    for (int r = 0; r < 4; ++r) Uv[r] = ug[(16 * wave + 4 * lg + r) * D + e0 + li];
+  };
+  auto load_q = [&](int cid) {
+    const int rr = min(16 * wave + li, ntok(cid) - 1);  // rows past the end re-read the last row; their scale is 0
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) Qr[s].load(qbase + (tok0(cid) + rr) * qk_stride + 32 * s + 8 * lg);
+  };
+  auto load_p = [&](int cid) {
+    const char* b = blk_of(cid);
+    const int row = 16 * wave + li;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + row * kChunk + 32 * s + 8 * lg);
+      Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + row * kChunk + 32 * s + 8 * lg);
+    }
+  };
+  load_k(c_begin);
+  load_wu(c_begin);
+  load_q(c_begin);
+  load_p(c_begin);
+  put_vectors(0);
+  __syncthreads();
+
+  for (int cid = c_begin; cid < c_end; ++cid) {
+    const int64_t t0 = tok0(cid);
+    const int n = ntok(cid);
+    const int b = (cid - c_begin) & 1;
+    const int cn = min(cid + 1, c_end - 1);
+    // this chunk's K^T to LDS, then start loading the next chunk's K and vectors
+    ktile.store(KTh, KTl, p.l2norm ? kn_s[b] : nullptr, n);
+    load_k(cn);
     __syncthreads();
-    if (p.l2norm) {
-      l2norm_rows<D>(Ks, LS, kChunk);
-      l2norm_rows<D>(Qs, LS, kChunk);
-      __syncthreads();
-    }
+
+    // split the state for the products
+    h8 Sh[NKS], Sl[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) split8(Sf + 8 * s, Sh[s], Sl[s]);
 
     // Delta rows of this wave's 16 tokens: U - W S0^T
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc = mfma16x16x4(Wf[j], Sf[j], acc);
+    for (int s = 0; s < NKS; ++s) {
+      acc = mfma_f16(Wfh[s], Sh[s], acc);
+      acc = mfma_f16(Wfh[s], Sl[s], acc);
+      acc = mfma_f16(Wfl[s], Sh[s], acc);
+    }
+    float dl[4], el[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ds[(16 * wave + 4 * lg + r) * 17 + li] = Uv[r] - acc[r];
-    // scale gamma_i Q S0^T
+    for (int r = 0; r < 4; ++r) {
+      dl[r] = Uv[r] - acc[r];
+      el[r] = dl[r] * dc_s[b][16 * wave + 4 * lg + r];
+    }
+    load_wu(cn);
+    {
+      // Delta^T and (exp(G_C - G_j) Delta)^T, 4 consecutive tokens per lane
+      uint32_t w[4][2];
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const _Float16 a0 = (_Float16)dl[2 * r2], a1 = (_Float16)dl[2 * r2 + 1];
+        const _Float16 b0 = (_Float16)(dl[2 * r2] - (float)a0), b1 = (_Float16)(dl[2 * r2 + 1] - (float)a1);
+        const _Float16 c0 = (_Float16)el[2 * r2], c1 = (_Float16)el[2 * r2 + 1];
+        const _Float16 d0 = (_Float16)(el[2 * r2] - (float)c0), d1 = (_Float16)(el[2 * r2 + 1] - (float)c1);
+        w[0][r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        w[1][r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        w[2][r2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+        w[3][r2] = (uint32_t)__builtin_bit_cast(uint16_t, d0) | ((uint32_t)__builtin_bit_cast(uint16_t, d1) << 16);
+      }
+      const int off = li * KTS + 16 * wave + 4 * lg;
+      *reinterpret_cast<uint2*>(DTh + off) = make_uint2(w[0][0], w[0][1]);
+      *reinterpret_cast<uint2*>(DTl + off) = make_uint2(w[1][0], w[1][1]);
+      *reinterpret_cast<uint2*>(ETh + off) = make_uint2(w[2][0], w[2][1]);
+      *reinterpret_cast<uint2*>(ETl + off) = make_uint2(w[3][0], w[3][1]);
+    }
+
+    // scale gamma_i (Q S0^T), with Q's row scale (L2 norm) folded in
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* qrow = Qs + row * LS;
+    const float qs = qn_s[b][16 * wave + li];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) o = mfma16x16x4(qrow[frag_col(lg, j)], Sf[j], o);
+    for (int s = 0; s < NKS; ++s) {
+      float qx[8];
+      Qr[s].get(qx);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= p.scale * gam_s[16 * wave + 4 * lg + r];
+      for (int i = 0; i < 8; ++i) qx[i] *= qs;
+      if constexpr (SPLIT) {
+        h8 qh, ql;
+        split8(qx, qh, ql);
+        o = mfma_f16(qh, Sh[s], o);
+        o = mfma_f16(qh, Sl[s], o);
+        o = mfma_f16(ql, Sh[s], o);
+      } else {
+        const h8 qh = to_h8(qx);
+        o = mfma_f16(qh, Sh[s], o);
+        o = mfma_f16(qh, Sl[s], o);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] *= p.scale * gam_s[b][16 * wave + 4 * lg + r];
+    load_q(cn);
     __syncthreads();
 
     // + P Delta over the token blocks up to this one
-    for (int J = 0; J <= wave; ++J) {
-      const float4 p4 = *reinterpret_cast<const float4*>(Pg + row * kChunk + 16 * J + 4 * lg);
-      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) o = mfma16x16x4(pv[s2], Ds[(16 * J + 4 * lg + s2) * 17 + li], o);
+    for (int s = 0; s < 2; ++s) {
+      if (s > (wave >> 1)) break;
+      const h8 dh = ld_h8(DTh + li * KTS + 32 * s + 8 * lg);
+      const h8 dlo = ld_h8(DTl + li * KTS + 32 * s + 8 * lg);
+      o = mfma_f16(Pfh[s], dh, o);
+      o = mfma_f16(Pfh[s], dlo, o);
+      o = mfma_f16(Pfl[s], dh, o);
     }
+    load_p(cn);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * wave + 4 * lg + r;
       if (i < n) Elem<QkvT>::store(obase + (t0 + i) * (int64_t)p.Hv * D, o[r]);
     }
 
-    // S^T tiles owned by this wave: S_new = gamma_C S0 + Delta^T diag(exp(G_C - G_j)) K
-    const float gC = gam_s[kChunk - 1];
+    // state column tiles owned by this wave: S' = gamma_C S0 + (exp(G_C - G_j) Delta)^T K
+    const float gC = gam_s[b][kChunk - 1];
+    const int nxt = cur ^ 1;
     for (int ct = wave; ct < NCT; ct += 4) {
       f32x4 a2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s2 = 0; s2 < kChunk / 4; ++s2) {
-        const int k = 4 * s2 + lg;
-        a2 = mfma16x16x4(dc_s[k] * Ks[k * LS + 16 * ct + li], Ds[k * 17 + li], a2);
+      for (int s = 0; s < 2; ++s) {
+        const h8 eh = ld_h8(ETh + li * KTS + 32 * s + 8 * lg);
+        const h8 elo = ld_h8(ETl + li * KTS + 32 * s + 8 * lg);
+        const h8 kk = ld_h8(KTh + (16 * ct + li) * KTS + 32 * s + 8 * lg);
+        a2 = mfma_f16(eh, kk, a2);
+        a2 = mfma_f16(elo, kk, a2);
+        if constexpr (SPLIT) a2 = mfma_f16(eh, ld_h8(KTl + (16 * ct + li) * KTS + 32 * s + 8 * lg), a2);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[li * LS + 16 * ct + 4 * lg + r] = gC * Sf[4 * ct + r] + a2[r];
+      for (int r = 0; r < 4; ++r) {
+        const int idx = (4 * lg + r) * SS + 16 * ct + li;
+        Ss[nxt][idx] = gC * Ss[cur][idx] + a2[r];
+      }
     }
+    put_vectors(b ^ 1);
     __syncthreads();
+    cur = nxt;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) Sf[j] = Ss[li * LS + frag_col(lg, j)];
-  }
-  if (wave == 0) {
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-    for (int q = 0; q < NCT; ++q) store_n<StT, 4>(Sg + 16 * q + 4 * lg, Sf + 4 * q);
+      for (int i4 = 0; i4 < 2; ++i4) {
+        const float4 v = *reinterpret_cast<const float4*>(&Ss[cur][li * SS + 32 * s + 8 * lg + 4 * i4]);
+        Sf[8 * s + 4 * i4] = v.x; Sf[8 * s + 4 * i4 + 1] = v.y; Sf[8 * s + 4 * i4 + 2] = v.z; Sf[8 * s + 4 * i4 + 3] = v.w;
+      }
   }
+  if (wave == 0)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) store_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf + 8 * s);
 }
 
 // ---------------------------------------------------------------------------
-// Token-sequential kernel (head dims above 128).
+// Token-sequential kernel (shapes the chunked kernels do not cover).
 // ---------------------------------------------------------------------------
 constexpr int kSeqRows = 16;  // value rows per wave
 
@@ -538,17 +907,17 @@ hipError_t launch_seq(const PrefillParams& p, hipStream_t stream) {
 template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
   chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
-  chunk_scan_kernel<QkvT, StT, D><<<dim3(D / 16, p.Hv, p.N), 256, 0, stream>>>(p, ws);
+  const int nwg = (D / 16) * p.Hv * p.N;
+  chunk_scan_kernel<QkvT, StT, D><<<(unsigned)((nwg + 7) / 8 * 8), 256, 0, stream>>>(p, ws);
   return hipGetLastError();
 }
 
 template <typename QkvT, typename StT>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
   if (!chunked_dims(p.Dk, p.Dv)) return launch_seq<QkvT, StT>(p, stream);
-  const ChunkWs ws = carve(p.workspace, p.Dk, p.Dv, p.N, p.T);
-  chunk_table_kernel<<<1, 1024, 0, stream>>>(p.cu, p.N, ws);
+  const ChunkWs ws = carve(p.workspace, p.N, p.T);
+  chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
   switch (p.Dk) {
-    case 16: return launch_chunked_d<QkvT, StT, 16>(p, ws, stream);
     case 32: return launch_chunked_d<QkvT, StT, 32>(p, ws, stream);
     case 64: return launch_chunked_d<QkvT, StT, 64>(p, ws, stream);
     default: return launch_chunked_d<QkvT, StT, 128>(p, ws, stream);
@@ -571,8 +940,7 @@ size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T,
   (void)chunk;
   if (N <= 0 || T <= 0 || !chunked_dims(Dk, Dv)) return 0;
   const int64_t nc = max_chunks(N, T);
-  return align256((size_t)(N + 1) * 4) + 2 * align256((size_t)nc * 4) +
-         (size_t)nc * Hv * block_floats(Dk, Dv) * sizeof(float);
+  return align256((size_t)(N + 1) * 4) + 2 * align256((size_t)nc * 4) + (size_t)nc * Hv * blk_bytes(Dk);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
