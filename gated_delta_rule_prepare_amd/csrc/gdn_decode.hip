@@ -26,9 +26,20 @@
 namespace gdn {
 namespace {
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// The state is read and written once per call.  Ordinary loads and
+// nontemporal stores measured fastest for this slot-scattered stream on
+// MI355X (nontemporal loads gained nothing here).
+__device__ __forceinline__ uint4 load_stream(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store_stream(void* p, const uint4& u) {
+  const v4u v = {u.x, u.y, u.z, u.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
+}
+
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kLoads = 8;  // 16-byte state loads in flight per lane
+constexpr int kLoads = 4;  // 16-byte state loads per lane per batch (two batches in flight)
 
 template <typename ActT, typename StT, int DK>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
@@ -65,7 +76,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
     const int row = row_of(0, u);
-    if (row < R) raw[u] = *reinterpret_cast<const uint4*>(S + (int64_t)row * DK + col);
+    raw[u] = load_stream(S + (int64_t)min(row, R - 1) * DK + col);
   }
 
   // ---- phase A: conv update + SiLU for the 2*DK + R channels of this key head
@@ -130,22 +141,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     qv[i] = s_y[col + i] * q_inv * p.scale;
   }
 
-  // ---- phase B: stream the R state rows
+  // ---- phase B: stream the R state rows, the next batch of loads in flight
+  // while the current one computes (rows past R re-read row R-1, unused)
   const int iters = (R + ROWS_PER_ITER - 1) / ROWS_PER_ITER;
-  for (int it = 0; it < iters; ++it) {
-    if (it > 0) {
+  auto load_batch = [&](uint4* buf, int it) {
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int row = row_of(it, u);
-        if (row < R) raw[u] = *reinterpret_cast<const uint4*>(S + (int64_t)row * DK + col);
-      }
-    }
+    for (int u = 0; u < kLoads; ++u) buf[u] = load_stream(S + (int64_t)min(row_of(it, u), R - 1) * DK + col);
+  };
+  auto compute_batch = [&](const uint4* buf, int it) {
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       const int row = row_of(it, u);
       if (row >= R) continue;  // uniform across the row's lanes
       float st[SV];
-      Elem<StT>::unpack(raw[u], st);
+      Elem<StT>::unpack(buf[u], st);
       float p1 = 0.0f, p2 = 0.0f;
 #pragma unroll
       for (int i = 0; i < SV; ++i) {
@@ -160,9 +169,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
       const float o = d * p2 + delta * kq;
 #pragma unroll
       for (int i = 0; i < SV; ++i) st[i] = d * st[i] + delta * kv[i];
-      *reinterpret_cast<uint4*>(S + (int64_t)row * DK + col) = Elem<StT>::pack(st);
+      store_stream(S + (int64_t)row * DK + col, Elem<StT>::pack(st));
       if ((lane % LPR) == 0) Elem<ActT>::store(out + row, o);
     }
+  };
+  uint4 raw2[kLoads];
+  for (int it = 0; it < iters; it += 2) {
+    load_batch(raw2, min(it + 1, iters - 1));
+    compute_batch(raw, it);
+    load_batch(raw, min(it + 2, iters - 1));
+    if (it + 1 < iters) compute_batch(raw2, it + 1);
   }
 }
 

@@ -44,16 +44,29 @@ __device__ int find_sequence(const int32_t* cu, int N, int64_t t) {
   return lo;
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+// Inputs are read once and outputs written once: nontemporal accesses.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(void* p, const uint4& u) {
+  const v4u v = {u.x, u.y, u.z, u.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
+}
+
 template <typename ActT, typename QkvT, int K>
 __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PrepareParams p) {
   constexpr int V = Elem<ActT>::kVec;
   constexpr int H = K > 1 ? K - 1 : 1;  // history length (storage for K = 1 unused)
+  constexpr int OW = (int)sizeof(QkvT) * V / 16;  // 16-byte words per lane of output
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c0 = (blockIdx.x * kConvWaves + wave) * 64 * V;
   if (c0 >= p.Cc) return;  // wave-uniform; the kernel uses no block barrier
   const int c = c0 + lane * V;
   const bool active = c < p.Cc;  // Cc is a multiple of 16, so lanes are all-in or all-out
+  const int cl = active ? c : 0;  // in-bounds column for lanes past the end
   const int64_t t0 = (int64_t)blockIdx.y * kStrip;
   const int64_t t1 = min(p.T, t0 + kStrip);
 
@@ -63,6 +76,14 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   const int key_dim = p.Hk * p.Dk;
   const int region = c < key_dim ? 0 : (c < 2 * key_dim ? 1 : 2);
   const int head_lanes = p.Dk / V;  // lanes sharing one q or k head
+
+  // block of kAhead token rows in flight; rows past t1 re-read row t1-1
+  uint4 bufA[kAhead], bufB[kAhead];
+  auto load_block = [&](uint4* buf, int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) buf[u] = load_stream(x + min(tb + u, t1 - 1) * p.x_stride + cl);
+  };
+  load_block(bufA, t0);
 
   // taps: wt[j][i] multiplies the input K-1-j tokens back, channel c+i
   float wt[K][V];
@@ -111,16 +132,7 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
     out_base = static_cast<QkvT*>(p.v); out_row = (int64_t)p.Hv * p.Dv; out_col = c - 2 * key_dim;
   }
 
-  for (int64_t tb = t0; tb < t1; tb += kAhead) {
-    float xv[kAhead][V];
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) {
-      const int64_t t = tb + u;
-      if (t < t1 && active) load_vec<ActT>(x + t * p.x_stride + c, xv[u]);
-      else
-#pragma unroll
-        for (int i = 0; i < V; ++i) xv[u][i] = 0.0f;
-    }
+  auto process = [&](const uint4* buf, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       const int64_t t = tb + u;
@@ -136,11 +148,13 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
             for (int i = 0; i < V; ++i) win[j][i] = hist_at(s, j + 1, i);
         }
       }
+      float xv[V];
+      Elem<ActT>::unpack(buf[u], xv);
       float y[V];
       float ss = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        float acc = wt[K - 1][i] * xv[u][i];
+        float acc = wt[K - 1][i] * xv[i];
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) acc += wt[K - 2 - j][i] * win[j][i];
         y[i] = silu_f(acc);
@@ -154,16 +168,33 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
           for (int i = 0; i < V; ++i) y[i] *= inv;
         }
       }
-      if (active) store_n<QkvT, V>(out_base + t * out_row + out_col, y);
+      if (active) {
+        QkvT* dst = out_base + t * out_row + out_col;
+        if constexpr (OW >= 1) {
+#pragma unroll
+          for (int o = 0; o < OW; ++o)
+            store_stream(dst + o * Elem<QkvT>::kVec, Elem<QkvT>::pack(y + o * Elem<QkvT>::kVec));
+        } else {
+          store_n<QkvT, V>(dst, y);
+        }
+      }
       if constexpr (K > 1) {
 #pragma unroll
         for (int j = K - 2; j > 0; --j)
 #pragma unroll
           for (int i = 0; i < V; ++i) win[j][i] = win[j - 1][i];
 #pragma unroll
-        for (int i = 0; i < V; ++i) win[0][i] = xv[u][i];
+        for (int i = 0; i < V; ++i) win[0][i] = xv[i];
       }
     }
+  };
+
+  // two blocks per trip, each loaded one block ahead of its use
+  for (int64_t tb = t0; tb < t1; tb += 2 * kAhead) {
+    load_block(bufB, tb + kAhead);
+    process(bufA, tb);
+    load_block(bufA, tb + 2 * kAhead);
+    process(bufB, tb + kAhead);
   }
 }
 
