@@ -29,16 +29,17 @@
 //     dependence: K K^T and Q K^T with operands read straight from memory,
 //     T = (I + A)^-1 (16x16 diagonal blocks by substitution in registers,
 //     off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ on MFMA), then W and U
-//     against K^T / V^T staged in LDS.  Writes W and P (f16 hi/lo), U,
-//     gamma, exp(G_C - G_j) and the q/k row scales to the workspace.
-//  3. chunk_scan_kernel, one workgroup (4 waves) per (sequence, value head,
+//     against K^T / V^T staged in LDS.  Writes W and P (f16 hi/lo), U^T
+//     (f32), the row-scaled K^T (f16), gamma, exp(G_C - G_j) and the q/k row
+//     scales to the workspace.
+//  3. chunk_scan_kernel, one workgroup (8 waves) per (sequence, value head,
 //     block of 16 value rows), placed so that the row blocks and value heads
-//     of one key head share an XCD's L2: walks the sequence's chunks in order with the
-//     16 x Dk state block in registers; each wave owns 16 tokens of Delta and
-//     O and a quarter of the state's column tiles, which are exchanged
-//     through LDS once per chunk.  The next chunk's operands are loaded while
-//     the current chunk computes.  Value rows of the state are independent,
-//     so row blocks never communicate.
+//     of one key head share an XCD's L2: walks the sequence's chunks in order.
+//     Four waves carry the 16 x Dk state block in registers and run only the
+//     serial part (Delta and the state update); four more do the bulk loads,
+//     staging W and K^T into LDS, and form the output of each chunk from the
+//     state and Delta published in LDS.  One barrier per chunk.  Value rows of
+//     the state are independent, so row blocks never communicate.
 //
 // Shapes the chunked kernels do not cover (Dk != Dv, or head dims 16 or
 // 256) run a token-sequential kernel: one wave per sequence, value head and
@@ -53,6 +54,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -113,14 +115,21 @@ constexpr int KTS = kChunk + 8;  // row stride (halves) of transposed [column][t
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Per (chunk, value head) block, byte offsets (D = head dim):
-//   W hi [64][D] f16, W lo [64][D] f16, P hi [64][64] f16, P lo [64][64] f16,
-//   U [64][D] f32, gamma [64], exp(G_C - G_j) [64], k row scale [64], q row scale [64] f32
+//   W hi [64][D] f16, W lo [64][D] f16, U^T [D][64] f32,
+//   P hi [64][64] f16, P lo [64][64] f16,
+//   K^T hi [D][64] f16, K^T lo [D][64] f16 (written for f32 q/k/v only; K
+//   already scaled by its row scale), gamma [64], exp(G_C - G_j) [64],
+//   k row scale [64], q row scale [64] f32
+// W's columns are stored in the scan's contraction order: within each group
+// of 32, position 8b + 4a + c holds column 16a + 4b + c (a < 2, b < 4, c < 4).
 __host__ __device__ constexpr int64_t blk_w_hi(int) { return 0; }
 __host__ __device__ constexpr int64_t blk_w_lo(int D) { return (int64_t)kChunk * D * 2; }
-__host__ __device__ constexpr int64_t blk_p_hi(int D) { return (int64_t)kChunk * D * 4; }
+__host__ __device__ constexpr int64_t blk_ut(int D) { return (int64_t)kChunk * D * 4; }
+__host__ __device__ constexpr int64_t blk_p_hi(int D) { return (int64_t)kChunk * D * 8; }
 __host__ __device__ constexpr int64_t blk_p_lo(int D) { return blk_p_hi(D) + kChunk * kChunk * 2; }
-__host__ __device__ constexpr int64_t blk_u(int D) { return blk_p_hi(D) + kChunk * kChunk * 4; }
-__host__ __device__ constexpr int64_t blk_vec(int D) { return blk_u(D) + (int64_t)kChunk * D * 4; }
+__host__ __device__ constexpr int64_t blk_kt_hi(int D) { return blk_p_hi(D) + kChunk * kChunk * 4; }
+__host__ __device__ constexpr int64_t blk_kt_lo(int D) { return blk_kt_hi(D) + (int64_t)D * kChunk * 2; }
+__host__ __device__ constexpr int64_t blk_vec(int D) { return blk_kt_hi(D) + (int64_t)D * kChunk * 4; }
 __host__ __device__ constexpr int64_t blk_bytes(int D) { return blk_vec(D) + 4 * kChunk * 4; }
 
 struct ChunkWs {
@@ -203,9 +212,13 @@ struct TransposedTile {
   }
   // row scales (l2 norm) are per token; null means 1
   __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, const float* rowscale, int n) const {
+    const int t = 2 * (threadIdx.x & 31);
+    store(hi, lo, rowscale ? rowscale[t] : 1.0f, rowscale ? rowscale[t + 1] : 1.0f, n);
+  }
+  // s0, s1: scales of this lane's two tokens 2(l%32), 2(l%32)+1
+  __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, float s0, float s1, int n) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = 2 * (lane & 31), seg0 = wave * 2 + (lane >> 5);
-    float s0 = rowscale ? rowscale[t] : 1.0f, s1 = rowscale ? rowscale[t + 1] : 1.0f;
     if (t >= n) s0 = 0.0f;
     if (t + 1 >= n) s1 = 0.0f;
 #pragma unroll
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
   _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
   _Float16* Ph = reinterpret_cast<_Float16*>(blk + blk_p_hi(D));
   _Float16* Pl = reinterpret_cast<_Float16*>(blk + blk_p_lo(D));
-  float* Ug = reinterpret_cast<float*>(blk + blk_u(D));
+  float* UTg = reinterpret_cast<float*>(blk + blk_ut(D));
   float* gam_g = reinterpret_cast<float*>(blk + blk_vec(D));
   float* dc_g = gam_g + kChunk;
   float* kn_g = dc_g + kChunk;
@@ -438,6 +451,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     }
   }
   __syncthreads();
+  // the scaled K^T tile for the scan, without the LDS row padding
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int v = tid + 256 * j, r = v >> 3, c8 = v & 7;
+    *reinterpret_cast<uint4*>(blk + blk_kt_hi(D) + (r * kChunk + 8 * c8) * 2) =
+        *reinterpret_cast<const uint4*>(KTh + r * KTS + 8 * c8);
+    if constexpr (SPLIT)
+      *reinterpret_cast<uint4*>(blk + blk_kt_lo(D) + (r * kChunk + 8 * c8) * 2) =
+          *reinterpret_cast<const uint4*>(KTl + r * KTS + 8 * c8);
+  }
 
   // T = (I + A)^-1.  Diagonal block w by wave w: lane li solves column li.
   {
@@ -531,11 +554,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
       if (ct >= 2 * NCT) break;
       const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
       if (ct < NCT) {
-        const int col = 16 * ct + 4 * lg;
-        store_h4_split(Wh + i * D + col, Wl + i * D + col, v);
+        // columns 16ct + 4lg .. +3, stored in the scan's contraction order
+        const int pos = 32 * (ct >> 1) + 8 * lg + 4 * (ct & 1);
+        store_h4_split(Wh + i * D + pos, Wl + i * D + pos, v);
       } else {
         const int col = 16 * (ct - NCT) + 4 * lg;
-        *reinterpret_cast<float4*>(Ug + i * D + col) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) UTg[(col + r) * kChunk + i] = v[r];
       }
     }
   }
@@ -544,24 +569,96 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
 // ---------------------------------------------------------------------------
 // 3. sequential pass over chunks
 // ---------------------------------------------------------------------------
-// Register fragments: lane (li = lane%16, lg = lane/16) holds, for each
-// 32-wide k step s, the 8 columns 32s + 8lg .. 32s + 8lg + 7 of row li of an
-// operand (rows of W, Q, P; the state row e0 + li).
+// Four consecutive input elements in their storage form (8 bytes for bf16,
+// 16 for f32).
+template <typename T>
+struct Raw4 {
+  static constexpr int kWords = (int)sizeof(T);  // 32-bit words holding four elements
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (kWords == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    }
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    if constexpr (kWords == 2) {
+      float t[8];
+      Elem<T>::unpack(make_uint4(w[0], w[1], 0u, 0u), t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = t[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+// Four consecutive outputs in one store.
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  uint2 w;
+  w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+
+// One workgroup of 8 waves carries rows e0 .. e0+15 of one value head's
+// state through the chunks of one sequence.
+//
+// Waves 0-3 (the state waves) run only the serial part.  Each holds the whole
+// 16 x D block in registers as the MFMA B operand of S^T: lane (li, lg) holds
+// row e0 + li at the columns
+//   k(s, i) = 32 s + 16 (i / 4) + 4 lg + i % 4,   s < D/32, i < 8,
+// so the contraction over k runs in this permuted order (W is stored so, Q is
+// loaded so).  The order is chosen so that the state update, computed as its
+// transpose S'^T = gamma_C S^T + K^T E one 16-column tile at a time, leaves
+// tile ct in exactly the registers that hold columns 16 ct .. 16 ct + 15.  Per
+// chunk a state wave splits the state into f16 hi/lo and publishes its share
+// of the split to LDS, forms Delta = U - W S^T for its 16 tokens (three
+// independent MFMA chains), writes Delta and E = diag(exp(G_C - G_j)) Delta
+// to LDS, and after the barrier applies the whole update (every state wave
+// the same; the matrix cores have room to spare).
+//
+// Waves 4-7 (the output waves) do all the bulk loading: they stage the next
+// chunk's W (before the barrier) and K^T (after it) into LDS for the state
+// waves, and after the barrier form O = diag(scale gamma) Q S^T + P Delta for
+// 16 tokens each from the published state and Delta, writing it out through
+// a small LDS transpose.  With f32 q/k/v the LDS holds no W; the state waves
+// then load W themselves.
+//
+// One barrier per chunk.  Every LDS buffer is double-buffered by chunk parity
+// and written and read in phases that a barrier separates.  Loads run one to
+// two chunks ahead and are unconditional (the last chunk re-loads itself) so
+// that none sits under a branch.  Sequences are never empty (the host rejects
+// them), so every workgroup has a chunk.
 template <typename QkvT, typename StT, int D>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillParams p, ChunkWs ws) {
+__global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
-  constexpr int NKS = D / 32;
-  constexpr int NCT = D / 16;
-  constexpr int SS = D + 4;  // f32 row stride of the state exchange
-  __shared__ __attribute__((aligned(16))) _Float16 KTh[D * KTS];
-  __shared__ __attribute__((aligned(16))) _Float16 KTl[SPLIT ? D * KTS : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 DTh[16 * KTS];  // Delta^T [e][token]
-  __shared__ __attribute__((aligned(16))) _Float16 DTl[16 * KTS];
-  __shared__ __attribute__((aligned(16))) _Float16 ETh[16 * KTS];  // (exp(G_C - G_j) Delta)^T
-  __shared__ __attribute__((aligned(16))) _Float16 ETl[16 * KTS];
-  __shared__ __attribute__((aligned(16))) float Ss[2][16 * SS];
-  // per-chunk vectors, double-buffered by chunk parity: gamma, exp(G_C - G_j), k and q row scales
-  __shared__ float gam_s[2][kChunk], dc_s[2][kChunk], kn_s[2][kChunk], qn_s[2][kChunk];
+  constexpr bool STAGE_W = !SPLIT;  // LDS room for W next to the f32 K^T lo tiles is lacking
+  constexpr int NKS = D / 32;     // 32-wide k steps
+  constexpr int NCT = D / 16;     // 16-column tiles of the state
+  constexpr int WS = D + 8;       // f16 row stride of W and of the published state
+  constexpr int KTV = D / 32;     // 16-byte K^T vectors per output-wave lane (per hi / lo)
+  constexpr int WV = D / 16;      // 16-byte W vectors per output-wave lane (hi and lo)
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[2][D * KTS];  // K^T [column][token]
+  __shared__ __attribute__((aligned(16))) _Float16 KTl[2][SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 Wsh[2][STAGE_W ? 2 * kChunk * WS : 8];  // W hi rows, then lo rows
+  __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
+  __shared__ __attribute__((aligned(16))) _Float16 DTl[2][16 * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 ETh[2][16 * KTS];  // (exp(G_C - G_j) Delta)^T
+  __shared__ __attribute__((aligned(16))) _Float16 ETl[2][16 * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 SSh[2][2 * 16 * WS];  // state hi rows, then lo rows
+  __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
 
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
@@ -575,222 +672,271 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillParams p, ChunkW
   const int s_idx = logical / ((D / 16) * p.Hv);
   const int kh = h / (p.Hv / p.Hk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int w4 = wave & 3;
+  const bool state_wave = wave < 4;
   const int slot = p.slots ? p.slots[s_idx] : s_idx;
   const bool has = p.has_init == nullptr || p.has_init[s_idx] != 0;
-  const int64_t seq_end = p.cu[s_idx + 1];
+  const int64_t seq_start = p.cu[s_idx], seq_end = p.cu[s_idx + 1];
   const int64_t qk_stride = (int64_t)p.Hk * D;
   StT* Sg = static_cast<StT*>(p.ssm_pool) + (((int64_t)slot * p.Hv + h) * D + e0 + li) * D;
-  const QkvT* kbase = static_cast<const QkvT*>(p.k) + (int64_t)kh * D;
   const QkvT* qbase = static_cast<const QkvT*>(p.q) + (int64_t)kh * D;
-  QkvT* obase = static_cast<QkvT*>(p.out) + (int64_t)h * D + e0 + li;
+  QkvT* obase = static_cast<QkvT*>(p.out) + (int64_t)h * D + e0;
   const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
-
-  // state fragment
-  float Sf[8 * NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    if (has) {
-      load_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf + 8 * s);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Sf[8 * s + i] = 0.0f;
-    }
-  }
-  if (wave == 0)
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Ss[0][li * SS + 32 * s + 8 * lg + i] = Sf[8 * s + i];
-  int cur = 0;
-
-  // operands of the chunk about to be computed; every load below is
-  // unconditional (the last chunk prefetches itself again) so that no load
-  // sits under a branch
-  TransposedTile<QkvT, D> ktile;
-  h8 Wfh[NKS], Wfl[NKS], Pfh[2], Pfl[2];
-  Raw8<QkvT> Qr[NKS];
-  float Uv[4], gd0, gd1, gd2, gd3;
-  const int64_t seq_start = p.cu[s_idx];
   auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D); };
   auto tok0 = [&](int cid) { return seq_start + (int64_t)kChunk * (cid - c_begin); };
   auto ntok = [&](int cid) { return (int)min((int64_t)kChunk, seq_end - tok0(cid)); };
-  auto load_k = [&](int cid) {
-    ktile.load(kbase + tok0(cid) * qk_stride, qk_stride, ntok(cid));
-    const float* v = reinterpret_cast<const float*>(blk_of(cid) + blk_vec(D));
-    gd0 = v[lane];
-    gd1 = v[kChunk + lane];
-    gd2 = v[2 * kChunk + lane];
-    gd3 = v[3 * kChunk + lane];
-  };
-  auto put_vectors = [&](int b) {  // after load_k's values have arrived
-    if (wave == 0) {
-      gam_s[b][lane] = gd0;
-      dc_s[b][lane] = gd1;
-      kn_s[b][lane] = gd2;
-      qn_s[b][lane] = gd3;
+
+  // ---- state-wave operands
+  float Sf[8 * NKS];
+  float4 utv, dcv;        // U^T and exp(G_C - G_j) at this lane's tokens 16 w4 + 4 lg + r
+  float gC;               // gamma at the chunk's last token
+  h8 Wgh[SPLIT ? NKS : 1], Wgl[SPLIT ? NKS : 1];  // W fragments when they come straight from memory
+  auto load_u = [&](int cid) {
+    const char* b = blk_of(cid);
+    utv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + li) * kChunk +
+                                           16 * w4 + 4 * lg);
+    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
+    dcv = *reinterpret_cast<const float4*>(v + kChunk + 16 * w4 + 4 * lg);
+    gC = v[kChunk - 1];
+    if constexpr (!STAGE_W) {
+      const int row = 16 * w4 + li;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        Wgh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_hi(D)) + row * D + 32 * s + 8 * lg);
+        Wgl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_lo(D)) + row * D + 32 * s + 8 * lg);
+      }
     }
   };
-  auto load_wu = [&](int cid) {
+
+  // ---- output-wave operands
+  Raw4<QkvT> Qa[NKS], Qb[NKS];   // Q row 16 w4 + li at columns k(s, 0..3) and k(s, 4..7)
+  h8 Pfh[2], Pfl[2];
+  float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
+  u32x4 KTr[KTV], KTrl[SPLIT ? KTV : 1];
+  u32x4 Wr[STAGE_W ? WV : 1];
+  const int ot = tid - 256;      // output-wave thread index
+  auto load_qp = [&](int cid) {
     const char* b = blk_of(cid);
-    const int row = 16 * wave + li;
+    const int rr = min(16 * w4 + li, ntok(cid) - 1);  // rows past the end re-read the last row; their scale is 0
+    const QkvT* qr = qbase + (tok0(cid) + rr) * qk_stride + 4 * lg;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      Wfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_hi(D)) + row * D + 32 * s + 8 * lg);
-      Wfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_w_lo(D)) + row * D + 32 * s + 8 * lg);
+      Qa[s].load(qr + 32 * s);
+      Qb[s].load(qr + 32 * s + 16);
     }
-    const float* ug = reinterpret_cast<const float*>(b + blk_u(D));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Uv[r] = ug[(16 * wave + 4 * lg + r) * D + e0 + li];
-  };
-  auto load_q = [&](int cid) {
-    const int rr = min(16 * wave + li, ntok(cid) - 1);  // rows past the end re-read the last row; their scale is 0
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) Qr[s].load(qbase + (tok0(cid) + rr) * qk_stride + 32 * s + 8 * lg);
-  };
-  auto load_p = [&](int cid) {
-    const char* b = blk_of(cid);
-    const int row = 16 * wave + li;
+    const int row = 16 * w4 + li;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + row * kChunk + 32 * s + 8 * lg);
       Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + row * kChunk + 32 * s + 8 * lg);
     }
+    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
+    gmv = *reinterpret_cast<const float4*>(v + 16 * w4 + 4 * lg);
+    qsv = *reinterpret_cast<const float4*>(v + 3 * kChunk + 16 * w4 + 4 * lg);
   };
-  load_k(c_begin);
-  load_wu(c_begin);
-  load_q(c_begin);
-  load_p(c_begin);
-  put_vectors(0);
+  auto load_kt = [&](int cid) {
+    const char* b = blk_of(cid);
+#pragma unroll
+    for (int j = 0; j < KTV; ++j) {
+      const int v = ot + 256 * j;
+      KTr[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_hi(D) + v * 16);
+      if constexpr (SPLIT) KTrl[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_lo(D) + v * 16);
+    }
+  };
+  auto stage_kt = [&](int bb) {
+#pragma unroll
+    for (int j = 0; j < KTV; ++j) {
+      const int v = ot + 256 * j, r = v >> 3, c8 = v & 7;
+      *reinterpret_cast<u32x4*>(KTh[bb] + r * KTS + 8 * c8) = KTr[j];
+      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(KTl[bb] + r * KTS + 8 * c8) = KTrl[j];
+    }
+  };
+  // W hi then W lo as 2 * 64 rows of D halves; vector v covers row v / (D/8)
+  auto load_wst = [&](int cid) {
+    if constexpr (STAGE_W) {
+      const char* b = blk_of(cid) + blk_w_hi(D);
+#pragma unroll
+      for (int j = 0; j < WV; ++j) Wr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
+    }
+  };
+  auto stage_w = [&](int bb) {
+    if constexpr (STAGE_W) {
+#pragma unroll
+      for (int j = 0; j < WV; ++j) {
+        const int v = ot + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
+        *reinterpret_cast<u32x4*>(Wsh[bb] + r * WS + 8 * c8) = Wr[j];
+      }
+    }
+  };
+
+  // ---- prologue
+  if (state_wave) {
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      if (has) {
+        load_n<StT, 4>(Sg + 32 * s + 4 * lg, Sf + 8 * s);
+        load_n<StT, 4>(Sg + 32 * s + 16 + 4 * lg, Sf + 8 * s + 4);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Sf[8 * s + i] = 0.0f;
+      }
+    }
+    load_u(c_begin);
+  } else {
+    load_wst(c_begin);
+    load_kt(c_begin);
+    load_qp(c_begin);
+    stage_w(0);
+    stage_kt(0);
+    load_wst(min(c_begin + 1, c_end - 1));
+    load_kt(min(c_begin + 1, c_end - 1));
+  }
   __syncthreads();
 
   for (int cid = c_begin; cid < c_end; ++cid) {
-    const int64_t t0 = tok0(cid);
-    const int n = ntok(cid);
     const int b = (cid - c_begin) & 1;
     const int cn = min(cid + 1, c_end - 1);
-    // this chunk's K^T to LDS, then start loading the next chunk's K and vectors
-    ktile.store(KTh, KTl, p.l2norm ? kn_s[b] : nullptr, n);
-    load_k(cn);
-    __syncthreads();
-
-    // split the state for the products
-    h8 Sh[NKS], Sl[NKS];
+    if (state_wave) {
+      h8 Sh[NKS], Sl[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) split8(Sf + 8 * s, Sh[s], Sl[s]);
-
-    // Delta rows of this wave's 16 tokens: U - W S0^T
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < NKS; ++s) split8(Sf + 8 * s, Sh[s], Sl[s]);
+      // publish k step w4 of the split state for the output waves
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      acc = mfma_f16(Wfh[s], Sh[s], acc);
-      acc = mfma_f16(Wfh[s], Sl[s], acc);
-      acc = mfma_f16(Wfl[s], Sh[s], acc);
-    }
-    float dl[4], el[4];
+      for (int s = 0; s < NKS; ++s)
+        if (s == w4) {
+          *reinterpret_cast<h8*>(SSh[b] + li * WS + 32 * s + 8 * lg) = Sh[s];
+          *reinterpret_cast<h8*>(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
+        }
+      // Delta rows of this wave's 16 tokens: U - W S0^T, three independent chains
+      f32x4 ahh = {0.0f, 0.0f, 0.0f, 0.0f}, ahl = ahh, alh = ahh;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dl[r] = Uv[r] - acc[r];
-      el[r] = dl[r] * dc_s[b][16 * wave + 4 * lg + r];
-    }
-    load_wu(cn);
-    {
-      // Delta^T and (exp(G_C - G_j) Delta)^T, 4 consecutive tokens per lane
-      uint32_t w[4][2];
-#pragma unroll
-      for (int r2 = 0; r2 < 2; ++r2) {
-        const _Float16 a0 = (_Float16)dl[2 * r2], a1 = (_Float16)dl[2 * r2 + 1];
-        const _Float16 b0 = (_Float16)(dl[2 * r2] - (float)a0), b1 = (_Float16)(dl[2 * r2 + 1] - (float)a1);
-        const _Float16 c0 = (_Float16)el[2 * r2], c1 = (_Float16)el[2 * r2 + 1];
-        const _Float16 d0 = (_Float16)(el[2 * r2] - (float)c0), d1 = (_Float16)(el[2 * r2 + 1] - (float)c1);
-        w[0][r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        w[1][r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w[2][r2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
-        w[3][r2] = (uint32_t)__builtin_bit_cast(uint16_t, d0) | ((uint32_t)__builtin_bit_cast(uint16_t, d1) << 16);
+      for (int s = 0; s < NKS; ++s) {
+        h8 wh, wl;
+        if constexpr (STAGE_W) {
+          wh = ld_h8(Wsh[b] + (16 * w4 + li) * WS + 32 * s + 8 * lg);
+          wl = ld_h8(Wsh[b] + (kChunk + 16 * w4 + li) * WS + 32 * s + 8 * lg);
+        } else {
+          wh = Wgh[s];
+          wl = Wgl[s];
+        }
+        ahh = mfma_f16(wh, Sh[s], ahh);
+        ahl = mfma_f16(wh, Sl[s], ahl);
+        alh = mfma_f16(wl, Sh[s], alh);
       }
-      const int off = li * KTS + 16 * wave + 4 * lg;
-      *reinterpret_cast<uint2*>(DTh + off) = make_uint2(w[0][0], w[0][1]);
-      *reinterpret_cast<uint2*>(DTl + off) = make_uint2(w[1][0], w[1][1]);
-      *reinterpret_cast<uint2*>(ETh + off) = make_uint2(w[2][0], w[2][1]);
-      *reinterpret_cast<uint2*>(ETl + off) = make_uint2(w[3][0], w[3][1]);
-    }
-
-    // scale gamma_i (Q S0^T), with Q's row scale (L2 norm) folded in
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float qs = qn_s[b][16 * wave + li];
+      const f32x4 acc = ahh + (ahl + alh);
+      const float us[4] = {utv.x, utv.y, utv.z, utv.w}, dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
+      const float gc = gC;
+      load_u(cn);
+      {
+        // Delta^T and E^T (f16 hi/lo), 4 consecutive tokens per lane
+        uint32_t w[4][2];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      float qx[8];
-      Qr[s].get(qx);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qx[i] *= qs;
-      if constexpr (SPLIT) {
-        h8 qh, ql;
-        split8(qx, qh, ql);
-        o = mfma_f16(qh, Sh[s], o);
-        o = mfma_f16(qh, Sl[s], o);
-        o = mfma_f16(ql, Sh[s], o);
-      } else {
-        const h8 qh = to_h8(qx);
-        o = mfma_f16(qh, Sh[s], o);
-        o = mfma_f16(qh, Sl[s], o);
+        for (int r2 = 0; r2 < 2; ++r2) {
+          const float d0 = us[2 * r2] - acc[2 * r2], d1 = us[2 * r2 + 1] - acc[2 * r2 + 1];
+          const float x0 = d0 * dcs[2 * r2], x1 = d1 * dcs[2 * r2 + 1];
+          const _Float16 a0 = (_Float16)d0, a1 = (_Float16)d1;
+          const _Float16 b0 = (_Float16)(d0 - (float)a0), b1 = (_Float16)(d1 - (float)a1);
+          const _Float16 c0 = (_Float16)x0, c1 = (_Float16)x1;
+          const _Float16 f0 = (_Float16)(x0 - (float)c0), f1 = (_Float16)(x1 - (float)c1);
+          w[0][r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+          w[1][r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          w[2][r2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+          w[3][r2] = (uint32_t)__builtin_bit_cast(uint16_t, f0) | ((uint32_t)__builtin_bit_cast(uint16_t, f1) << 16);
+        }
+        const int off = li * KTS + 16 * w4 + 4 * lg;
+        *reinterpret_cast<uint2*>(DTh[b] + off) = make_uint2(w[0][0], w[0][1]);
+        *reinterpret_cast<uint2*>(DTl[b] + off) = make_uint2(w[1][0], w[1][1]);
+        *reinterpret_cast<uint2*>(ETh[b] + off) = make_uint2(w[2][0], w[2][1]);
+        *reinterpret_cast<uint2*>(ETl[b] + off) = make_uint2(w[3][0], w[3][1]);
       }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= p.scale * gam_s[b][16 * wave + 4 * lg + r];
-    load_q(cn);
-    __syncthreads();
-
-    // + P Delta over the token blocks up to this one
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s > (wave >> 1)) break;
-      const h8 dh = ld_h8(DTh + li * KTS + 32 * s + 8 * lg);
-      const h8 dlo = ld_h8(DTl + li * KTS + 32 * s + 8 * lg);
-      o = mfma_f16(Pfh[s], dh, o);
-      o = mfma_f16(Pfh[s], dlo, o);
-      o = mfma_f16(Pfl[s], dh, o);
-    }
-    load_p(cn);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * wave + 4 * lg + r;
-      if (i < n) Elem<QkvT>::store(obase + (t0 + i) * (int64_t)p.Hv * D, o[r]);
-    }
-
-    // state column tiles owned by this wave: S' = gamma_C S0 + (exp(G_C - G_j) Delta)^T K
-    const float gC = gam_s[b][kChunk - 1];
-    const int nxt = cur ^ 1;
-    for (int ct = wave; ct < NCT; ct += 4) {
-      f32x4 a2 = {0.0f, 0.0f, 0.0f, 0.0f};
+      __syncthreads();
+      // S'^T = gamma_C S0^T + K^T E, tile ct = columns 16ct .. 16ct+15
+      h8 eh[2], el[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const h8 eh = ld_h8(ETh + li * KTS + 32 * s + 8 * lg);
-        const h8 elo = ld_h8(ETl + li * KTS + 32 * s + 8 * lg);
-        const h8 kk = ld_h8(KTh + (16 * ct + li) * KTS + 32 * s + 8 * lg);
-        a2 = mfma_f16(eh, kk, a2);
-        a2 = mfma_f16(elo, kk, a2);
-        if constexpr (SPLIT) a2 = mfma_f16(eh, ld_h8(KTl + (16 * ct + li) * KTS + 32 * s + 8 * lg), a2);
+        eh[s] = ld_h8(ETh[b] + li * KTS + 32 * s + 8 * lg);
+        el[s] = ld_h8(ETl[b] + li * KTS + 32 * s + 8 * lg);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int idx = (4 * lg + r) * SS + 16 * ct + li;
-        Ss[nxt][idx] = gC * Ss[cur][idx] + a2[r];
+      for (int ct = 0; ct < NCT; ++ct) {
+        float* sc = Sf + 8 * (ct >> 1) + 4 * (ct & 1);
+        f32x4 a2 = {gc * sc[0], gc * sc[1], gc * sc[2], gc * sc[3]};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const h8 kk = ld_h8(KTh[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg);
+          a2 = mfma_f16(kk, eh[s], a2);
+          a2 = mfma_f16(kk, el[s], a2);
+          if constexpr (SPLIT) a2 = mfma_f16(ld_h8(KTl[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg), eh[s], a2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = a2[r];
       }
+    } else {
+      // next chunk's W into the other buffer, then start loading the one after
+      stage_w(b ^ 1);
+      load_wst(min(cid + 2, c_end - 1));
+      __syncthreads();
+      // O of this chunk: diag(scale gamma) Q S0^T with Q's row scale, + P Delta
+      f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        float qx[8];
+        Qa[s].get(qx);
+        Qb[s].get(qx + 4);
+        const h8 sh = ld_h8(SSh[b] + li * WS + 32 * s + 8 * lg);
+        const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
+        if constexpr (SPLIT) {
+          h8 qh, ql;
+          split8(qx, qh, ql);
+          o = mfma_f16(qh, sh, o);
+          o2 = mfma_f16(qh, sl, o2);
+          o2 = mfma_f16(ql, sh, o2);
+        } else {
+          const h8 qh = to_h8(qx);
+          o = mfma_f16(qh, sh, o);
+          o2 = mfma_f16(qh, sl, o2);
+        }
+      }
+      o += o2;
+      const float qs[4] = {qsv.x, qsv.y, qsv.z, qsv.w}, gm[4] = {gmv.x, gmv.y, gmv.z, gmv.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] *= qs[r] * p.scale * gm[r];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s > (w4 >> 1)) break;
+        const h8 dh = ld_h8(DTh[b] + li * KTS + 32 * s + 8 * lg);
+        const h8 dlo = ld_h8(DTl[b] + li * KTS + 32 * s + 8 * lg);
+        o = mfma_f16(Pfh[s], dh, o);
+        o = mfma_f16(Pfh[s], dlo, o);
+        o = mfma_f16(Pfl[s], dh, o);
+      }
+      // lane holds O[token 16 w4 + 4 lg + r][e0 + li]; transpose so that each
+      // lane writes four consecutive e of one token
+      float* os = Os[w4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) os[(4 * lg + r) * 20 + li] = o[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int tt = lane >> 2, ec = 4 * (lane & 3);
+      const float4 ov = *reinterpret_cast<const float4*>(os + tt * 20 + ec);
+      const int i = 16 * w4 + tt;
+      if (i < ntok(cid)) {
+        const float vals[4] = {ov.x, ov.y, ov.z, ov.w};
+        store4(obase + (tok0(cid) + i) * (int64_t)p.Hv * D + ec, vals);
+      }
+      // next chunk's K^T into the other buffer; operands of the chunks ahead
+      stage_kt(b ^ 1);
+      load_qp(cn);
+      load_kt(min(cid + 2, c_end - 1));
     }
-    put_vectors(b ^ 1);
-    __syncthreads();
-    cur = nxt;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int i4 = 0; i4 < 2; ++i4) {
-        const float4 v = *reinterpret_cast<const float4*>(&Ss[cur][li * SS + 32 * s + 8 * lg + 4 * i4]);
-        Sf[8 * s + 4 * i4] = v.x; Sf[8 * s + 4 * i4 + 1] = v.y; Sf[8 * s + 4 * i4 + 2] = v.z; Sf[8 * s + 4 * i4 + 3] = v.w;
-      }
   }
   if (wave == 0)
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) store_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf + 8 * s);
+    for (int s = 0; s < NKS; ++s) {
+      store_n<StT, 4>(Sg + 32 * s + 4 * lg, Sf + 8 * s);
+      store_n<StT, 4>(Sg + 32 * s + 16 + 4 * lg, Sf + 8 * s + 4);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -908,7 +1054,7 @@ template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
   chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
   const int nwg = (D / 16) * p.Hv * p.N;
-  chunk_scan_kernel<QkvT, StT, D><<<(unsigned)((nwg + 7) / 8 * 8), 256, 0, stream>>>(p, ws);
+  chunk_scan_kernel<QkvT, StT, D><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
   return hipGetLastError();
 }
 
