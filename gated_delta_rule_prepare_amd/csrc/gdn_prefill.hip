@@ -18,7 +18,10 @@
 // two f16 halves hi = f16(x), lo = f16(x - hi), and a product of two such
 // operands as hi*hi + hi*lo + lo*hi (f32 accumulation): about 22 significant
 // bits, where bf16 q/k/v need no split at all (every bf16 value of the
-// normalised q/k range is exact in f16).  The small inverse T uses the f32
+// normalised q/k range is exact in f16).  Products that feed only a bf16
+// output (Q S^T and P Delta with bf16 q/k/v) use the f16 hi parts alone: one
+// f16 rounding (2^-11) of an operand, several times below the bf16 rounding
+// (2^-9) of the output itself; everything that feeds the state keeps the split.  The small inverse T uses the f32
 // 16x16x4 MFMA.  The running sums G are formed in double precision and every
 // decay factor is exp of a difference taken in double.
 //
@@ -402,7 +405,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     for (int J = 0; J < 4; ++J) {
       if (J > wave) {
         float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, z);
+        if constexpr (SPLIT)
+          store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, z);
+        else
+          store_h4(Ph + i * kChunk + 16 * J + 4 * lg, z);
         continue;
       }
       const float sj = kn[16 * J + li];  // scale of the K row this lane feeds as operand A
@@ -447,7 +453,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
         pv[r] = j <= i ? p.scale * dec * aqk[r] : 0.0f;
       }
       *reinterpret_cast<float4*>(As + i * TS + 16 * J + 4 * lg) = make_float4(av[0], av[1], av[2], av[3]);
-      store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, pv);
+      if constexpr (SPLIT)
+        store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, pv);
+      else
+        store_h4(Ph + i * kChunk + 16 * J + 4 * lg, pv);
     }
   }
   __syncthreads();
@@ -629,9 +638,9 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 // to LDS, and after the barrier applies the whole update (every state wave
 // the same; the matrix cores have room to spare).
 //
-// Waves 4-7 (the output waves) do all the bulk loading: they stage the next
-// chunk's W (before the barrier) and K^T (after it) into LDS for the state
-// waves, and after the barrier form O = diag(scale gamma) Q S^T + P Delta for
+// Waves 4-7 (the output waves) do all the loading: they stage the next
+// chunk's W, U^T rows and decay factors (before the barrier) and K^T (after
+// it) into LDS for the state waves, and after the barrier form O = diag(scale gamma) Q S^T + P Delta for
 // 16 tokens each from the published state and Delta, writing it out through
 // a small LDS transpose.  With f32 q/k/v the LDS holds no W; the state waves
 // then load W themselves.
@@ -654,11 +663,13 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) _Float16 KTl[2][SPLIT ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 Wsh[2][STAGE_W ? 2 * kChunk * WS : 8];  // W hi rows, then lo rows
   __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
-  __shared__ __attribute__((aligned(16))) _Float16 DTl[2][16 * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 DTl[2][SPLIT ? 16 * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 ETh[2][16 * KTS];  // (exp(G_C - G_j) Delta)^T
   __shared__ __attribute__((aligned(16))) _Float16 ETl[2][16 * KTS];
-  __shared__ __attribute__((aligned(16))) _Float16 SSh[2][2 * 16 * WS];  // state hi rows, then lo rows
+  __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
+  __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T rows e0 .. e0+15
+  __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk];        // exp(G_C - G_j), then gamma
 
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
@@ -688,17 +699,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 
   // ---- state-wave operands
   float Sf[8 * NKS];
-  float4 utv, dcv;        // U^T and exp(G_C - G_j) at this lane's tokens 16 w4 + 4 lg + r
-  float gC;               // gamma at the chunk's last token
   h8 Wgh[SPLIT ? NKS : 1], Wgl[SPLIT ? NKS : 1];  // W fragments when they come straight from memory
-  auto load_u = [&](int cid) {
-    const char* b = blk_of(cid);
-    utv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + li) * kChunk +
-                                           16 * w4 + 4 * lg);
-    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
-    dcv = *reinterpret_cast<const float4*>(v + kChunk + 16 * w4 + 4 * lg);
-    gC = v[kChunk - 1];
+  auto load_wg = [&](int cid) {
     if constexpr (!STAGE_W) {
+      const char* b = blk_of(cid);
       const int row = 16 * w4 + li;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
@@ -710,7 +714,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 
   // ---- output-wave operands
   Raw4<QkvT> Qa[NKS], Qb[NKS];   // Q row 16 w4 + li at columns k(s, 0..3) and k(s, 4..7)
-  h8 Pfh[2], Pfl[2];
+  h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
   u32x4 KTr[KTV], KTrl[SPLIT ? KTV : 1];
   u32x4 Wr[STAGE_W ? WV : 1];
@@ -728,7 +732,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + row * kChunk + 32 * s + 8 * lg);
-      Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + row * kChunk + 32 * s + 8 * lg);
+      if constexpr (SPLIT)
+        Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + row * kChunk + 32 * s + 8 * lg);
     }
     const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
     gmv = *reinterpret_cast<const float4*>(v + 16 * w4 + 4 * lg);
@@ -759,6 +764,19 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       for (int j = 0; j < WV; ++j) Wr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
     }
   };
+  // U^T rows e0 .. e0+15 (one float4 per lane), exp(G_C - G_j) and gamma
+  float4 Ur, Vr;
+  auto load_uv = [&](int cid) {
+    const char* b = blk_of(cid);
+    Ur = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + (ot >> 4)) * kChunk +
+                                          4 * (ot & 15));
+    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
+    Vr = *reinterpret_cast<const float4*>(v + (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)));
+  };
+  auto stage_uv = [&](int bb) {
+    *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
+    if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
+  };
   auto stage_w = [&](int bb) {
     if constexpr (STAGE_W) {
 #pragma unroll
@@ -781,14 +799,17 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int i = 0; i < 8; ++i) Sf[8 * s + i] = 0.0f;
       }
     }
-    load_u(c_begin);
+    load_wg(c_begin);
   } else {
     load_wst(c_begin);
+    load_uv(c_begin);
     load_kt(c_begin);
     load_qp(c_begin);
     stage_w(0);
+    stage_uv(0);
     stage_kt(0);
     load_wst(min(c_begin + 1, c_end - 1));
+    load_uv(min(c_begin + 1, c_end - 1));
     load_kt(min(c_begin + 1, c_end - 1));
   }
   __syncthreads();
@@ -805,7 +826,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       for (int s = 0; s < NKS; ++s)
         if (s == w4) {
           *reinterpret_cast<h8*>(SSh[b] + li * WS + 32 * s + 8 * lg) = Sh[s];
-          *reinterpret_cast<h8*>(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
+          if constexpr (SPLIT) *reinterpret_cast<h8*>(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
         }
       // Delta rows of this wave's 16 tokens: U - W S0^T, three independent chains
       f32x4 ahh = {0.0f, 0.0f, 0.0f, 0.0f}, ahl = ahh, alh = ahh;
@@ -824,9 +845,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         alh = mfma_f16(wl, Sh[s], alh);
       }
       const f32x4 acc = ahh + (ahl + alh);
+      const float4 utv = *reinterpret_cast<const float4*>(Us[b] + li * 68 + 16 * w4 + 4 * lg);
+      const float4 dcv = *reinterpret_cast<const float4*>(Vs[b] + 16 * w4 + 4 * lg);
+      const float gc = Vs[b][kChunk + kChunk - 1];
       const float us[4] = {utv.x, utv.y, utv.z, utv.w}, dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
-      const float gc = gC;
-      load_u(cn);
+      load_wg(cn);
       {
         // Delta^T and E^T (f16 hi/lo), 4 consecutive tokens per lane
         uint32_t w[4][2];
@@ -845,7 +868,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         }
         const int off = li * KTS + 16 * w4 + 4 * lg;
         *reinterpret_cast<uint2*>(DTh[b] + off) = make_uint2(w[0][0], w[0][1]);
-        *reinterpret_cast<uint2*>(DTl[b] + off) = make_uint2(w[1][0], w[1][1]);
+        if constexpr (SPLIT) *reinterpret_cast<uint2*>(DTl[b] + off) = make_uint2(w[1][0], w[1][1]);
         *reinterpret_cast<uint2*>(ETh[b] + off) = make_uint2(w[2][0], w[2][1]);
         *reinterpret_cast<uint2*>(ETl[b] + off) = make_uint2(w[3][0], w[3][1]);
       }
@@ -874,7 +897,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     } else {
       // next chunk's W into the other buffer, then start loading the one after
       stage_w(b ^ 1);
+      stage_uv(b ^ 1);
       load_wst(min(cid + 2, c_end - 1));
+      load_uv(min(cid + 2, c_end - 1));
       __syncthreads();
       // O of this chunk: diag(scale gamma) Q S0^T with Q's row scale, + P Delta
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
@@ -884,17 +909,15 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         Qa[s].get(qx);
         Qb[s].get(qx + 4);
         const h8 sh = ld_h8(SSh[b] + li * WS + 32 * s + 8 * lg);
-        const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
         if constexpr (SPLIT) {
+          const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
           h8 qh, ql;
           split8(qx, qh, ql);
           o = mfma_f16(qh, sh, o);
           o2 = mfma_f16(qh, sl, o2);
           o2 = mfma_f16(ql, sh, o2);
         } else {
-          const h8 qh = to_h8(qx);
-          o = mfma_f16(qh, sh, o);
-          o2 = mfma_f16(qh, sl, o2);
+          o = mfma_f16(to_h8(qx), sh, o);
         }
       }
       o += o2;
@@ -905,10 +928,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       for (int s = 0; s < 2; ++s) {
         if (s > (w4 >> 1)) break;
         const h8 dh = ld_h8(DTh[b] + li * KTS + 32 * s + 8 * lg);
-        const h8 dlo = ld_h8(DTl[b] + li * KTS + 32 * s + 8 * lg);
         o = mfma_f16(Pfh[s], dh, o);
-        o = mfma_f16(Pfh[s], dlo, o);
-        o = mfma_f16(Pfl[s], dh, o);
+        if constexpr (SPLIT) {
+          o = mfma_f16(Pfh[s], ld_h8(DTl[b] + li * KTS + 32 * s + 8 * lg), o);
+          o = mfma_f16(Pfl[s], dh, o);
+        }
       }
       // lane holds O[token 16 w4 + 4 lg + r][e0 + li]; transpose so that each
       // lane writes four consecutive e of one token
