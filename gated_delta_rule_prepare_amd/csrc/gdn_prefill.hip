@@ -119,7 +119,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 
 // Per (chunk, value head) block, byte offsets (D = head dim):
 //   W hi [64][D] f16, W lo [64][D] f16, U^T [D][64] f32,
-//   P hi [64][64] f16, P lo [64][64] f16,
+//   P hi [64 x 64] f16, P lo [64 x 64] f16 (MFMA fragment order, p_frag),
 //   K^T hi [D][64] f16, K^T lo [D][64] f16 (written for f32 q/k/v only; K
 //   already scaled by its row scale), gamma [64], exp(G_C - G_j) [64],
 //   k row scale [64], q row scale [64] f32
@@ -277,6 +277,14 @@ __device__ __forceinline__ void store_h4_split(_Float16* hi, _Float16* lo, const
   store_h4(lo, l);
 }
 
+// P is stored in MFMA fragment order: for row block I and 32-column step s,
+// the A-operand fragments of the 64 lanes (lane li + 16 g holds row 16I + li,
+// columns 32s + 8g .. +7) are one contiguous 1 KiB run.  Offset (in halves)
+// of the four columns 16J + 4q .. +3 of row 16I + li:
+__device__ __forceinline__ int p_frag(int I, int li, int J, int q) {
+  return ((2 * I + (J >> 1)) * 64 + li + 16 * (2 * (J & 1) + (q >> 1))) * 8 + 4 * (q & 1);
+}
+
 template <typename QkvT, int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
@@ -406,9 +414,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
       if (J > wave) {
         float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (SPLIT)
-          store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, z);
+          store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), z);
         else
-          store_h4(Ph + i * kChunk + 16 * J + 4 * lg, z);
+          store_h4(Ph + p_frag(wave, li, J, lg), z);
         continue;
       }
       const float sj = kn[16 * J + li];  // scale of the K row this lane feeds as operand A
@@ -454,9 +462,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
       }
       *reinterpret_cast<float4*>(As + i * TS + 16 * J + 4 * lg) = make_float4(av[0], av[1], av[2], av[3]);
       if constexpr (SPLIT)
-        store_h4_split(Ph + i * kChunk + 16 * J + 4 * lg, Pl + i * kChunk + 16 * J + 4 * lg, pv);
+        store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), pv);
       else
-        store_h4(Ph + i * kChunk + 16 * J + 4 * lg, pv);
+        store_h4(Ph + p_frag(wave, li, J, lg), pv);
     }
   }
   __syncthreads();
@@ -670,6 +678,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
   __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T rows e0 .. e0+15
   __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk];        // exp(G_C - G_j), then gamma
+  constexpr int QEV = 16 / (int)sizeof(QkvT);   // q elements per 16-byte vector
+  constexpr int QVPR = D / QEV;                  // vectors per q row
+  constexpr int NQV = 16 * QVPR / 64;            // vectors per lane for a wave's 16 rows
+  constexpr int QS = D + QEV;                    // row stride (elements) of the staged rows
+  __shared__ __attribute__((aligned(16))) QkvT Qsm[4][16 * QS];       // each output wave's 16 q rows
 
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
@@ -713,27 +726,37 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   };
 
   // ---- output-wave operands
-  Raw4<QkvT> Qa[NKS], Qb[NKS];   // Q row 16 w4 + li at columns k(s, 0..3) and k(s, 4..7)
+  u32x4 Qraw[NQV];               // q rows 16 w4 .. 16 w4 + 15 of a chunk ahead, as stored
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
   u32x4 KTr[KTV], KTrl[SPLIT ? KTV : 1];
   u32x4 Wr[STAGE_W ? WV : 1];
   const int ot = tid - 256;      // output-wave thread index
-  auto load_qp = [&](int cid) {
-    const char* b = blk_of(cid);
-    const int rr = min(16 * w4 + li, ntok(cid) - 1);  // rows past the end re-read the last row; their scale is 0
-    const QkvT* qr = qbase + (tok0(cid) + rr) * qk_stride + 4 * lg;
+  // a wave's q rows move whole 16-byte vectors (contiguous per row) and are
+  // read back in the contraction order from its own LDS slice
+  auto load_q = [&](int cid) {
+    const int n = ntok(cid);
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      Qa[s].load(qr + 32 * s);
-      Qb[s].load(qr + 32 * s + 16);
+    for (int j = 0; j < NQV; ++j) {
+      const int v = lane + 64 * j, r = v / QVPR, c = v % QVPR;
+      const int rr = min(16 * w4 + r, n - 1);  // rows past the end re-read the last row; their scale is 0
+      Qraw[j] = *reinterpret_cast<const u32x4*>(qbase + (tok0(cid) + rr) * qk_stride + c * QEV);
     }
-    const int row = 16 * w4 + li;
+  };
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int j = 0; j < NQV; ++j) {
+      const int v = lane + 64 * j, r = v / QVPR, c = v % QVPR;
+      *reinterpret_cast<u32x4*>(Qsm[w4] + r * QS + c * QEV) = Qraw[j];
+    }
+  };
+  auto load_pv = [&](int cid) {
+    const char* b = blk_of(cid);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + row * kChunk + 32 * s + 8 * lg);
+      Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + ((2 * w4 + s) * 64 + lane) * 8);
       if constexpr (SPLIT)
-        Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + row * kChunk + 32 * s + 8 * lg);
+        Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + ((2 * w4 + s) * 64 + lane) * 8);
     }
     const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
     gmv = *reinterpret_cast<const float4*>(v + 16 * w4 + 4 * lg);
@@ -804,13 +827,16 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     load_wst(c_begin);
     load_uv(c_begin);
     load_kt(c_begin);
-    load_qp(c_begin);
+    load_q(c_begin);
+    load_pv(c_begin);
     stage_w(0);
     stage_uv(0);
     stage_kt(0);
+    stage_q();
     load_wst(min(c_begin + 1, c_end - 1));
     load_uv(min(c_begin + 1, c_end - 1));
     load_kt(min(c_begin + 1, c_end - 1));
+    load_q(min(c_begin + 1, c_end - 1));
   }
   __syncthreads();
 
@@ -905,9 +931,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
+        Raw4<QkvT> qa, qb;
+        qa.load(Qsm[w4] + li * QS + 32 * s + 4 * lg);
+        qb.load(Qsm[w4] + li * QS + 32 * s + 16 + 4 * lg);
         float qx[8];
-        Qa[s].get(qx);
-        Qb[s].get(qx + 4);
+        qa.get(qx);
+        qb.get(qx + 4);
         const h8 sh = ld_h8(SSh[b] + li * WS + 32 * s + 8 * lg);
         if constexpr (SPLIT) {
           const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
@@ -949,9 +978,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         const float vals[4] = {ov.x, ov.y, ov.z, ov.w};
         store4(obase + (tok0(cid) + i) * (int64_t)p.Hv * D + ec, vals);
       }
-      // next chunk's K^T into the other buffer; operands of the chunks ahead
+      // next chunk's K^T and q rows; operands of the chunks ahead
       stage_kt(b ^ 1);
-      load_qp(cn);
+      stage_q();
+      load_pv(cn);
+      load_q(min(cid + 2, c_end - 1));
       load_kt(min(cid + 2, c_end - 1));
     }
   }
