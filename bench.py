@@ -36,7 +36,7 @@ METRIC = "GDN prefill tokens/s + decode tokens/s; % of HBM/MFMA roofline, 1 GPU"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -93,6 +93,27 @@ def source_sha(*names):
     return h.hexdigest()[:16]
 
 
+def profile_record(name, kernel, sources):
+    """A kernel's record from a committed rocprofv3 counter summary, only if
+    the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha(*sources):
+        return None
+    return rec
+
+
+def stats_us(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"mean_us": float(a.mean()), "median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90))}
+
+
 def measured_traffic(kernel, sources):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     only if the kernel source is unchanged since the counters were taken."""
@@ -135,10 +156,29 @@ def cpu_baseline(dec, pre, threads):
                    p_inp["slots"], p_inp["has_init"], p_cfg.scale, False, "f32", "bf16", nthreads=threads)
     t_pre = (time.perf_counter() - t0) / ntok
     step = d_cfg.batch * t_dec + p_cfg.T * t_pre
+    # one thread on a smaller sample of the same work
+    n1, nt1 = 16, 128
+    t0 = time.perf_counter()
+    oracle.decode(d, d_inp["x"][:n1], d_inp["w"], d_inp["a"][:n1], d_inp["b"][:n1], d_inp["A_log"],
+                  d_inp["dt_bias"], conv[:n1], ssm[:n1], np.arange(n1, dtype=np.int32), d_cfg.scale, "f32", "bf16",
+                  nthreads=1)
+    t1_dec = (time.perf_counter() - t0) / n1
+    cu1 = np.array([0, nt1], np.int32)
+    t0 = time.perf_counter()
+    prep1 = oracle.prepare(d, cu1, p_inp["x"][:nt1], p_inp["w"], p_inp["a"][:nt1], p_inp["b"][:nt1],
+                           p_inp["A_log"], p_inp["dt_bias"], p_inp["conv_pool"], p_inp["slots"], p_inp["has_init"],
+                           True, "bf16", nthreads=1)
+    oracle.prefill(d, cu1, prep1["q"], prep1["k"], prep1["v"], prep1["g"], prep1["beta"], p_inp["ssm_pool"],
+                   p_inp["slots"], p_inp["has_init"], p_cfg.scale, False, "f32", "bf16", nthreads=1)
+    t1_pre = (time.perf_counter() - t0) / nt1
+    step1 = d_cfg.batch * t1_dec + p_cfg.T * t1_pre
     return {"value": (d_cfg.batch + p_cfg.T) / step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{nrow} decode rows + first {ntok} prefill tokens (all heads), f64 oracle; "
                       f"scaled to the step's 256 decode + 4096 prefill tokens",
-            "decode_tokens_per_s": 1.0 / t_dec, "prefill_tokens_per_s": 1.0 / t_pre}
+            "decode_tokens_per_s": 1.0 / t_dec, "prefill_tokens_per_s": 1.0 / t_pre,
+            "host_cpus": os.cpu_count(),
+            "single_thread": {"value": (d_cfg.batch + p_cfg.T) / step1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} decode rows + first {nt1} prefill tokens, scaled likewise"}}
 
 
 def main():
@@ -233,25 +273,60 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    pre_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    dec_l = [e[0].elapsed_time(e[1]) for e in ev]
+    prep_l = [e[1].elapsed_time(e[2]) for e in ev]
+    pre_l = [e[2].elapsed_time(e[3]) for e in ev]
+    dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
+
+    # untimed extras, after the timed region: a device-to-device copy of the
+    # decode call's size (second bandwidth denominator), and decode with the
+    # 256 MB Infinity Cache flushed by a 512 MiB scratch write before each call
+    half = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K) // 2 // 4
+    csrc = torch.empty(half, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(6):
+        if i:
+            cev[i - 1][0].record(stream)
+        cdst.copy_(csrc)
+        if i:
+            cev[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * half * 4 / (float(np.median([e[0].elapsed_time(e[1]) for e in cev])) * 1e-3) / 1e9
+    del csrc, cdst
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(5):
+        flush.fill_(float(i))
+        cold_ev[i][0].record(stream)
+        gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i % nsets], dout, dcfg.scale,
+                       slot_idx_host=slot_sets_h[i % nsets], stream=stream)
+        cold_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold_l = [e[0].elapsed_time(e[1]) for e in cold_ev]
+    del flush
 
     dec_b = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
     dec_gbs = dec_b / (dec_ms * 1e-3) / 1e9
     pre_b = prefill_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv)
     pre_flops = prefill_chunked_flops(T, d.Hk, d.Hv, d.Dk, d.Dv)
     prep_b = prepare_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    mfma = {k2: profile_record("mfma.json", k2, ["gdn_prefill.hip", "gdn_device.h"])
+            for k2 in ("chunk_prep_kernel", "chunk_scan_kernel")}
     kernels = {
-        "decode": {"avg_ms": dec_ms, "tokens_per_s": B / (dec_ms * 1e-3),
+        "decode": {"avg_ms": dec_ms, "tokens_per_s": B / (dec_ms * 1e-3), **stats_us(dec_l),
+                   "frac_of_copy": dec_gbs / copy_gbs,
+                   "cold_cache": {**stats_us(cold_l), "GBps": dec_b / (float(np.median(cold_l)) * 1e-3) / 1e9,
+                                  "note": "512 MiB scratch write before each call"},
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_launch": dec_b,
                                 "traffic": measured_traffic("decode_kernel", ["gdn_decode.hip", "gdn_device.h"])}},
-        "prepare": {"avg_ms": prep_ms, "tokens_per_s": T / (prep_ms * 1e-3),
+        "prepare": {"avg_ms": prep_ms, "tokens_per_s": T / (prep_ms * 1e-3), **stats_us(prep_l),
                     "roofline": {"bound": "hbm", "achieved": prep_b / (prep_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": prep_b / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                  "bytes_per_launch": prep_b}},
-        "prefill": {"avg_ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3),
+        "prefill": {"avg_ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3), **stats_us(pre_l),
+                    "mfma_counters": mfma,
                     "kernels": "chunk_table_kernel + chunk_prep_kernel + chunk_scan_kernel",
                     "roofline": {"bound": "mfma", "achieved": pre_flops / (pre_ms * 1e-3) / 1e12,
                                  "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -276,6 +351,7 @@ def main():
         "decode_tokens_per_s": kernels["decode"]["tokens_per_s"],
         "prefill_tokens_per_s": T / ((prep_ms + pre_ms) * 1e-3),
         "roofline": rl,
+        "copy_GBps": copy_gbs,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
