@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
@@ -181,6 +183,39 @@ def cpu_baseline(dec, pre, threads):
                               "sample": f"{n1} decode rows + first {nt1} prefill tokens, scaled likewise"}}
 
 
+def extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout, scale, stream, nsets):
+    """After the timed region: a device-to-device copy of the decode call's
+    size (read + write bytes / time), and decode with the 256 MB Infinity
+    Cache flushed by a 512 MiB scratch write before each call."""
+    dev = dx.device
+    B = dx.shape[0]
+    half = decode_bytes(B, gd.Hk, gd.Hv, gd.Dk, gd.Dv, gd.K) // 2 // 4
+    csrc = torch.empty(half, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(6):
+        if i:
+            cev[i - 1][0].record(stream)
+        cdst.copy_(csrc)
+        if i:
+            cev[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * half * 4 / (float(np.median([e[0].elapsed_time(e[1]) for e in cev])) * 1e-3) / 1e9
+    del csrc, cdst
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(5):
+        flush.fill_(float(i))
+        cold_ev[i][0].record(stream)
+        gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i % nsets], dout, scale,
+                       slot_idx_host=slot_sets_h[i % nsets], stream=stream)
+        cold_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold_l = [e[0].elapsed_time(e[1]) for e in cold_ev]
+    del flush
+    return copy_gbs, cold_l
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,33 +313,11 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    # untimed extras, after the timed region: a device-to-device copy of the
-    # decode call's size (second bandwidth denominator), and decode with the
-    # 256 MB Infinity Cache flushed by a 512 MiB scratch write before each call
-    half = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K) // 2 // 4
-    csrc = torch.empty(half, dtype=torch.float32, device=dev).fill_(1.0)
-    cdst = torch.empty_like(csrc)
-    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-    for i in range(6):
-        if i:
-            cev[i - 1][0].record(stream)
-        cdst.copy_(csrc)
-        if i:
-            cev[i - 1][1].record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * half * 4 / (float(np.median([e[0].elapsed_time(e[1]) for e in cev])) * 1e-3) / 1e9
-    del csrc, cdst
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
-    for i in range(5):
-        flush.fill_(float(i))
-        cold_ev[i][0].record(stream)
-        gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i % nsets], dout, dcfg.scale,
-                       slot_idx_host=slot_sets_h[i % nsets], stream=stream)
-        cold_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    cold_l = [e[0].elapsed_time(e[1]) for e in cold_ev]
-    del flush
+    copy_gbs, cold_l = None, None
+    if not args.no_extras:
+        copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
+                                  dcfg.scale, stream, nsets)
+
 
     dec_b = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
     dec_gbs = dec_b / (dec_ms * 1e-3) / 1e9
@@ -315,9 +328,9 @@ def main():
             for k2 in ("chunk_prep_kernel", "chunk_scan_kernel")}
     kernels = {
         "decode": {"avg_ms": dec_ms, "tokens_per_s": B / (dec_ms * 1e-3), **stats_us(dec_l),
-                   "frac_of_copy": dec_gbs / copy_gbs,
+                   "frac_of_copy": dec_gbs / copy_gbs if copy_gbs else None,
                    "cold_cache": {**stats_us(cold_l), "GBps": dec_b / (float(np.median(cold_l)) * 1e-3) / 1e9,
-                                  "note": "512 MiB scratch write before each call"},
+                                  "note": "512 MiB scratch write before each call"} if cold_l else None,
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_launch": dec_b,
                                 "traffic": measured_traffic("decode_kernel", ["gdn_decode.hip", "gdn_device.h"])}},

@@ -162,6 +162,8 @@ gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tok
   if (!aligned16(mixed_qkv) || (mixed_row_stride * (int64_t)dtype_size(act_dtype)) % 16 != 0 ||
       !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: mixed_qkv rows and q/k/v outputs must be 16-byte aligned", fn);
+  if (!aligned16(conv_weight) || (K > 1 && !aligned16(conv_state_pool)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: the conv weight and conv-history pool must be 16-byte aligned", fn);
   if ((slot_idx_host == nullptr) != (slot_idx_dev == nullptr))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: pass both slot index copies or neither", fn);
   if (K > 1) {

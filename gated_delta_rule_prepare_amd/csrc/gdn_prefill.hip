@@ -323,17 +323,44 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
   const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
   const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
 
-  // all loads first: K^T / V^T tiles, this wave's K and Q row fragments, the gates
+  // All loads first: the K and V tiles, this wave's Q row fragments, the
+  // gates.  With bf16 inputs the K and V rows are read whole (contiguous
+  // 16-byte vectors) into row-major LDS tiles that borrow the T and A
+  // buffers (not yet in use), and the K row fragments and the transposed
+  // tiles are formed from there; with f32 inputs the tiles are read in the
+  // transposed pattern and the fragments straight from memory.
+  constexpr bool STAGE = !SPLIT;
+  constexpr int RS = D + 8;  // row stride (elements) of the staged rows
+  static_assert(!STAGE || kChunk * RS * 2 <= kChunk * TS * 4, "staged rows fit the A / T buffers");
+  QkvT* Ks = reinterpret_cast<QkvT*>(Ts);
+  QkvT* Vs = reinterpret_cast<QkvT*>(As);
   TransposedTile<QkvT, D> ktile, vtile;
-  ktile.load(kp, qk_stride, n);
-  vtile.load(vp, v_stride, n);
   Raw8<QkvT> kf[4][NKS], qf[NKS];
+  if constexpr (STAGE) {
+    constexpr int VPR = D / 8, NV = kChunk * VPR / 256;
+    u32x4 kr[NV], vr[NV];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    if (J > wave) break;
-    const int rr = min(16 * J + li, n - 1);
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      kr[j] = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
+      vr[j] = *reinterpret_cast<const u32x4*>(vp + rr * v_stride + 8 * c);
+    }
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + 256 * j, r = v / VPR, c = v % VPR;
+      *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = kr[j];
+      *reinterpret_cast<u32x4*>(Vs + r * RS + 8 * c) = vr[j];
+    }
+  } else {
+    ktile.load(kp, qk_stride, n);
+    vtile.load(vp, v_stride, n);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > wave) break;
+      const int rr = min(16 * J + li, n - 1);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
+    }
   }
   {
     const int rr = min(16 * wave + li, n - 1);
@@ -345,6 +372,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
   // keeps the running sums finite when g = -inf
   const float graw = fmaxf(p.g[(t0 + gt) * p.Hv + h], -200.0f);
   const float braw = p.beta[(t0 + gt) * p.Hv + h];
+  if constexpr (STAGE) {
+    __syncthreads();
+    // rows past the end hold the last row again (their scale is 0)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > wave) break;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) kf[J][s].load(Ks + (16 * J + li) * RS + 32 * s + 8 * lg);
+    }
+  }
 
   // row scales of this wave's block: 1/sqrt(|row|^2 + 1e-6) with the L2 norm, else 1; zero past the end
   const int row = 16 * wave + li;
@@ -401,8 +438,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     dc_g[lane] = expf((float)(Glast - G));
   }
   __syncthreads();
+  if constexpr (STAGE) {
+    ktile.load(Ks, RS, n);
+    vtile.load(Vs, RS, n);
+  }
   ktile.store(KTh, KTl, kn, n);
   vtile.store(VTh, VTl, nullptr, n);
+  if constexpr (STAGE) __syncthreads();  // V rows are read before A overwrites them
 
   // (K_J K_w^T) and (K_J Q_w^T): lane holds row i = 16w + li, columns j = 16J + 4lg + r
   {

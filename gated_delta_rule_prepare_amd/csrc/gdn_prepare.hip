@@ -85,12 +85,24 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   };
   load_block(bufA, t0);
 
-  // taps: wt[j][i] multiplies the input K-1-j tokens back, channel c+i
+  // taps: wt[j][i] multiplies the input K-1-j tokens back, channel c+i.
+  // A lane's V channels hold V*K consecutive weights: K 16-byte words.
   float wt[K][V];
+  {
+    float wf[K * V];
+    if (active) {
+      const uint4* wp = reinterpret_cast<const uint4*>(w + (int64_t)c * K);
 #pragma unroll
-  for (int i = 0; i < V; ++i)
+      for (int j = 0; j < K; ++j) Elem<ActT>::unpack(wp[j], wf + j * V);
+    } else {
 #pragma unroll
-    for (int j = 0; j < K; ++j) wt[j][i] = active ? Elem<ActT>::load(w + (int64_t)(c + i) * K + j) : 0.0f;
+      for (int e = 0; e < K * V; ++e) wf[e] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) wt[j][i] = wf[i * K + j];
+  }
 
   // win[j][i]: raw input j+1 tokens back
   float win[H][V];
@@ -98,14 +110,31 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   int64_t seq_start = p.cu[s];
   int64_t seq_end = p.cu[s + 1];
 
-  // history value d tokens before the start of sequence s (1 <= d <= K-1)
-  auto hist_at = [&](int seq, int d, int i) -> float {
-    const bool has = p.has_init == nullptr || p.has_init[seq] != 0;
-    if (!has || !active) return 0.0f;
-    const int slot = p.slots ? p.slots[seq] : seq;
-    return Elem<ActT>::load(hist + ((int64_t)slot * p.Cc + c + i) * (K - 1) + (K - 1 - d));
+  // the history of sequence seq for this lane's channels: hw[d-1][i] is the
+  // input d tokens before the sequence start (1 <= d <= K-1), zero without
+  // an initial state.  A lane's V channels hold (K-1)*V consecutive
+  // history values: K-1 16-byte words.
+  auto hist_window = [&](int seq, float (&hw)[H][V]) {
+    float hf[H * V];
+    const bool has = active && (p.has_init == nullptr || p.has_init[seq] != 0);
+    if (has) {
+      const int slot = p.slots ? p.slots[seq] : seq;
+      const uint4* hp = reinterpret_cast<const uint4*>(hist + ((int64_t)slot * p.Cc + c) * (K - 1));
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) Elem<ActT>::unpack(hp[j], hf + j * V);
+    } else {
+#pragma unroll
+      for (int e = 0; e < H * V; ++e) hf[e] = 0.0f;
+    }
+    // channel c+i's history column m holds the input K-1-m tokens back
+#pragma unroll
+    for (int d = 1; d <= K - 1; ++d)
+#pragma unroll
+      for (int i = 0; i < V; ++i) hw[d - 1][i] = hf[i * (K - 1) + (K - 1 - d)];
   };
   if constexpr (K > 1) {
+    float hw[H][V];
+    if (t0 - (K - 1) < seq_start) hist_window(s, hw);
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
       const int64_t tp = t0 - 1 - j;
@@ -115,8 +144,12 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
 #pragma unroll
           for (int i = 0; i < V; ++i) win[j][i] = 0.0f;
       } else {
+        const int d = (int)(seq_start - tp);  // 1 <= d <= K-1
 #pragma unroll
-        for (int i = 0; i < V; ++i) win[j][i] = hist_at(s, (int)(seq_start - tp), i);
+        for (int dd = 1; dd <= K - 1; ++dd)
+          if (dd == d)
+#pragma unroll
+            for (int i = 0; i < V; ++i) win[j][i] = hw[dd - 1][i];
       }
     }
   }
@@ -132,6 +165,27 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
     out_base = static_cast<QkvT*>(p.v); out_row = (int64_t)p.Hv * p.Dv; out_col = c - 2 * key_dim;
   }
 
+  // sum over the lanes of one q/k head (head_lanes a power of two <= 32):
+  // a fixed butterfly whose steps wider than the head add nothing
+  auto head_sum = [&](float v) {
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+      const float o = __shfl_xor(v, off, 64);
+      v += off < head_lanes ? o : 0.0f;
+    }
+    return v;
+  };
+  auto store_row = [&](int64_t t, const float* y) {
+    if (!active) return;
+    QkvT* dst = out_base + t * out_row + out_col;
+    if constexpr (OW >= 1) {
+#pragma unroll
+      for (int o = 0; o < OW; ++o)
+        store_stream(dst + o * Elem<QkvT>::kVec, Elem<QkvT>::pack(y + o * Elem<QkvT>::kVec));
+    } else {
+      store_n<QkvT, V>(dst, y);
+    }
+  };
   auto process = [&](const uint4* buf, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
@@ -141,12 +195,7 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
         ++s;
         seq_start = t;
         seq_end = p.cu[s + 1];
-        if constexpr (K > 1) {
-#pragma unroll
-          for (int j = 0; j < K - 1; ++j)
-#pragma unroll
-            for (int i = 0; i < V; ++i) win[j][i] = hist_at(s, j + 1, i);
-        }
+        if constexpr (K > 1) hist_window(s, win);
       }
       float xv[V];
       Elem<ActT>::unpack(buf[u], xv);
@@ -160,24 +209,12 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
         y[i] = silu_f(acc);
         ss += y[i] * y[i];
       }
-      if (p.l2norm) {
-        for (int off = head_lanes >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if (region < 2) {
-          const float inv = 1.0f / sqrtf(ss + 1e-6f);
+      if (p.l2norm && region < 2) {
+        const float inv = __builtin_amdgcn_rsqf(head_sum(ss) + 1e-6f);
 #pragma unroll
-          for (int i = 0; i < V; ++i) y[i] *= inv;
-        }
+        for (int i = 0; i < V; ++i) y[i] *= inv;
       }
-      if (active) {
-        QkvT* dst = out_base + t * out_row + out_col;
-        if constexpr (OW >= 1) {
-#pragma unroll
-          for (int o = 0; o < OW; ++o)
-            store_stream(dst + o * Elem<QkvT>::kVec, Elem<QkvT>::pack(y + o * Elem<QkvT>::kVec));
-        } else {
-          store_n<QkvT, V>(dst, y);
-        }
-      }
+      store_row(t, y);
       if constexpr (K > 1) {
 #pragma unroll
         for (int j = K - 2; j > 0; --j)
