@@ -60,8 +60,9 @@ def _load():
     lib.gdn_oracle_recurrence.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i32, f64,
                                           P, P, P, P, i32]
     lib.gdn_oracle_round.argtypes = [P, P, i64, i32]
+    lib.gdn_oracle_gated_rmsnorm.argtypes = [i64, i32, P, P, P, f64, i32, P]
     for fn in (lib.gdn_oracle_conv_silu, lib.gdn_oracle_split_l2, lib.gdn_oracle_gates,
-               lib.gdn_oracle_recurrence, lib.gdn_oracle_round):
+               lib.gdn_oracle_recurrence, lib.gdn_oracle_round, lib.gdn_oracle_gated_rmsnorm):
         fn.restype = None
     _lib = lib
     return lib
@@ -88,6 +89,21 @@ def round_to(x, dtype: str) -> np.ndarray:
     y = np.empty_like(x)
     _load().gdn_oracle_round(_ptr(x), _ptr(y), x.size, _DTYPE_CODE[dtype])
     return y
+
+
+def gated_rmsnorm(x, z, w, eps: float, sigmoid_gate: bool = False) -> np.ndarray:
+    """Gated RMS norm over the last axis: x / sqrt(mean(x^2) + eps) * w * act(z),
+    act = silu (or the logistic function).  x and z have the same shape
+    [..., D]; w is [D].  [P1] RmsNormGatedKernel; [P3] gated_rms_norm_f32."""
+    x = _f64(x)
+    z = _f64(z)
+    w = _f64(w)
+    D = x.shape[-1]
+    assert z.shape == x.shape and w.shape == (D,)
+    out = np.empty_like(x)
+    _load().gdn_oracle_gated_rmsnorm(x.size // D, D, _ptr(x), _ptr(z), _ptr(w), float(eps), int(sigmoid_gate),
+                                     _ptr(out))
+    return out
 
 
 def conv_silu(x, w, cu, hist, has_init, nthreads: Optional[int] = None):

@@ -256,6 +256,31 @@ void gdn_oracle_recurrence(int Hk, int Hv, int Dk, int Dv, int N, const int32_t*
 }
 
 /* ---------------------------------------------------------------------- */
+/* Gated RMS norm of the output, the layer's epilogue.  For each row r of  */
+/* D values (one (token, value head) pair):                                */
+/*   out[r][j] = x[r][j] / sqrt(ms + eps) * w[j] * act(z[r][j]),           */
+/*   ms = (sum_j x[r][j]^2) / D,                                           */
+/* act = silu, or the logistic function when sigmoid_gate is set: the norm */
+/* is taken before the gate, with one group per row.  [P1]                 */
+/* RmsNormGatedKernel; [P3] gated_rms_norm_f32.  x, z and out are dense    */
+/* [rows][D]; the caller lays the gate out from wherever it lives.         */
+/* ---------------------------------------------------------------------- */
+void gdn_oracle_gated_rmsnorm(int64_t rows, int D, const double* x, const double* z, const double* w,
+                              double eps, int sigmoid_gate, double* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* xr = x + r * D;
+    const double* zr = z + r * D;
+    double sumsq = 0.0;
+    for (int j = 0; j < D; ++j) sumsq += xr[j] * xr[j];
+    const double inv = 1.0 / sqrt(sumsq / (double)D + eps);
+    for (int j = 0; j < D; ++j) {
+      const double act = sigmoid_gate ? sigmoid(zr[j]) : silu(zr[j]);
+      out[r * D + j] = xr[j] * inv * w[j] * act;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Rounding to a storage dtype, round-to-nearest-even, straight from the   */
 /* double value (no intermediate float).  [P1] LoadF32/StoreF32 round at   */
 /* every store; [P2] GatherStateF32/ScatterStateF32 round the compressed   */

@@ -356,3 +356,63 @@ def test_round_bf16_hand_values():
     bits = x32.view(np.uint32).astype(np.uint64)
     ref = (((bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)).view(np.float32)
     np.testing.assert_array_equal(oracle.round_to(x32, "bf16"), ref.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Gated RMS norm of the output (vllm.cpp cpu_ops.cpp, RmsNormGatedKernel;
+# ferrum-kernels cpu.rs, gated_rms_norm_f32)
+# ---------------------------------------------------------------------------
+def _zval(s):
+    return {"0": 0.0, "ln3": np.log(3.0)}[s]
+
+
+def test_golden_gated_rmsnorm():
+    fx = json.load(open(os.path.join(GOLDEN, "worked_gated_rmsnorm.json")))
+    for c in fx["cases"]:
+        x = np.array([c["x"]], np.float64)
+        z = np.array([[_zval(v) for v in c["z"]]])
+        out = oracle.gated_rmsnorm(x, z, np.array(c["w"], np.float64), c["eps"], c["sigmoid_gate"])
+        np.testing.assert_allclose(out[0], c["expected"], rtol=1e-14, atol=1e-15)
+
+
+def test_gated_rmsnorm_rows_have_unit_rms_before_gate():
+    # with eps = 0 the normalised row x / rms(x) has mean square exactly 1:
+    # fixes the mean (not the sum) and the square root
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(5, 3, 48)) * rng.uniform(0.1, 10.0, size=(5, 3, 1))
+    z = rng.normal(size=x.shape)
+    w = rng.uniform(0.5, 2.0, size=48)
+    out = oracle.gated_rmsnorm(x, z, w, 0.0)
+    unit = out / (w * z / (1.0 + np.exp(-z)))
+    np.testing.assert_allclose(np.mean(unit * unit, axis=-1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(unit * np.sqrt(np.mean(x * x, axis=-1, keepdims=True)), x, rtol=1e-12)
+
+
+def test_gated_rmsnorm_eps_inside_the_root_is_homogeneous():
+    # x / sqrt(mean(x^2) + eps) is unchanged by x -> c x, eps -> c^2 eps only
+    # when eps sits inside the root next to the mean
+    rng = np.random.default_rng(8)
+    x = rng.normal(size=(4, 2, 32))
+    z = rng.normal(size=x.shape)
+    w = rng.normal(size=32)
+    a = oracle.gated_rmsnorm(x, z, w, 0.3)
+    b = oracle.gated_rmsnorm(5.0 * x, z, w, 0.3 * 25.0)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    c = oracle.gated_rmsnorm(5.0 * x, z, w, 0.3)
+    assert np.max(np.abs(c - a)) > 1e-3  # the eps term is not scale-free on its own
+
+
+def test_gated_rmsnorm_gate_and_weight_act_per_column():
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(3, 16))
+    z = rng.normal(size=x.shape)
+    # a zero gate gives zero under silu and half the normalised value under sigmoid
+    w = rng.normal(size=16)
+    assert np.all(oracle.gated_rmsnorm(x, np.zeros_like(x), w, 1e-6) == 0.0)
+    half = oracle.gated_rmsnorm(x, np.zeros_like(x), w, 0.0, sigmoid_gate=True)
+    np.testing.assert_allclose(half, 0.5 * w * x / np.sqrt(np.mean(x * x, -1, keepdims=True)), rtol=1e-12)
+    # a one-hot weight keeps exactly one column
+    e = np.zeros(16)
+    e[5] = 1.0
+    out = oracle.gated_rmsnorm(x, z, e, 1e-6)
+    assert np.all(out[:, np.arange(16) != 5] == 0.0) and np.all(out[:, 5] != 0.0)
