@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--epilogue-only", action="store_true",
+                    help="only run the output epilogue kernels (fused gated decode, standalone gated RMS norm)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -216,6 +218,70 @@ def extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot
     return copy_gbs, cold_l
 
 
+def gated_decode_bytes(B, Hk, Hv, Dk, Dv, K, act_bytes=2):
+    """gdn_decode bytes plus the gate (B*Hv*Dv) and the norm weight (Dv)."""
+    return decode_bytes(B, Hk, Hv, Dk, Dv, K) + B * Hv * Dv * act_bytes + Dv * act_bytes
+
+
+def gated_norm_bytes(T, Hv, Dv, io_bytes=2):
+    """gdn_gated_rmsnorm bytes: x, z read, out written, the weight once."""
+    return 3 * T * Hv * Dv * io_bytes + Dv * io_bytes
+
+
+def epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, scale, stream, T,
+             reps=10):
+    """The output epilogue (gated RMS norm) at the step's shapes: fused into
+    decode over the 256 rows, and standalone over the 4096-token prefill
+    output.  HIP events on the kernels' stream, median of ``reps`` calls."""
+    dev = dx.device
+    B = dx.shape[0]
+    HvDv = gd.Hv * gd.Dv
+    g = torch.Generator(device=dev)
+    g.manual_seed(91)
+    zd = torch.randn(B, HvDv, device=dev, generator=g).to(torch.bfloat16)
+    wn = (torch.rand(gd.Dv, device=dev, generator=g) + 0.5).to(torch.bfloat16)
+    outd = torch.empty(B, gd.Hv, gd.Dv, device=dev, dtype=torch.bfloat16)
+    xp = torch.randn(T, gd.Hv, gd.Dv, device=dev, generator=g).to(torch.bfloat16)
+    zp = torch.randn(T, HvDv, device=dev, generator=g).to(torch.bfloat16)
+    outp = torch.empty_like(xp)
+    # plain and fused decode alternate on the same slot sets, so their times compare like for like
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(reps)]
+    n = len(slot_sets)
+    for i in range(reps + 2):
+        e = ev[i - 2] if i >= 2 else None
+        if e:
+            e[0].record(stream)
+        gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i % n], outd, scale,
+                       slot_idx_host=slot_sets_h[i % n], stream=stream)
+        if e:
+            e[1].record(stream)
+            e[2].record(stream)
+        gdn.gdn_decode_gated(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[(i + 1) % n], zd, wn, outd, scale,
+                             1e-6, slot_idx_host=slot_sets_h[(i + 1) % n], stream=stream)
+        if e:
+            e[3].record(stream)
+            e[4].record(stream)
+        gdn.gdn_gated_rmsnorm(xp, zp, wn, outp, 1e-6, stream=stream)
+        if e:
+            e[5].record(stream)
+    torch.cuda.synchronize()
+    dp = [e[0].elapsed_time(e[1]) for e in ev]
+    dg = [e[2].elapsed_time(e[3]) for e in ev]
+    nm = [e[4].elapsed_time(e[5]) for e in ev]
+    db_ = gated_decode_bytes(B, gd.Hk, gd.Hv, gd.Dk, gd.Dv, gd.K)
+    nb = gated_norm_bytes(T, gd.Hv, gd.Dv)
+    gbs = lambda b, l: b / (float(np.median(l)) * 1e-3) / 1e9
+    return {
+        "decode_gated": {**stats_us(dg), "bytes_per_launch": db_,
+                         "plain_decode_same_loop": stats_us(dp),
+                         "roofline": {"bound": "hbm", "achieved": gbs(db_, dg), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": gbs(db_, dg) / HBM_PEAK_GBS}},
+        "gated_rmsnorm_T4096": {**stats_us(nm), "bytes_per_launch": nb,
+                                "roofline": {"bound": "hbm", "achieved": gbs(nb, nm), "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": gbs(nb, nm) / HBM_PEAK_GBS}},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +365,11 @@ def main():
         if rec is not None:
             rec[3].record(stream)
 
+    if args.epilogue_only:
+        ep = epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dcfg.scale, stream,
+                      T, reps=args.steps)
+        print(json.dumps({"epilogue": ep}), flush=True)
+        return
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -313,8 +384,10 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l = None, None
+    copy_gbs, cold_l, epi = None, None, None
     if not args.no_extras:
+        epi = epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dcfg.scale,
+                       stream, T)
         copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
                                   dcfg.scale, stream, nsets)
 
@@ -365,6 +438,7 @@ def main():
         "prefill_tokens_per_s": T / ((prep_ms + pre_ms) * 1e-3),
         "roofline": rl,
         "copy_GBps": copy_gbs,
+        "epilogue": epi,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

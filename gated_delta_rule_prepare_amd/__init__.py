@@ -5,7 +5,8 @@ kernels behind the C ABI declared in ``include/gdn.h``.  PyTorch supplies
 device memory and the current HIP stream.  If the library is not built, the
 first call raises; there is no fallback path.
 
-Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`,
+Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`, :func:`gdn_decode_gated`,
+:func:`gdn_gated_rmsnorm`,
 :func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
 """
 from __future__ import annotations
@@ -55,8 +56,8 @@ class Dims:
 
 
 _lib = None
-EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_prefill_varlen", "gdn_prefill_workspace_size",
-           "gdn_status_string", "gdn_last_error", "gdn_version")
+EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_prefill_varlen", "gdn_prefill_workspace_size",
+           "gdn_gated_rmsnorm", "gdn_status_string", "gdn_last_error", "gdn_version")
 
 
 def load_library():
@@ -73,11 +74,14 @@ def load_library():
     lib.gdn_prepare.argtypes = [D, i32, i64, P, P, P, i64, P, i64, P, i64, i32, P, P, P, P, i32, P, P, P, i32,
                                 P, P, P, i32, P, P, P]
     lib.gdn_decode.argtypes = [D, i32, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, P, P, f32, P, P]
+    lib.gdn_decode_gated.argtypes = [D, i32, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, P, P, f32,
+                                     P, i64, P, f32, i32, P, P]
+    lib.gdn_gated_rmsnorm.argtypes = [i32, i32, i32, P, P, i64, P, f32, i32, P, i32, P]
     lib.gdn_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32, i32,
                                        i32, P, P, sz, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
     lib.gdn_prefill_workspace_size.restype = sz
-    for fn in ("gdn_prepare", "gdn_decode", "gdn_prefill_varlen"):
+    for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_prefill_varlen", "gdn_gated_rmsnorm"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -159,6 +163,39 @@ def gdn_decode(dims: Dims, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias,
                         _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
                         _ptr(slot_idx), _hptr(sl_h), float(scale), _ptr(out), _stream(stream))
     _check("gdn_decode", st)
+
+
+def gdn_decode_gated(dims: Dims, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias, conv_state_pool,
+                     ssm_state_pool, slot_idx, z, norm_weight, out, scale: float, eps: float,
+                     sigmoid_gate: bool = False, slot_idx_host=None, validate: bool = True, stream=None) -> None:
+    """gdn_decode with the gated RMS norm epilogue fused.  ``z`` is a 2-D
+    view [B, >= Hv*Dv] with unit column stride (for example the z columns of
+    a packed [q|k|v|z] row); row b head h sits at z[b, h*Dv:(h+1)*Dv]."""
+    lib = load_library()
+    sl_h = None
+    if validate:
+        sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    if z.stride(-1) != 1:
+        raise ValueError("z must have unit column stride")
+    st = lib.gdn_decode_gated(ctypes.byref(dims.c()), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
+                              _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0), _dtype_code(mixed_qkv),
+                              _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_pool),
+                              _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
+                              _ptr(slot_idx), _hptr(sl_h), float(scale), _ptr(z), z.stride(0), _ptr(norm_weight),
+                              float(eps), int(bool(sigmoid_gate)), _ptr(out), _stream(stream))
+    _check("gdn_decode_gated", st)
+
+
+def gdn_gated_rmsnorm(x, z, weight, out, eps: float, sigmoid_gate: bool = False, stream=None) -> None:
+    """Gated RMS norm of the output rows: x and out [T, Hv, Dv]; ``z`` a 2-D
+    view [T, >= Hv*Dv] with unit column stride; weight [Dv].  out may be x."""
+    lib = load_library()
+    if z.stride(-1) != 1:
+        raise ValueError("z must have unit column stride")
+    T, Hv, Dv = x.shape
+    st = lib.gdn_gated_rmsnorm(T, Hv, Dv, _ptr(x), _ptr(z), z.stride(0), _ptr(weight), float(eps),
+                               int(bool(sigmoid_gate)), _ptr(out), _dtype_code(x), _stream(stream))
+    _check("gdn_gated_rmsnorm", st)
 
 
 def gdn_prefill_workspace_size(dims: Dims, num_seqs: int, total_tokens: int, chunk_size: int = 64) -> int:

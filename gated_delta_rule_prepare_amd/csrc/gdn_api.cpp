@@ -128,7 +128,7 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 110; }
 
 gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -189,14 +189,25 @@ gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tok
   return launched(fn, gdn::launch_prepare(p, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
-                      int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
-                      const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
-                      const void* conv_weight, const float* A_log, const float* dt_bias,
-                      void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
-                      int32_t num_slots, const int32_t* slot_idx_dev,
-                      const int32_t* slot_idx_host, float scale, void* out, void* stream) {
-  const char* fn = "gdn_decode";
+namespace {
+
+struct GateArgs {
+  const void* z;
+  int64_t z_row_stride;
+  const void* weight;
+  float eps;
+  int32_t sigmoid_gate;
+};
+
+bool good_eps(float eps) { return eps == eps && eps >= 0.0f && eps <= 3.0e38f; }
+
+gdn_status decode_common(const char* fn, const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
+                         int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
+                         const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
+                         const void* conv_weight, const float* A_log, const float* dt_bias,
+                         void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
+                         int32_t num_slots, const int32_t* slot_idx_dev, const int32_t* slot_idx_host,
+                         float scale, const GateArgs* gate, void* out, void* stream) {
   gdn_status st = check_dims(fn, dims);
   if (st != GDN_OK) return st;
   if (batch < 0) return fail(GDN_ERR_SHAPE, "%s: negative batch %d", fn, batch);
@@ -222,6 +233,14 @@ gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv
     if (st != GDN_OK) return st;
   }
   if (!(scale == scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
+  if (gate) {
+    if (!gate->z || !gate->weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a required pointer is null", fn);
+    if (gate->z_row_stride < (int64_t)dims->num_v_heads * dims->head_v_dim)
+      return fail(GDN_ERR_SHAPE, "%s: z_row_stride %lld below Hv*Dv", fn, (long long)gate->z_row_stride);
+    if (!good_eps(gate->eps)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    if (gate->sigmoid_gate != 0 && gate->sigmoid_gate != 1)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: sigmoid_gate must be 0 or 1", fn);
+  }
 
   gdn::DecodeParams p{};
   p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.Dk = dims->head_k_dim; p.Dv = dims->head_v_dim;
@@ -229,8 +248,68 @@ gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv
   p.a_stride = a_row_stride; p.b = b_raw; p.b_stride = b_row_stride; p.w = conv_weight; p.A_log = A_log;
   p.dt_bias = dt_bias; p.conv_pool = conv_state_pool; p.ssm_pool = ssm_state_pool; p.num_slots = num_slots;
   p.slots = slot_idx_dev; p.scale = scale; p.out = out; p.act = act_dtype; p.state = state_dtype;
+  if (gate) {
+    p.gated = 1; p.gz = gate->z; p.gz_stride = gate->z_row_stride; p.gw = gate->weight; p.geps = gate->eps;
+    p.gsig = gate->sigmoid_gate;
+  }
   return launched(fn, gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
+                      int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
+                      const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
+                      const void* conv_weight, const float* A_log, const float* dt_bias,
+                      void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
+                      int32_t num_slots, const int32_t* slot_idx_dev,
+                      const int32_t* slot_idx_host, float scale, void* out, void* stream) {
+  return decode_common("gdn_decode", dims, batch, mixed_qkv, mixed_row_stride, a_raw, a_row_stride, b_raw,
+                       b_row_stride, act_dtype, conv_weight, A_log, dt_bias, conv_state_pool, ssm_state_pool,
+                       state_dtype, num_slots, slot_idx_dev, slot_idx_host, scale, nullptr, out, stream);
+}
+
+gdn_status gdn_decode_gated(const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
+                            int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
+                            const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
+                            const void* conv_weight, const float* A_log, const float* dt_bias,
+                            void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
+                            int32_t num_slots, const int32_t* slot_idx_dev,
+                            const int32_t* slot_idx_host, float scale, const void* z,
+                            int64_t z_row_stride, const void* norm_weight, float eps,
+                            int32_t sigmoid_gate, void* out, void* stream) {
+  const GateArgs gate{z, z_row_stride, norm_weight, eps, sigmoid_gate};
+  return decode_common("gdn_decode_gated", dims, batch, mixed_qkv, mixed_row_stride, a_raw, a_row_stride,
+                       b_raw, b_row_stride, act_dtype, conv_weight, A_log, dt_bias, conv_state_pool,
+                       ssm_state_pool, state_dtype, num_slots, slot_idx_dev, slot_idx_host, scale, &gate, out,
+                       stream);
+}
+
+gdn_status gdn_gated_rmsnorm(int32_t num_tokens, int32_t num_heads, int32_t head_dim, const void* x,
+                             const void* z, int64_t z_row_stride, const void* weight, float eps,
+                             int32_t sigmoid_gate, void* out, gdn_dtype io_dtype, void* stream) {
+  const char* fn = "gdn_gated_rmsnorm";
+  if (num_tokens < 0 || num_heads <= 0)
+    return fail(GDN_ERR_SHAPE, "%s: bad sizes T=%d Hv=%d", fn, num_tokens, num_heads);
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(GDN_ERR_SHAPE, "%s: head_dim must be 16, 32, 64, 128 or 256, got %d", fn, head_dim);
+  if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "%s: io dtype must be f32 or bf16", fn);
+  if (num_tokens == 0) return ok();
+  if (!x || !z || !weight || !out) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a required pointer is null", fn);
+  if (z_row_stride < (int64_t)num_heads * head_dim)
+    return fail(GDN_ERR_SHAPE, "%s: z_row_stride %lld below Hv*Dv", fn, (long long)z_row_stride);
+  if (!aligned16(x) || !aligned16(z) || !aligned16(weight) || !aligned16(out) ||
+      (z_row_stride * (int64_t)dtype_size(io_dtype)) % 16 != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, z rows, weight and out must be 16-byte aligned", fn);
+  if (!good_eps(eps)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (sigmoid_gate != 0 && sigmoid_gate != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: sigmoid_gate must be 0 or 1", fn);
+  gdn::GatedNormParams p{};
+  p.T = num_tokens; p.H = num_heads; p.D = head_dim; p.x = x; p.z = z; p.z_stride = z_row_stride; p.w = weight;
+  p.eps = eps; p.sig = sigmoid_gate; p.out = out; p.io = io_dtype;
+  return launched(fn, gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream)));
+}
+
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                                   int32_t chunk_size) {

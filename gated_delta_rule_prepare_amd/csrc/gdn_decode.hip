@@ -20,6 +20,13 @@
 //   S' = d S + delta k
 // which is the token step written so that the row is read once and written
 // once.  Value rows are independent, so rows need no synchronisation.
+//
+// With the output epilogue (gdn_decode_gated) the outputs stay in LDS,
+// rounded as they would be stored, and after the stream each wave applies
+// the gated RMS norm to one value head: the workgroup owns all Dv outputs of
+// its heads.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -41,7 +48,14 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kLoads = 4;  // 16-byte state loads per lane per batch (two batches in flight)
 
-template <typename ActT, typename StT, int DK>
+// value as stored in ActT and read back
+template <typename ActT>
+__device__ __forceinline__ float round_act(float v) {
+  if constexpr (std::is_same<ActT, float>::value) return v;
+  else return bf16_to_f32(f32_to_bf16(v));
+}
+
+template <typename ActT, typename StT, int DK, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
   constexpr int SV = Elem<StT>::kVec;       // state elements per lane load
   constexpr int LPR = DK / SV;              // lanes per state row
@@ -84,6 +98,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
   float* s_decay = smem + 2 * DK + R;     // [r]
   float* s_beta = s_decay + r;            // [r]
   float* s_red = s_beta + r;              // [4]: 1/|q|, 1/|k|, k.q
+  float* s_o = s_red + 4;                 // [R] with the epilogue: o as stored in ActT
+  float* s_z = s_o + R;                   // [R] with the epilogue: the gate of this row's heads
+  float* s_w = s_z + R;                   // [Dv] with the epilogue: the norm weight
   const int K = p.K;
   const ActT* __restrict__ x = static_cast<const ActT*>(p.x) + (int64_t)b * p.x_stride;
   const ActT* __restrict__ w = static_cast<const ActT*>(p.w);
@@ -110,6 +127,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
       Elem<ActT>::store(h + (K - 2), xv);
     }
     s_y[ch] = silu_f(acc);
+  }
+  if constexpr (GATED) {
+    // the epilogue's operands, read now so that their latency hides behind the stream
+    const ActT* zr = static_cast<const ActT*>(p.gz) + (int64_t)b * p.gz_stride + (int64_t)kh * R;
+    for (int i = tid; i < R; i += kDecThreads) s_z[i] = Elem<ActT>::load(zr + i);
+    for (int j = tid; j < Dv; j += kDecThreads) s_w[j] = Elem<ActT>::load(static_cast<const ActT*>(p.gw) + j);
   }
   __syncthreads();
   if (wave < 3) {
@@ -170,7 +193,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < SV; ++i) st[i] = d * st[i] + delta * kv[i];
       store_stream(S + (int64_t)row * DK + col, Elem<StT>::pack(st));
-      if ((lane % LPR) == 0) Elem<ActT>::store(out + row, o);
+      if ((lane % LPR) == 0) {
+        if constexpr (GATED) s_o[row] = round_act<ActT>(o);
+        else Elem<ActT>::store(out + row, o);
+      }
     }
   };
   uint4 raw2[kLoads];
@@ -180,36 +206,56 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     load_batch(raw, min(it + 2, iters - 1));
     if (it + 1 < iters) compute_batch(raw2, it + 1);
   }
+
+  // ---- epilogue: gated RMS norm of each value head over its Dv outputs
+  // (vllm.cpp cpu_ops.cpp RmsNormGatedKernel; ferrum-kernels cpu.rs
+  // gated_rms_norm_f32), one wave per value head
+  if constexpr (GATED) {
+    __syncthreads();
+    for (int hl = wave; hl < r; hl += kDecWaves) {
+      const float* ov = s_o + hl * Dv;
+      const float* zv = s_z + hl * Dv;
+      float ss = 0.0f;
+      for (int j = lane; j < Dv; j += 64) ss += ov[j] * ov[j];
+      ss = group_sum<64>(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)Dv + p.geps);
+      for (int j = lane; j < Dv; j += 64) {
+        const float act = p.gsig ? sigmoid_f(zv[j]) : silu_f(zv[j]);
+        Elem<ActT>::store(out + hl * Dv + j, ov[j] * inv * s_w[j] * act);
+      }
+    }
+  }
 }
 
-template <typename ActT, typename StT>
+template <typename ActT, typename StT, bool GATED>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
   const int r = p.Hv / p.Hk;
-  const size_t smem = (size_t)(2 * p.Dk + r * p.Dv + 2 * r + 4) * sizeof(float);
+  const size_t smem = (size_t)(2 * p.Dk + r * p.Dv + 2 * r + 4 + (GATED ? 2 * r * p.Dv + p.Dv : 0)) * sizeof(float);
   dim3 grid(p.Hk, p.B);
   switch (p.Dk) {
-    case 16: decode_kernel<ActT, StT, 16><<<grid, kDecThreads, smem, stream>>>(p); break;
-    case 32: decode_kernel<ActT, StT, 32><<<grid, kDecThreads, smem, stream>>>(p); break;
-    case 64: decode_kernel<ActT, StT, 64><<<grid, kDecThreads, smem, stream>>>(p); break;
-    case 128: decode_kernel<ActT, StT, 128><<<grid, kDecThreads, smem, stream>>>(p); break;
-    default: decode_kernel<ActT, StT, 256><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 16: decode_kernel<ActT, StT, 16, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 32: decode_kernel<ActT, StT, 32, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 64: decode_kernel<ActT, StT, 64, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
+    case 128: decode_kernel<ActT, StT, 128, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
+    default: decode_kernel<ActT, StT, 256, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
   }
   return hipGetLastError();
 }
 
-template <typename ActT>
+template <typename ActT, bool GATED>
 hipError_t launch_state(const DecodeParams& p, hipStream_t stream) {
   switch (p.state) {
-    case GDN_F32: return launch_dk<ActT, float>(p, stream);
-    case GDN_BF16: return launch_dk<ActT, bf16>(p, stream);
-    default: return launch_dk<ActT, f16>(p, stream);
+    case GDN_F32: return launch_dk<ActT, float, GATED>(p, stream);
+    case GDN_BF16: return launch_dk<ActT, bf16, GATED>(p, stream);
+    default: return launch_dk<ActT, f16, GATED>(p, stream);
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  return p.act == GDN_F32 ? launch_state<float>(p, stream) : launch_state<bf16>(p, stream);
+  if (p.gated) return p.act == GDN_F32 ? launch_state<float, true>(p, stream) : launch_state<bf16, true>(p, stream);
+  return p.act == GDN_F32 ? launch_state<float, false>(p, stream) : launch_state<bf16, false>(p, stream);
 }
 
 }  // namespace gdn

@@ -59,6 +59,25 @@ struct DecodeParams {
   float scale;
   void* out;              // [B, Hv, Dv] act
   gdn_dtype act, state;
+  // fused output epilogue (gated RMS norm), when gated is set
+  int gated;
+  const void* gz;         // gate, row b head h at gz[b * gz_stride + h * Dv + j], act
+  int64_t gz_stride;
+  const void* gw;         // [Dv] act
+  float geps;
+  int gsig;               // logistic gate instead of silu
+};
+
+struct GatedNormParams {
+  int T, H, D;
+  const void* x;          // [T, H, D] io
+  const void* z;          // token t head h at z[t * z_stride + h * D + j], io
+  int64_t z_stride;
+  const void* w;          // [D] io
+  float eps;
+  int sig;
+  void* out;              // [T, H, D] io
+  gdn_dtype io;
 };
 
 struct PrefillParams {
@@ -90,6 +109,7 @@ struct PrefillParams {
 // of the launch.
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const GatedNormParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
 

@@ -146,6 +146,16 @@ def make_inputs(cfg: Config, slot_seed: Optional[int] = None) -> Dict[str, np.nd
     return out
 
 
+def epilogue_inputs(T: int, Hv: int, Dv: int, dtype: str, seed: int) -> Dict[str, np.ndarray]:
+    """Inputs of the output epilogue (gated RMS norm): the gate ``z`` [T, Hv*Dv]
+    ~ N(0, 1) (the z columns of a packed [q|k|v|z] projection row) and the
+    norm weight [Dv] ~ U(0.5, 1.5), both rounded to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    z = _normal(rng, (T, Hv * Dv), 1.0, dtype)
+    w = round_to_dtype(rng.uniform(0.5, 1.5, size=Dv).astype(np.float32), dtype)
+    return {"z": z, "norm_w": w}
+
+
 def decode_slot_sets(cfg: Config, count: int, seed: int) -> np.ndarray:
     """``count`` independent draws of the decode slot subset (distinct slots
     within each draw), so that repeated timed calls touch different slots."""

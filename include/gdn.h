@@ -159,6 +159,62 @@ gdn_status gdn_decode(const gdn_dims* dims, int32_t batch, const void* mixed_qkv
                       const int32_t* slot_idx_host, float scale, void* out, void* stream);
 
 /*
+ * gdn_decode_gated -- gdn_decode with the layer's output epilogue fused (the
+ * gated RMS norm of gdn_gated_rmsnorm, below): equal to gdn_decode followed
+ * by gdn_gated_rmsnorm on the same rows, including the rounding of o to
+ * act_dtype that storing and reloading it would make.  The fusion is
+ * possible because one workgroup of the decode kernel owns every value row
+ * of its heads.  [P1] RmsNormGatedKernel; [P3] gated_rms_norm_f32.
+ *
+ * Arguments: those of gdn_decode, plus
+ *   z, z_row_stride       device gate in act_dtype: row b, value head h, element j at
+ *                         z[b * z_row_stride + h * Dv + j]; z_row_stride >= Hv * Dv, so z may be
+ *                         the z columns of a packed [q | k | v | z] projection row.
+ *   norm_weight           device [Dv] in act_dtype.
+ *   eps                   finite, >= 0 (inside the square root, next to the mean of squares).
+ *   sigmoid_gate          0: silu gate; 1: logistic gate.
+ *   out                   device [B, Hv, Dv] in act_dtype: the gated, normalised output.
+ * Errors: those of gdn_decode; a null z or norm_weight, a short z_row_stride or a bad eps or
+ * sigmoid_gate is GDN_ERR_INVALID_ARGUMENT / GDN_ERR_SHAPE.
+ */
+gdn_status gdn_decode_gated(const gdn_dims* dims, int32_t batch, const void* mixed_qkv,
+                            int64_t mixed_row_stride, const void* a_raw, int64_t a_row_stride,
+                            const void* b_raw, int64_t b_row_stride, gdn_dtype act_dtype,
+                            const void* conv_weight, const float* A_log, const float* dt_bias,
+                            void* conv_state_pool, void* ssm_state_pool, gdn_dtype state_dtype,
+                            int32_t num_slots, const int32_t* slot_idx_dev,
+                            const int32_t* slot_idx_host, float scale, const void* z,
+                            int64_t z_row_stride, const void* norm_weight, float eps,
+                            int32_t sigmoid_gate, void* out, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- the layer's output epilogue, for the output of
+ * gdn_prefill_varlen (or of gdn_decode): for every token t and value head h,
+ * over the Dv values of the head,
+ *   out[t,h,:] = x[t,h,:] / sqrt(mean_j x[t,h,j]^2 + eps) * weight[:] * act(z[t,h,:])
+ * with act = silu, or the logistic function when sigmoid_gate is set: the
+ * norm is taken before the gate, one group per head.  [P1]
+ * RmsNormGatedKernel; [P3] gated_rms_norm_f32.
+ *
+ * Arguments:
+ *   num_tokens            T >= 0 (T = 0 is a no-op).
+ *   num_heads, head_dim   Hv > 0; Dv in {16, 32, 64, 128, 256}.
+ *   x                     device [T, Hv, Dv] in io_dtype.
+ *   z, z_row_stride       device gate in io_dtype: token t, head h, element j at
+ *                         z[t * z_row_stride + h * Dv + j]; z_row_stride >= Hv * Dv.
+ *   weight                device [Dv] in io_dtype.
+ *   eps                   finite, >= 0.
+ *   sigmoid_gate          0: silu gate; 1: logistic gate.
+ *   out                   device [T, Hv, Dv] in io_dtype; may be x itself (in place), must not
+ *                         otherwise overlap x or z.
+ *   io_dtype              GDN_F32 or GDN_BF16.
+ * x, z, weight and out must be 16-byte aligned and z_row_stride a whole number of 16-byte words.
+ */
+gdn_status gdn_gated_rmsnorm(int32_t num_tokens, int32_t num_heads, int32_t head_dim, const void* x,
+                             const void* z, int64_t z_row_stride, const void* weight, float eps,
+                             int32_t sigmoid_gate, void* out, gdn_dtype io_dtype, void* stream);
+
+/*
  * gdn_prefill_varlen -- the gated delta rule over whole sequences, computed
  * in chunks of chunk_size tokens with the WY / UT-transform form, equal to
  * the token-by-token recurrence of gdn_decode up to rounding order ([P1]

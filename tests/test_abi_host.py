@@ -54,13 +54,13 @@ def _arr(a):
 
 
 def _prepare(lib, dims=None, N=2, T=10, cu=(0, 4, 10), stride=None, act=1, qkv=1, slots=(0, 1), num_slots=4,
-             x=FAKE, l2=1, ptr_q=FAKE):
+             x=FAKE, l2=1, ptr_q=FAKE, w=FAKE, pool=FAKE):
     cu_a, cu_p = _arr(cu)
     sl_a, sl_p = _arr(slots) if slots is not None else (None, None)
     d = dims if dims is not None else _dims()
     cc = 2 * 2 * 128 + 4 * 128
-    return lib.gdn_prepare(d, N, T, cu_p, FAKE, x, cc if stride is None else stride, FAKE, 4, FAKE, 4, act, FAKE,
-                           FAKE, FAKE, FAKE, num_slots, sl_p, FAKE if slots is not None else None, None, l2, ptr_q,
+    return lib.gdn_prepare(d, N, T, cu_p, FAKE, x, cc if stride is None else stride, FAKE, 4, FAKE, 4, act, w,
+                           FAKE, FAKE, pool, num_slots, sl_p, FAKE if slots is not None else None, None, l2, ptr_q,
                            FAKE, FAKE, qkv, FAKE, FAKE, None)
 
 
@@ -91,6 +91,8 @@ def test_prepare_rejects_bad_arguments(lib):
     assert _prepare(lib, slots=(0, -1)) == INDEX
     assert _prepare(lib, slots=None, num_slots=1) == INDEX
     assert _prepare(lib, l2=2) == INVALID
+    assert _prepare(lib, w=FAKE + 2) == INVALID and "conv weight" in _err(lib)
+    assert _prepare(lib, pool=FAKE + 8) == INVALID
 
 
 def test_prepare_empty_batch_is_a_no_op(lib):
@@ -159,3 +161,47 @@ def test_workspace_size_query(lib):
     a = lib.gdn_prefill_workspace_size(_dims(), 2, 100, 64)
     b = lib.gdn_prefill_workspace_size(_dims(), 2, 1000, 0)
     assert b >= a
+
+
+def _decode_gated(lib, B=3, slots=(2, -1, 0), z=FAKE, zs=4 * 128, w=FAKE, eps=1e-6, sig=0):
+    sl_a, sl_p = _arr(slots)
+    cc = 2 * 2 * 128 + 4 * 128
+    return lib.gdn_decode_gated(_dims(), B, FAKE, cc, FAKE, 4, FAKE, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, FAKE,
+                                sl_p, ctypes.c_float(0.125), z, zs, w, ctypes.c_float(eps), sig, FAKE, None)
+
+
+def test_decode_gated_rejects_bad_arguments(lib):
+    assert _decode_gated(lib, z=None) == INVALID
+    assert _decode_gated(lib, w=None) == INVALID
+    assert _decode_gated(lib, zs=100) == SHAPE and "z_row_stride" in _err(lib)
+    assert _decode_gated(lib, eps=-1.0) == INVALID
+    assert _decode_gated(lib, eps=float("nan")) == INVALID
+    assert _decode_gated(lib, eps=float("inf")) == INVALID
+    assert _decode_gated(lib, sig=2) == INVALID
+    assert _decode_gated(lib, slots=(2, 2, 0)) == INDEX  # the decode checks still apply
+    assert _decode_gated(lib, B=0) == OK
+
+
+def _norm(lib, T=4, H=4, D=128, x=FAKE, z=FAKE, zs=None, w=FAKE, eps=1e-6, sig=0, out=FAKE, io=1):
+    return lib.gdn_gated_rmsnorm(T, H, D, x, z, H * D if zs is None else zs, w, ctypes.c_float(eps), sig, out, io,
+                                 None)
+
+
+def test_gated_rmsnorm_rejects_bad_arguments(lib):
+    assert _norm(lib, D=48) == SHAPE
+    assert _norm(lib, H=0) == SHAPE
+    assert _norm(lib, T=-1) == SHAPE
+    assert _norm(lib, io=2) == DTYPE
+    assert _norm(lib, x=None) == INVALID
+    assert _norm(lib, out=None) == INVALID
+    assert _norm(lib, zs=100) == SHAPE
+    assert _norm(lib, zs=4 * 128 + 4) == INVALID and "aligned" in _err(lib)
+    assert _norm(lib, z=FAKE + 8) == INVALID
+    assert _norm(lib, w=FAKE + 2) == INVALID
+    assert _norm(lib, eps=-1.0) == INVALID
+    assert _norm(lib, eps=float("nan")) == INVALID
+    assert _norm(lib, sig=3) == INVALID
+
+
+def test_gated_rmsnorm_empty_is_a_no_op(lib):
+    assert _norm(lib, T=0) == OK
