@@ -21,10 +21,11 @@
 // which is the token step written so that the row is read once and written
 // once.  Value rows are independent, so rows need no synchronisation.
 //
-// With the output epilogue (gdn_decode_gated) the outputs stay in LDS,
-// rounded as they would be stored, and after the stream each wave applies
-// the gated RMS norm to one value head: the workgroup owns all Dv outputs of
-// its heads.
+// The outputs of a row's R value rows are kept in LDS and written out in
+// one coalesced pass after the stream (rather than as scattered 2-byte
+// stores during it).  With the output epilogue (gdn_decode_gated) they are
+// kept rounded as they would be stored, and each wave applies the gated RMS
+// norm to one value head: the workgroup owns all Dv outputs of its heads.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
   float* s_decay = smem + 2 * DK + R;     // [r]
   float* s_beta = s_decay + r;            // [r]
   float* s_red = s_beta + r;              // [4]: 1/|q|, 1/|k|, k.q
-  float* s_o = s_red + 4;                 // [R] with the epilogue: o as stored in ActT
+  float* s_o = s_red + 4;                 // [R] outputs, written out coalesced after the stream
   float* s_z = s_o + R;                   // [R] with the epilogue: the gate of this row's heads
   float* s_w = s_z + R;                   // [Dv] with the epilogue: the norm weight
   const int K = p.K;
@@ -194,8 +195,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
       for (int i = 0; i < SV; ++i) st[i] = d * st[i] + delta * kv[i];
       store_stream(S + (int64_t)row * DK + col, Elem<StT>::pack(st));
       if ((lane % LPR) == 0) {
-        if constexpr (GATED) s_o[row] = round_act<ActT>(o);
-        else Elem<ActT>::store(out + row, o);
+        s_o[row] = GATED ? round_act<ActT>(o) : o;
       }
     }
   };
@@ -205,6 +205,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     compute_batch(raw, it);
     load_batch(raw, min(it + 2, iters - 1));
     if (it + 1 < iters) compute_batch(raw2, it + 1);
+  }
+
+  if constexpr (!GATED) {
+    // the R outputs of this workgroup are contiguous: one coalesced pass
+    __syncthreads();
+    for (int i = tid; i < R; i += kDecThreads) Elem<ActT>::store(out + i, s_o[i]);
   }
 
   // ---- epilogue: gated RMS norm of each value head over its Dv outputs
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
 template <typename ActT, typename StT, bool GATED>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
   const int r = p.Hv / p.Hk;
-  const size_t smem = (size_t)(2 * p.Dk + r * p.Dv + 2 * r + 4 + (GATED ? 2 * r * p.Dv + p.Dv : 0)) * sizeof(float);
+  const size_t smem = (size_t)(2 * p.Dk + 2 * r * p.Dv + 2 * r + 4 + (GATED ? r * p.Dv + p.Dv : 0)) * sizeof(float);
   dim3 grid(p.Hk, p.B);
   switch (p.Dk) {
     case 16: decode_kernel<ActT, StT, 16, GATED><<<grid, kDecThreads, smem, stream>>>(p); break;
