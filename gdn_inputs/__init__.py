@@ -156,6 +156,50 @@ def epilogue_inputs(T: int, Hv: int, Dv: int, dtype: str, seed: int) -> Dict[str
     return {"z": z, "norm_w": w}
 
 
+def spec_inputs(dims: Dims, num_reqs: int, cols: int, num_slots: int, act_dtype: str, state_dtype: str,
+                seed: int, lens: Optional[Sequence[int]] = None, conv_len: Optional[int] = None,
+                null_reqs: int = 0, null_cols: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of one speculative decode step.
+
+    ``num_reqs`` requests of ``cols`` tokens each (or ``lens[i]`` tokens,
+    1 <= lens[i] <= cols); x, a, b ~ N(0, 1), conv weight ~ N(0, 0.5), A_log ~
+    U(0, log 16), dt_bias ~ U(-1, 1); the conv pool [num_slots, Cc, W] ~ N(0, 1)
+    with W = (K-1) + (cols-1) unless ``conv_len`` is given; the state pool
+    ~ N(0, 0.05).  ``state_idx`` [num_reqs, cols] holds distinct slots drawn
+    from one permutation; ``num_accepted`` ~ U[1, cols].  ``null_reqs``
+    requests have every column -1 (padding rows); ``null_cols`` further
+    columns of live requests, never column 0 nor the initial column
+    num_accepted-1, are set to -1."""
+    rng = np.random.default_rng(seed)
+    lens = [cols] * num_reqs if lens is None else [int(v) for v in lens]
+    assert len(lens) == num_reqs and all(1 <= v <= cols for v in lens)
+    W = (dims.K - 1) + (cols - 1) if conv_len is None else conv_len
+    T = int(sum(lens))
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = _normal(rng, (T, dims.Cc), 1.0, act_dtype)
+    out["w"] = _normal(rng, (dims.Cc, dims.K), 0.5, act_dtype)
+    out["a"] = _normal(rng, (T, dims.Hv), 1.0, act_dtype)
+    out["b"] = _normal(rng, (T, dims.Hv), 1.0, act_dtype)
+    out["A_log"] = rng.uniform(0.0, math.log(16.0), size=dims.Hv).astype(np.float32)
+    out["dt_bias"] = rng.uniform(-1.0, 1.0, size=dims.Hv).astype(np.float32)
+    out["conv_pool"] = _normal(rng, (num_slots, dims.Cc, W), 1.0, act_dtype)
+    out["ssm_pool"] = _normal(rng, (num_slots, dims.Hv, dims.Dv, dims.Dk), 0.05, state_dtype)
+    out["cu"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert num_reqs * cols <= num_slots
+    sidx = rng.permutation(num_slots)[: num_reqs * cols].astype(np.int32).reshape(num_reqs, cols)
+    nat = rng.integers(1, cols + 1, size=num_reqs).astype(np.int32)
+    if null_reqs:
+        sidx[rng.choice(num_reqs, size=null_reqs, replace=False)] = -1
+    if null_cols:
+        cand = [(i, c) for i in range(num_reqs) for c in range(1, cols)
+                if c != nat[i] - 1 and sidx[i, 0] >= 0]
+        for j in rng.choice(len(cand), size=min(null_cols, len(cand)), replace=False):
+            sidx[cand[j]] = -1
+    out["state_idx"] = sidx
+    out["num_accepted"] = nat
+    return out
+
+
 def decode_slot_sets(cfg: Config, count: int, seed: int) -> np.ndarray:
     """``count`` independent draws of the decode slot subset (distinct slots
     within each draw), so that repeated timed calls touch different slots."""

@@ -15,6 +15,15 @@ and calls the C functions in the order the library's entry points define:
   out rounded to its dtype, the state rounded once to the pool dtype.
 * :func:`decode`   -- prepare + recurrence for one token per row against the
   slot-indexed pools; slot -1 gives a zero output and writes nothing.
+* :func:`decode_spec` -- speculative multi-token decode: the widened-window
+  conv update, prepare, and the recurrence with a state snapshot per token.
+
+Conv history pools are [S, Cc, W] with W >= K-1 taps per channel.  W = K-1 is
+the ordinary layout; a wider row (speculative decoding keeps
+(K-1) + (max_query_len-1) taps) is used by the non-speculative steps through
+its leading K-1 taps only, the rest left as it is (vllm.cpp cpu_ops.cpp,
+CausalConv1dUpdateKernel and GdnStateGatherKernel / GdnStateScatterKernel on
+widened rows).
 
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, invariants, library routines and brute-force algebra.
@@ -84,8 +93,10 @@ def _ptr(a: np.ndarray):
 # Thin wrappers over the C functions.
 # ---------------------------------------------------------------------------
 def round_to(x, dtype: str) -> np.ndarray:
-    """Round values to ``dtype`` (RNE, directly from double)."""
+    """Round values to ``dtype`` (RNE, directly from double); "f64" keeps them."""
     x = _f64(x)
+    if dtype == "f64":
+        return x.copy()
     y = np.empty_like(x)
     _load().gdn_oracle_round(_ptr(x), _ptr(y), x.size, _DTYPE_CODE[dtype])
     return y
@@ -165,6 +176,62 @@ def recurrence(q, k, v, g, beta, cu, state_in, has_init, scale: float, l2norm: b
     return out, state_out
 
 
+def _silu(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def conv_spec(x, w, cu, rows, num_accepted):
+    """Speculative multi-token conv update + SiLU, per request i with tokens
+    cu[i] .. cu[i+1]-1 ([P1] CausalConv1dSpecUpdateKernel).
+
+    rows [N, Cc, W] is each request's widened conv row.  With off =
+    num_accepted[i] - 1 and L the request's token count, the stream the conv
+    reads is the K-1 taps of the row starting at tap off, followed by the L
+    inputs; token t's pre-activation is the K-tap product of w with stream
+    positions t .. t+K-1.  The row then becomes its taps off+1 .. off+W-L
+    followed by the L inputs.  A tap index past the row's end reads as zero.
+    Returns (y [T, Cc], rows_out [N, Cc, W])."""
+    x, w = _f64(x), _f64(w)
+    cu = np.asarray(cu, dtype=np.int64)
+    nat = np.asarray(num_accepted, dtype=np.int64)
+    N = cu.size - 1
+    Cc, K = w.shape
+    rows = _f64(rows)
+    assert rows.shape[:2] == (N, Cc)
+    W = rows.shape[2]
+    y = np.zeros((x.shape[0], Cc))
+    rows_out = rows.copy()
+    zero = np.zeros(Cc)
+    for i in range(N):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        L = hi - lo
+        if L == 0:
+            continue
+        assert L <= W, "the widened row must hold at least the request's tokens"
+        off = int(nat[i]) - 1
+        row = rows[i]
+
+        def tap(j):
+            return row[:, j] if j < W else zero
+
+        stream = np.stack([tap(off + j) for j in range(K - 1)] + [x[lo + t] for t in range(L)], axis=1)
+        for t in range(L):
+            y[lo + t] = _silu(np.sum(w * stream[:, t:t + K], axis=1))
+        keep = W - L
+        rows_out[i] = np.stack([tap(off + 1 + j) for j in range(keep)] + [x[lo + t] for t in range(L)], axis=1)
+    return y, rows_out
+
+
+def _conv_pool(dims, conv_pool) -> np.ndarray:
+    """The conv pool as [S, Cc, W] f64 (W >= K-1 taps per channel)."""
+    pool = _f64(conv_pool)
+    if pool.ndim != 3:
+        pool = pool.reshape(pool.shape[0], dims.Cc, -1)
+    assert pool.shape[2] >= dims.K - 1
+    return pool
+
+
 # ---------------------------------------------------------------------------
 # Compositions matching the library's entry points.
 # ---------------------------------------------------------------------------
@@ -174,14 +241,15 @@ def prepare(dims, cu, x, w, a, b, A_log, dt_bias, conv_pool, slots, has_init, l2
     ``qkv_dtype``), g, beta (rounded to f32) and the updated conv pool (the
     history rows of ``slots`` replaced by each sequence's last K-1 inputs)."""
     slots = np.asarray(slots, dtype=np.int64)
-    conv_pool = _f64(conv_pool)
-    hist = conv_pool[slots] if dims.K > 1 else np.zeros((len(slots), dims.Cc, 0))
+    conv_pool = _conv_pool(dims, conv_pool)
+    Km1 = dims.K - 1
+    hist = conv_pool[slots, :, :Km1]
     y, hist_out = conv_silu(x, w, cu, hist, has_init, nthreads)
     q, k, v = split_l2(y, dims.Hk, dims.Hv, dims.Dk, dims.Dv, l2norm)
     g, beta = gates(a, b, A_log, dt_bias)
     new_pool = conv_pool.copy()
     if dims.K > 1:
-        new_pool[slots] = hist_out
+        new_pool[slots, :, :Km1] = hist_out
     return dict(q=round_to(q, qkv_dtype), k=round_to(k, qkv_dtype), v=round_to(v, qkv_dtype),
                 g=round_to(g, "f32"), beta=round_to(beta, "f32"), conv_pool=new_pool)
 
@@ -207,7 +275,7 @@ def decode(dims, x, w, a, b, A_log, dt_bias, conv_pool, ssm_pool, slots, scale: 
     Returns (out [B, Hv, Dv], conv_pool, ssm_pool)."""
     slots = np.asarray(slots, dtype=np.int64)
     B = slots.size
-    conv_pool = _f64(conv_pool)
+    conv_pool = _conv_pool(dims, conv_pool)
     ssm_pool = _f64(ssm_pool)
     out = np.zeros((B, dims.Hv, dims.Dv))
     live = np.nonzero(slots >= 0)[0]
@@ -217,13 +285,71 @@ def decode(dims, x, w, a, b, A_log, dt_bias, conv_pool, ssm_pool, slots, scale: 
         n = live.size
         cu = np.arange(n + 1, dtype=np.int32)
         ones = np.ones(n, np.uint8)
-        hist = conv_pool[ls] if dims.K > 1 else np.zeros((n, dims.Cc, 0))
+        hist = conv_pool[ls, :, :dims.K - 1]
         y, hist_out = conv_silu(_f64(x)[live], w, cu, hist, ones, nthreads)
         q, k, v = split_l2(y, dims.Hk, dims.Hv, dims.Dk, dims.Dv, True)
         g, beta = gates(_f64(a)[live], _f64(b)[live], A_log, dt_bias)
         o, st = recurrence(q, k, v, g, beta, cu, ssm_pool[ls], ones, scale, False, nthreads)
         out[live] = o
         if dims.K > 1:
-            new_conv[ls] = hist_out
+            new_conv[ls, :, :dims.K - 1] = hist_out
         new_ssm[ls] = round_to(st, state_dtype)
+    return round_to(out, out_dtype), new_conv, new_ssm
+
+
+def decode_spec(dims, cu, x, w, a, b, A_log, dt_bias, conv_pool, ssm_pool, state_idx, num_accepted,
+                scale: float, state_dtype: str = "f32", out_dtype: str = "f32",
+                nthreads: Optional[int] = None):
+    """Speculative multi-token decode ([P1] CausalConv1dSpecUpdateKernel,
+    GdnSpecDecodeKernel; [P2] the speculative part of
+    ValidateGdnAttentionMetadata).
+
+    Request i has tokens cu[i] .. cu[i+1]-1 (L_i of them) and a row of
+    C = state_idx.shape[1] state slots.  Its recurrence starts from the state
+    in slot state_idx[i, num_accepted[i]-1] (the snapshot taken after the
+    last accepted token of the previous step) and, after its token t, the
+    state is stored into slot state_idx[i, t] (rounded to ``state_dtype``;
+    the running state itself stays unrounded); a -1 column skips that store.
+    A request whose initial slot is -1 gets zero outputs and touches neither
+    pool.  Its conv row is the widened row of slot state_idx[i, 0] (the pages
+    leave the conv slot open; column 0 is the request's fixed slot), updated
+    by :func:`conv_spec`.  q/k are L2-normalised as in :func:`decode`.
+    Returns (out [T, Hv, Dv], conv_pool, ssm_pool)."""
+    cu = np.asarray(cu, dtype=np.int64)
+    N = cu.size - 1
+    sidx = np.asarray(state_idx, dtype=np.int64).reshape(N, -1)
+    nat = np.asarray(num_accepted, dtype=np.int64).reshape(N)
+    T = int(cu[-1])
+    conv_pool = _conv_pool(dims, conv_pool)
+    ssm_pool = _f64(ssm_pool)
+    x, a, b = _f64(x), _f64(a), _f64(b)
+    out = np.zeros((T, dims.Hv, dims.Dv))
+    new_conv, new_ssm = conv_pool.copy(), ssm_pool.copy()
+    init = sidx[np.arange(N), nat - 1] if N else np.zeros(0, np.int64)
+    live = np.nonzero(init >= 0)[0]
+    if live.size == 0:
+        return round_to(out, out_dtype), new_conv, new_ssm
+    assert np.all(sidx[live, 0] >= 0), "a live request needs its conv slot (column 0)"
+    lens = (cu[1:] - cu[:-1])[live]
+    toks = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in live])
+    cu_l = np.concatenate([[0], np.cumsum(lens)])
+    conv_slots = sidx[live, 0]
+    y, rows_out = conv_spec(x[toks], w, cu_l, conv_pool[conv_slots], nat[live])
+    new_conv[conv_slots] = rows_out
+    q, k, v = split_l2(y, dims.Hk, dims.Hv, dims.Dk, dims.Dv, True)
+    g, beta = gates(a[toks], b[toks], A_log, dt_bias)
+    S = ssm_pool[init[live]]                    # every initial state is read before any store
+    o_l = np.zeros((toks.size, dims.Hv, dims.Dv))
+    for t in range(int(lens.max())):
+        act = np.nonzero(lens > t)[0]           # live requests that have a token t
+        tok = cu_l[act] + t
+        one = np.arange(act.size + 1, dtype=np.int32)
+        o, S_new = recurrence(q[tok], k[tok], v[tok], g[tok], beta[tok], one, S[act],
+                              np.ones(act.size, np.uint8), scale, False, nthreads)
+        o_l[tok] = o
+        S[act] = S_new
+        snap = sidx[live[act], t]
+        keep = snap >= 0
+        new_ssm[snap[keep]] = round_to(S_new[keep], state_dtype)
+    out[toks] = o_l
     return round_to(out, out_dtype), new_conv, new_ssm
