@@ -6,7 +6,7 @@ device memory and the current HIP stream.  If the library is not built, the
 first call raises; there is no fallback path.
 
 Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`, :func:`gdn_decode_gated`,
-:func:`gdn_gated_rmsnorm`,
+:func:`gdn_decode_spec`, :func:`gdn_gated_rmsnorm`,
 :func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
 """
 from __future__ import annotations
@@ -36,7 +36,7 @@ class GdnError(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
                 ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
-                ("conv_kernel", ctypes.c_int32)]
+                ("conv_kernel", ctypes.c_int32), ("conv_state_len", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -51,13 +51,16 @@ class Dims:
     def Cc(self) -> int:
         return 2 * self.Hk * self.Dk + self.Hv * self.Dv
 
-    def c(self) -> _Dims:
-        return _Dims(self.Hk, self.Hv, self.Dk, self.Dv, self.K)
+    def c(self, conv_pool=None) -> _Dims:
+        """The C struct; the conv-history row length is taken from a 3-D
+        conv pool [S, Cc, W] (0, meaning K-1, otherwise)."""
+        W = int(conv_pool.shape[-1]) if conv_pool is not None and conv_pool.dim() == 3 else 0
+        return _Dims(self.Hk, self.Hv, self.Dk, self.Dv, self.K, W)
 
 
 _lib = None
-EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_prefill_varlen", "gdn_prefill_workspace_size",
-           "gdn_gated_rmsnorm", "gdn_status_string", "gdn_last_error", "gdn_version")
+EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
+           "gdn_prefill_workspace_size", "gdn_gated_rmsnorm", "gdn_status_string", "gdn_last_error", "gdn_version")
 
 
 def load_library():
@@ -76,12 +79,15 @@ def load_library():
     lib.gdn_decode.argtypes = [D, i32, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, P, P, f32, P, P]
     lib.gdn_decode_gated.argtypes = [D, i32, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, P, P, f32,
                                      P, i64, P, f32, i32, P, P]
+    lib.gdn_decode_spec.argtypes = [D, i32, i64, P, P, P, i64, P, i64, P, i64, i32, P, P, P, P, P, i32, i32, i32,
+                                    P, P, P, P, f32, P, P]
     lib.gdn_gated_rmsnorm.argtypes = [i32, i32, i32, P, P, i64, P, f32, i32, P, i32, P]
     lib.gdn_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32, i32,
                                        i32, P, P, sz, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
     lib.gdn_prefill_workspace_size.restype = sz
-    for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_prefill_varlen", "gdn_gated_rmsnorm"):
+    for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
+               "gdn_gated_rmsnorm"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -137,7 +143,7 @@ def gdn_prepare(dims: Dims, cu_seqlens, mixed_qkv, a_raw, b_raw, conv_weight, A_
     sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
     n = int(cu_h.size - 1)
     T = int(cu_h[-1]) if n > 0 else 0
-    st = lib.gdn_prepare(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(mixed_qkv),
+    st = lib.gdn_prepare(ctypes.byref(dims.c(conv_state_pool)), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(mixed_qkv),
                          mixed_qkv.stride(0), _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0),
                          _dtype_code(mixed_qkv), _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias),
                          _ptr(conv_state_pool), conv_state_pool.shape[0] if conv_state_pool is not None else 0,
@@ -157,7 +163,7 @@ def gdn_decode(dims: Dims, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias,
     sl_h = None
     if validate:
         sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
-    st = lib.gdn_decode(ctypes.byref(dims.c()), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
+    st = lib.gdn_decode(ctypes.byref(dims.c(conv_state_pool)), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
                         _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0), _dtype_code(mixed_qkv),
                         _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_pool),
                         _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
@@ -177,13 +183,42 @@ def gdn_decode_gated(dims: Dims, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt
         sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
     if z.stride(-1) != 1:
         raise ValueError("z must have unit column stride")
-    st = lib.gdn_decode_gated(ctypes.byref(dims.c()), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
+    st = lib.gdn_decode_gated(ctypes.byref(dims.c(conv_state_pool)), mixed_qkv.shape[0], _ptr(mixed_qkv), mixed_qkv.stride(0),
                               _ptr(a_raw), a_raw.stride(0), _ptr(b_raw), b_raw.stride(0), _dtype_code(mixed_qkv),
                               _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_pool),
                               _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
                               _ptr(slot_idx), _hptr(sl_h), float(scale), _ptr(z), z.stride(0), _ptr(norm_weight),
                               float(eps), int(bool(sigmoid_gate)), _ptr(out), _stream(stream))
     _check("gdn_decode_gated", st)
+
+
+def gdn_decode_spec(dims: Dims, cu_seqlens, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias, conv_state_pool,
+                    ssm_state_pool, state_idx, num_accepted, out, scale: float, cu_seqlens_host=None,
+                    state_idx_host=None, num_accepted_host=None, validate: bool = True, stream=None) -> None:
+    """Speculative multi-token decode; pools updated in place.
+
+    ``conv_state_pool`` is [S, Cc, W] with W >= (K-1) + (C-1); ``state_idx``
+    [N, C] and ``num_accepted`` [N] are int32 device tensors, ``cu_seqlens``
+    [N+1] too (its host copy is always taken).  With ``validate`` the slot
+    table is checked on the host (copies are made from the device tensors
+    unless the ``*_host`` arrays are given)."""
+    lib = load_library()
+    if conv_state_pool.dim() != 3 or state_idx.dim() != 2:
+        raise ValueError("conv_state_pool must be [S, Cc, W] and state_idx [N, C]")
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    si_h = na_h = None
+    if validate:
+        si_h = _host_i32(state_idx_host if state_idx_host is not None else state_idx)
+        na_h = _host_i32(num_accepted_host if num_accepted_host is not None else num_accepted)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    st = lib.gdn_decode_spec(ctypes.byref(dims.c(conv_state_pool)), n, T, _hptr(cu_h), _ptr(cu_seqlens),
+                             _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(a_raw), a_raw.stride(0), _ptr(b_raw),
+                             b_raw.stride(0), _dtype_code(mixed_qkv), _ptr(conv_weight), _ptr(A_log), _ptr(dt_bias),
+                             _ptr(conv_state_pool), _ptr(ssm_state_pool), _dtype_code(ssm_state_pool),
+                             ssm_state_pool.shape[0], state_idx.shape[1], _ptr(state_idx), _ptr(num_accepted),
+                             _hptr(si_h), _hptr(na_h), float(scale), _ptr(out), _stream(stream))
+    _check("gdn_decode_spec", st)
 
 
 def gdn_gated_rmsnorm(x, z, weight, out, eps: float, sigmoid_gate: bool = False, stream=None) -> None:

@@ -57,8 +57,14 @@ gdn_status check_dims(const char* fn, const gdn_dims* d) {
     return fail(GDN_ERR_SHAPE, "%s: conv_kernel must be 1..4, got %d", fn, d->conv_kernel);
   const int64_t cc = 2LL * d->num_k_heads * d->head_k_dim + (int64_t)d->num_v_heads * d->head_v_dim;
   if (cc > (1LL << 30)) return fail(GDN_ERR_SHAPE, "%s: too many channels", fn);
+  if (d->conv_state_len != 0 && (d->conv_state_len < d->conv_kernel - 1 || d->conv_state_len > 1024))
+    return fail(GDN_ERR_SHAPE, "%s: conv_state_len must be 0 or in [K-1, 1024], got %d (K=%d)", fn,
+                d->conv_state_len, d->conv_kernel);
   return GDN_OK;
 }
+
+// Taps per conv-history row: dims.conv_state_len, 0 meaning K-1.
+int conv_row_len(const gdn_dims* d) { return d->conv_state_len ? d->conv_state_len : d->conv_kernel - 1; }
 
 int conv_channels(const gdn_dims* d) {
   return 2 * d->num_k_heads * d->head_k_dim + d->num_v_heads * d->head_v_dim;
@@ -128,7 +134,7 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
-int32_t gdn_version(void) { return 110; }
+int32_t gdn_version(void) { return 120; }
 
 gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -183,7 +189,7 @@ gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tok
   p.K = K; p.Cc = cc; p.N = num_seqs; p.T = total_tokens; p.cu = cu_seqlens_dev;
   p.x = mixed_qkv; p.x_stride = mixed_row_stride; p.a = a_raw; p.a_stride = a_row_stride;
   p.b = b_raw; p.b_stride = b_row_stride; p.w = conv_weight; p.A_log = A_log; p.dt_bias = dt_bias;
-  p.conv_pool = conv_state_pool; p.num_slots = num_slots; p.slots = slot_idx_dev;
+  p.conv_pool = conv_state_pool; p.W = conv_row_len(dims); p.num_slots = num_slots; p.slots = slot_idx_dev;
   p.has_init = has_initial_state_dev; p.l2norm = apply_qk_l2norm; p.q = q_out; p.k = k_out; p.v = v_out;
   p.g = g_out; p.beta = beta_out; p.act = act_dtype; p.qkv = qkv_dtype;
   return launched(fn, gdn::launch_prepare(p, static_cast<hipStream_t>(stream)));
@@ -246,7 +252,8 @@ gdn_status decode_common(const char* fn, const gdn_dims* dims, int32_t batch, co
   p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.Dk = dims->head_k_dim; p.Dv = dims->head_v_dim;
   p.K = K; p.Cc = cc; p.B = batch; p.x = mixed_qkv; p.x_stride = mixed_row_stride; p.a = a_raw;
   p.a_stride = a_row_stride; p.b = b_raw; p.b_stride = b_row_stride; p.w = conv_weight; p.A_log = A_log;
-  p.dt_bias = dt_bias; p.conv_pool = conv_state_pool; p.ssm_pool = ssm_state_pool; p.num_slots = num_slots;
+  p.dt_bias = dt_bias; p.conv_pool = conv_state_pool; p.W = conv_row_len(dims); p.ssm_pool = ssm_state_pool;
+  p.num_slots = num_slots;
   p.slots = slot_idx_dev; p.scale = scale; p.out = out; p.act = act_dtype; p.state = state_dtype;
   if (gate) {
     p.gated = 1; p.gz = gate->z; p.gz_stride = gate->z_row_stride; p.gw = gate->weight; p.geps = gate->eps;
@@ -283,6 +290,85 @@ gdn_status gdn_decode_gated(const gdn_dims* dims, int32_t batch, const void* mix
                        b_raw, b_row_stride, act_dtype, conv_weight, A_log, dt_bias, conv_state_pool,
                        ssm_state_pool, state_dtype, num_slots, slot_idx_dev, slot_idx_host, scale, &gate, out,
                        stream);
+}
+
+gdn_status gdn_decode_spec(const gdn_dims* dims, int32_t num_reqs, int64_t total_tokens,
+                           const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                           const void* mixed_qkv, int64_t mixed_row_stride, const void* a_raw,
+                           int64_t a_row_stride, const void* b_raw, int64_t b_row_stride,
+                           gdn_dtype act_dtype, const void* conv_weight, const float* A_log,
+                           const float* dt_bias, void* conv_state_pool, void* ssm_state_pool,
+                           gdn_dtype state_dtype, int32_t num_slots, int32_t num_cols,
+                           const int32_t* state_idx_dev, const int32_t* num_accepted_dev,
+                           const int32_t* state_idx_host, const int32_t* num_accepted_host,
+                           float scale, void* out, void* stream) {
+  const char* fn = "gdn_decode_spec";
+  gdn_status st = check_dims(fn, dims);
+  if (st != GDN_OK) return st;
+  st = check_offsets(fn, num_reqs, total_tokens, cu_seqlens_host, cu_seqlens_dev);
+  if (st != GDN_OK) return st;
+  if (num_reqs == 0) return ok();
+  if (act_dtype != GDN_F32 && act_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "%s: activations must be f32 or bf16", fn);
+  if (state_dtype != GDN_F32 && state_dtype != GDN_BF16 && state_dtype != GDN_F16)
+    return fail(GDN_ERR_DTYPE, "%s: state must be f32, bf16 or f16", fn);
+  const int K = dims->conv_kernel;
+  if (K < 2) return fail(GDN_ERR_SHAPE, "%s: speculative decode needs conv_kernel >= 2, got %d", fn, K);
+  if (num_cols < 1 || num_cols > 8)
+    return fail(GDN_ERR_SHAPE, "%s: num_cols must be in [1, 8], got %d", fn, num_cols);
+  const int W = conv_row_len(dims);
+  if (W < (K - 1) + (num_cols - 1))
+    return fail(GDN_ERR_SHAPE, "%s: conv rows of %d taps are narrower than (K-1)+(num_cols-1) = %d", fn, W,
+                (K - 1) + (num_cols - 1));
+  for (int32_t i = 0; i < num_reqs; ++i)
+    if (cu_seqlens_host[i + 1] - cu_seqlens_host[i] > num_cols)
+      return fail(GDN_ERR_SHAPE, "%s: request %d has %d tokens, more than num_cols=%d", fn, i,
+                  cu_seqlens_host[i + 1] - cu_seqlens_host[i], num_cols);
+  const int cc = conv_channels(dims);
+  if (!mixed_qkv || !a_raw || !b_raw || !conv_weight || !A_log || !dt_bias || !conv_state_pool ||
+      !ssm_state_pool || !state_idx_dev || !num_accepted_dev || !out)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a required pointer is null", fn);
+  if (mixed_row_stride < cc || a_row_stride < dims->num_v_heads || b_row_stride < dims->num_v_heads)
+    return fail(GDN_ERR_SHAPE, "%s: row strides below widths", fn);
+  if (!aligned16(ssm_state_pool))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: the state pool must be 16-byte aligned", fn);
+  if (gdn::decode_spec_lds_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_k_dim, dims->head_v_dim,
+                                 num_cols) > 64 * 1024)
+    return fail(GDN_ERR_SHAPE, "%s: num_cols * (2*Dk + 2*(Hv/Hk)*Dv) too large for one workgroup", fn);
+  if (num_slots <= 0) return fail(GDN_ERR_SHAPE, "%s: num_slots must be positive", fn);
+  if ((state_idx_host == nullptr) != (num_accepted_host == nullptr))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: pass both index host copies or neither", fn);
+  if (state_idx_host) {
+    std::vector<uint8_t> seen((size_t)num_slots, 0);
+    for (int32_t i = 0; i < num_reqs; ++i) {
+      const int32_t acc = num_accepted_host[i];
+      if (acc < 1 || acc > num_cols)
+        return fail(GDN_ERR_INDEX, "%s: request %d num_accepted %d not in [1, %d]", fn, i, acc, num_cols);
+      const int32_t* row = state_idx_host + (int64_t)i * num_cols;
+      const bool live = row[acc - 1] >= 0;
+      if (live && row[0] < 0)
+        return fail(GDN_ERR_INDEX, "%s: request %d is live but its conv slot (column 0) is -1", fn, i);
+      for (int32_t c = 0; c < num_cols; ++c) {
+        const int32_t s = row[c];
+        if (s < -1 || s >= num_slots)
+          return fail(GDN_ERR_INDEX, "%s: request %d column %d slot %d out of range [0, %d)", fn, i, c, s, num_slots);
+        if (s < 0) continue;
+        if (seen[(size_t)s]) return fail(GDN_ERR_INDEX, "%s: slot %d appears more than once", fn, s);
+        seen[(size_t)s] = 1;
+      }
+    }
+  }
+  if (!(scale == scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
+
+  gdn::SpecDecodeParams p{};
+  p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.Dk = dims->head_k_dim; p.Dv = dims->head_v_dim;
+  p.K = K; p.Cc = cc; p.N = num_reqs; p.cols = num_cols; p.W = W; p.T = total_tokens; p.cu = cu_seqlens_dev;
+  p.x = mixed_qkv; p.x_stride = mixed_row_stride; p.a = a_raw; p.a_stride = a_row_stride; p.b = b_raw;
+  p.b_stride = b_row_stride; p.w = conv_weight; p.A_log = A_log; p.dt_bias = dt_bias;
+  p.conv_pool = conv_state_pool; p.ssm_pool = ssm_state_pool; p.num_slots = num_slots;
+  p.state_idx = state_idx_dev; p.num_accepted = num_accepted_dev; p.scale = scale; p.out = out;
+  p.act = act_dtype; p.state = state_dtype;
+  return launched(fn, gdn::launch_decode_spec(p, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_gated_rmsnorm(int32_t num_tokens, int32_t num_heads, int32_t head_dim, const void* x,

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     const float xv = Elem<ActT>::load(x + cg);
     float acc = Elem<ActT>::load(w + (int64_t)cg * K + (K - 1)) * xv;
     if (K > 1) {
-      ActT* h = hist + ((int64_t)slot * p.Cc + cg) * (K - 1);
+      ActT* h = hist + ((int64_t)slot * p.Cc + cg) * p.W;  // leading K-1 of W taps
       float old[3];
 #pragma unroll
       for (int j = 0; j < 3; ++j)

@@ -26,7 +26,8 @@ struct PrepareParams {
   const void* w;          // [Cc, K] act
   const float* A_log;     // [Hv]
   const float* dt_bias;   // [Hv]
-  void* conv_pool;        // [S, Cc, K-1] act
+  void* conv_pool;        // [S, Cc, W] act; the leading K-1 taps are used
+  int W;                  // taps per conv-history row
   int num_slots;
   const int32_t* slots;   // device [N] or null (slot = s)
   const uint8_t* has_init;  // device [N] or null (all 1)
@@ -52,7 +53,8 @@ struct DecodeParams {
   const void* w;
   const float* A_log;
   const float* dt_bias;
-  void* conv_pool;        // [S, Cc, K-1] act
+  void* conv_pool;        // [S, Cc, W] act; the leading K-1 taps are used
+  int W;                  // taps per conv-history row
   void* ssm_pool;         // [S, Hv, Dv, Dk] state
   int num_slots;
   const int32_t* slots;   // device [B]
@@ -66,6 +68,33 @@ struct DecodeParams {
   const void* gw;         // [Dv] act
   float geps;
   int gsig;               // logistic gate instead of silu
+};
+
+struct SpecDecodeParams {
+  int Hk, Hv, Dk, Dv, K;
+  int Cc;
+  int N;                  // requests
+  int cols;               // slot columns per request (1..8)
+  int W;                  // taps per conv-history row, >= (K-1) + (cols-1)
+  int64_t T;
+  const int32_t* cu;      // device [N+1]
+  const void* x;          // [T, x_stride] act
+  int64_t x_stride;
+  const void* a;
+  int64_t a_stride;
+  const void* b;
+  int64_t b_stride;
+  const void* w;          // [Cc, K] act
+  const float* A_log;
+  const float* dt_bias;
+  void* conv_pool;        // [S, Cc, W] act
+  void* ssm_pool;         // [S, Hv, Dv, Dk] state
+  int num_slots;
+  const int32_t* state_idx;     // device [N, cols]
+  const int32_t* num_accepted;  // device [N]
+  float scale;
+  void* out;              // [T, Hv, Dv] act
+  gdn_dtype act, state;
 };
 
 struct GatedNormParams {
@@ -109,6 +138,8 @@ struct PrefillParams {
 // of the launch.
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_spec(const SpecDecodeParams& p, hipStream_t stream);
+size_t decode_spec_lds_bytes(int Hk, int Hv, int Dk, int Dv, int cols);
 hipError_t launch_gated_rmsnorm(const GatedNormParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);

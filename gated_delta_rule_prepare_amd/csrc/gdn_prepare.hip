@@ -112,16 +112,25 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
 
   // the history of sequence seq for this lane's channels: hw[d-1][i] is the
   // input d tokens before the sequence start (1 <= d <= K-1), zero without
-  // an initial state.  A lane's V channels hold (K-1)*V consecutive
-  // history values: K-1 16-byte words.
+  // an initial state.  In rows of exactly K-1 taps a lane's V channels hold
+  // (K-1)*V consecutive history values: K-1 16-byte words.  Widened rows
+  // (W > K-1 taps) are read tap by tap.
   auto hist_window = [&](int seq, float (&hw)[H][V]) {
     float hf[H * V];
     const bool has = active && (p.has_init == nullptr || p.has_init[seq] != 0);
-    if (has) {
+    if (has && p.W == K - 1) {
       const int slot = p.slots ? p.slots[seq] : seq;
       const uint4* hp = reinterpret_cast<const uint4*>(hist + ((int64_t)slot * p.Cc + c) * (K - 1));
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) Elem<ActT>::unpack(hp[j], hf + j * V);
+    } else if (has) {
+      // widened rows (speculative decoding): the leading K-1 of W taps per channel
+      const int slot = p.slots ? p.slots[seq] : seq;
+      const ActT* hp = hist + ((int64_t)slot * p.Cc + c) * p.W;
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) hf[i * (K - 1) + j] = Elem<ActT>::load(hp + (int64_t)i * p.W + j);
     } else {
 #pragma unroll
       for (int e = 0; e < H * V; ++e) hf[e] = 0.0f;
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(256) void prepare_finish_kernel(PrepareParams p, in
     const int64_t len = p.cu[s + 1] - start;
     const int slot = p.slots ? p.slots[s] : s;
     const bool has = p.has_init == nullptr || p.has_init[s] != 0;
-    ActT* row = static_cast<ActT*>(p.conv_pool) + ((int64_t)slot * p.Cc + c) * (K - 1);
+    ActT* row = static_cast<ActT*>(p.conv_pool) + ((int64_t)slot * p.Cc + c) * p.W;
     const ActT* x = static_cast<const ActT*>(p.x);
     float old[K - 1];
 #pragma unroll

@@ -29,9 +29,16 @@
  *   enqueued; a failing check returns a non-zero gdn_status, enqueues
  *   nothing and records a message retrievable with gdn_last_error() on the
  *   calling thread.  GDN_ERR_DEVICE reports a failed kernel launch.
- * State pools: the conv history pool is [num_slots, Cc, K-1] in the
- *   activation dtype (column j holds the j-th oldest of the last K-1 raw
- *   inputs); the recurrent state pool is [num_slots, Hv, Dv, Dk] (Dk
+ * State pools: the conv history pool is [num_slots, Cc, W] in the
+ *   activation dtype, W = dims.conv_state_len taps per channel (0 means
+ *   K-1).  gdn_prepare, gdn_decode and gdn_decode_gated use the leading K-1
+ *   taps of each row (column j holds the j-th oldest of the last K-1 raw
+ *   inputs) and leave the others as they are; a wider row is the one that
+ *   speculative decoding keeps (gdn_decode_spec), so both kinds of step can
+ *   share one pool ([P1] CausalConv1dUpdateKernel on widened rows,
+ *   GdnStateGatherKernel / GdnStateScatterKernel; [P2]
+ *   ValidateGdnStateCacheLayout, CopyStateRowsStrided).  The recurrent state
+ *   pool is [num_slots, Hv, Dv, Dk] (Dk
  *   contiguous) in f32, bf16 or f16 ([P2] ValidateGdnStateCacheLayout,
  *   ResolveMambaSsmCacheDType).  A call reads a slot's state at its storage
  *   dtype, computes in f32 and stores it back rounded (round to nearest
@@ -72,6 +79,7 @@ typedef struct gdn_dims {
   int32_t head_k_dim;  /* Dk */
   int32_t head_v_dim;  /* Dv */
   int32_t conv_kernel; /* K */
+  int32_t conv_state_len; /* W, taps per conv-history row: 0 (= K-1) or K-1 <= W <= 1024 */
 } gdn_dims;
 
 /*
@@ -103,7 +111,7 @@ typedef struct gdn_dims {
  *   act_dtype             GDN_F32 or GDN_BF16; also the dtype of conv_weight and of the history pool.
  *   conv_weight           device [Cc, K] in act_dtype.
  *   A_log, dt_bias        device f32 [Hv].
- *   conv_state_pool       device [num_slots, Cc, K-1] in act_dtype, read and written in place
+ *   conv_state_pool       device [num_slots, Cc, W] in act_dtype, read and written in place
  *                         (may be NULL when K = 1).
  *   slot_idx_host/_dev    int32 [N] slot of each sequence; both NULL means slot s for sequence s.
  *   has_initial_state_dev device uint8 [N], or NULL for "every sequence continues its slot".
@@ -141,7 +149,7 @@ gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tok
  * Arguments:
  *   batch                 B >= 0 rows (B = 0 is a no-op).
  *   mixed_qkv, a_raw, b_raw, act_dtype, conv_weight, A_log, dt_bias: as gdn_prepare, with B rows.
- *   conv_state_pool       device [num_slots, Cc, K-1] in act_dtype, in place.
+ *   conv_state_pool       device [num_slots, Cc, W] in act_dtype, in place.
  *   ssm_state_pool        device [num_slots, Hv, Dv, Dk] in state_dtype, in place.
  *   slot_idx_dev          device int32 [B]; -1 = inert row.
  *   slot_idx_host         host copy for validation (range, -1 only negative, no duplicate live slot),
@@ -186,6 +194,66 @@ gdn_status gdn_decode_gated(const gdn_dims* dims, int32_t batch, const void* mix
                             const int32_t* slot_idx_host, float scale, const void* z,
                             int64_t z_row_stride, const void* norm_weight, float eps,
                             int32_t sigmoid_gate, void* out, void* stream);
+
+/*
+ * gdn_decode_spec -- speculative multi-token decode: each request carries up
+ * to C = num_cols tokens (the last accepted token and the draft tokens after
+ * it) and a row of C state slots, and every token's state is kept so that
+ * the next step can resume after whichever token was accepted last.
+ * Defined by [P1] CausalConv1dSpecUpdateKernel and GdnSpecDecodeKernel, with
+ * the metadata rules of the speculative part of [P2]
+ * ValidateGdnAttentionMetadata.
+ *
+ * Request i has tokens cu[i] .. cu[i+1]-1 (1 <= L_i <= C of them), slot row
+ * state_idx[i, 0..C-1] and n_i = num_accepted[i] in [1, C].
+ *   Conv: the request's conv-history row is that of slot state_idx[i, 0],
+ *     widened to W >= (K-1) + (C-1) taps.  With off = n_i - 1, the conv reads
+ *     the K-1 taps of the row starting at tap off followed by the L_i raw
+ *     inputs (a tap past the row's end reads as zero); token t's output is
+ *     silu of the K-tap product at stream positions t .. t+K-1.  The row then
+ *     becomes its taps off+1 .. off+W-L_i followed by the L_i inputs, so that
+ *     the next step's offset selects the window ending at its last accepted
+ *     token.
+ *   Recurrence: starts from the state in slot state_idx[i, n_i - 1] (the state
+ *     after the last accepted token of the previous step); q/k L2 norm, gates
+ *     and the token step are those of gdn_decode.  After token t the state is
+ *     stored into slot state_idx[i, t], rounded to state_dtype (the running
+ *     state is not rounded); a -1 column skips only that store.
+ *   A request whose slot state_idx[i, n_i - 1] is -1 is padding: zero output,
+ *     neither pool touched.
+ * The pages leave open which slot holds a request's conv row; column 0 is
+ * taken (the row is shifted in place rather than copied per token, so it
+ * needs one fixed slot per request).
+ *
+ * Arguments:
+ *   dims                  as gdn_decode; K >= 2; dims.conv_state_len = W >= (K-1) + (C-1).
+ *   num_reqs, total_tokens, cu_seqlens_host/_dev: as gdn_prepare (N requests, T tokens), with
+ *                         every request's token count at most C.
+ *   mixed_qkv, a_raw, b_raw, act_dtype, conv_weight, A_log, dt_bias: as gdn_prepare, T rows.
+ *   conv_state_pool       device [num_slots, Cc, W] in act_dtype, in place.
+ *   ssm_state_pool        device [num_slots, Hv, Dv, Dk] in state_dtype, in place.
+ *   num_cols              C, 1 <= C <= 8.
+ *   state_idx_dev         device int32 [N, C].
+ *   num_accepted_dev      device int32 [N].
+ *   state_idx_host, num_accepted_host  host copies for validation (both or neither): n_i in
+ *                         [1, C]; every entry -1 or in [0, num_slots); a live request's column 0
+ *                         live; live slots distinct across the whole table.  With neither, the
+ *                         kernel treats a request whose n_i, initial slot or column-0 slot is out
+ *                         of range as padding and skips stores to out-of-range columns, and
+ *                         repeated slots race.
+ *   scale                 query scale.
+ *   out                   device [T, Hv, Dv] in act_dtype.
+ */
+gdn_status gdn_decode_spec(const gdn_dims* dims, int32_t num_reqs, int64_t total_tokens,
+                           const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                           const void* mixed_qkv, int64_t mixed_row_stride, const void* a_raw,
+                           int64_t a_row_stride, const void* b_raw, int64_t b_row_stride,
+                           gdn_dtype act_dtype, const void* conv_weight, const float* A_log,
+                           const float* dt_bias, void* conv_state_pool, void* ssm_state_pool,
+                           gdn_dtype state_dtype, int32_t num_slots, int32_t num_cols,
+                           const int32_t* state_idx_dev, const int32_t* num_accepted_dev,
+                           const int32_t* state_idx_host, const int32_t* num_accepted_host,
+                           float scale, void* out, void* stream);
 
 /*
  * gdn_gated_rmsnorm -- the layer's output epilogue, for the output of

@@ -62,3 +62,16 @@ def prefill(d, cu, q, k, v, g, beta, ssm_pool, slots, has_init, qkv: str, state:
                            has_initial_state=dev(np.asarray(has_init, np.uint8)), use_qk_l2norm=l2norm)
     torch.cuda.synchronize()
     return host(out), host(sp)
+
+
+def decode_spec(d, inp, act: str, state: str, scale: float, conv_pool=None, ssm_pool=None, validate: bool = True):
+    T = int(inp["cu"][-1])
+    cp = dev(inp["conv_pool"] if conv_pool is None else conv_pool, act)
+    sp = dev(inp["ssm_pool"] if ssm_pool is None else ssm_pool, state)
+    out = torch.empty(T, d.Hv, d.Dv, device=DEV, dtype=TORCH_DTYPE[act])
+    gdn.gdn_decode_spec(gdims(d), dev(inp["cu"]), dev(inp["x"], act), dev(inp["a"], act), dev(inp["b"], act),
+                        dev(inp["w"], act), dev(inp["A_log"]), dev(inp["dt_bias"]), cp, sp,
+                        dev(np.ascontiguousarray(inp["state_idx"], np.int32)),
+                        dev(np.ascontiguousarray(inp["num_accepted"], np.int32)), out, scale, validate=validate)
+    torch.cuda.synchronize()
+    return host(out), host(cp), host(sp)

@@ -205,3 +205,51 @@ def test_gated_rmsnorm_rejects_bad_arguments(lib):
 
 def test_gated_rmsnorm_empty_is_a_no_op(lib):
     assert _norm(lib, T=0) == OK
+
+
+def _wdims(Hk=2, Hv=4, Dk=128, Dv=128, K=4, W=0):
+    return ctypes.byref(gdn._Dims(Hk, Hv, Dk, Dv, K, W))
+
+
+def test_conv_state_len_is_checked(lib):
+    # conv rows narrower than K-1 taps, or absurdly wide, are refused by every entry point
+    assert _prepare(lib, dims=_wdims(W=2)) == SHAPE and "conv_state_len" in _err(lib)
+    assert _prepare(lib, dims=_wdims(W=2000)) == SHAPE
+    assert _decode(lib, dims=_wdims(W=1)) == SHAPE and "conv_state_len" in _err(lib)
+
+
+def _spec(lib, dims=None, N=2, T=8, cu=(0, 4, 8), cols=4, sidx=((0, 1, 2, 3), (4, 5, 6, 7)), nat=(1, 2),
+          num_slots=8, act=1, state=0, validate=True, ssm=FAKE, W=6):
+    cu_a, cu_p = _arr(cu)
+    si_a, si_p = _arr(np.asarray(sidx).ravel())
+    na_a, na_p = _arr(nat)
+    d = dims if dims is not None else _wdims(W=W)
+    return lib.gdn_decode_spec(d, N, T, cu_p, FAKE, FAKE, 1 << 20, FAKE, 64, FAKE, 64, act, FAKE, FAKE, FAKE, FAKE, ssm,
+                               state, num_slots, cols, FAKE, FAKE, si_p if validate else None,
+                               na_p if validate else None, ctypes.c_float(0.1), FAKE, None)
+
+
+def test_decode_spec_rejects_bad_arguments(lib):
+    assert _spec(lib, dims=_wdims(K=1, W=3)) == SHAPE and "conv_kernel" in _err(lib)
+    assert _spec(lib, cols=9, sidx=np.arange(18).reshape(2, 9), num_slots=18, W=12) == SHAPE
+    assert _spec(lib, W=5) == SHAPE and "narrower" in _err(lib)          # needs (K-1)+(cols-1) = 6
+    assert _spec(lib, dims=_wdims(W=0)) == SHAPE                          # rows of K-1 taps are too narrow
+    assert _spec(lib, cu=(0, 5, 8)) == SHAPE and "more than num_cols" in _err(lib)
+    assert _spec(lib, cu=(0, 4, 4), T=4) == SHAPE and "empty" in _err(lib)
+    assert _spec(lib, nat=(0, 1)) == INDEX and "num_accepted" in _err(lib)
+    assert _spec(lib, nat=(5, 1)) == INDEX
+    assert _spec(lib, sidx=((0, 1, 2, 3), (4, 5, 6, 8))) == INDEX and "out of range" in _err(lib)
+    assert _spec(lib, sidx=((0, 1, 2, 3), (4, 5, 6, 3))) == INDEX and "more than once" in _err(lib)
+    assert _spec(lib, sidx=((0, 1, 2, 3), (-1, 5, 6, 7))) == INDEX and "column 0" in _err(lib)
+    assert _spec(lib, sidx=((0, 1, 2, 3), (4, -2, 6, 7))) == INDEX
+    assert _spec(lib, act=2) == DTYPE
+    assert _spec(lib, state=3) == DTYPE
+    assert _spec(lib, ssm=FAKE + 4) == INVALID
+    assert _spec(lib, num_slots=0) == SHAPE
+    # Hv/Hk = 32 value heads per key head of Dv = 256 do not fit one workgroup's LDS at 8 columns
+    assert _spec(lib, dims=_wdims(Hk=1, Hv=32, Dv=256, W=10), cols=8, sidx=np.arange(16).reshape(2, 8),
+                 num_slots=16, cu=(0, 8, 16), T=16) == SHAPE and "too large" in _err(lib)
+
+
+def test_decode_spec_empty_is_a_no_op(lib):
+    assert _spec(lib, N=0, T=0, cu=(0,), sidx=np.zeros((0, 4)), nat=()) == OK
