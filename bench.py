@@ -11,7 +11,9 @@ shapes (Hk=16, Hv=32, Dk=Dv=128, K=4):
 value = (256 + 4096) tokens / step time.  Per-kernel times come from HIP
 events recorded on the stream the kernels run on.  A bounded sample of the
 same work is also run through the f64 CPU oracle on the host cores
-(cpu_baseline).
+(cpu_baseline).  After the timed region the output epilogue and the
+speculative multi-token decode (256 requests x 4 tokens) are timed on their
+own and reported beside the step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--epilogue-only", action="store_true",
                     help="only run the output epilogue kernels (fused gated decode, standalone gated RMS norm)")
+    ap.add_argument("--spec-only", action="store_true",
+                    help="only run the speculative multi-token decode (gdn_decode_spec) workload")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -282,6 +286,84 @@ def epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, sl
     }
 
 
+def spec_bytes(N, L, Hk, Hv, Dk, Dv, K, W, state_bytes=4, act_bytes=2):
+    """Algorithmic HBM bytes of one gdn_decode_spec call with N requests of L
+    tokens: the initial state read once and L snapshots written per request,
+    the widened conv row read and written, every other operand once."""
+    Cc = 2 * Hk * Dk + Hv * Dv
+    T = N * L
+    return ((1 + L) * N * Hv * Dv * Dk * state_bytes   # state: one read, L snapshot writes
+            + 2 * N * Cc * W * act_bytes               # conv rows read + write
+            + T * Cc * act_bytes                       # raw projections
+            + 2 * T * Hv * act_bytes                   # a, b
+            + T * Hv * Dv * act_bytes                  # out
+            + N * (L + 1 + 1) * 4                      # slot table, num_accepted, offsets
+            + Cc * K * act_bytes + 2 * Hv * 4)         # conv weight, A_log, dt_bias
+
+
+def speculative(torch, gdn, reps=20):
+    """The speculative decode workload (gdn_inputs.spec_batch): HIP events on
+    the kernel's stream, median of ``reps`` calls after 3 untimed ones.  Each
+    call draws its own num_accepted (seeded), so successive calls start from
+    different columns."""
+    from gdn_inputs import spec_batch, spec_inputs
+    sb = spec_batch()
+    d = sb["dims"]
+    N, C = sb["num_reqs"], sb["cols"]
+    inp = spec_inputs(d, N, C, sb["num_slots"], sb["act_dtype"], sb["state_dtype"], sb["seed"])
+    dev = torch.device("cuda:0")
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt=f32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    x, w, a, b = t(inp["x"], bf), t(inp["w"], bf), t(inp["a"], bf), t(inp["b"], bf)
+    A, dt_ = t(inp["A_log"]), t(inp["dt_bias"])
+    conv, ssm = t(inp["conv_pool"], bf), t(inp["ssm_pool"])
+    del inp["ssm_pool"]
+    cu_h, sidx_h = inp["cu"], inp["state_idx"]
+    cu, sidx = torch.from_numpy(cu_h).to(dev), torch.from_numpy(sidx_h).to(dev)
+    rng = np.random.default_rng(sb["seed"] + 1)
+    nat_h = [rng.integers(1, C + 1, size=N).astype(np.int32) for _ in range(reps + 3)]
+    nat = [torch.from_numpy(n).to(dev) for n in nat_h]
+    out = torch.empty(N * C, d.Hv, d.Dv, device=dev, dtype=bf)
+    gd = gdn.Dims(d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    scale = 1.0 / math.sqrt(d.Dk)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps + 3):
+        e = ev[i - 3] if i >= 3 else None
+        if e:
+            e[0].record(stream)
+        gdn.gdn_decode_spec(gd, cu, x, a, b, w, A, dt_, conv, ssm, sidx, nat[i], out, scale, cu_seqlens_host=cu_h,
+                            state_idx_host=sidx_h, num_accepted_host=nat_h[i], stream=stream)
+        if e:
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    W = conv.shape[2]
+    nb = spec_bytes(N, C, d.Hk, d.Hv, d.Dk, d.Dv, d.K, W)
+    gbs = nb / (float(np.median(ms)) * 1e-3) / 1e9
+    # reference for a write-dominated stream: torch's fill of a buffer the
+    # size of one call's snapshot writes (HBM writes run well below 8 TB/s)
+    del conv, ssm
+    fill = torch.empty(N * C * d.Hv * d.Dv * d.Dk, dtype=f32, device=dev)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for i in range(6):
+        if i:
+            fev[i - 1][0].record(stream)
+        fill.fill_(float(i))
+        if i:
+            fev[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    fill_gbs = fill.numel() * 4 / (float(np.median([e[0].elapsed_time(e[1]) for e in fev])) * 1e-3) / 1e9
+    del fill
+    return {"workload": f"{sb['name']}: {N} requests x {C} tokens, {sb['num_slots']}-slot f32 state pool, "
+                        f"conv rows of {W} taps, bf16 activations",
+            "tokens_per_s": N * C / (float(np.median(ms)) * 1e-3), **stats_us(ms), "bytes_per_launch": nb,
+            "fill_GBps": fill_gbs, "frac_of_fill": gbs / fill_gbs,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "kernel": "spec_decode_kernel",
+                         "traffic": measured_traffic("spec_decode_kernel", ["gdn_spec.hip", "gdn_device.h"])}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -304,6 +386,9 @@ def main():
     from gdn_inputs import decode_batch, decode_slot_sets, make_inputs, prefill_single
 
     gdn.load_library()
+    if args.spec_only:
+        print(json.dumps({"decode_spec": speculative(torch, gdn, reps=args.steps)}), flush=True)
+        return
     dev = torch.device("cuda:0")
     bf, f32 = torch.bfloat16, torch.float32
 
@@ -384,8 +469,9 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l, epi = None, None, None
+    copy_gbs, cold_l, epi, spec = None, None, None, None
     if not args.no_extras:
+        spec = speculative(torch, gdn)
         epi = epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dcfg.scale,
                        stream, T)
         copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
@@ -439,6 +525,7 @@ def main():
         "roofline": rl,
         "copy_GBps": copy_gbs,
         "epilogue": epi,
+        "decode_spec": spec,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -41,6 +41,10 @@ constexpr int kSpecWaves = 4;
 constexpr int kSpecThreads = kSpecWaves * 64;
 constexpr int kSpecLoads = 4;     // 16-byte state loads per lane per batch (two batches in flight)
 constexpr int kSpecMaxCols = 8;
+// 16-byte state loads per row per lane: with two, a row of 128 f32 columns
+// spans 16 lanes, and its sums reduce within a 16-lane row of the wave
+constexpr int kSpecVecsPerRow = 2;
+constexpr int kSpecMaxKeep = 16;  // conv-row taps kept in registers across the shift
 
 // LDS floats: per token the 2*Dk + R conv outputs, R outputs, r decays, r betas
 // and 4 reductions; plus the C slot columns.
@@ -50,11 +54,14 @@ __host__ __device__ inline int spec_lds_floats(int Dk, int R, int r, int cols) {
 
 template <typename ActT, typename StT, int DK>
 __global__ __launch_bounds__(kSpecThreads) void spec_decode_kernel(SpecDecodeParams p) {
-  constexpr int SV = Elem<StT>::kVec;       // state elements per lane load
-  constexpr int LPR = DK / SV;              // lanes per state row
+  constexpr int SV = Elem<StT>::kVec;       // state elements per 16-byte load
+  constexpr int NV = kSpecVecsPerRow < DK / SV ? kSpecVecsPerRow : DK / SV;  // 16-byte loads per row per lane
+  constexpr int LPR = DK / (SV * NV);       // lanes per state row
   static_assert(LPR >= 1 && LPR <= 64, "lanes per row");
+  static_assert(kSpecLoads % NV == 0, "whole rows per batch");
   constexpr int RPL = 64 / LPR;             // rows per wave load
-  constexpr int ROWS_PER_ITER = kSpecWaves * kSpecLoads * RPL;
+  constexpr int RPB = kSpecLoads / NV;      // rows per lane per batch
+  constexpr int ROWS_PER_ITER = kSpecWaves * RPB * RPL;
 
   extern __shared__ float smem[];
   const int kh = blockIdx.x;
@@ -84,14 +91,22 @@ __global__ __launch_bounds__(kSpecThreads) void spec_decode_kernel(SpecDecodePar
   }
   const StT* __restrict__ S0 = static_cast<const StT*>(p.ssm_pool) + ((int64_t)init * p.Hv + (int64_t)kh * r) * Dv * DK;
 
+  // a lane holds NV groups of SV columns of a row, LPR*SV columns apart, so
+  // that each load instruction of a wave reads whole 256-byte row segments
   const int sub = lane / LPR;          // row within this wave's load
-  const int col = (lane % LPR) * SV;   // first state column of this lane
+  const int col = (lane % LPR) * SV;   // first column of the lane's first group
   auto row_of = [&](int it, int u) { return it * ROWS_PER_ITER + (u * kSpecWaves + wave) * RPL + sub; };
+  auto load_batch = [&](uint4* buf, int it) {
+#pragma unroll
+    for (int u = 0; u < RPB; ++u)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        buf[u * NV + v] = load_state(S0 + (int64_t)min(row_of(it, u), R - 1) * DK + v * LPR * SV + col);
+  };
 
   // the first batch of state loads goes out before the prepare work
   uint4 raw[kSpecLoads];
-#pragma unroll
-  for (int u = 0; u < kSpecLoads; ++u) raw[u] = load_state(S0 + (int64_t)min(row_of(0, u), R - 1) * DK + col);
+  load_batch(raw, 0);
 
   float* s_y = smem;                          // [L][nch] conv outputs; q, k normalised in place
   float* s_o = s_y + p.cols * nch;            // [L][R] outputs
@@ -138,11 +153,23 @@ __global__ __launch_bounds__(kSpecThreads) void spec_decode_kernel(SpecDecodePar
           for (int j = 0; j < 3; ++j) win[j] = j < K - 2 ? win[(j + 1) % 3] : (j == K - 2 ? xs[t] : win[j]);
         }
       }
-      // the row becomes taps off+1 .. off+W-L, then the L inputs; reading
-      // ahead of the write position makes the in-place shift safe
-      for (int j = 0; j < keep; ++j) {
-        const int src = off + 1 + j;
-        Elem<ActT>::store(row + j, src < W ? Elem<ActT>::load(row + src) : 0.0f);
+      // the row becomes taps off+1 .. off+W-L, then the L inputs.  The kept
+      // taps are all read before the first write; for rows wider than the
+      // register buffer, reading ahead of the write position keeps the
+      // in-place shift safe
+      if (keep <= kSpecMaxKeep) {
+        float kept[kSpecMaxKeep];
+#pragma unroll
+        for (int j = 0; j < kSpecMaxKeep; ++j)
+          kept[j] = (j < keep && off + 1 + j < W) ? Elem<ActT>::load(row + off + 1 + j) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kSpecMaxKeep; ++j)
+          if (j < keep) Elem<ActT>::store(row + j, kept[j]);
+      } else {
+        for (int j = 0; j < keep; ++j) {
+          const int src = off + 1 + j;
+          Elem<ActT>::store(row + j, src < W ? Elem<ActT>::load(row + src) : 0.0f);
+        }
       }
 #pragma unroll
       for (int t = 0; t < kSpecMaxCols; ++t)
@@ -195,42 +222,50 @@ __global__ __launch_bounds__(kSpecThreads) void spec_decode_kernel(SpecDecodePar
   StT* __restrict__ pool = static_cast<StT*>(p.ssm_pool);
   const int64_t head_off = (int64_t)kh * r * Dv * DK;
   const int iters = (R + ROWS_PER_ITER - 1) / ROWS_PER_ITER;
-  auto load_batch = [&](uint4* buf, int it) {
-#pragma unroll
-    for (int u = 0; u < kSpecLoads; ++u) buf[u] = load_state(S0 + (int64_t)min(row_of(it, u), R - 1) * DK + col);
-  };
+  // token-outer, row-inner: the kSpecLoads rows of a lane advance together,
+  // so their reductions overlap and one token's q and k are read from LDS
+  // once for all of them
   auto compute_batch = [&](const uint4* buf, int it) {
+    float st[RPB][NV * SV];
 #pragma unroll
-    for (int u = 0; u < kSpecLoads; ++u) {
-      const int row = row_of(it, u);
-      if (row >= R) continue;  // uniform across the row's lanes
-      float st[SV];
-      Elem<StT>::unpack(buf[u], st);
-      const int hl = row / Dv;
-      for (int t = 0; t < L; ++t) {
-        const float* y = s_y + t * nch;
-        float kv[SV], qv[SV];
+    for (int u = 0; u < RPB; ++u)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) Elem<StT>::unpack(buf[u * NV + v], st[u] + v * SV);
+    for (int t = 0; t < L; ++t) {
+      const float* y = s_y + t * nch;
+      float kv[NV * SV], qv[NV * SV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
-          kv[i] = y[DK + col + i];
-          qv[i] = y[col + i];
+          kv[v * SV + i] = y[DK + v * LPR * SV + col + i];
+          qv[v * SV + i] = y[v * LPR * SV + col + i];
         }
+      const float kq = s_red[t * 4 + 3];
+      const int slot = s_snap[t];
+      StT* __restrict__ snap = pool + (int64_t)max(slot, 0) * p.Hv * Dv * DK + head_off;
+#pragma unroll
+      for (int u = 0; u < RPB; ++u) {
+        const int row = row_of(it, u);
+        if (row >= R) continue;  // uniform across the row's lanes
         float p1 = 0.0f, p2 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < SV; ++i) {
-          p1 += st[i] * kv[i];
-          p2 += st[i] * qv[i];
+        for (int i = 0; i < NV * SV; ++i) {
+          p1 += st[u][i] * kv[i];
+          p2 += st[u][i] * qv[i];
         }
         p1 = group_sum<LPR>(p1);
         p2 = group_sum<LPR>(p2);
+        const int hl = row / Dv;
         const float d = s_decay[t * r + hl];
         const float delta = s_beta[t * r + hl] * (y[2 * DK + row] - d * p1);
-        const float o = d * p2 + delta * s_red[t * 4 + 3];
+        const float o = d * p2 + delta * kq;
 #pragma unroll
-        for (int i = 0; i < SV; ++i) st[i] = d * st[i] + delta * kv[i];
-        const int slot = s_snap[t];
-        if (slot >= 0) store_state(pool + (int64_t)slot * p.Hv * Dv * DK + head_off + (int64_t)row * DK + col,
-                                   Elem<StT>::pack(st));
+        for (int i = 0; i < NV * SV; ++i) st[u][i] = d * st[u][i] + delta * kv[i];
+        if (slot >= 0)
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            store_state(snap + (int64_t)row * DK + v * LPR * SV + col, Elem<StT>::pack(st[u] + v * SV));
         if ((lane % LPR) == 0) s_o[t * R + row] = o;
       }
     }

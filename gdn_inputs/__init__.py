@@ -260,3 +260,12 @@ def prefill_long(tokens: int = 32768) -> Config:
 def named_configs() -> Dict[str, Config]:
     cs = [tiny(), decode_batch(), prefill_single(), prefill_varlen(), prefill_long()]
     return {c.name: c for c in cs}
+
+
+def spec_batch() -> Dict[str, object]:
+    """The speculative decode workload at the layer's shapes: 256 requests x
+    4 tokens (the last accepted token and 3 drafts), Hk=16, Hv=32,
+    Dk=Dv=128, K=4; bf16 activations, a 1024-slot f32 state pool (4 slot
+    columns per request), conv rows of (K-1)+3 = 6 taps."""
+    return dict(name="spec_decode_n256_c4_hk16_hv32_d128", dims=QWEN_DIMS, num_reqs=256, cols=4, num_slots=1024,
+                act_dtype="bf16", state_dtype="f32", seed=1006)

@@ -202,3 +202,41 @@ def test_prefill_then_speculative_steps():
     assert_close(sp, s2, "f32", "step two state")
     np.testing.assert_array_equal(cp, c2)
     torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+def test_decode_spec_full_size_sampled_heads():
+    """The benchmarked workload (256 requests x 4 tokens, Hk=16 Hv=32
+    Dk=Dv=128, 1024-slot f32 pool), in the launch configuration the bench
+    times; the oracle checks three sampled key-head groups (heads are
+    independent: a key head's channels, value heads and state rows form a
+    complete smaller problem)."""
+    import torch
+    from gdn_inputs import spec_batch
+    from tests import gpu_runner as R
+    from tests.test_gpu_parity import slice_key_head
+    sb = spec_batch()
+    d = sb["dims"]
+    N, C = sb["num_reqs"], sb["cols"]
+    inp = spec_inputs(d, N, C, sb["num_slots"], sb["act_dtype"], sb["state_dtype"], sb["seed"])
+    scale = 1.0 / np.sqrt(d.Dk)
+    _say(f"[spec full] {sb['name']}")
+    cp = R.dev(inp["conv_pool"], "bf16")
+    sp = R.dev(inp["ssm_pool"])
+    out = torch.empty(N * C, d.Hv, d.Dv, device=R.DEV, dtype=torch.bfloat16)
+    import gated_delta_rule_prepare_amd as gdn
+    gdn.gdn_decode_spec(R.gdims(d), R.dev(inp["cu"]), R.dev(inp["x"], "bf16"), R.dev(inp["a"], "bf16"),
+                        R.dev(inp["b"], "bf16"), R.dev(inp["w"], "bf16"), R.dev(inp["A_log"]), R.dev(inp["dt_bias"]),
+                        cp, sp, R.dev(inp["state_idx"]), R.dev(inp["num_accepted"]), out, scale)
+    torch.cuda.synchronize()
+    for kh in (0, 7, 15):
+        ch, hs, sd = slice_key_head(d, kh)
+        sub = dict(inp)
+        sub["x"], sub["w"] = inp["x"][:, ch], inp["w"][ch]
+        sub["a"], sub["b"] = inp["a"][:, hs], inp["b"][:, hs]
+        sub["A_log"], sub["dt_bias"] = inp["A_log"][hs], inp["dt_bias"][hs]
+        o_ref, c_ref, s_ref = _oracle(sd, sub, scale, "f32", "bf16", conv_pool=inp["conv_pool"][:, ch],
+                                      ssm_pool=inp["ssm_pool"][:, hs])
+        assert_close(R.host(out[:, hs]), o_ref, "bf16", f"key head {kh} out")
+        assert_close(R.host(sp[:, hs]), s_ref, "f32", f"key head {kh} state pool")
+        np.testing.assert_array_equal(R.host(cp[:, torch.from_numpy(ch).to(R.DEV)]), c_ref)
