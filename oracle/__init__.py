@@ -17,6 +17,8 @@ and calls the C functions in the order the library's entry points define:
   slot-indexed pools; slot -1 gives a zero output and writes nothing.
 * :func:`decode_spec` -- speculative multi-token decode: the widened-window
   conv update, prepare, and the recurrence with a state snapshot per token.
+* :func:`kda`      -- the KDA variant (one log-decay per key channel), with
+  its optional gate, against the slot-indexed pool.
 
 Conv history pools are [S, Cc, W] with W >= K-1 taps per channel.  W = K-1 is
 the ordinary layout; a wider row (speculative decoding keeps
@@ -70,8 +72,12 @@ def _load():
                                           P, P, P, P, i32]
     lib.gdn_oracle_round.argtypes = [P, P, i64, i32]
     lib.gdn_oracle_gated_rmsnorm.argtypes = [i64, i32, P, P, P, f64, i32, P]
+    lib.gdn_oracle_kda_recurrence.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i32, f64,
+                                              P, P, P, P, i32]
+    lib.gdn_oracle_kda_gate.argtypes = [i64, i32, i32, P, P, P, P]
     for fn in (lib.gdn_oracle_conv_silu, lib.gdn_oracle_split_l2, lib.gdn_oracle_gates,
-               lib.gdn_oracle_recurrence, lib.gdn_oracle_round, lib.gdn_oracle_gated_rmsnorm):
+               lib.gdn_oracle_recurrence, lib.gdn_oracle_round, lib.gdn_oracle_gated_rmsnorm,
+               lib.gdn_oracle_kda_recurrence, lib.gdn_oracle_kda_gate):
         fn.restype = None
     _lib = lib
     return lib
@@ -232,6 +238,40 @@ def _conv_pool(dims, conv_pool) -> np.ndarray:
     return pool
 
 
+def kda_gate(g_raw, A_log, dt_bias=None):
+    """KDA gate per (token, value head, key channel):
+    g = -exp(A_log[h]) softplus(g_raw + dt_bias[h, d]); g_raw [T, Hv, Dk],
+    dt_bias [Hv, Dk] or None.  [P1] KdaChunkPrefillKernel."""
+    g_raw, A_log = _f64(g_raw), _f64(A_log)
+    T, Hv, Dk = g_raw.shape
+    db = None if dt_bias is None else _f64(dt_bias).reshape(Hv, Dk)
+    g = np.empty_like(g_raw)
+    _load().gdn_oracle_kda_gate(T, Hv, Dk, _ptr(g_raw), _ptr(A_log), None if db is None else _ptr(db), _ptr(g))
+    return g
+
+
+def kda_recurrence(q, k, v, g, beta, cu, state_in, has_init, scale: float, l2norm: bool = False,
+                   nthreads: Optional[int] = None):
+    """Token-by-token KDA (one log-decay per key channel, g [T, Hv, Dk]).
+    q, k [T, Hk, Dk]; v [T, Hv, Dv]; beta [T, Hv]; state_in [N, Hv, Dv, Dk].
+    Returns (out [T, Hv, Dv], state_out [N, Hv, Dv, Dk]).  [P1]
+    KdaHeadTokenStep, KdaGatedDeltaRuleKernel."""
+    q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    assert g.shape == (T, Hv, Dk)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    N = cu.size - 1
+    state_in = _f64(state_in).reshape(N, Hv, Dv, Dk)
+    has_init = np.ascontiguousarray(has_init, dtype=np.uint8)
+    out = np.empty((T, Hv, Dv))
+    state_out = np.empty((N, Hv, Dv, Dk))
+    _load().gdn_oracle_kda_recurrence(Hk, Hv, Dk, Dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _ptr(beta), float(scale), int(l2norm), EPS, _ptr(state_in),
+                                      _ptr(has_init), _ptr(out), _ptr(state_out), nthreads or default_threads())
+    return out, state_out
+
+
 # ---------------------------------------------------------------------------
 # Compositions matching the library's entry points.
 # ---------------------------------------------------------------------------
@@ -353,3 +393,21 @@ def decode_spec(dims, cu, x, w, a, b, A_log, dt_bias, conv_pool, ssm_pool, state
         new_ssm[snap[keep]] = round_to(S_new[keep], state_dtype)
     out[toks] = o_l
     return round_to(out, out_dtype), new_conv, new_ssm
+
+
+def kda(dims, cu, q, k, v, g, beta, ssm_pool, slots, has_init, scale: float, A_log=None, dt_bias=None,
+        state_dtype: str = "f32", out_dtype: str = "f32", nthreads: Optional[int] = None):
+    """KDA over varlen sequences against the slot-indexed state pool ([P1]
+    KdaGatedDeltaRuleKernel; with A_log given, g is the raw gate input and the
+    gate of :func:`kda_gate` is applied first, as [P1] KdaChunkPrefillKernel
+    does).  Each sequence starts from its slot's state (zero when has_init is
+    0) and its final state is written back, rounded to ``state_dtype``; a
+    sequence with no tokens writes back its initial state.  Returns
+    (out rounded to ``out_dtype``, updated pool)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    ssm_pool = _f64(ssm_pool)
+    gg = kda_gate(g, A_log, dt_bias) if A_log is not None else _f64(g)
+    out, st = kda_recurrence(q, k, v, gg, beta, cu, ssm_pool[slots], has_init, scale, False, nthreads)
+    new_pool = ssm_pool.copy()
+    new_pool[slots] = round_to(st, state_dtype)
+    return round_to(out, out_dtype), new_pool

@@ -256,6 +256,86 @@ void gdn_oracle_recurrence(int Hk, int Hv, int Dk, int Dv, int N, const int32_t*
 }
 
 /* ---------------------------------------------------------------------- */
+/* KDA: the gated delta rule with one log-decay per key channel instead of */
+/* one per head.  g is [T, Hv, Dk]; per token, for value head h:           */
+/*   S[:, d] <- exp(g[t,h,d]) S[:, d] ;  u = S k ;  delta = beta (v - u) ; */
+/*   S <- S + delta k^T ;  o = S (scale q)                                 */
+/* i.e. the state's Dk columns decay independently ([P1] KdaHeadTokenStep, */
+/* KdaGatedDeltaRuleKernel).  q and k are used as given unless l2norm.     */
+/* ---------------------------------------------------------------------- */
+static void kda_item(void* vctx, int64_t item) {
+  const rec_ctx* c = (const rec_ctx*)vctx;
+  const int64_t s = item / c->Hv;
+  const int h = (int)(item % c->Hv);
+  const int Dk = c->Dk, Dv = c->Dv, Hk = c->Hk, Hv = c->Hv;
+  const int kh = h / (Hv / Hk);
+  double* S = c->state_out + (s * Hv + h) * (int64_t)Dv * Dk;
+  const double* S0 = c->state_in + (s * Hv + h) * (int64_t)Dv * Dk;
+  for (int64_t e = 0; e < (int64_t)Dv * Dk; ++e) S[e] = c->has_init[s] ? S0[e] : 0.0;
+  double* kk = (double*)malloc(sizeof(double) * (size_t)Dk);
+  double* qq = (double*)malloc(sizeof(double) * (size_t)Dk);
+  double* dec = (double*)malloc(sizeof(double) * (size_t)Dk);
+  for (int64_t t = c->cu[s]; t < c->cu[s + 1]; ++t) {
+    const double* kr = c->k + (t * Hk + kh) * Dk;
+    const double* qr = c->q + (t * Hk + kh) * Dk;
+    double kn = 0.0, qn = 0.0;
+    for (int d = 0; d < Dk; ++d) {
+      kn += kr[d] * kr[d];
+      qn += qr[d] * qr[d];
+    }
+    const double ki = c->l2norm ? 1.0 / sqrt(kn + c->eps) : 1.0;
+    const double qi = c->l2norm ? 1.0 / sqrt(qn + c->eps) : 1.0;
+    for (int d = 0; d < Dk; ++d) {
+      kk[d] = kr[d] * ki;
+      qq[d] = qr[d] * qi * c->scale;
+      dec[d] = exp(c->g[(t * Hv + h) * Dk + d]);
+    }
+    const double bt = c->beta[t * Hv + h];
+    for (int e = 0; e < Dv; ++e) {
+      double* row = S + (int64_t)e * Dk;
+      for (int d = 0; d < Dk; ++d) row[d] *= dec[d];
+      double u = 0.0;
+      for (int d = 0; d < Dk; ++d) u += row[d] * kk[d];
+      const double delta = bt * (c->v[(t * Hv + h) * Dv + e] - u);
+      for (int d = 0; d < Dk; ++d) row[d] += delta * kk[d];
+      double o = 0.0;
+      for (int d = 0; d < Dk; ++d) o += row[d] * qq[d];
+      c->out[(t * Hv + h) * Dv + e] = o;
+    }
+  }
+  free(kk);
+  free(qq);
+  free(dec);
+}
+
+void gdn_oracle_kda_recurrence(int Hk, int Hv, int Dk, int Dv, int N, const int32_t* cu,
+                               const double* q, const double* k, const double* v, const double* g,
+                               const double* beta, double scale, int l2norm, double eps,
+                               const double* state_in, const uint8_t* has_init, double* out,
+                               double* state_out, int nthreads) {
+  rec_ctx c = {Hk, Hv, Dk, Dv, N, cu, q, k, v, g, beta, scale, l2norm, eps,
+               state_in, has_init, out, state_out};
+  parallel_for((int64_t)N * Hv, nthreads, kda_item, &c);
+}
+
+/* ---------------------------------------------------------------------- */
+/* KDA gate, per (token, value head, key channel):                         */
+/*   g = -exp(A_log[h]) * softplus(g_raw + dt_bias[h][d])                  */
+/* with softplus(x) = ln(1 + e^x); dt_bias may be absent (zero).           */
+/* [P1] KdaChunkPrefillKernel.                                             */
+/* ---------------------------------------------------------------------- */
+void gdn_oracle_kda_gate(int64_t T, int Hv, int Dk, const double* g_raw, const double* A_log,
+                         const double* dt_bias, double* g) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < Hv; ++h)
+      for (int d = 0; d < Dk; ++d) {
+        const int64_t i = (t * Hv + h) * Dk + d;
+        const double x = g_raw[i] + (dt_bias ? dt_bias[h * Dk + d] : 0.0);
+        g[i] = -exp(A_log[h]) * softplus(x);
+      }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Gated RMS norm of the output, the layer's epilogue.  For each row r of  */
 /* D values (one (token, value head) pair):                                */
 /*   out[r][j] = x[r][j] / sqrt(ms + eps) * w[j] * act(z[r][j]),           */
