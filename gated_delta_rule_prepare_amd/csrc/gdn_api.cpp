@@ -92,6 +92,26 @@ gdn_status check_offsets(const char* fn, int32_t n, int64_t t, const int32_t* cu
   return GDN_OK;
 }
 
+// Offsets that may repeat (empty sequences): cu[0] = 0, non-decreasing, cu[N] = T.
+gdn_status check_offsets_nondecreasing(const char* fn, int32_t n, int64_t t, const int32_t* cu_host,
+                                       const int32_t* cu_dev) {
+  if (n < 0 || t < 0) return fail(GDN_ERR_SHAPE, "%s: negative sizes N=%d T=%lld", fn, n, (long long)t);
+  if (n == 0) {
+    if (t != 0) return fail(GDN_ERR_SHAPE, "%s: N=0 sequences but T=%lld tokens", fn, (long long)t);
+    return GDN_OK;
+  }
+  if (t > INT32_MAX) return fail(GDN_ERR_SHAPE, "%s: T=%lld exceeds int32 offsets", fn, (long long)t);
+  if (cu_host == nullptr || cu_dev == nullptr)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens host and device pointers are required", fn);
+  if (cu_host[0] != 0 || cu_host[n] != t)
+    return fail(GDN_ERR_SHAPE, "%s: cu_seqlens must start at 0 and end at T=%lld, got %d and %d", fn,
+                (long long)t, cu_host[0], cu_host[n]);
+  for (int32_t s = 0; s < n; ++s)
+    if (cu_host[s + 1] < cu_host[s])
+      return fail(GDN_ERR_SHAPE, "%s: offsets decrease at sequence %d (%d..%d)", fn, s, cu_host[s], cu_host[s + 1]);
+  return GDN_OK;
+}
+
 // Slots: live slot in [0, num_slots), unique; -1 allowed only if allow_null.
 gdn_status check_slots(const char* fn, const int32_t* idx, int32_t n, int32_t num_slots, bool allow_null) {
   std::vector<uint8_t> seen((size_t)(num_slots > 0 ? num_slots : 0), 0);
@@ -134,7 +154,7 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
-int32_t gdn_version(void) { return 120; }
+int32_t gdn_version(void) { return 130; }
 
 gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -396,6 +416,73 @@ gdn_status gdn_gated_rmsnorm(int32_t num_tokens, int32_t num_heads, int32_t head
   return launched(fn, gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream)));
 }
 
+
+namespace {
+
+// Checks shared by the KDA entry points; fills p on success.
+gdn_status kda_common(const char* fn, const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                      const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q, const void* k,
+                      const void* v, gdn_dtype qkv_dtype, const float* g, const float* A_log, const float* dt_bias,
+                      const float* beta, void* ssm_state_pool, gdn_dtype state_dtype, int32_t num_slots,
+                      const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                      const uint8_t* has_initial_state_dev, float scale, int32_t use_qk_l2norm, void* out,
+                      gdn::KdaParams& p) {
+  gdn_status st = check_dims(fn, dims);
+  if (st != GDN_OK) return st;
+  st = check_offsets_nondecreasing(fn, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev);
+  if (st != GDN_OK) return st;
+  if (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "%s: q/k/v must be f32 or bf16", fn);
+  if (state_dtype != GDN_F32 && state_dtype != GDN_BF16 && state_dtype != GDN_F16)
+    return fail(GDN_ERR_DTYPE, "%s: state must be f32, bf16 or f16", fn);
+  if (num_seqs > 0) {
+    if (!ssm_state_pool || (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a required pointer is null", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ssm_state_pool) ||
+        !aligned16(g) || !aligned16(dt_bias))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q/k/v/out/state/g/dt_bias must be 16-byte aligned", fn);
+    if (dt_bias && !A_log)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dt_bias is only used with A_log", fn);
+    if ((slot_idx_host == nullptr) != (slot_idx_dev == nullptr))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: pass both slot index copies or neither", fn);
+    if (num_slots <= 0) return fail(GDN_ERR_SHAPE, "%s: num_slots must be positive", fn);
+    if (slot_idx_host) {
+      st = check_slots(fn, slot_idx_host, num_seqs, num_slots, false);
+      if (st != GDN_OK) return st;
+    } else if (num_seqs > num_slots) {
+      return fail(GDN_ERR_INDEX, "%s: %d sequences but only %d slots", fn, num_seqs, num_slots);
+    }
+  }
+  if (use_qk_l2norm != 0 && use_qk_l2norm != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: use_qk_l2norm must be 0 or 1", fn);
+  if (!(scale == scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
+  p = gdn::KdaParams{};
+  p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.Dk = dims->head_k_dim; p.Dv = dims->head_v_dim;
+  p.N = num_seqs; p.T = total_tokens; p.cu = cu_seqlens_dev; p.q = q; p.k = k; p.v = v; p.g = g;
+  p.A_log = A_log; p.dt_bias = dt_bias; p.beta = beta; p.ssm_pool = ssm_state_pool; p.num_slots = num_slots;
+  p.slots = slot_idx_dev; p.has_init = has_initial_state_dev; p.scale = scale; p.l2norm = use_qk_l2norm;
+  p.out = out; p.qkv = qkv_dtype; p.state = state_dtype;
+  return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status gdn_kda_recurrent(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                             const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q,
+                             const void* k, const void* v, gdn_dtype qkv_dtype, const float* g,
+                             const float* A_log, const float* dt_bias, const float* beta, void* ssm_state_pool,
+                             gdn_dtype state_dtype, int32_t num_slots, const int32_t* slot_idx_host,
+                             const int32_t* slot_idx_dev, const uint8_t* has_initial_state_dev, float scale,
+                             int32_t use_qk_l2norm, void* out, void* stream) {
+  const char* fn = "gdn_kda_recurrent";
+  gdn::KdaParams p;
+  const gdn_status st = kda_common(fn, dims, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev, q, k, v,
+                                   qkv_dtype, g, A_log, dt_bias, beta, ssm_state_pool, state_dtype, num_slots,
+                                   slot_idx_host, slot_idx_dev, has_initial_state_dev, scale, use_qk_l2norm, out, p);
+  if (st != GDN_OK) return st;
+  if (num_seqs == 0) return ok();
+  return launched(fn, gdn::launch_kda_recurrent(p, static_cast<hipStream_t>(stream)));
+}
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                                   int32_t chunk_size) {

@@ -134,6 +134,28 @@ struct PrefillParams {
   gdn_dtype qkv, state;
 };
 
+struct KdaParams {
+  int Hk, Hv, Dk, Dv;
+  int N;
+  int64_t T;
+  const int32_t* cu;      // device [N+1]
+  const void* q;          // [T, Hk, Dk] qkv
+  const void* k;
+  const void* v;          // [T, Hv, Dv] qkv
+  const float* g;         // [T, Hv, Dk]: log-decay, or the gate's input when A_log is set
+  const float* A_log;     // [Hv] or null
+  const float* dt_bias;   // [Hv, Dk] or null
+  const float* beta;      // [T, Hv]
+  void* ssm_pool;         // [S, Hv, Dv, Dk] state
+  int num_slots;
+  const int32_t* slots;   // device [N] or null
+  const uint8_t* has_init;  // device [N] or null
+  float scale;
+  int l2norm;
+  void* out;              // [T, Hv, Dv] qkv
+  gdn_dtype qkv, state;
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the HIP status
 // of the launch.
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
@@ -141,6 +163,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_spec(const SpecDecodeParams& p, hipStream_t stream);
 size_t decode_spec_lds_bytes(int Hk, int Hv, int Dk, int Dv, int cols);
 hipError_t launch_gated_rmsnorm(const GatedNormParams& p, hipStream_t stream);
+hipError_t launch_kda_recurrent(const KdaParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
 

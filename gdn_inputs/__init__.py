@@ -269,3 +269,38 @@ def spec_batch() -> Dict[str, object]:
     columns per request), conv rows of (K-1)+3 = 6 taps."""
     return dict(name="spec_decode_n256_c4_hk16_hv32_d128", dims=QWEN_DIMS, num_reqs=256, cols=4, num_slots=1024,
                 act_dtype="bf16", state_dtype="f32", seed=1006)
+
+
+def kda_inputs(dims: Dims, seqlens: Sequence[int], num_slots: int, qkv_dtype: str, state_dtype: str, seed: int,
+               gate: bool = True, dt_bias: bool = True, A_log_range=(0.0, math.log(16.0)), qk_std: float = 1.0,
+               init_std: float = 0.05, has_init: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the KDA variant (one log-decay per key channel).
+
+    q, k [T, Hk, Dk] ~ N(0, qk_std^2) and v [T, Hv, Dv] ~ N(0, 1), rounded to
+    ``qkv_dtype``; with ``gate`` the gate input g [T, Hv, Dk] ~ N(0, 1),
+    A_log ~ U(A_log_range), dt_bias [Hv, Dk] ~ U(-1, 1) (or none); without,
+    g is a log-decay -|N(0, 1)| * 0.5 directly.  beta = logistic(N(0, 1)) as
+    f32.  The state pool ~ N(0, init_std^2) in ``state_dtype``; each sequence
+    gets a distinct slot from one permutation.  Empty sequences are allowed."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(seqlens))
+    N = len(seqlens)
+    out: Dict[str, np.ndarray] = {}
+    out["q"] = _normal(rng, (T, dims.Hk, dims.Dk), qk_std, qkv_dtype)
+    out["k"] = _normal(rng, (T, dims.Hk, dims.Dk), qk_std, qkv_dtype)
+    out["v"] = _normal(rng, (T, dims.Hv, dims.Dv), 1.0, qkv_dtype)
+    if gate:
+        out["g"] = rng.standard_normal((T, dims.Hv, dims.Dk), dtype=np.float32)
+        out["A_log"] = rng.uniform(A_log_range[0], A_log_range[1], size=dims.Hv).astype(np.float32)
+        out["dt_bias"] = rng.uniform(-1.0, 1.0, size=(dims.Hv, dims.Dk)).astype(np.float32) if dt_bias else None
+    else:
+        out["g"] = (-0.5 * np.abs(rng.standard_normal((T, dims.Hv, dims.Dk)))).astype(np.float32)
+        out["A_log"] = None
+        out["dt_bias"] = None
+    z = rng.standard_normal((T, dims.Hv))
+    out["beta"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    out["ssm_pool"] = _normal(rng, (num_slots, dims.Hv, dims.Dv, dims.Dk), init_std, state_dtype)
+    out["cu"] = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    out["slots"] = rng.permutation(num_slots)[:N].astype(np.int32)
+    out["has_init"] = (np.ones(N, np.uint8) if has_init is None else np.asarray(has_init, np.uint8))
+    return out

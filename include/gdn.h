@@ -256,6 +256,46 @@ gdn_status gdn_decode_spec(const gdn_dims* dims, int32_t num_reqs, int64_t total
                            float scale, void* out, void* stream);
 
 /*
+ * gdn_kda_recurrent -- KDA, the gated delta rule with one log-decay per key
+ * channel, token by token over varlen sequences against the slot-indexed
+ * state pool ([P1] KdaHeadTokenStep, KdaGatedDeltaRuleKernel).  Per token t
+ * of a sequence, value head h, key head kh = h / (Hv/Hk), [Dv, Dk] state S:
+ *   S[:, d] <- exp(g[t,h,d]) S[:, d]   (each state column decays on its own)
+ *   u = S k;  delta = beta[t,h] (v - u);  S <- S + delta k^T;  o = S (scale q)
+ * With A_log non-NULL, g holds the gate's input and the log-decay is
+ *   -exp(A_log[h]) * softplus(g[t,h,d] + dt_bias[h,d])   (dt_bias NULL = 0)
+ * as [P1] KdaChunkPrefillKernel computes it.  q and k are used as given unless
+ * use_qk_l2norm is set.  Sequence s starts from its slot's state (zero when
+ * has_initial_state[s] is 0) and its final state is written back, rounded to
+ * state_dtype; an empty sequence writes back its initial state.
+ *
+ * Arguments:
+ *   dims                  as the other entry points (conv_kernel unused).
+ *   num_seqs, total_tokens, cu_seqlens_host/_dev: N >= 0 sequences, T tokens; cu[0] = 0,
+ *                         non-decreasing (empty sequences allowed), cu[N] = T.
+ *   q, k                  device [T, Hk, Dk] in qkv_dtype (GDN_F32 or GDN_BF16).
+ *   v                     device [T, Hv, Dv] in qkv_dtype.
+ *   g                     device f32 [T, Hv, Dk].
+ *   A_log                 device f32 [Hv] or NULL (g is then the log-decay itself).
+ *   dt_bias               device f32 [Hv, Dk] or NULL; only with A_log.
+ *   beta                  device f32 [T, Hv].
+ *   ssm_state_pool        device [num_slots, Hv, Dv, Dk] in state_dtype, in place.
+ *   slot_idx_host/_dev    int32 [N] (both NULL: slot s); -1 is refused.
+ *   has_initial_state_dev device uint8 [N] or NULL (= all 1).
+ *   scale                 query scale.
+ *   use_qk_l2norm         1: L2-normalise q and k per (token, key head), eps 1e-6.
+ *   out                   device [T, Hv, Dv] in qkv_dtype.
+ * q, k, v, g, dt_bias, out and the pool must be 16-byte aligned.
+ */
+gdn_status gdn_kda_recurrent(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                             const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q,
+                             const void* k, const void* v, gdn_dtype qkv_dtype, const float* g,
+                             const float* A_log, const float* dt_bias, const float* beta, void* ssm_state_pool,
+                             gdn_dtype state_dtype, int32_t num_slots, const int32_t* slot_idx_host,
+                             const int32_t* slot_idx_dev, const uint8_t* has_initial_state_dev, float scale,
+                             int32_t use_qk_l2norm, void* out, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- the layer's output epilogue, for the output of
  * gdn_prefill_varlen (or of gdn_decode): for every token t and value head h,
  * over the Dv values of the head,

@@ -396,18 +396,19 @@ def decode_spec(dims, cu, x, w, a, b, A_log, dt_bias, conv_pool, ssm_pool, state
 
 
 def kda(dims, cu, q, k, v, g, beta, ssm_pool, slots, has_init, scale: float, A_log=None, dt_bias=None,
-        state_dtype: str = "f32", out_dtype: str = "f32", nthreads: Optional[int] = None):
+        state_dtype: str = "f32", out_dtype: str = "f32", l2norm: bool = False, nthreads: Optional[int] = None):
     """KDA over varlen sequences against the slot-indexed state pool ([P1]
     KdaGatedDeltaRuleKernel; with A_log given, g is the raw gate input and the
     gate of :func:`kda_gate` is applied first, as [P1] KdaChunkPrefillKernel
     does).  Each sequence starts from its slot's state (zero when has_init is
     0) and its final state is written back, rounded to ``state_dtype``; a
-    sequence with no tokens writes back its initial state.  Returns
+    sequence with no tokens writes back its initial state.  With ``l2norm``
+    q and k are L2-normalised per (token, key head) first (eps 1e-6).  Returns
     (out rounded to ``out_dtype``, updated pool)."""
     slots = np.asarray(slots, dtype=np.int64)
     ssm_pool = _f64(ssm_pool)
     gg = kda_gate(g, A_log, dt_bias) if A_log is not None else _f64(g)
-    out, st = kda_recurrence(q, k, v, gg, beta, cu, ssm_pool[slots], has_init, scale, False, nthreads)
+    out, st = kda_recurrence(q, k, v, gg, beta, cu, ssm_pool[slots], has_init, scale, l2norm, nthreads)
     new_pool = ssm_pool.copy()
     new_pool[slots] = round_to(st, state_dtype)
     return round_to(out, out_dtype), new_pool

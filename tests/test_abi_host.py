@@ -253,3 +253,32 @@ def test_decode_spec_rejects_bad_arguments(lib):
 
 def test_decode_spec_empty_is_a_no_op(lib):
     assert _spec(lib, N=0, T=0, cu=(0,), sidx=np.zeros((0, 4)), nat=()) == OK
+
+
+def _kda(lib, dims=None, N=2, T=10, cu=(0, 4, 10), qkv=1, state=0, slots=(1, 0), num_slots=2, g=FAKE, A=None,
+         bias=None, q=FAKE, l2=0, ssm=FAKE):
+    cu_a, cu_p = _arr(cu)
+    sl_a, sl_p = _arr(slots) if slots is not None else (None, None)
+    d = dims if dims is not None else _dims()
+    return lib.gdn_kda_recurrent(d, N, T, cu_p, FAKE, q, FAKE, FAKE, qkv, g, A, bias, FAKE, ssm, state, num_slots,
+                                 sl_p, FAKE if slots is not None else None, None, ctypes.c_float(0.1), l2, FAKE, None)
+
+
+def test_kda_recurrent_rejects_bad_arguments(lib):
+    assert _kda(lib, dims=_dims(Hk=3, Hv=4)) == SHAPE
+    assert _kda(lib, cu=(0, 5, 4)) == SHAPE and "decrease" in _err(lib)
+    assert _kda(lib, cu=(1, 4, 10)) == SHAPE
+    assert _kda(lib, qkv=2) == DTYPE
+    assert _kda(lib, state=5) == DTYPE
+    assert _kda(lib, g=None) == INVALID
+    assert _kda(lib, g=FAKE + 4) == INVALID and "aligned" in _err(lib)
+    assert _kda(lib, bias=FAKE) == INVALID and "A_log" in _err(lib)
+    assert _kda(lib, slots=(0, 0)) == INDEX
+    assert _kda(lib, slots=(0, 2)) == INDEX
+    assert _kda(lib, slots=(-1, 0)) == INDEX
+    assert _kda(lib, l2=2) == INVALID
+    assert _kda(lib, num_slots=0) == SHAPE
+
+
+def test_kda_recurrent_empty_is_a_no_op(lib):
+    assert _kda(lib, N=0, T=0, cu=(0,), slots=()) == OK

@@ -1,0 +1,63 @@
+"""Parity of the KDA entry points (one log-decay per key channel; vllm.cpp
+cpu_ops.cpp KdaHeadTokenStep, KdaGatedDeltaRuleKernel, KdaChunkPrefillKernel)
+with the f64 oracle, through the C ABI.
+
+Tolerances as for the GDN path: f32 allclose(atol=1e-4, rtol=1e-4); bf16
+max-abs 2e-2; f16 max-abs 2e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gdn_inputs import Dims, kda_inputs
+from tests.test_gpu_parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _runner():
+    from tests import gpu_runner
+    return gpu_runner
+
+
+def _oracle(d, inp, scale, l2norm, qkv, sdt, ssm_pool=None):
+    return oracle.kda(d, inp["cu"], inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                      inp["ssm_pool"] if ssm_pool is None else ssm_pool, inp["slots"], inp["has_init"], scale,
+                      A_log=inp["A_log"], dt_bias=inp["dt_bias"], state_dtype=sdt, out_dtype=qkv, l2norm=l2norm)
+
+
+REC_CASES = [
+    # name, dims, seqlens, qkv, state, options
+    ("bf16_f32_gate_bias_l2", Dims(2, 4, 128, 128, 4), (1, 2, 17, 64, 100), "bf16", "f32",
+     dict(gate=True, dt_bias=True, l2=True)),
+    ("f32_bf16_nogate_small_qk", Dims(1, 2, 64, 64, 4), (5, 33), "f32", "bf16",
+     dict(gate=False, l2=False, qk_std=0.125)),
+    ("f32_f16_gate_nobias_dk64_dv32", Dims(2, 2, 64, 32, 4), (9, 0, 40), "f32", "f16",
+     dict(gate=True, dt_bias=False, l2=True, has_init=(1, 0, 0))),
+    ("bf16_f32_mild_decay_d16", Dims(2, 8, 16, 16, 4), (3, 70), "bf16", "f32",
+     dict(gate=True, dt_bias=True, l2=True, A_log_range=(-3.0, 0.0))),
+    ("f32_f32_d256_dv128", Dims(1, 2, 256, 128, 4), (12,), "f32", "f32", dict(gate=True, dt_bias=True, l2=True)),
+    ("decode_like_256x1", Dims(4, 8, 128, 128, 4), (1,) * 64, "bf16", "f32", dict(gate=True, dt_bias=True, l2=True)),
+]
+
+
+@pytest.mark.parametrize("name,d,lens,qkv,sdt,opts", REC_CASES, ids=[c[0] for c in REC_CASES])
+def test_kda_recurrent_parity(name, d, lens, qkv, sdt, opts):
+    R = _runner()
+    opts = dict(opts)
+    l2 = opts.pop("l2")
+    seed = 500 + [c[0] for c in REC_CASES].index(name)
+    inp = kda_inputs(d, lens, len(lens) + 3, qkv, sdt, seed, **opts)
+    scale = 1.0 / np.sqrt(d.Dk)
+    _say(f"[kda recurrent] {name} T={inp['cu'][-1]}")
+    out, sp = R.kda_recurrent(d, inp, qkv, sdt, scale, l2)
+    o_ref, s_ref = _oracle(d, inp, scale, l2, qkv, sdt)
+    assert_close(out, o_ref, qkv, f"{name} out")
+    assert_close(sp, s_ref, sdt, f"{name} state pool")
