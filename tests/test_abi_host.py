@@ -266,7 +266,7 @@ def _kda(lib, dims=None, N=2, T=10, cu=(0, 4, 10), qkv=1, state=0, slots=(1, 0),
 
 def test_kda_recurrent_rejects_bad_arguments(lib):
     assert _kda(lib, dims=_dims(Hk=3, Hv=4)) == SHAPE
-    assert _kda(lib, cu=(0, 5, 4)) == SHAPE and "decrease" in _err(lib)
+    assert _kda(lib, cu=(0, 5, 4), T=4) == SHAPE and "decrease" in _err(lib)
     assert _kda(lib, cu=(1, 4, 10)) == SHAPE
     assert _kda(lib, qkv=2) == DTYPE
     assert _kda(lib, state=5) == DTYPE
