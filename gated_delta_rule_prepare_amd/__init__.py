@@ -7,6 +7,7 @@ first call raises; there is no fallback path.
 
 Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`, :func:`gdn_decode_gated`,
 :func:`gdn_decode_spec`, :func:`gdn_gated_rmsnorm`, :func:`gdn_kda_recurrent`,
+:func:`gdn_kda_prefill_varlen`, :func:`gdn_kda_prefill_workspace_size`,
 :func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
 """
 from __future__ import annotations
@@ -60,7 +61,8 @@ class Dims:
 
 _lib = None
 EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
-           "gdn_prefill_workspace_size", "gdn_gated_rmsnorm", "gdn_kda_recurrent", "gdn_status_string", "gdn_last_error", "gdn_version")
+           "gdn_prefill_workspace_size", "gdn_gated_rmsnorm", "gdn_kda_recurrent",
+           "gdn_kda_prefill_varlen", "gdn_kda_prefill_workspace_size", "gdn_status_string", "gdn_last_error", "gdn_version")
 
 
 def load_library():
@@ -83,13 +85,17 @@ def load_library():
                                     P, P, P, P, f32, P, P]
     lib.gdn_kda_recurrent.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, P, P, i32, i32, P, P, P, f32, i32,
                                       P, P]
+    lib.gdn_kda_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, P, P, i32, i32, P, P, P, f32,
+                                           i32, i32, P, P, sz, P]
+    lib.gdn_kda_prefill_workspace_size.argtypes = [D, i32, i64, i32, i32]
+    lib.gdn_kda_prefill_workspace_size.restype = sz
     lib.gdn_gated_rmsnorm.argtypes = [i32, i32, i32, P, P, i64, P, f32, i32, P, i32, P]
     lib.gdn_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32, i32,
                                        i32, P, P, sz, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
     lib.gdn_prefill_workspace_size.restype = sz
     for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
-               "gdn_gated_rmsnorm", "gdn_kda_recurrent"):
+               "gdn_gated_rmsnorm", "gdn_kda_recurrent", "gdn_kda_prefill_varlen"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -281,3 +287,36 @@ def gdn_kda_recurrent(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool, 
                                _ptr(has_initial_state), float(scale), int(bool(use_qk_l2norm)), _ptr(out),
                                _stream(stream))
     _check("gdn_kda_recurrent", st)
+
+
+def gdn_kda_prefill_workspace_size(dims: Dims, num_seqs: int, total_tokens: int, qkv_dtype: int = GDN_BF16,
+                                   chunk_size: int = 64) -> int:
+    lib = load_library()
+    return int(lib.gdn_kda_prefill_workspace_size(ctypes.byref(dims.c()), num_seqs, total_tokens, chunk_size,
+                                                  qkv_dtype))
+
+
+def gdn_kda_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool, out, scale: float, A_log=None,
+                           dt_bias=None, slot_idx=None, has_initial_state=None, use_qk_l2norm: bool = False,
+                           chunk_size: int = 64, workspace=None, cu_seqlens_host=None, slot_idx_host=None,
+                           stream=None) -> None:
+    """Chunked KDA over varlen sequences (empty ones allowed); arguments as
+    :func:`gdn_kda_recurrent`.  ``workspace`` (a uint8 device tensor) is
+    allocated here with torch if not given."""
+    lib = load_library()
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    need = gdn_kda_prefill_workspace_size(dims, n, T, _dtype_code(q), chunk_size)
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_kda_prefill_varlen(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                    _ptr(v), _dtype_code(q), _ptr(g), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+                                    _ptr(ssm_state_pool), _dtype_code(ssm_state_pool), ssm_state_pool.shape[0],
+                                    _hptr(sl_h), _ptr(slot_idx), _ptr(has_initial_state), float(scale),
+                                    int(bool(use_qk_l2norm)), int(chunk_size), _ptr(out), _ptr(workspace), ws_bytes,
+                                    _stream(stream))
+    _check("gdn_kda_prefill_varlen", st)

@@ -484,6 +484,53 @@ gdn_status gdn_kda_recurrent(const gdn_dims* dims, int32_t num_seqs, int64_t tot
   return launched(fn, gdn::launch_kda_recurrent(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_kda_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                      int32_t chunk_size, gdn_dtype qkv_dtype) {
+  if (check_dims("gdn_kda_prefill_workspace_size", dims) != GDN_OK || num_seqs < 0 || total_tokens < 0) return 0;
+  if (chunk_size == 0) chunk_size = 64;
+  if (chunk_size != 64 || (qkv_dtype != GDN_F32 && qkv_dtype != GDN_BF16)) return 0;
+  return gdn::kda_prefill_workspace_bytes(dims->num_v_heads, dims->head_k_dim, dims->head_v_dim, num_seqs,
+                                          total_tokens, qkv_dtype);
+}
+
+gdn_status gdn_kda_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                  const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q,
+                                  const void* k, const void* v, gdn_dtype qkv_dtype, const float* g,
+                                  const float* A_log, const float* dt_bias, const float* beta, void* ssm_state_pool,
+                                  gdn_dtype state_dtype, int32_t num_slots, const int32_t* slot_idx_host,
+                                  const int32_t* slot_idx_dev, const uint8_t* has_initial_state_dev, float scale,
+                                  int32_t use_qk_l2norm, int32_t chunk_size, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_kda_prefill_varlen";
+  gdn::KdaParams p;
+  gdn_status st = kda_common(fn, dims, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev, q, k, v, qkv_dtype,
+                             g, A_log, dt_bias, beta, ssm_state_pool, state_dtype, num_slots, slot_idx_host,
+                             slot_idx_dev, has_initial_state_dev, scale, use_qk_l2norm, out, p);
+  if (st != GDN_OK) return st;
+  if (chunk_size == 0) chunk_size = 64;
+  if (chunk_size != 64) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: chunk_size must be 0 or 64", fn);
+  if (num_seqs == 0) return ok();
+  const size_t need = gdn::kda_prefill_workspace_bytes(dims->num_v_heads, dims->head_k_dim, dims->head_v_dim,
+                                                       num_seqs, total_tokens, qkv_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  int64_t nchunks = 0;
+  int max_chunks = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int c = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + 63) / 64;
+    nchunks += c;
+    if (c > max_chunks) max_chunks = c;
+  }
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.num_chunks = nchunks;
+  p.max_chunks_per_seq = max_chunks;
+  return launched(fn, gdn::launch_kda_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                                   int32_t chunk_size) {
   if (check_dims("gdn_prefill_workspace_size", dims) != GDN_OK || num_seqs < 0 || total_tokens < 0)

@@ -154,6 +154,11 @@ struct KdaParams {
   int l2norm;
   void* out;              // [T, Hv, Dv] qkv
   gdn_dtype qkv, state;
+  // chunked form only
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t num_chunks;     // sum over sequences of ceil(L / 64)
+  int max_chunks_per_seq;
 };
 
 // Each launcher enqueues its kernels on `stream` and returns the HIP status
@@ -164,6 +169,9 @@ hipError_t launch_decode_spec(const SpecDecodeParams& p, hipStream_t stream);
 size_t decode_spec_lds_bytes(int Hk, int Hv, int Dk, int Dv, int cols);
 hipError_t launch_gated_rmsnorm(const GatedNormParams& p, hipStream_t stream);
 hipError_t launch_kda_recurrent(const KdaParams& p, hipStream_t stream);
+hipError_t launch_kda_prefill(const KdaParams& p, hipStream_t stream);
+size_t kda_prefill_workspace_bytes(int Hv, int Dk, int Dv, int N, int64_t T, gdn_dtype qkv);
+bool kda_chunked_dims(int Dk, int Dv);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
 

@@ -115,7 +115,7 @@ constexpr int KTS = kChunk + 8;  // row stride (halves) of transposed [column][t
 // ---------------------------------------------------------------------------
 // Workspace layout.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Per (chunk, value head) block, byte offsets (D = head dim):
 //   W hi [64][D] f16, W lo [64][D] f16, U^T [D][64] f32,
@@ -283,6 +283,128 @@ __device__ __forceinline__ void store_h4_split(_Float16* hi, _Float16* lo, const
 // of the four columns 16J + 4q .. +3 of row 16I + li:
 __device__ __forceinline__ int p_frag(int I, int li, int J, int q) {
   return ((2 * I + (J >> 1)) * 64 + li + 16 * (2 * (J & 1) + (q >> 1))) * 8 + 4 * (q & 1);
+}
+
+// T = (I + A)^-1 of the 64 x 64 strictly lower A (row stride TS) into Ts;
+// Ms is 4 x 16 x 17 floats of scratch.  Diagonal block w by wave w, lane li
+// solving column li by substitution; off-diagonal blocks by distance on the
+// f32 MFMA: T_IJ = -T_II sum_K A_IK T_KJ.  Ends with a barrier.
+template <int TS>
+__device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, float* Ms) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  {
+    const int B0 = 16 * wave, j = li;
+    float tc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        const float4 v = *reinterpret_cast<const float4*>(As + (B0 + i) * TS + B0 + 4 * m4);
+        arow[4 * m4] = v.x; arow[4 * m4 + 1] = v.y; arow[4 * m4 + 2] = v.z; arow[4 * m4 + 3] = v.w;
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc += arow[m] * tc[m];  // tc[m] = 0 for m < j
+      tc[i] = i < j ? 0.0f : (i == j ? 1.0f : -acc);
+    }
+    if (lg == 0)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Ts[(B0 + i) * TS + B0 + j] = tc[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks, by distance: wave I computes T_{I, I-dist}
+  for (int dist = 1; dist < 4; ++dist) {
+    const int I = wave, J = wave - dist;
+    if (J >= 0) {
+      f32x4 M = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int K = J; K < I; ++K)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          M = mfma_f32(As[(16 * I + li) * TS + 16 * K + 4 * s + lg], Ts[(16 * K + 4 * s + lg) * TS + 16 * J + li], M);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ms[wave * 272 + (4 * lg + r) * 17 + li] = M[r];
+    }
+    __syncthreads();
+    if (J >= 0) {
+      f32x4 X = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        X = mfma_f32(Ts[(16 * I + li) * TS + 16 * I + 4 * s + lg], Ms[wave * 272 + (4 * s + lg) * 17 + li], X);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * lg + r) * TS + 16 * J + li] = -X[r];
+    }
+    __syncthreads();
+  }
+}
+
+// W = T diag(bw) K and U = T diag(bu) V, computed as W^T = K^T (T diag(bw))^T
+// and U^T = V^T (T diag(bu))^T so that each lane gets four consecutive
+// columns of a row of W / U; column tiles over the waves.  K^T and V^T are
+// [D][KTS] f16 tiles (with lo halves when K_LO / V_LO).  W is written f16 hi/lo
+// in the scan's contraction order, U^T as f32 [D][64].
+template <bool K_LO, bool V_LO, int TS, int D>
+__device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, const float* bu, const _Float16* KTh,
+                                             const _Float16* KTl, const _Float16* VTh, const _Float16* VTl,
+                                             _Float16* Wh, _Float16* Wl, float* UTg) {
+  constexpr int NCT = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  constexpr int NT = (2 * NCT + 3) / 4;  // tiles per wave
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const int i = 16 * I + li;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s <= I / 2; ++s) {
+      float tw[8], tu[8];
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const float4 v = *reinterpret_cast<const float4*>(Ts + i * TS + 32 * s + 8 * lg + 4 * e4);
+        tu[4 * e4] = v.x; tu[4 * e4 + 1] = v.y; tu[4 * e4 + 2] = v.z; tu[4 * e4 + 3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tk = 32 * s + 8 * lg + e;
+        const float tv = tk <= i ? tu[e] : 0.0f;
+        tw[e] = tv * bw[tk];
+        tu[e] = tv * bu[tk];
+      }
+      h8 twh, twl, tuh, tul;
+      split8(tw, twh, twl);
+      split8(tu, tuh, tul);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const int ct = wave + 4 * m;
+        if (ct >= 2 * NCT) break;
+        const bool isW = ct < NCT;
+        const int col0 = 16 * (isW ? ct : ct - NCT);
+        const h8 xh = ld_h8((isW ? KTh : VTh) + (col0 + li) * KTS + 32 * s + 8 * lg);
+        acc[m] = mfma_f16(xh, isW ? twh : tuh, acc[m]);
+        acc[m] = mfma_f16(xh, isW ? twl : tul, acc[m]);
+        if constexpr (K_LO || V_LO) {
+          if (isW ? K_LO : V_LO)
+            acc[m] = mfma_f16(ld_h8((isW ? KTl : VTl) + (col0 + li) * KTS + 32 * s + 8 * lg), isW ? twh : tuh, acc[m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int ct = wave + 4 * m;
+      if (ct >= 2 * NCT) break;
+      const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+      if (ct < NCT) {
+        // columns 16ct + 4lg .. +3, stored in the scan's contraction order
+        const int pos = 32 * (ct >> 1) + 8 * lg + 4 * (ct & 1);
+        store_h4_split(Wh + i * D + pos, Wl + i * D + pos, v);
+      } else {
+        const int col = 16 * (ct - NCT) + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) UTg[(col + r) * kChunk + i] = v[r];
+      }
+    }
+  }
 }
 
 template <typename QkvT, int D>
@@ -521,108 +643,345 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
           *reinterpret_cast<const uint4*>(KTl + r * KTS + 8 * c8);
   }
 
-  // T = (I + A)^-1.  Diagonal block w by wave w: lane li solves column li.
-  {
-    const int B0 = 16 * wave, j = li;
-    float tc[16];
+  unit_lower_inverse<TS>(As, Ts, Ms);
+
+  w_u_products<SPLIT, SPLIT, TS, D>(Ts, bg, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+}
+
+// ---------------------------------------------------------------------------
+// 2b. per-chunk work of KDA (one log-decay per key channel)
+// ---------------------------------------------------------------------------
+// Within a chunk, with G_t[d] the log-decay of channel d summed from the
+// chunk start through token t (vllm.cpp cpu_ops.cpp, KdaHeadTokenStep):
+//   A[t][i] = beta_t sum_d k_t[d] k_i[d] exp(G_t[d] - G_i[d])   (i < t)
+//   P[t][i] = scale sum_d q_t[d] k_i[d] exp(G_t[d] - G_i[d])    (i <= t)
+//   W = T diag(beta) (K * exp(G)),  U = T diag(beta) V,  T = (I + A)^-1
+//   O = (scale Q * exp(G)) S0^T + P Delta,  Delta = U - W S0^T
+//   S_C = S0 diag(exp(G_C)) + Delta^T (K * exp(G_C - G))
+// exp(G_t - G_i) is never formed as exp(G_t) exp(-G_i), which overflows once
+// a channel decays strongly.  With rho_I the sum through the token before
+// block I (16 tokens), for t in block I and i in an earlier block J
+//   exp(G_t - G_i) = exp(G_t - rho_I) exp(rho_I - rho_{J+1}) exp(rho_{J+1} - G_i),
+// three factors each at most 1, so the off-diagonal blocks are matrix
+// products of scaled rows (f16 hi/lo MFMA); inside a diagonal block the
+// factor is taken per pair.  The scan kernel runs unchanged on the result,
+// given q * exp(G) in place of q, exp(G_C) per state column in place of the
+// chunk's scalar decay, and 1 for every per-token decay it would apply.
+//
+// KDA block: the GDN block, then q * exp(G) rows [64][D] (f32 with f32 q/k/v,
+// else f16), then exp(G_C) [D] f32.
+template <typename QT>
+__host__ __device__ constexpr int64_t blk_kda_q(int D) { return blk_bytes(D); }
+template <typename QT>
+__host__ __device__ constexpr int64_t blk_kda_gam(int D) { return blk_bytes(D) + (int64_t)kChunk * D * (int64_t)sizeof(QT); }
+template <typename QT>
+__host__ __device__ constexpr int64_t blk_kda_bytes(int D) { return align256(blk_kda_gam<QT>(D) + (int64_t)D * 4); }
+
+template <typename QkvT>
+using KdaQ = typename std::conditional<std::is_same<QkvT, float>::value, float, f16>::type;
+
+// the log-decay of channel d at token t (the gate applied when A_log is set)
+__device__ __forceinline__ float kda_g(const KdaParams& p, int64_t t, int h, int d, int D) {
+  float x = p.g[(t * p.Hv + h) * D + d];
+  if (p.A_log) x = -expf(p.A_log[h]) * softplus_f(x + (p.dt_bias ? p.dt_bias[(int64_t)h * D + d] : 0.0f));
+  return fmaxf(x, -200.0f);  // exp below e^-200 is 0 in f32; keeps the sums finite for g = -inf
+}
+
+template <typename QkvT, int D>
+__global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) {
+  constexpr bool SPLIT = std::is_same<QkvT, float>::value;
+  using QT = KdaQ<QkvT>;
+  constexpr int NKS = D / 32;
+  constexpr int TS = kChunk + 4;        // f32 row stride of A and T
+  constexpr int GS = D + 4;             // f32 row stride of the log-decay rows
+  constexpr int CPL = D / 4;            // channels per lane in the diagonal blocks
+  static_assert(kChunk * GS <= 2 * kChunk * TS, "decay rows fit the A and T buffers");
+  __shared__ __attribute__((aligned(16))) float GA[2 * kChunk * TS];  // Gb rows, later A then T
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[D * KTS];     // (k exp(G))^T hi
+  __shared__ __attribute__((aligned(16))) _Float16 KTl[D * KTS];     // and lo
+  __shared__ __attribute__((aligned(16))) _Float16 VTh[D * KTS];
+  __shared__ __attribute__((aligned(16))) _Float16 VTl[SPLIT ? D * KTS : 8];
+  __shared__ float Ms[4 * 16 * 17];
+  __shared__ __attribute__((aligned(16))) float Bk[4][D];   // block totals rho_{J+1} - rho_J
+  __shared__ __attribute__((aligned(16))) float Er[4][D];   // exp(rho_I)
+  __shared__ __attribute__((aligned(16))) float Ec[4][D];   // exp(rho_4 - rho_{I+1})
+  __shared__ __attribute__((aligned(16))) float Em[3][D];   // exp(rho_I - rho_{J+1}): (2,0), (3,1), (3,0)
+  __shared__ float bs[kChunk], kn[kChunk], qn[kChunk];
+  float* Gb = GA;                        // [64][GS]: G_t - rho_{I(t)}
+  float* As = GA;
+  float* Ts = GA + kChunk * TS;
+
+  const int cid = blockIdx.x, h = blockIdx.y;
+  const int kh = h / (p.Hv / p.Hk);
+  const int seq = ws.chunk_seq[cid];
+  const int64_t t0 = ws.chunk_start[cid];
+  const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_kda_bytes<QT>(D);
+  _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
+  _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
+  _Float16* Ph = reinterpret_cast<_Float16*>(blk + blk_p_hi(D));
+  _Float16* Pl = reinterpret_cast<_Float16*>(blk + blk_p_lo(D));
+  _Float16* KBh = reinterpret_cast<_Float16*>(blk + blk_kt_hi(D));
+  _Float16* KBl = reinterpret_cast<_Float16*>(blk + blk_kt_lo(D));
+  float* UTg = reinterpret_cast<float*>(blk + blk_ut(D));
+  float* vec_g = reinterpret_cast<float*>(blk + blk_vec(D));
+  QT* Qg = reinterpret_cast<QT*>(blk + blk_kda_q<QT>(D));
+  float* gam_g = reinterpret_cast<float*>(blk + blk_kda_gam<QT>(D));
+
+  const int64_t qk_stride = (int64_t)p.Hk * D, v_stride = (int64_t)p.Hv * D;
+  const QkvT* kp = static_cast<const QkvT*>(p.k) + (t0 * p.Hk + kh) * D;
+  const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
+  const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
+
+  // ---- loads: V tile, the K / Q fragments of this wave's blocks
+  TransposedTile<QkvT, D> vtile;
+  vtile.load(vp, v_stride, n);
+  Raw8<QkvT> kf[4][NKS], qf[NKS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float arow[16];
+  for (int J = 0; J < 4; ++J) {
+    if (J > wave) break;
+    const int rr = min(16 * J + li, n - 1);
 #pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) {
-        const float4 v = *reinterpret_cast<const float4*>(As + (B0 + i) * TS + B0 + 4 * m4);
-        arow[4 * m4] = v.x; arow[4 * m4 + 1] = v.y; arow[4 * m4 + 2] = v.z; arow[4 * m4 + 3] = v.w;
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) acc += arow[m] * tc[m];  // tc[m] = 0 for m < j
-      tc[i] = i < j ? 0.0f : (i == j ? 1.0f : -acc);
-    }
-    if (lg == 0)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Ts[(B0 + i) * TS + B0 + j] = tc[i];
+    for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
   }
-  __syncthreads();
-  // off-diagonal blocks, by distance: wave I computes T_{I, I-dist}
-  for (int dist = 1; dist < 4; ++dist) {
-    const int I = wave, J = wave - dist;
-    if (J >= 0) {
-      f32x4 M = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int K = J; K < I; ++K)
+  {
+    const int rr = min(16 * wave + li, n - 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          M = mfma_f32(As[(16 * I + li) * TS + 16 * K + 4 * s + lg], Ts[(16 * K + 4 * s + lg) * TS + 16 * J + li], M);
+    for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
+  }
+  if (tid < kChunk) bs[tid] = tid < n ? p.beta[(t0 + tid) * p.Hv + h] : 0.0f;
+
+  // ---- per-channel running sums (f64), one thread per channel
+  if (tid < D) {
+    const int d = tid;
+    double G = 0.0, rho[5];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ms[wave * 272 + (4 * lg + r) * 17 + li] = M[r];
+    for (int I = 0; I < 4; ++I) {
+      rho[I] = G;
+      for (int j = 0; j < 16; ++j) {
+        const int t = 16 * I + j;
+        if (t < n) G += (double)kda_g(p, t0 + t, h, d, D);
+        Gb[t * GS + d] = (float)(G - rho[I]);
+      }
     }
-    __syncthreads();
-    if (J >= 0) {
-      f32x4 X = {0.0f, 0.0f, 0.0f, 0.0f};
+    rho[4] = G;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        X = mfma_f32(Ts[(16 * I + li) * TS + 16 * I + 4 * s + lg], Ms[wave * 272 + (4 * s + lg) * 17 + li], X);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * lg + r) * TS + 16 * J + li] = -X[r];
+    for (int I = 0; I < 4; ++I) {
+      Bk[I][d] = (float)(rho[I + 1] - rho[I]);
+      Er[I][d] = (float)exp(rho[I]);
+      Ec[I][d] = (float)exp(rho[4] - rho[I + 1]);
     }
-    __syncthreads();
+    Em[0][d] = (float)exp(rho[2] - rho[1]);
+    Em[1][d] = (float)exp(rho[3] - rho[2]);
+    Em[2][d] = (float)exp(rho[3] - rho[1]);
+    gam_g[d] = (float)exp(rho[4]);
   }
 
-  // W^T = K^T (T diag(beta gamma))^T and U^T = V^T (T diag(beta))^T, so each lane
-  // gets four consecutive columns of a row of W / U.  Column tiles over the waves.
-  constexpr int NT = (2 * NCT + 3) / 4;  // tiles per wave
+  // ---- row scales of this wave's block (L2 norm, else 1; zero past the end)
+  const int row = 16 * wave + li;
+  float ksc, qsc;
+  {
+    float sk = 0.0f, sq = 0.0f;
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const int i = 16 * I + li;
-    f32x4 acc[NT];
+    for (int s = 0; s < NKS; ++s) {
+      float xq[8], xk[8];
+      qf[s].get(xq);
 #pragma unroll
-    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int J = 0; J < 4; ++J)
+        if (J == wave) kf[J][s].get(xk);
 #pragma unroll
-    for (int s = 0; s <= I / 2; ++s) {
-      float tw[8], tu[8];
-#pragma unroll
-      for (int e4 = 0; e4 < 2; ++e4) {
-        const float4 v = *reinterpret_cast<const float4*>(Ts + i * TS + 32 * s + 8 * lg + 4 * e4);
-        tu[4 * e4] = v.x; tu[4 * e4 + 1] = v.y; tu[4 * e4 + 2] = v.z; tu[4 * e4 + 3] = v.w;
+      for (int i = 0; i < 8; ++i) {
+        sq += xq[i] * xq[i];
+        sk += xk[i] * xk[i];
       }
+    }
+    sk += __shfl_xor(sk, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    const bool valid = row < n;
+    ksc = valid ? (p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
+    qsc = valid ? (p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.0f;
+    if (lg == 0) {
+      kn[row] = ksc;
+      qn[row] = qsc;
+      vec_g[row] = 1.0f;                 // gamma: the decays are folded into q * exp(G)
+      vec_g[kChunk + row] = 1.0f;        // exp(G_C - G_j): folded into K^T
+      vec_g[2 * kChunk + row] = 1.0f;    // k row scale (folded)
+      vec_g[3 * kChunk + row] = valid ? 1.0f : 0.0f;  // q row scale (folded), zero past the end
+    }
+  }
+  __syncthreads();
+
+  // ---- element-wise tiles: (k exp(G))^T into LDS, (k exp(G_C - G))^T and
+  // q exp(G) into the block.  Item (t, 8 channels), t fastest.
+  vtile.store(VTh, VTl, nullptr, n);
+  for (int item = tid; item < kChunk * (D / 8); item += 256) {
+    const int t = item & (kChunk - 1), c0 = 8 * (item / kChunk), I = t >> 4;
+    const int rr = min(t, n - 1);
+    Raw8<QkvT> kr, qr;
+    kr.load(kp + rr * qk_stride + c0);
+    qr.load(qp + rr * qk_stride + c0);
+    float kx[8], qx[8];
+    kr.get(kx);
+    qr.get(qx);
+    const float ks = kn[t], qs = qn[t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = c0 + i;
+      const float gb = Gb[t * GS + d];
+      const float eg = expf(gb) * Er[I][d];                      // exp(G_t)
+      const float ec = expf(Bk[I][d] - gb) * Ec[I][d];           // exp(G_C - G_t)
+      const float kt = kx[i] * ks * eg, kb = kx[i] * ks * ec, qt = qx[i] * qs * eg;
+      const _Float16 hi = (_Float16)kt, bh = (_Float16)kb;
+      KTh[d * KTS + t] = hi;
+      KTl[d * KTS + t] = (_Float16)(kt - (float)hi);
+      KBh[d * kChunk + t] = bh;
+      KBl[d * kChunk + t] = (_Float16)(kb - (float)bh);
+      qx[i] = qt;
+    }
+    if constexpr (SPLIT) {
+      *reinterpret_cast<float4*>(Qg + t * D + c0) = make_float4(qx[0], qx[1], qx[2], qx[3]);
+      *reinterpret_cast<float4*>(Qg + t * D + c0 + 4) = make_float4(qx[4], qx[5], qx[6], qx[7]);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_f16(qx[2 * i]) | ((uint32_t)f32_to_f16(qx[2 * i + 1]) << 16);
+      *reinterpret_cast<uint4*>(Qg + t * D + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+
+  // ---- A and P of row block I = wave: lane holds row t = 16I + li,
+  // columns 16J + 4lg + r of each block J <= I
+  float av[4][4], pv[4][4];
+  {
+    const int t = row;
+    const float bt = bs[t];
+    // off-diagonal blocks on the MFMA: A operand = rows i of block J scaled by
+    // exp(rho_{J+1} - G_i) exp(rho_I - rho_{J+1}), B operand = this wave's rows
+    // scaled by exp(G_t - rho_I)
+    float lk[NKS][8], lq[NKS][8];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      float xk[8], xq[8];
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J == wave) kf[J][s].get(xk);
+      qf[s].get(xq);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int tk = 32 * s + 8 * lg + e;
-        const float tv = tk <= i ? tu[e] : 0.0f;
-        tw[e] = tv * bg[tk];
-        tu[e] = tv * bs[tk];
-      }
-      h8 twh, twl, tuh, tul;
-      split8(tw, twh, twl);
-      split8(tu, tuh, tul);
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const int ct = wave + 4 * m;
-        if (ct >= 2 * NCT) break;
-        const bool isW = ct < NCT;
-        const int col0 = 16 * (isW ? ct : ct - NCT);
-        const h8 xh = ld_h8((isW ? KTh : VTh) + (col0 + li) * KTS + 32 * s + 8 * lg);
-        acc[m] = mfma_f16(xh, isW ? twh : tuh, acc[m]);
-        acc[m] = mfma_f16(xh, isW ? twl : tul, acc[m]);
-        if constexpr (SPLIT)
-          acc[m] = mfma_f16(ld_h8((isW ? KTl : VTl) + (col0 + li) * KTS + 32 * s + 8 * lg), isW ? twh : tuh, acc[m]);
+        const float ea = expf(Gb[t * GS + 32 * s + 8 * lg + e]);
+        lk[s][e] = xk[e] * ksc * ea;
+        lq[s][e] = xq[e] * qsc * ea;
       }
     }
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-      const int ct = wave + 4 * m;
-      if (ct >= 2 * NCT) break;
-      const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
-      if (ct < NCT) {
-        // columns 16ct + 4lg .. +3, stored in the scan's contraction order
-        const int pos = 32 * (ct >> 1) + 8 * lg + 4 * (ct & 1);
-        store_h4_split(Wh + i * D + pos, Wl + i * D + pos, v);
-      } else {
-        const int col = 16 * (ct - NCT) + 4 * lg;
+    for (int J = 0; J < 3; ++J) {
+      if (J >= wave) break;
+      const int i = 16 * J + li;  // the A-operand row this lane feeds
+      const float si = kn[i];
+      const float* em = (wave - J >= 2) ? Em[wave == 2 ? 0 : (J == 1 ? 1 : 2)] : nullptr;
+      f32x4 akk = {0.0f, 0.0f, 0.0f, 0.0f}, aqk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) UTg[(col + r) * kChunk + i] = v[r];
+      for (int s = 0; s < NKS; ++s) {
+        float a[8];
+        kf[J][s].get(a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * s + 8 * lg + e;
+          float f = expf(Bk[J][d] - Gb[i * GS + d]);
+          if (em) f *= em[d];
+          a[e] *= si * f;
+        }
+        h8 ah, al, kh8, kl8, qh8, ql8;
+        split8(a, ah, al);
+        split8(lk[s], kh8, kl8);
+        split8(lq[s], qh8, ql8);
+        akk = mfma_f16(ah, kh8, akk);
+        akk = mfma_f16(ah, kl8, akk);
+        akk = mfma_f16(al, kh8, akk);
+        aqk = mfma_f16(ah, qh8, aqk);
+        if constexpr (SPLIT) {
+          aqk = mfma_f16(ah, ql8, aqk);
+          aqk = mfma_f16(al, qh8, aqk);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        av[J][r] = bt * akk[r];
+        pv[J][r] = p.scale * aqk[r];
       }
     }
   }
+  {
+    // diagonal block I = wave, exactly per pair: lane (tl, dl) takes row
+    // t = 16I + tl over channels dl*CPL .. +CPL-1; sums over the four channel
+    // groups by two exchanges.  Lane (li, lg) keeps columns 4lg .. 4lg+3.
+    const int tl = lane & 15, dl = lane >> 4;
+    const int t = 16 * wave + tl;
+    const int rt = min(t, n - 1);
+    float kt[CPL], qt[CPL], gt[CPL];
+    load_n<QkvT, CPL>(kp + rt * qk_stride + dl * CPL, kt);
+    load_n<QkvT, CPL>(qp + rt * qk_stride + dl * CPL, qt);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) gt[c] = Gb[t * GS + dl * CPL + c];
+    const float ks = kn[t], qs = qn[t];
+    float ad[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = 16 * wave + ii;
+      const int ri = min(i, n - 1);
+      float ki[CPL];
+      load_n<QkvT, CPL>(kp + ri * qk_stride + dl * CPL, ki);
+      const float si = kn[i];
+      float sa = 0.0f, sp = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float e = ii <= tl ? expf(fminf(gt[c] - Gb[i * GS + dl * CPL + c], 0.0f)) : 0.0f;
+        const float ke = ki[c] * e;
+        sa += kt[c] * ke;
+        sp += qt[c] * ke;
+      }
+      sa += __shfl_xor(sa, 16, 64);
+      sa += __shfl_xor(sa, 32, 64);
+      sp += __shfl_xor(sp, 16, 64);
+      sp += __shfl_xor(sp, 32, 64);
+      if ((ii >> 2) == dl) {
+        ad[ii & 3] = ii < tl ? bs[t] * ks * si * sa : 0.0f;
+        pd[ii & 3] = ii <= tl ? p.scale * qs * si * sp : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      if (J == wave)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          av[J][r] = ad[r];
+          pv[J][r] = pd[r];
+        }
+  }
+  // P fragments go straight to the block; blocks above the diagonal are zero
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float* v = J <= wave ? pv[J] : z;
+    if constexpr (SPLIT)
+      store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), v);
+    else
+      store_h4(Ph + p_frag(wave, li, J, lg), v);
+  }
+  __syncthreads();  // every read of the decay rows is done: A may overwrite them
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float* v = J <= wave ? av[J] : z;
+    *reinterpret_cast<float4*>(As + row * TS + 16 * J + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();
+  unit_lower_inverse<TS>(As, Ts, Ms);
+  w_u_products<true, SPLIT, TS, D>(Ts, bs, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
 }
 
 // ---------------------------------------------------------------------------
@@ -700,17 +1059,22 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 // two chunks ahead and are unconditional (the last chunk re-loads itself) so
 // that none sits under a branch.  Sequences are never empty (the host rejects
 // them), so every workgroup has a chunk.
-template <typename QkvT, typename StT, int D>
+// With KDA the block is a KDA block (kda_prep_kernel): q * exp(G) replaces q,
+// exp(G_C) per state column replaces the chunk's scalar decay, and the K^T
+// tile always has its lo half (it carries per-channel decays).
+template <typename QkvT, typename StT, int D, bool KDA>
 __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
-  constexpr bool STAGE_W = !SPLIT;  // LDS room for W next to the f32 K^T lo tiles is lacking
+  constexpr bool KT_LO = SPLIT || KDA;  // K^T lo tiles
+  constexpr bool STAGE_W = !KT_LO;      // LDS room for W next to K^T lo tiles is lacking
+  using QT = typename std::conditional<KDA, KdaQ<QkvT>, QkvT>::type;  // q rows as the scan reads them
   constexpr int NKS = D / 32;     // 32-wide k steps
   constexpr int NCT = D / 16;     // 16-column tiles of the state
   constexpr int WS = D + 8;       // f16 row stride of W and of the published state
   constexpr int KTV = D / 32;     // 16-byte K^T vectors per output-wave lane (per hi / lo)
   constexpr int WV = D / 16;      // 16-byte W vectors per output-wave lane (hi and lo)
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][D * KTS];  // K^T [column][token]
-  __shared__ __attribute__((aligned(16))) _Float16 KTl[2][SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 KTl[2][KT_LO ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 Wsh[2][STAGE_W ? 2 * kChunk * WS : 8];  // W hi rows, then lo rows
   __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
   __shared__ __attribute__((aligned(16))) _Float16 DTl[2][SPLIT ? 16 * KTS : 8];
@@ -720,11 +1084,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
   __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T rows e0 .. e0+15
   __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk];        // exp(G_C - G_j), then gamma
-  constexpr int QEV = 16 / (int)sizeof(QkvT);   // q elements per 16-byte vector
+  __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
+  constexpr int QEV = 16 / (int)sizeof(QT);     // q elements per 16-byte vector
   constexpr int QVPR = D / QEV;                  // vectors per q row
   constexpr int NQV = 16 * QVPR / 64;            // vectors per lane for a wave's 16 rows
   constexpr int QS = D + QEV;                    // row stride (elements) of the staged rows
-  __shared__ __attribute__((aligned(16))) QkvT Qsm[4][16 * QS];       // each output wave's 16 q rows
+  __shared__ __attribute__((aligned(16))) QT Qsm[4][16 * QS];         // each output wave's 16 q rows
 
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
@@ -748,13 +1113,23 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   const QkvT* qbase = static_cast<const QkvT*>(p.q) + (int64_t)kh * D;
   QkvT* obase = static_cast<QkvT*>(p.out) + (int64_t)h * D + e0;
   const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
-  auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D); };
+  constexpr int64_t kBlk = KDA ? blk_kda_bytes<QT>(D) : blk_bytes(D);
+  auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * kBlk; };
+  if (c_begin == c_end) {
+    // an empty sequence (KDA allows them): its final state is its initial
+    // state, zero without one
+    if (!has) {
+      StT* S0 = static_cast<StT*>(p.ssm_pool) + (((int64_t)slot * p.Hv + h) * D + e0) * D;
+      for (int e = tid; e < 16 * D; e += 512) Elem<StT>::store(S0 + e, 0.0f);
+    }
+    return;
+  }
   auto tok0 = [&](int cid) { return seq_start + (int64_t)kChunk * (cid - c_begin); };
   auto ntok = [&](int cid) { return (int)min((int64_t)kChunk, seq_end - tok0(cid)); };
 
   // ---- state-wave operands
   float Sf[8 * NKS];
-  h8 Wgh[SPLIT ? NKS : 1], Wgl[SPLIT ? NKS : 1];  // W fragments when they come straight from memory
+  h8 Wgh[STAGE_W ? 1 : NKS], Wgl[STAGE_W ? 1 : NKS];  // W fragments when they come straight from memory
   auto load_wg = [&](int cid) {
     if constexpr (!STAGE_W) {
       const char* b = blk_of(cid);
@@ -771,7 +1146,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   u32x4 Qraw[NQV];               // q rows 16 w4 .. 16 w4 + 15 of a chunk ahead, as stored
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
-  u32x4 KTr[KTV], KTrl[SPLIT ? KTV : 1];
+  u32x4 KTr[KTV], KTrl[KT_LO ? KTV : 1];
   u32x4 Wr[STAGE_W ? WV : 1];
   const int ot = tid - 256;      // output-wave thread index
   // a wave's q rows move whole 16-byte vectors (contiguous per row) and are
@@ -782,7 +1157,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     for (int j = 0; j < NQV; ++j) {
       const int v = lane + 64 * j, r = v / QVPR, c = v % QVPR;
       const int rr = min(16 * w4 + r, n - 1);  // rows past the end re-read the last row; their scale is 0
-      Qraw[j] = *reinterpret_cast<const u32x4*>(qbase + (tok0(cid) + rr) * qk_stride + c * QEV);
+      if constexpr (KDA)
+        Qraw[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const QT*>(blk_of(cid) + blk_kda_q<QT>(D)) +
+                                                  rr * D + c * QEV);
+      else
+        Qraw[j] = *reinterpret_cast<const u32x4*>(qbase + (tok0(cid) + rr) * qk_stride + c * QEV);
     }
   };
   auto stage_q = [&]() {
@@ -810,7 +1189,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     for (int j = 0; j < KTV; ++j) {
       const int v = ot + 256 * j;
       KTr[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_hi(D) + v * 16);
-      if constexpr (SPLIT) KTrl[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_lo(D) + v * 16);
+      if constexpr (KT_LO) KTrl[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_lo(D) + v * 16);
     }
   };
   auto stage_kt = [&](int bb) {
@@ -818,7 +1197,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     for (int j = 0; j < KTV; ++j) {
       const int v = ot + 256 * j, r = v >> 3, c8 = v & 7;
       *reinterpret_cast<u32x4*>(KTh[bb] + r * KTS + 8 * c8) = KTr[j];
-      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(KTl[bb] + r * KTS + 8 * c8) = KTrl[j];
+      if constexpr (KT_LO) *reinterpret_cast<u32x4*>(KTl[bb] + r * KTS + 8 * c8) = KTrl[j];
     }
   };
   // W hi then W lo as 2 * 64 rows of D halves; vector v covers row v / (D/8)
@@ -830,17 +1209,22 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     }
   };
   // U^T rows e0 .. e0+15 (one float4 per lane), exp(G_C - G_j) and gamma
-  float4 Ur, Vr;
+  // (and with KDA exp(G_C) per column)
+  float4 Ur, Vr, Gr;
   auto load_uv = [&](int cid) {
     const char* b = blk_of(cid);
     Ur = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + (ot >> 4)) * kChunk +
                                           4 * (ot & 15));
     const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
     Vr = *reinterpret_cast<const float4*>(v + (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)));
+    if constexpr (KDA)
+      Gr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_kda_gam<QT>(D)) + 4 * (ot % (D / 4)));
   };
   auto stage_uv = [&](int bb) {
     *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
     if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
+    if constexpr (KDA)
+      if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
   };
   auto stage_w = [&](int bb) {
     if constexpr (STAGE_W) {
@@ -951,13 +1335,20 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         float* sc = Sf + 8 * (ct >> 1) + 4 * (ct & 1);
-        f32x4 a2 = {gc * sc[0], gc * sc[1], gc * sc[2], gc * sc[3]};
+        f32x4 a2;
+        if constexpr (KDA) {
+          // this lane's four columns 16 ct + 4 lg .. +3 decay by exp(G_C) of each
+          const float4 gv = *reinterpret_cast<const float4*>(Gm[b] + 16 * ct + 4 * lg);
+          a2 = f32x4{gv.x * sc[0], gv.y * sc[1], gv.z * sc[2], gv.w * sc[3]};
+        } else {
+          a2 = f32x4{gc * sc[0], gc * sc[1], gc * sc[2], gc * sc[3]};
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const h8 kk = ld_h8(KTh[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg);
           a2 = mfma_f16(kk, eh[s], a2);
           a2 = mfma_f16(kk, el[s], a2);
-          if constexpr (SPLIT) a2 = mfma_f16(ld_h8(KTl[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg), eh[s], a2);
+          if constexpr (KT_LO) a2 = mfma_f16(ld_h8(KTl[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg), eh[s], a2);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = a2[r];
@@ -973,7 +1364,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        Raw4<QkvT> qa, qb;
+        Raw4<QT> qa, qb;
         qa.load(Qsm[w4] + li * QS + 32 * s + 4 * lg);
         qb.load(Qsm[w4] + li * QS + 32 * s + 16 + 4 * lg);
         float qx[8];
@@ -1151,7 +1542,7 @@ template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
   chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
   const int nwg = (D / 16) * p.Hv * p.N;
-  chunk_scan_kernel<QkvT, StT, D><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
+  chunk_scan_kernel<QkvT, StT, D, false><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
   return hipGetLastError();
 }
 
@@ -1176,7 +1567,57 @@ hipError_t launch_state(const PrefillParams& p, hipStream_t stream) {
   }
 }
 
+// ---- KDA
+template <typename QkvT, typename StT, int D>
+hipError_t launch_kda_chunked_d(const KdaParams& p, const ChunkWs& ws, hipStream_t stream) {
+  if (p.num_chunks > 0) kda_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
+  // the scan reads what it needs of the layer through the GDN parameter block
+  PrefillParams pp{};
+  pp.Hk = p.Hk; pp.Hv = p.Hv; pp.Dk = p.Dk; pp.Dv = p.Dv; pp.N = p.N; pp.T = p.T; pp.cu = p.cu;
+  pp.q = p.q; pp.k = p.k; pp.v = p.v; pp.beta = p.beta; pp.ssm_pool = p.ssm_pool; pp.num_slots = p.num_slots;
+  pp.slots = p.slots; pp.has_init = p.has_init; pp.scale = p.scale; pp.l2norm = p.l2norm; pp.chunk = kChunk;
+  pp.out = p.out; pp.workspace = p.workspace; pp.workspace_bytes = p.workspace_bytes; pp.num_chunks = p.num_chunks;
+  pp.max_chunks_per_seq = p.max_chunks_per_seq; pp.qkv = p.qkv; pp.state = p.state;
+  const int nwg = (D / 16) * p.Hv * p.N;
+  chunk_scan_kernel<QkvT, StT, D, true><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(pp, ws);
+  return hipGetLastError();
+}
+
+template <typename QkvT, typename StT>
+hipError_t launch_kda_typed(const KdaParams& p, hipStream_t stream) {
+  const ChunkWs ws = carve(p.workspace, p.N, p.T);
+  chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
+  switch (p.Dk) {
+    case 32: return launch_kda_chunked_d<QkvT, StT, 32>(p, ws, stream);
+    case 64: return launch_kda_chunked_d<QkvT, StT, 64>(p, ws, stream);
+    default: return launch_kda_chunked_d<QkvT, StT, 128>(p, ws, stream);
+  }
+}
+
+template <typename QkvT>
+hipError_t launch_kda_state(const KdaParams& p, hipStream_t stream) {
+  switch (p.state) {
+    case GDN_F32: return launch_kda_typed<QkvT, float>(p, stream);
+    case GDN_BF16: return launch_kda_typed<QkvT, bf16>(p, stream);
+    default: return launch_kda_typed<QkvT, f16>(p, stream);
+  }
+}
+
 }  // namespace
+
+size_t kda_prefill_workspace_bytes(int Hv, int Dk, int Dv, int N, int64_t T, gdn_dtype qkv) {
+  if (N <= 0 || !chunked_dims(Dk, Dv)) return 0;
+  const int64_t nc = max_chunks(N, T);
+  const int64_t blk = qkv == GDN_F32 ? blk_kda_bytes<float>(Dk) : blk_kda_bytes<f16>(Dk);
+  return align256((size_t)(N + 1) * 4) + 2 * align256((size_t)nc * 4) + (size_t)nc * Hv * blk;
+}
+
+bool kda_chunked_dims(int Dk, int Dv) { return chunked_dims(Dk, Dv); }
+
+hipError_t launch_kda_prefill(const KdaParams& p, hipStream_t stream) {
+  if (!chunked_dims(p.Dk, p.Dv)) return launch_kda_recurrent(p, stream);
+  return p.qkv == GDN_F32 ? launch_kda_state<float>(p, stream) : launch_kda_state<bf16>(p, stream);
+}
 
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk) {
   (void)Hk;

@@ -296,6 +296,33 @@ gdn_status gdn_kda_recurrent(const gdn_dims* dims, int32_t num_seqs, int64_t tot
                              int32_t use_qk_l2norm, void* out, void* stream);
 
 /*
+ * gdn_kda_prefill_varlen -- gdn_kda_recurrent's result computed in chunks of
+ * 64 tokens (the WY / UT form with one decay per key channel), equal to it up
+ * to rounding order ([P1] KdaChunkPrefillKernel, which defines the chunked
+ * forward as the recurrence's output).  Head dims other than Dk = Dv in
+ * {32, 64, 128} run the token-by-token kernel of gdn_kda_recurrent.
+ *
+ * Arguments: those of gdn_kda_recurrent, plus
+ *   chunk_size            0 (= 64) or 64.
+ *   workspace             device scratch of at least gdn_kda_prefill_workspace_size() bytes,
+ *                         256-byte aligned; its contents need not be initialised.
+ */
+gdn_status gdn_kda_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                  const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q,
+                                  const void* k, const void* v, gdn_dtype qkv_dtype, const float* g,
+                                  const float* A_log, const float* dt_bias, const float* beta, void* ssm_state_pool,
+                                  gdn_dtype state_dtype, int32_t num_slots, const int32_t* slot_idx_host,
+                                  const int32_t* slot_idx_dev, const uint8_t* has_initial_state_dev, float scale,
+                                  int32_t use_qk_l2norm, int32_t chunk_size, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_kda_prefill_varlen needs for N sequences of T tokens
+ * in total with q/k/v of qkv_dtype (0 when no workspace is used, or for
+ * invalid arguments). */
+size_t gdn_kda_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                      int32_t chunk_size, gdn_dtype qkv_dtype);
+
+/*
  * gdn_gated_rmsnorm -- the layer's output epilogue, for the output of
  * gdn_prefill_varlen (or of gdn_decode): for every token t and value head h,
  * over the Dv values of the head,

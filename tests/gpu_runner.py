@@ -88,3 +88,16 @@ def kda_recurrent(d, inp, qkv: str, state: str, scale: float, l2norm: bool, ssm_
                           has_initial_state=dev(inp["has_init"]), use_qk_l2norm=l2norm)
     torch.cuda.synchronize()
     return host(out[:T]), host(sp)
+
+
+def kda_prefill(d, inp, qkv: str, state: str, scale: float, l2norm: bool, ssm_pool=None):
+    T = int(inp["cu"][-1])
+    sp = dev(inp["ssm_pool"] if ssm_pool is None else ssm_pool, state)
+    out = torch.empty(max(T, 1), d.Hv, d.Dv, device=DEV, dtype=TORCH_DTYPE[qkv])
+    opt = lambda a: None if a is None else dev(a)
+    gdn.gdn_kda_prefill_varlen(gdims(d), dev(inp["cu"]), dev(inp["q"], qkv), dev(inp["k"], qkv), dev(inp["v"], qkv),
+                               dev(inp["g"]), dev(inp["beta"]), sp, out, scale, A_log=opt(inp["A_log"]),
+                               dt_bias=opt(inp["dt_bias"]), slot_idx=dev(inp["slots"]),
+                               has_initial_state=dev(inp["has_init"]), use_qk_l2norm=l2norm)
+    torch.cuda.synchronize()
+    return host(out[:T]), host(sp)

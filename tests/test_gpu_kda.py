@@ -61,3 +61,37 @@ def test_kda_recurrent_parity(name, d, lens, qkv, sdt, opts):
     o_ref, s_ref = _oracle(d, inp, scale, l2, qkv, sdt)
     assert_close(out, o_ref, qkv, f"{name} out")
     assert_close(sp, s_ref, sdt, f"{name} state pool")
+
+
+CHUNK_CASES = [
+    # name, dims, seqlens, qkv, state, options
+    ("bf16_f32_ragged_d128", Dims(2, 4, 128, 128, 4), (1, 63, 64, 65, 200, 0, 130), "bf16", "f32",
+     dict(gate=True, dt_bias=True, l2=True, has_init=(1, 0, 1, 1, 0, 0, 1))),
+    ("f32_f16_d64_nobias", Dims(2, 2, 64, 64, 4), (100, 7), "f32", "f16", dict(gate=True, dt_bias=False, l2=True)),
+    ("bf16_bf16_d32_nogate", Dims(1, 4, 32, 32, 4), (129, 3), "bf16", "bf16",
+     dict(gate=False, l2=False, qk_std=0.17)),
+    ("f32_f32_strong_decay", Dims(1, 2, 128, 128, 4), (150,), "f32", "f32",
+     dict(gate=True, dt_bias=True, l2=True, A_log_range=(2.5, 3.5))),
+    ("bf16_f32_mild_decay_long", Dims(2, 4, 128, 128, 4), (700,), "bf16", "f32",
+     dict(gate=True, dt_bias=True, l2=True, A_log_range=(-4.0, -1.0))),
+    ("f32_f32_mild_decay_d64", Dims(1, 1, 64, 64, 4), (257,), "f32", "f32",
+     dict(gate=True, dt_bias=True, l2=True, A_log_range=(-4.0, -1.0))),
+    ("fallback_dk64_dv32", Dims(2, 2, 64, 32, 4), (70, 0), "bf16", "f32", dict(gate=True, dt_bias=True, l2=True)),
+    ("all_empty", Dims(1, 2, 64, 64, 4), (0, 0), "bf16", "f32", dict(gate=True, has_init=(0, 1), l2=True)),
+]
+
+
+@pytest.mark.parametrize("name,d,lens,qkv,sdt,opts", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_kda_prefill_parity(name, d, lens, qkv, sdt, opts):
+    R = _runner()
+    opts = dict(opts)
+    l2 = opts.pop("l2")
+    seed = 600 + [c[0] for c in CHUNK_CASES].index(name)
+    inp = kda_inputs(d, lens, len(lens) + 2, qkv, sdt, seed, **opts)
+    scale = 1.0 / np.sqrt(d.Dk)
+    _say(f"[kda prefill] {name} T={inp['cu'][-1]}")
+    out, sp = R.kda_prefill(d, inp, qkv, sdt, scale, l2)
+    o_ref, s_ref = _oracle(d, inp, scale, l2, qkv, sdt)
+    if o_ref.size:
+        assert_close(out, o_ref, qkv, f"{name} out")
+    assert_close(sp, s_ref, sdt, f"{name} state pool")
