@@ -13,7 +13,8 @@ events recorded on the stream the kernels run on.  A bounded sample of the
 same work is also run through the f64 CPU oracle on the host cores
 (cpu_baseline).  After the timed region the output epilogue and the
 speculative multi-token decode (256 requests x 4 tokens) are timed on their
-own and reported beside the step.
+own and reported beside the step, and so are the KDA variant's chunked
+prefill (4096 tokens) and token-by-token decode (256 sequences).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -45,6 +46,8 @@ def parse():
                     help="only run the output epilogue kernels (fused gated decode, standalone gated RMS norm)")
     ap.add_argument("--spec-only", action="store_true",
                     help="only run the speculative multi-token decode (gdn_decode_spec) workload")
+    ap.add_argument("--kda-only", action="store_true",
+                    help="only run the KDA workloads (chunked prefill, token-by-token decode)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -364,6 +367,96 @@ def speculative(torch, gdn, reps=20):
                          "traffic": measured_traffic("spec_decode_kernel", ["gdn_spec.hip", "gdn_device.h"])}}
 
 
+def kda_prefill_flops(T, Hk, Hv, Dk, Dv, c=64):
+    """Algorithmic flops of the chunked KDA prefill on full chunks of c tokens,
+    per token and value head (the decays are per value head and channel, so
+    the chunk's K K^T and Q K^T products are per value head too):
+      A and P with the per-pair decays           4 c Dk
+      (I + A)^-1 by substitution                 2 c^2 / 3
+      W = T diag(beta) (K e^G)                   2 c Dk
+      U = T diag(beta) V,  P Delta               4 c Dv
+      W S^T, (Q e^G) S^T, Delta^T (K e^(G_C-G))  6 Dk Dv
+    Each product once; the f16 hi/lo split is not counted."""
+    return T * Hv * (4 * c * Dk + 2 * c * c / 3 + 2 * c * Dk + 4 * c * Dv + 6 * Dk * Dv)
+
+
+def kda_prefill_bytes(T, Hk, Hv, Dk, Dv, qkv_bytes=2, state_bytes=4):
+    """Algorithmic HBM bytes of one KDA prefill call from a zero state: q, k,
+    v, the gate input g [T, Hv, Dk] f32 and beta read, out and the final state
+    written."""
+    return (T * (2 * Hk * Dk + Hv * Dv) * qkv_bytes + T * Hv * Dk * 4 + T * Hv * 4
+            + T * Hv * Dv * qkv_bytes + Hv * Dv * Dk * state_bytes)
+
+
+def kda_decode_bytes(B, Hk, Hv, Dk, Dv, qkv_bytes=2, state_bytes=4):
+    """Algorithmic HBM bytes of one KDA recurrent call over B one-token
+    sequences: the state read and written, q, k, v, g, beta and out."""
+    return (2 * B * Hv * Dv * Dk * state_bytes + B * (2 * Hk * Dk + Hv * Dv) * qkv_bytes + B * Hv * Dk * 4
+            + B * Hv * 4 + B * Hv * Dv * qkv_bytes + B * 4 * 2)
+
+
+def kda(torch, gdn, reps=20):
+    """The KDA workloads (gdn_inputs.kda_prefill_workload, kda_decode_workload):
+    HIP events on the kernels' stream, median of ``reps`` calls after 3
+    untimed ones."""
+    from gdn_inputs import kda_decode_workload, kda_inputs, kda_prefill_workload
+    dev = torch.device("cuda:0")
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt=f32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for wl in (kda_prefill_workload(), kda_decode_workload()):
+        d = wl["dims"]
+        inp = kda_inputs(d, wl["seqlens"], wl["num_slots"], wl["qkv_dtype"], wl["state_dtype"], wl["seed"],
+                         has_init=wl["has_init"])
+        gd = gdn.Dims(d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+        q, k, v = t(inp["q"], bf), t(inp["k"], bf), t(inp["v"], bf)
+        g, beta, A, dtb = t(inp["g"]), t(inp["beta"]), t(inp["A_log"]), t(inp["dt_bias"])
+        pool = t(inp["ssm_pool"])
+        cu_h, sl_h = inp["cu"], inp["slots"]
+        cu, sl, hi = t(cu_h, torch.int32), t(sl_h, torch.int32), t(inp["has_init"], torch.uint8)
+        T = int(cu_h[-1])
+        out = torch.empty(T, d.Hv, d.Dv, device=dev, dtype=bf)
+        scale = 1.0 / math.sqrt(d.Dk)
+        chunked = wl["name"].startswith("kda_prefill")
+        ws = None
+        if chunked:
+            ws = torch.empty(max(gdn.gdn_kda_prefill_workspace_size(gd, len(sl_h), T, gdn.GDN_BF16), 1),
+                             dtype=torch.uint8, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps + 3):
+            e = ev[i - 3] if i >= 3 else None
+            if e:
+                e[0].record(stream)
+            if chunked:
+                gdn.gdn_kda_prefill_varlen(gd, cu, q, k, v, g, beta, pool, out, scale, A_log=A, dt_bias=dtb,
+                                           slot_idx=sl, has_initial_state=hi, use_qk_l2norm=True, workspace=ws,
+                                           cu_seqlens_host=cu_h, slot_idx_host=sl_h, stream=stream)
+            else:
+                gdn.gdn_kda_recurrent(gd, cu, q, k, v, g, beta, pool, out, scale, A_log=A, dt_bias=dtb, slot_idx=sl,
+                                      has_initial_state=hi, use_qk_l2norm=True, cu_seqlens_host=cu_h,
+                                      slot_idx_host=sl_h, stream=stream)
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        sec = float(np.median(ms)) * 1e-3
+        if chunked:
+            fl = kda_prefill_flops(T, d.Hk, d.Hv, d.Dk, d.Dv)
+            nb = kda_prefill_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv)
+            rl = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": fl / sec / 1e12 / F16_MFMA_PEAK_TFLOPS, "flops_per_launch": fl, "bytes_per_launch": nb,
+                  "hbm_frac": nb / sec / 1e9 / HBM_PEAK_GBS,
+                  "kernels": "chunk_table_kernel + kda_prep_kernel + chunk_scan_kernel (KDA)"}
+        else:
+            nb = kda_decode_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv)
+            rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb, "kernel": "kda_recurrent_kernel"}
+        res[wl["name"]] = {"tokens_per_s": T / sec, **stats_us(ms), "roofline": rl}
+        del q, k, v, g, beta, pool, out, ws
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -388,6 +481,9 @@ def main():
     gdn.load_library()
     if args.spec_only:
         print(json.dumps({"decode_spec": speculative(torch, gdn, reps=args.steps)}), flush=True)
+        return
+    if args.kda_only:
+        print(json.dumps({"kda": kda(torch, gdn, reps=args.steps)}), flush=True)
         return
     dev = torch.device("cuda:0")
     bf, f32 = torch.bfloat16, torch.float32
@@ -469,9 +565,10 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l, epi, spec = None, None, None, None
+    copy_gbs, cold_l, epi, spec, kda_r = None, None, None, None, None
     if not args.no_extras:
         spec = speculative(torch, gdn)
+        kda_r = kda(torch, gdn)
         epi = epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dcfg.scale,
                        stream, T)
         copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
@@ -526,6 +623,7 @@ def main():
         "copy_GBps": copy_gbs,
         "epilogue": epi,
         "decode_spec": spec,
+        "kda": kda_r,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

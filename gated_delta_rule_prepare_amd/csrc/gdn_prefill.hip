@@ -680,11 +680,20 @@ __host__ __device__ constexpr int64_t blk_kda_bytes(int D) { return align256(blk
 template <typename QkvT>
 using KdaQ = typename std::conditional<std::is_same<QkvT, float>::value, float, f16>::type;
 
-// the log-decay of channel d at token t (the gate applied when A_log is set)
-__device__ __forceinline__ float kda_g(const KdaParams& p, int64_t t, int h, int d, int D) {
-  float x = p.g[(t * p.Hv + h) * D + d];
-  if (p.A_log) x = -expf(p.A_log[h]) * softplus_f(x + (p.dt_bias ? p.dt_bias[(int64_t)h * D + d] : 0.0f));
-  return fmaxf(x, -200.0f);  // exp below e^-200 is 0 in f32; keeps the sums finite for g = -inf
+constexpr double kLog2e = 1.4426950408889634;
+// 2^x with the hardware exponential (about 1 ulp; 0 far below the f32 range)
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+// four consecutive elements (one 8-byte read for bf16, 16 for f32)
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* o) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
 template <typename QkvT, int D>
@@ -702,12 +711,20 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   __shared__ __attribute__((aligned(16))) _Float16 VTh[D * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 VTl[SPLIT ? D * KTS : 8];
   __shared__ float Ms[4 * 16 * 17];
-  __shared__ __attribute__((aligned(16))) float Bk[4][D];   // block totals rho_{J+1} - rho_J
+  __shared__ __attribute__((aligned(16))) float Bk[4][D];   // block totals (rho_{J+1} - rho_J) log2(e)
   __shared__ __attribute__((aligned(16))) float Er[4][D];   // exp(rho_I)
   __shared__ __attribute__((aligned(16))) float Ec[4][D];   // exp(rho_4 - rho_{I+1})
   __shared__ __attribute__((aligned(16))) float Em[3][D];   // exp(rho_I - rho_{J+1}): (2,0), (3,1), (3,0)
   __shared__ float bs[kChunk], kn[kChunk], qn[kChunk];
-  float* Gb = GA;                        // [64][GS]: G_t - rho_{I(t)}
+  // with bf16 q/k/v the chunk's K and Q rows are staged once (the diagonal
+  // blocks and the element-wise tiles read them many times)
+  constexpr bool STAGE = !SPLIT;
+  constexpr int RS = D + 8;              // row stride (elements) of the staged rows
+  __shared__ __attribute__((aligned(16))) QkvT Ks[STAGE ? kChunk * RS : 8];
+  __shared__ __attribute__((aligned(16))) QkvT Qs[STAGE ? kChunk * RS : 8];
+  // [64][GS]: the log-decays, then (G_t - rho_{I(t)}) log2(e): in base 2 every
+  // decay factor below is one exp2
+  float* Gb = GA;
   float* As = GA;
   float* Ts = GA + kChunk * TS;
 
@@ -751,24 +768,60 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
   }
   if (tid < kChunk) bs[tid] = tid < n ? p.beta[(t0 + tid) * p.Hv + h] : 0.0f;
+  if constexpr (STAGE) {
+    constexpr int VPR = D / 8, NV = kChunk * VPR / 256;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
+      *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+    }
+  }
+  // the chunk's log-decays, gate applied, all threads, 4 channels each
+  {
+    const float a = p.A_log ? -expf(p.A_log[h]) : 0.0f;
+    for (int v = tid; v < kChunk * (D / 4); v += 256) {
+      const int t = v / (D / 4), c = 4 * (v % (D / 4));
+      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < n) {
+        const float4 raw = *reinterpret_cast<const float4*>(p.g + ((t0 + t) * p.Hv + h) * D + c);
+        x[0] = raw.x; x[1] = raw.y; x[2] = raw.z; x[3] = raw.w;
+        if (p.A_log) {
+          float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (p.dt_bias) {
+            const float4 bv = *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + c);
+            bias[0] = bv.x; bias[1] = bv.y; bias[2] = bv.z; bias[3] = bv.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = a * softplus_f(x[i] + bias[i]);
+        }
+        // exp below e^-200 is 0 in f32; the clamp keeps the sums finite for g = -inf
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = fmaxf(x[i], -200.0f);
+      }
+      *reinterpret_cast<float4*>(Gb + t * GS + c) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+  __syncthreads();
 
-  // ---- per-channel running sums (f64), one thread per channel
+  // ---- per-channel running sums (f64), one thread per channel, in place
   if (tid < D) {
     const int d = tid;
     double G = 0.0, rho[5];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       rho[I] = G;
+#pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int t = 16 * I + j;
-        if (t < n) G += (double)kda_g(p, t0 + t, h, d, D);
-        Gb[t * GS + d] = (float)(G - rho[I]);
+        G += (double)Gb[t * GS + d];
+        Gb[t * GS + d] = (float)((G - rho[I]) * kLog2e);
       }
     }
     rho[4] = G;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      Bk[I][d] = (float)(rho[I + 1] - rho[I]);
+      Bk[I][d] = (float)((rho[I + 1] - rho[I]) * kLog2e);
       Er[I][d] = (float)exp(rho[I]);
       Ec[I][d] = (float)exp(rho[4] - rho[I + 1]);
     }
@@ -821,8 +874,13 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     const int t = item & (kChunk - 1), c0 = 8 * (item / kChunk), I = t >> 4;
     const int rr = min(t, n - 1);
     Raw8<QkvT> kr, qr;
-    kr.load(kp + rr * qk_stride + c0);
-    qr.load(qp + rr * qk_stride + c0);
+    if constexpr (STAGE) {
+      kr.load(Ks + t * RS + c0);
+      qr.load(Qs + t * RS + c0);
+    } else {
+      kr.load(kp + rr * qk_stride + c0);
+      qr.load(qp + rr * qk_stride + c0);
+    }
     float kx[8], qx[8];
     kr.get(kx);
     qr.get(qx);
@@ -831,8 +889,8 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     for (int i = 0; i < 8; ++i) {
       const int d = c0 + i;
       const float gb = Gb[t * GS + d];
-      const float eg = expf(gb) * Er[I][d];                      // exp(G_t)
-      const float ec = expf(Bk[I][d] - gb) * Ec[I][d];           // exp(G_C - G_t)
+      const float eg = exp2_f(gb) * Er[I][d];                    // exp(G_t)
+      const float ec = exp2_f(Bk[I][d] - gb) * Ec[I][d];         // exp(G_C - G_t)
       const float kt = kx[i] * ks * eg, kb = kx[i] * ks * ec, qt = qx[i] * qs * eg;
       const _Float16 hi = (_Float16)kt, bh = (_Float16)kb;
       KTh[d * KTS + t] = hi;
@@ -872,7 +930,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
       qf[s].get(xq);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ea = expf(Gb[t * GS + 32 * s + 8 * lg + e]);
+        const float ea = exp2_f(Gb[t * GS + 32 * s + 8 * lg + e]);
         lk[s][e] = xk[e] * ksc * ea;
         lq[s][e] = xq[e] * qsc * ea;
       }
@@ -891,7 +949,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * s + 8 * lg + e;
-          float f = expf(Bk[J][d] - Gb[i * GS + d]);
+          float f = exp2_f(Bk[J][d] - Gb[i * GS + d]);
           if (em) f *= em[d];
           a[e] *= si * f;
         }
@@ -917,40 +975,60 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   }
   {
     // diagonal block I = wave, exactly per pair: lane (tl, dl) takes row
-    // t = 16I + tl over channels dl*CPL .. +CPL-1; sums over the four channel
-    // groups by two exchanges.  Lane (li, lg) keeps columns 4lg .. 4lg+3.
+    // t = 16I + tl over the channels 16m + 4dl + j (m < D/16, j < 4), so that
+    // the four channel groups read different LDS banks; sums over the groups
+    // by two exchanges.  Lane (li, lg) keeps columns 4lg .. 4lg+3.
+    constexpr int NM = D / 16;
     const int tl = lane & 15, dl = lane >> 4;
     const int t = 16 * wave + tl;
     const int rt = min(t, n - 1);
-    float kt[CPL], qt[CPL], gt[CPL];
-    load_n<QkvT, CPL>(kp + rt * qk_stride + dl * CPL, kt);
-    load_n<QkvT, CPL>(qp + rt * qk_stride + dl * CPL, qt);
+    float kt[NM][4], qt[NM][4], gt[NM][4];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) gt[c] = Gb[t * GS + dl * CPL + c];
+    for (int m = 0; m < NM; ++m) {
+      const int c = 16 * m + 4 * dl;
+      if constexpr (STAGE) {
+        load4(Ks + t * RS + c, kt[m]);
+        load4(Qs + t * RS + c, qt[m]);
+      } else {
+        load4(kp + rt * qk_stride + c, kt[m]);
+        load4(qp + rt * qk_stride + c, qt[m]);
+      }
+      const float4 gv = *reinterpret_cast<const float4*>(Gb + t * GS + c);
+      gt[m][0] = gv.x; gt[m][1] = gv.y; gt[m][2] = gv.z; gt[m][3] = gv.w;
+    }
     const float ks = kn[t], qs = qn[t];
     float ad[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
       const int i = 16 * wave + ii;
       const int ri = min(i, n - 1);
-      float ki[CPL];
-      load_n<QkvT, CPL>(kp + ri * qk_stride + dl * CPL, ki);
       const float si = kn[i];
-      float sa = 0.0f, sp = 0.0f;
+      float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float e = ii <= tl ? expf(fminf(gt[c] - Gb[i * GS + dl * CPL + c], 0.0f)) : 0.0f;
-        const float ke = ki[c] * e;
-        sa += kt[c] * ke;
-        sp += qt[c] * ke;
+      for (int m = 0; m < NM; ++m) {
+        const int c = 16 * m + 4 * dl;
+        float ki[4];
+        if constexpr (STAGE) load4(Ks + i * RS + c, ki);
+        else load4(kp + ri * qk_stride + c, ki);
+        const float4 gv = *reinterpret_cast<const float4*>(Gb + i * GS + c);
+        const float gi[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // exponent <= 0 for i <= t; the clamp keeps the masked lanes finite
+          const float e = ii <= tl ? exp2_f(fminf(gt[m][j] - gi[j], 0.0f)) : 0.0f;
+          const float ke = ki[j] * e;
+          sa[j] += kt[m][j] * ke;
+          sp[j] += qt[m][j] * ke;
+        }
       }
-      sa += __shfl_xor(sa, 16, 64);
-      sa += __shfl_xor(sa, 32, 64);
-      sp += __shfl_xor(sp, 16, 64);
-      sp += __shfl_xor(sp, 32, 64);
+      float a = (sa[0] + sa[1]) + (sa[2] + sa[3]), pp = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      pp += __shfl_xor(pp, 16, 64);
+      pp += __shfl_xor(pp, 32, 64);
       if ((ii >> 2) == dl) {
-        ad[ii & 3] = ii < tl ? bs[t] * ks * si * sa : 0.0f;
-        pd[ii & 3] = ii <= tl ? p.scale * qs * si * sp : 0.0f;
+        ad[ii & 3] = ii < tl ? bs[t] * ks * si * a : 0.0f;
+        pd[ii & 3] = ii <= tl ? p.scale * qs * si * pp : 0.0f;
       }
     }
 #pragma unroll

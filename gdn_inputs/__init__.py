@@ -304,3 +304,20 @@ def kda_inputs(dims: Dims, seqlens: Sequence[int], num_slots: int, qkv_dtype: st
     out["slots"] = rng.permutation(num_slots)[:N].astype(np.int32)
     out["has_init"] = (np.ones(N, np.uint8) if has_init is None else np.asarray(has_init, np.uint8))
     return out
+
+
+def kda_prefill_workload() -> Dict[str, object]:
+    """The KDA prefill workload at the layer's shapes: one 4096-token sequence,
+    Hk=16, Hv=32, Dk=Dv=128, bf16 q/k/v, f32 state from zero, the gate applied
+    in the kernel (A_log ~ U(0, ln 16), dt_bias [Hv, Dk] ~ U(-1, 1)), q/k L2
+    normalised in the kernel."""
+    return dict(name="kda_prefill_T4096_hk16_hv32_d128", dims=QWEN_DIMS, seqlens=(4096,), num_slots=1,
+                qkv_dtype="bf16", state_dtype="f32", seed=1007, has_init=(0,))
+
+
+def kda_decode_workload() -> Dict[str, object]:
+    """The KDA decode workload: 256 sequences x 1 token, Hk=16, Hv=32,
+    Dk=Dv=128, bf16 q/k/v, a 512-slot f32 state pool ~ N(0, 0.05), gate in
+    the kernel, q/k L2 normalised."""
+    return dict(name="kda_decode_b256_hk16_hv32_d128", dims=QWEN_DIMS, seqlens=(1,) * 256, num_slots=512,
+                qkv_dtype="bf16", state_dtype="f32", seed=1008, has_init=None)
