@@ -711,6 +711,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   __shared__ __attribute__((aligned(16))) _Float16 VTh[D * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 VTl[SPLIT ? D * KTS : 8];
   __shared__ float Ms[4 * 16 * 17];
+  __shared__ float Px[4 * 16 * 17];     // exact same-sub-block entries of P (those of A go to Ms)
   __shared__ __attribute__((aligned(16))) float Bk[4][D];   // block totals (rho_{J+1} - rho_J) log2(e)
   __shared__ __attribute__((aligned(16))) float Er[4][D];   // exp(rho_I)
   __shared__ __attribute__((aligned(16))) float Ec[4][D];   // exp(rho_4 - rho_{I+1})
@@ -777,27 +778,39 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
       *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
     }
   }
-  // the chunk's log-decays, gate applied, all threads, 4 channels each
+  // the chunk's log-decays, gate applied, all threads, 4 channels each: every
+  // load is issued before any is used
   {
+    constexpr int NG = kChunk * (D / 4) / 256;
     const float a = p.A_log ? -expf(p.A_log[h]) : 0.0f;
-    for (int v = tid; v < kChunk * (D / 4); v += 256) {
-      const int t = v / (D / 4), c = 4 * (v % (D / 4));
-      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < n) {
-        const float4 raw = *reinterpret_cast<const float4*>(p.g + ((t0 + t) * p.Hv + h) * D + c);
-        x[0] = raw.x; x[1] = raw.y; x[2] = raw.z; x[3] = raw.w;
+    float4 raw[NG], bias[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int v = tid + 256 * j, t = v / (D / 4), c = 4 * (v % (D / 4));
+      raw[j] = *reinterpret_cast<const float4*>(p.g + ((t0 + min(t, n - 1)) * p.Hv + h) * D + c);
+      bias[j] = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + c)
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int v = tid + 256 * j, t = v / (D / 4), c = 4 * (v % (D / 4));
+      float x[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const float bb[4] = {bias[j].x, bias[j].y, bias[j].z, bias[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // gate: a softplus(x + bias), softplus(z) = ln(1 + u), u = e^z, by the
+        // hardware exp2/log2 with the correction ln(1 + u) = ln(w) u / (w - 1),
+        // w = 1 + u rounded, which keeps the relative accuracy for small u;
+        // e^-200 and below is 0 in f32, and the clamp keeps the sums finite
+        // for g = -inf
+        float y = x[i];
         if (p.A_log) {
-          float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (p.dt_bias) {
-            const float4 bv = *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + c);
-            bias[0] = bv.x; bias[1] = bv.y; bias[2] = bv.z; bias[3] = bv.w;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = a * softplus_f(x[i] + bias[i]);
+          const float z = y + bb[i];
+          const float u = exp2_f(z * 1.44269504f), w = 1.0f + u;
+          const float lp = w == 1.0f ? u : 0.69314718f * __builtin_amdgcn_logf(w) * (u / (w - 1.0f));
+          y = a * (z > 20.0f ? z : lp);
         }
-        // exp below e^-200 is 0 in f32; the clamp keeps the sums finite for g = -inf
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = fmaxf(x[i], -200.0f);
+        x[i] = t < n ? fmaxf(y, -200.0f) : 0.0f;
       }
       *reinterpret_cast<float4*>(Gb + t * GS + c) = make_float4(x[0], x[1], x[2], x[3]);
     }
@@ -974,70 +987,101 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     }
   }
   {
-    // diagonal block I = wave, exactly per pair: lane (tl, dl) takes row
-    // t = 16I + tl over the channels 16m + 4dl + j (m < D/16, j < 4), so that
-    // the four channel groups read different LDS banks; sums over the groups
-    // by two exchanges.  Lane (li, lg) keeps columns 4lg .. 4lg+3.
-    constexpr int NM = D / 16;
-    const int tl = lane & 15, dl = lane >> 4;
-    const int t = 16 * wave + tl;
-    const int rt = min(t, n - 1);
-    float kt[NM][4], qt[NM][4], gt[NM][4];
+    // diagonal block I = wave, in sub-blocks of 4 tokens.  With sigma_b the
+    // running sum at the token before sub-block b, a pair in different
+    // sub-blocks (i in b' < b, t in b) factors as
+    //   exp(G_t - G_i) = exp(G_t - sigma_b) exp(sigma_b - G_i),  both <= 1,
+    // so for each b one MFMA product of rows i < 4b (scaled by the second
+    // factor) with the rows t of sub-block b (scaled by the first) gives those
+    // entries, the other rows zeroed.  Pairs inside a sub-block are taken
+    // exactly, one pair per lane.
+    const float* gb_row = Gb + row * GS;
+    f32x4 ck = {0.0f, 0.0f, 0.0f, 0.0f}, cq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int c = 16 * m + 4 * dl;
-      if constexpr (STAGE) {
-        load4(Ks + t * RS + c, kt[m]);
-        load4(Qs + t * RS + c, qt[m]);
-      } else {
-        load4(kp + rt * qk_stride + c, kt[m]);
-        load4(qp + rt * qk_stride + c, qt[m]);
-      }
-      const float4 gv = *reinterpret_cast<const float4*>(Gb + t * GS + c);
-      gt[m][0] = gv.x; gt[m][1] = gv.y; gt[m][2] = gv.z; gt[m][3] = gv.w;
-    }
-    const float ks = kn[t], qs = qn[t];
-    float ad[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 1; b < 4; ++b) {
+      const bool rmask = li < 4 * b;        // this lane's row feeds the product as a row i
+      const bool lmask = (li >> 2) == b;    // and as a row t
+      const float* sig = Gb + (16 * wave + 4 * b - 1) * GS;
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-      const int i = 16 * wave + ii;
-      const int ri = min(i, n - 1);
-      const float si = kn[i];
-      float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < NKS; ++s) {
+        float xk[8], xq[8], r8[8], l8[8], m8[8];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const int c = 16 * m + 4 * dl;
-        float ki[4];
-        if constexpr (STAGE) load4(Ks + i * RS + c, ki);
-        else load4(kp + ri * qk_stride + c, ki);
-        const float4 gv = *reinterpret_cast<const float4*>(Gb + i * GS + c);
-        const float gi[4] = {gv.x, gv.y, gv.z, gv.w};
+        for (int J = 0; J < 4; ++J)
+          if (J == wave) kf[J][s].get(xk);
+        qf[s].get(xq);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // exponent <= 0 for i <= t; the clamp keeps the masked lanes finite
-          const float e = ii <= tl ? exp2_f(fminf(gt[m][j] - gi[j], 0.0f)) : 0.0f;
-          const float ke = ki[j] * e;
-          sa[j] += kt[m][j] * ke;
-          sp[j] += qt[m][j] * ke;
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * s + 8 * lg + e;
+          const float x = gb_row[d] - sig[d];
+          const float fl = exp2_f(fminf(x, 0.0f)), fr = exp2_f(fminf(-x, 0.0f));
+          r8[e] = rmask ? xk[e] * ksc * fr : 0.0f;
+          l8[e] = lmask ? xk[e] * ksc * fl : 0.0f;
+          m8[e] = lmask ? xq[e] * qsc * fl : 0.0f;
+        }
+        h8 rh, rl, lh, ll, mh, ml;
+        split8(r8, rh, rl);
+        split8(l8, lh, ll);
+        split8(m8, mh, ml);
+        ck = mfma_f16(rh, lh, ck);
+        ck = mfma_f16(rh, ll, ck);
+        ck = mfma_f16(rl, lh, ck);
+        cq = mfma_f16(rh, mh, cq);
+        if constexpr (SPLIT) {
+          cq = mfma_f16(rh, ml, cq);
+          cq = mfma_f16(rl, mh, cq);
         }
       }
-      float a = (sa[0] + sa[1]) + (sa[2] + sa[3]), pp = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-      a += __shfl_xor(a, 16, 64);
-      a += __shfl_xor(a, 32, 64);
-      pp += __shfl_xor(pp, 16, 64);
-      pp += __shfl_xor(pp, 32, 64);
-      if ((ii >> 2) == dl) {
-        ad[ii & 3] = ii < tl ? bs[t] * ks * si * a : 0.0f;
-        pd[ii & 3] = ii <= tl ? p.scale * qs * si * pp : 0.0f;
-      }
     }
+    {
+      // lane (b, tt, ii) = (lg, (li >> 2), li & 3): pair t = 4b + tt, i = 4b + ii
+      const int tt = li >> 2, ii = li & 3;
+      const int tl = 4 * lg + tt, il = 4 * lg + ii;
+      const int t = 16 * wave + tl, i = 16 * wave + il;
+      float sa = 0.0f, sp = 0.0f;
+      if (ii <= tt) {
+        const int rt = min(t, n - 1), ri = min(i, n - 1);
+        float sa4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sp4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+        for (int c = 0; c < D; c += 4) {
+          float kt4[4], ki4[4], qt4[4];
+          if constexpr (STAGE) {
+            load4(Ks + t * RS + c, kt4);
+            load4(Ks + i * RS + c, ki4);
+            load4(Qs + t * RS + c, qt4);
+          } else {
+            load4(kp + rt * qk_stride + c, kt4);
+            load4(kp + ri * qk_stride + c, ki4);
+            load4(qp + rt * qk_stride + c, qt4);
+          }
+          const float4 gt = *reinterpret_cast<const float4*>(Gb + t * GS + c);
+          const float4 gi = *reinterpret_cast<const float4*>(Gb + i * GS + c);
+          const float ex[4] = {gt.x - gi.x, gt.y - gi.y, gt.z - gi.z, gt.w - gi.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float ke = ki4[j] * exp2_f(fminf(ex[j], 0.0f));
+            sa4[j] += kt4[j] * ke;
+            sp4[j] += qt4[j] * ke;
+          }
+        }
+        sa = (sa4[0] + sa4[1]) + (sa4[2] + sa4[3]);
+        sp = (sp4[0] + sp4[1]) + (sp4[2] + sp4[3]);
+      }
+      Ms[wave * 272 + tl * 17 + il] = ii < tt ? bs[t] * kn[t] * kn[i] * sa : 0.0f;
+      Px[wave * 272 + tl * 17 + il] = ii <= tt ? p.scale * qn[t] * kn[i] * sp : 0.0f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane (li, lg) holds row t = 16 wave + li, columns 4 lg + r of the block
+    const bool same = lg == (li >> 2);
+    const float bt = bs[row];
 #pragma unroll
     for (int J = 0; J < 4; ++J)
       if (J == wave)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          av[J][r] = ad[r];
-          pv[J][r] = pd[r];
+          av[J][r] = same ? Ms[wave * 272 + li * 17 + 4 * lg + r] : bt * ck[r];
+          pv[J][r] = same ? Px[wave * 272 + li * 17 + 4 * lg + r] : p.scale * cq[r];
         }
   }
   // P fragments go straight to the block; blocks above the diagonal are zero
