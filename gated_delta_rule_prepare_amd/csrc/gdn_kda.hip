@@ -7,9 +7,10 @@
 // With the gate, g[t,h,d] = -exp(A_log[h]) softplus(g_raw[t,h,d] + dt_bias[h,d]).
 //
 // Token-sequential kernel: one wave per (sequence, value head, 16 value
-// rows), the rows in registers for the whole sequence.  A lane holds four
-// consecutive columns of a row.  With d_i = exp(g_i) for the lane's columns,
-// the decay folds into the two dot products:
+// rows), four waves to a workgroup, the rows in registers for the whole
+// sequence.  A lane holds four consecutive columns of a row.  With
+// d_i = exp(g_i) for the lane's columns, the decay folds into the two dot
+// products:
 //   u = sum_i st_i d_i k_i,   o = sum_i st_i d_i q_i + delta (k . q),
 //   st_i <- d_i st_i + delta k_i
 // so each row is read once and updated once per token.
@@ -22,6 +23,7 @@ namespace gdn {
 namespace {
 
 constexpr int kKdaRows = 16;  // value rows per wave
+constexpr int kKdaWaves = 4;  // waves per workgroup
 
 // the lane's four log-decays of token t (gate applied when A_log is given)
 __device__ __forceinline__ void kda_log_decay(const KdaParams& p, int64_t t, int h, int DK, int col, float* gv) {
@@ -46,14 +48,14 @@ __device__ __forceinline__ void kda_log_decay(const KdaParams& p, int64_t t, int
 }
 
 template <typename QkvT, typename StT, int DK>
-__global__ __launch_bounds__(64) void kda_recurrent_kernel(KdaParams p) {
+__global__ __launch_bounds__(64 * kKdaWaves) void kda_recurrent_kernel(KdaParams p) {
   constexpr int LPR = DK / 4;           // lanes per row; a lane holds 4 columns
   constexpr int RPL = 64 / LPR >= 1 ? 64 / LPR : 1;
   constexpr int NS = kKdaRows / RPL > 0 ? kKdaRows / RPL : 1;  // rows held per lane
-  const int blk = blockIdx.x;
+  const int blk = blockIdx.x * kKdaWaves + (threadIdx.x >> 6);
   const int h = blockIdx.y;
   const int s = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int r = p.Hv / p.Hk;
   const int kh = h / r;
   const int Dv = p.Dv;
@@ -140,13 +142,15 @@ __global__ __launch_bounds__(64) void kda_recurrent_kernel(KdaParams p) {
 
 template <typename QkvT, typename StT>
 hipError_t launch_rec(const KdaParams& p, hipStream_t stream) {
-  dim3 grid((p.Dv + kKdaRows - 1) / kKdaRows, p.Hv, p.N);
+  const int blocks = (p.Dv + kKdaRows - 1) / kKdaRows;  // 16-row blocks per head
+  dim3 grid((blocks + kKdaWaves - 1) / kKdaWaves, p.Hv, p.N);
+  constexpr int threads = 64 * kKdaWaves;
   switch (p.Dk) {
-    case 16: kda_recurrent_kernel<QkvT, StT, 16><<<grid, 64, 0, stream>>>(p); break;
-    case 32: kda_recurrent_kernel<QkvT, StT, 32><<<grid, 64, 0, stream>>>(p); break;
-    case 64: kda_recurrent_kernel<QkvT, StT, 64><<<grid, 64, 0, stream>>>(p); break;
-    case 128: kda_recurrent_kernel<QkvT, StT, 128><<<grid, 64, 0, stream>>>(p); break;
-    default: kda_recurrent_kernel<QkvT, StT, 256><<<grid, 64, 0, stream>>>(p); break;
+    case 16: kda_recurrent_kernel<QkvT, StT, 16><<<grid, threads, 0, stream>>>(p); break;
+    case 32: kda_recurrent_kernel<QkvT, StT, 32><<<grid, threads, 0, stream>>>(p); break;
+    case 64: kda_recurrent_kernel<QkvT, StT, 64><<<grid, threads, 0, stream>>>(p); break;
+    case 128: kda_recurrent_kernel<QkvT, StT, 128><<<grid, threads, 0, stream>>>(p); break;
+    default: kda_recurrent_kernel<QkvT, StT, 256><<<grid, threads, 0, stream>>>(p); break;
   }
   return hipGetLastError();
 }
