@@ -19,6 +19,8 @@ and calls the C functions in the order the library's entry points define:
   conv update, prepare, and the recurrence with a state snapshot per token.
 * :func:`kda`      -- the KDA variant (one log-decay per key channel), with
   its optional gate, against the slot-indexed pool.
+* :func:`mamba2`   -- Mamba2 / SSD (no delta term; a scalar decay per head,
+  B and C shared by head groups), prefill or decode, against a slot pool.
 
 Conv history pools are [S, Cc, W] with W >= K-1 taps per channel.  W = K-1 is
 the ordinary layout; a wider row (speculative decoding keeps
@@ -75,9 +77,12 @@ def _load():
     lib.gdn_oracle_kda_recurrence.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, i32, f64,
                                               P, P, P, P, i32]
     lib.gdn_oracle_kda_gate.argtypes = [i64, i32, i32, P, P, P, P]
+    lib.gdn_oracle_mamba2.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P, P, P, P, i32]
+    lib.gdn_oracle_mamba2_dt.argtypes = [i64, i32, P, P, i32, f64, f64, P]
     for fn in (lib.gdn_oracle_conv_silu, lib.gdn_oracle_split_l2, lib.gdn_oracle_gates,
                lib.gdn_oracle_recurrence, lib.gdn_oracle_round, lib.gdn_oracle_gated_rmsnorm,
-               lib.gdn_oracle_kda_recurrence, lib.gdn_oracle_kda_gate):
+               lib.gdn_oracle_kda_recurrence, lib.gdn_oracle_kda_gate, lib.gdn_oracle_mamba2,
+               lib.gdn_oracle_mamba2_dt):
         fn.restype = None
     _lib = lib
     return lib
@@ -272,6 +277,40 @@ def kda_recurrence(q, k, v, g, beta, cu, state_in, has_init, scale: float, l2nor
     return out, state_out
 
 
+def mamba2_dt(dt_raw, dt_bias=None, softplus: bool = True, dt_min: float = 0.0, dt_max: float = float("inf")):
+    """Mamba2 step size dt = clamp(softplus(dt_raw + dt_bias), dt_min, dt_max)
+    ([P1] Mamba2ChunkScanKernel stage 1).  dt_raw [T, H]."""
+    dt_raw = _f64(dt_raw)
+    T, H = dt_raw.shape
+    db = None if dt_bias is None else _f64(dt_bias)
+    out = np.empty_like(dt_raw)
+    _load().gdn_oracle_mamba2_dt(T, H, _ptr(dt_raw), None if db is None else _ptr(db), int(softplus),
+                                 float(dt_min), float(dt_max), _ptr(out))
+    return out
+
+
+def mamba2_recurrence(x, dt, A, B, C, cu, state_in, has_init, D=None, z=None, nthreads: Optional[int] = None):
+    """Token-by-token Mamba2 / SSD.  x [T, H, P]; dt [T, H] (already processed);
+    A [H]; B, C [T, G, N]; D [H] or [H, P] or None; z [T, H, P] or None;
+    state_in [N_seq, H, P, N].  Returns (out [T, H, P], state_out)."""
+    x, dt, A, B, C = _f64(x), _f64(dt), _f64(A), _f64(B), _f64(C)
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    Ns = cu.size - 1
+    state_in = _f64(state_in).reshape(Ns, H, P, N)
+    has_init = np.ascontiguousarray(has_init, dtype=np.uint8)
+    Dv = None if D is None else _f64(D)
+    zz = None if z is None else _f64(z)
+    out = np.empty((T, H, P))
+    state_out = np.empty((Ns, H, P, N))
+    _load().gdn_oracle_mamba2(H, P, G, N, Ns, _ptr(cu), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                              None if Dv is None else _ptr(Dv), int(Dv is not None and Dv.ndim == 2),
+                              None if zz is None else _ptr(zz), _ptr(state_in), _ptr(has_init), _ptr(out),
+                              _ptr(state_out), nthreads or default_threads())
+    return out, state_out
+
+
 # ---------------------------------------------------------------------------
 # Compositions matching the library's entry points.
 # ---------------------------------------------------------------------------
@@ -411,4 +450,34 @@ def kda(dims, cu, q, k, v, g, beta, ssm_pool, slots, has_init, scale: float, A_l
     out, st = kda_recurrence(q, k, v, gg, beta, cu, ssm_pool[slots], has_init, scale, l2norm, nthreads)
     new_pool = ssm_pool.copy()
     new_pool[slots] = round_to(st, state_dtype)
+    return round_to(out, out_dtype), new_pool
+
+
+def mamba2(cu, x, dt_raw, A, B, C, ssm_pool, slots, has_init, D=None, z=None, dt_bias=None, softplus: bool = True,
+           dt_min: float = 0.0, dt_max: float = float("inf"), state_dtype: str = "f32", out_dtype: str = "f32",
+           nthreads: Optional[int] = None):
+    """Mamba2 / SSD over varlen sequences against a slot-indexed pool [S, H, P, N]
+    ([P1] Mamba2ChunkScanKernel, Mamba2StateUpdateKernel): dt processed by
+    :func:`mamba2_dt`, then the recurrence; each sequence starts from its
+    slot's state (zero when has_init is 0), its final state is written back
+    rounded to ``state_dtype``; a slot of -1 (decode rows only) gives zero
+    output and touches nothing.  Returns (out rounded to ``out_dtype``, pool)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    pool = _f64(ssm_pool)
+    cu = np.asarray(cu, dtype=np.int64)
+    x = _f64(x)
+    T, H, P = x.shape
+    out = np.zeros((T, H, P))
+    new_pool = pool.copy()
+    live = np.nonzero(slots >= 0)[0]
+    if live.size:
+        toks = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in live]).astype(np.int64)
+        lens = (cu[1:] - cu[:-1])[live]
+        cu_l = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        dt = mamba2_dt(_f64(dt_raw)[toks], dt_bias, softplus, dt_min, dt_max)
+        o, st = mamba2_recurrence(x[toks], dt, A, _f64(B)[toks], _f64(C)[toks], cu_l, pool[slots[live]],
+                                  np.asarray(has_init, np.uint8)[live], D, None if z is None else _f64(z)[toks],
+                                  nthreads)
+        out[toks] = o
+        new_pool[slots[live]] = round_to(st, state_dtype)
     return round_to(out, out_dtype), new_pool

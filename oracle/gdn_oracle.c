@@ -336,6 +336,79 @@ void gdn_oracle_kda_gate(int64_t T, int Hv, int Dk, const double* g_raw, const d
 }
 
 /* ---------------------------------------------------------------------- */
+/* Mamba2 / SSD (not the delta rule): per sequence and head h, with group  */
+/* g = h / (H/G) and the [P, N] state S:                                   */
+/*   S <- exp(A[h] dt[t,h]) S + dt[t,h] x[t,h,:] B[t,g,:]^T                */
+/*   y[t,h,p] = sum_n S[p,n] C[t,g,n] + D x[t,h,p];  y *= silu(z[t,h,p])   */
+/* dt is taken as given (see gdn_oracle_mamba2_dt); D is per head (D_per_p */
+/* = 0) or per (head, p), and may be absent, as may z.  [P1]              */
+/* Mamba2ChunkScanKernel (what its five stages compute),                   */
+/* Mamba2StateUpdateKernel.                                                */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+  int H, P, G, N, Nseq;
+  const int32_t* cu;
+  const double *x, *dt, *A, *B, *C, *D, *z;
+  int D_per_p;
+  const double* state_in; /* [Nseq, H, P, N] */
+  const uint8_t* has_init;
+  double* out;       /* [T, H, P] */
+  double* state_out; /* [Nseq, H, P, N] */
+} ssd_ctx;
+
+static void ssd_item(void* vctx, int64_t item) {
+  const ssd_ctx* c = (const ssd_ctx*)vctx;
+  const int64_t s = item / c->H;
+  const int h = (int)(item % c->H);
+  const int H = c->H, P = c->P, G = c->G, N = c->N;
+  const int g = h / (H / G);
+  double* S = c->state_out + (s * H + h) * (int64_t)P * N;
+  const double* S0 = c->state_in + (s * H + h) * (int64_t)P * N;
+  for (int64_t e = 0; e < (int64_t)P * N; ++e) S[e] = c->has_init[s] ? S0[e] : 0.0;
+  for (int64_t t = c->cu[s]; t < c->cu[s + 1]; ++t) {
+    const double dt = c->dt[t * H + h];
+    const double da = exp(c->A[h] * dt);
+    const double* xr = c->x + (t * H + h) * P;
+    const double* Br = c->B + (t * G + g) * N;
+    const double* Cr = c->C + (t * G + g) * N;
+    for (int p = 0; p < P; ++p) {
+      double* row = S + (int64_t)p * N;
+      double y = 0.0;
+      for (int n = 0; n < N; ++n) {
+        row[n] = da * row[n] + dt * xr[p] * Br[n];
+        y += row[n] * Cr[n];
+      }
+      if (c->D) y += (c->D_per_p ? c->D[h * P + p] : c->D[h]) * xr[p];
+      if (c->z) y *= silu(c->z[(t * H + h) * P + p]);
+      c->out[(t * H + h) * P + p] = y;
+    }
+  }
+}
+
+void gdn_oracle_mamba2(int H, int P, int G, int N, int Nseq, const int32_t* cu, const double* x,
+                       const double* dt, const double* A, const double* B, const double* C,
+                       const double* D, int D_per_p, const double* z, const double* state_in,
+                       const uint8_t* has_init, double* out, double* state_out, int nthreads) {
+  ssd_ctx c = {H, P, G, N, Nseq, cu, x, dt, A, B, C, D, z, D_per_p, state_in, has_init, out, state_out};
+  parallel_for((int64_t)Nseq * H, nthreads, ssd_item, &c);
+}
+
+/* Mamba2 step size: dt = clamp(softplus(dt_raw + dt_bias[h]), dt_min,     */
+/* dt_max), the softplus optional and the identity above 20 as the pages   */
+/* guard it; dt_bias may be absent.  [P1] Mamba2ChunkScanKernel stage 1,   */
+/* SoftplusGuarded.                                                        */
+void gdn_oracle_mamba2_dt(int64_t T, int H, const double* dt_raw, const double* dt_bias, int use_softplus,
+                          double dt_min, double dt_max, double* dt) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      double d = dt_raw[t * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+      if (use_softplus) d = d <= 20.0 ? log1p(exp(d)) : d;
+      d = fmin(fmax(d, dt_min), dt_max);
+      dt[t * H + h] = d;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Gated RMS norm of the output, the layer's epilogue.  For each row r of  */
 /* D values (one (token, value head) pair):                                */
 /*   out[r][j] = x[r][j] / sqrt(ms + eps) * w[j] * act(z[r][j]),           */
