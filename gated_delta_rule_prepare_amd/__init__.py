@@ -7,7 +7,8 @@ first call raises; there is no fallback path.
 
 Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`, :func:`gdn_decode_gated`,
 :func:`gdn_decode_spec`, :func:`gdn_gated_rmsnorm`, :func:`gdn_kda_recurrent`,
-:func:`gdn_kda_prefill_varlen`, :func:`gdn_kda_prefill_workspace_size`,
+:func:`gdn_kda_prefill_varlen`, :func:`gdn_kda_prefill_workspace_size`, :func:`gdn_mamba2_state_update`,
+:func:`gdn_mamba2_chunk_scan`, :func:`gdn_mamba2_workspace_size`,
 :func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
 """
 from __future__ import annotations
@@ -40,6 +41,16 @@ class _Dims(ctypes.Structure):
                 ("conv_kernel", ctypes.c_int32), ("conv_state_len", ctypes.c_int32)]
 
 
+class _SsmDims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("state_dim", ctypes.c_int32)]
+
+
+class _SsmDt(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("softplus", ctypes.c_int32), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float)]
+
+
 @dataclass(frozen=True)
 class Dims:
     Hk: int
@@ -62,7 +73,8 @@ class Dims:
 _lib = None
 EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
            "gdn_prefill_workspace_size", "gdn_gated_rmsnorm", "gdn_kda_recurrent",
-           "gdn_kda_prefill_varlen", "gdn_kda_prefill_workspace_size", "gdn_status_string", "gdn_last_error", "gdn_version")
+           "gdn_kda_prefill_varlen", "gdn_kda_prefill_workspace_size", "gdn_mamba2_state_update",
+           "gdn_mamba2_chunk_scan", "gdn_mamba2_workspace_size", "gdn_status_string", "gdn_last_error", "gdn_version")
 
 
 def load_library():
@@ -89,13 +101,20 @@ def load_library():
                                            i32, i32, P, P, sz, P]
     lib.gdn_kda_prefill_workspace_size.argtypes = [D, i32, i64, i32, i32]
     lib.gdn_kda_prefill_workspace_size.restype = sz
+    SD, ST = ctypes.POINTER(_SsmDims), ctypes.POINTER(_SsmDt)
+    lib.gdn_mamba2_state_update.argtypes = [SD, i32, P, P, P, P, P, P, i32, P, ST, i32, P, i32, i32, P, P, P, P]
+    lib.gdn_mamba2_chunk_scan.argtypes = [SD, i32, i64, P, P, P, P, P, P, P, P, i32, P, ST, i32, P, i32, i32, P, P,
+                                          P, P, P, sz, P]
+    lib.gdn_mamba2_workspace_size.argtypes = [SD, i32, i64]
+    lib.gdn_mamba2_workspace_size.restype = sz
     lib.gdn_gated_rmsnorm.argtypes = [i32, i32, i32, P, P, i64, P, f32, i32, P, i32, P]
     lib.gdn_prefill_varlen.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32, i32,
                                        i32, P, P, sz, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
     lib.gdn_prefill_workspace_size.restype = sz
     for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
-               "gdn_gated_rmsnorm", "gdn_kda_recurrent", "gdn_kda_prefill_varlen"):
+               "gdn_gated_rmsnorm", "gdn_kda_recurrent", "gdn_kda_prefill_varlen", "gdn_mamba2_state_update",
+               "gdn_mamba2_chunk_scan"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -320,3 +339,59 @@ def gdn_kda_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_p
                                     int(bool(use_qk_l2norm)), int(chunk_size), _ptr(out), _ptr(workspace), ws_bytes,
                                     _stream(stream))
     _check("gdn_kda_prefill_varlen", st)
+
+
+def _ssm(x, B, dt_bias, dt_softplus, dt_min, dt_max):
+    H, P = x.shape[1], x.shape[2]
+    G, N = B.shape[1], B.shape[2]
+    d = _SsmDims(H, P, G, N)
+    t = _SsmDt(_ptr(dt_bias), int(bool(dt_softplus)), float(dt_min), float(dt_max))
+    return d, t
+
+
+def gdn_mamba2_state_update(x, dt, A, B, C, state_pool, slot_idx, out, D=None, z=None, dt_bias=None,
+                            dt_softplus: bool = True, dt_min: float = 0.0, dt_max: float = float("inf"),
+                            slot_idx_host=None, validate: bool = True, stream=None) -> None:
+    """One Mamba2 / SSD step per row: x, z, out [B, H, P]; dt [B, H]; A [H];
+    B, C [B, G, N]; D [H] or [H, P]; the pool [S, H, P, N] is updated in place."""
+    lib = load_library()
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx) if validate else None
+    d, t = _ssm(x, B, dt_bias, dt_softplus, dt_min, dt_max)
+    st = lib.gdn_mamba2_state_update(ctypes.byref(d), x.shape[0], _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                     _ptr(D), int(D is not None and D.dim() == 2), _ptr(z), ctypes.byref(t),
+                                     _dtype_code(x), _ptr(state_pool), _dtype_code(state_pool), state_pool.shape[0],
+                                     _ptr(slot_idx), _hptr(sl_h), _ptr(out), _stream(stream))
+    _check("gdn_mamba2_state_update", st)
+
+
+def gdn_mamba2_workspace_size(num_heads: int, head_dim: int, state_dim: int, num_seqs: int, total_tokens: int,
+                              num_groups: int = 1) -> int:
+    lib = load_library()
+    d = _SsmDims(num_heads, head_dim, num_groups, state_dim)
+    return int(lib.gdn_mamba2_workspace_size(ctypes.byref(d), num_seqs, total_tokens))
+
+
+def gdn_mamba2_chunk_scan(cu_seqlens, x, dt, A, B, C, state_pool, out, D=None, z=None, dt_bias=None,
+                          dt_softplus: bool = True, dt_min: float = 0.0, dt_max: float = float("inf"), slot_idx=None,
+                          has_initial_state=None, workspace=None, cu_seqlens_host=None, slot_idx_host=None,
+                          stream=None) -> None:
+    """Chunked Mamba2 / SSD over varlen sequences; the pool slot of each
+    sequence is its initial and final state.  ``workspace`` (uint8 device
+    tensor) is allocated here with torch if not given."""
+    lib = load_library()
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    d, t = _ssm(x, B, dt_bias, dt_softplus, dt_min, dt_max)
+    need = int(lib.gdn_mamba2_workspace_size(ctypes.byref(d), n, T))
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_mamba2_chunk_scan(ctypes.byref(d), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), int(D is not None and D.dim() == 2), _ptr(z),
+                                   ctypes.byref(t), _dtype_code(x), _ptr(state_pool), _dtype_code(state_pool),
+                                   state_pool.shape[0], _hptr(sl_h), _ptr(slot_idx), _ptr(has_initial_state),
+                                   _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("gdn_mamba2_chunk_scan", st)

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_prepare.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_epilogue.hip", "gdn_spec.hip", "gdn_kda.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_prepare.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_epilogue.hip", "gdn_spec.hip", "gdn_kda.hip", "gdn_mamba2.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

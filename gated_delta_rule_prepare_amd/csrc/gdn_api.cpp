@@ -154,7 +154,7 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
-int32_t gdn_version(void) { return 130; }
+int32_t gdn_version(void) { return 140; }
 
 gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -529,6 +529,130 @@ gdn_status gdn_kda_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_
   p.num_chunks = nchunks;
   p.max_chunks_per_seq = max_chunks;
   return launched(fn, gdn::launch_kda_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+// Checks shared by the Mamba2 entry points; fills p's common fields.
+gdn_status mamba2_common(const char* fn, const gdn_ssm_dims* d, const void* x, const void* dt, const float* A,
+                         const void* B, const void* C, const float* D, int32_t D_per_head_dim, const void* z,
+                         const gdn_ssm_dt* dtp, gdn_dtype act_dtype, void* state_pool, gdn_dtype state_dtype,
+                         int32_t num_slots, void* out, bool any_tokens, gdn::Mamba2Params& p) {
+  if (d == nullptr || dtp == nullptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: sdims or dtp is null", fn);
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->num_groups <= 0 || d->num_heads % d->num_groups != 0)
+    return fail(GDN_ERR_SHAPE, "%s: need H > 0, P > 0, G > 0 and H a multiple of G, got H=%d P=%d G=%d", fn,
+                d->num_heads, d->head_dim, d->num_groups);
+  if (!pow2_in(d->state_dim, 16, 256))
+    return fail(GDN_ERR_SHAPE, "%s: state_dim must be 16, 32, 64, 128 or 256, got %d", fn, d->state_dim);
+  if (act_dtype != GDN_F32 && act_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "%s: activations must be f32 or bf16", fn);
+  if (state_dtype != GDN_F32 && state_dtype != GDN_BF16 && state_dtype != GDN_F16)
+    return fail(GDN_ERR_DTYPE, "%s: state must be f32, bf16 or f16", fn);
+  if (!state_pool || !A || (any_tokens && (!x || !dt || !B || !C || !out)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a required pointer is null", fn);
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(z) || !aligned16(out) || !aligned16(state_pool))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, B, C, z, out and the pool must be 16-byte aligned", fn);
+  if (D_per_head_dim != 0 && D_per_head_dim != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: D_per_head_dim must be 0 or 1", fn);
+  if (dtp->softplus != 0 && dtp->softplus != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dt softplus flag must be 0 or 1", fn);
+  if (!(dtp->dt_min >= 0.0f) || !(dtp->dt_max >= dtp->dt_min))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: need 0 <= dt_min <= dt_max, got %g and %g", fn, dtp->dt_min,
+                dtp->dt_max);
+  if (num_slots <= 0) return fail(GDN_ERR_SHAPE, "%s: num_slots must be positive", fn);
+  p = gdn::Mamba2Params{};
+  p.H = d->num_heads; p.P = d->head_dim; p.G = d->num_groups; p.N = d->state_dim;
+  p.x = x; p.dt = dt; p.B = B; p.C = C; p.z = z; p.A = A; p.dt_bias = dtp->dt_bias; p.D = D;
+  p.D_per_p = D_per_head_dim; p.dt_softplus = dtp->softplus; p.dt_min = dtp->dt_min; p.dt_max = dtp->dt_max;
+  p.ssm_pool = state_pool; p.num_slots = num_slots; p.out = out; p.act = act_dtype; p.state = state_dtype;
+  return GDN_OK;
+}
+
+bool mamba2_chunked_dims(const gdn_ssm_dims* d) {
+  return (d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128) &&
+         (d->state_dim == 32 || d->state_dim == 64 || d->state_dim == 128);
+}
+
+}  // namespace
+
+gdn_status gdn_mamba2_state_update(const gdn_ssm_dims* sdims, int32_t batch, const void* x, const void* dt,
+                                   const float* A, const void* B, const void* C, const float* D,
+                                   int32_t D_per_head_dim, const void* z, const gdn_ssm_dt* dtp,
+                                   gdn_dtype act_dtype, void* state_pool, gdn_dtype state_dtype,
+                                   int32_t num_slots, const int32_t* slot_idx_dev, const int32_t* slot_idx_host,
+                                   void* out, void* stream) {
+  const char* fn = "gdn_mamba2_state_update";
+  if (batch < 0) return fail(GDN_ERR_SHAPE, "%s: negative batch %d", fn, batch);
+  gdn::Mamba2Params p;
+  gdn_status st = mamba2_common(fn, sdims, x, dt, A, B, C, D, D_per_head_dim, z, dtp, act_dtype, state_pool,
+                                state_dtype, num_slots, out, batch > 0, p);
+  if (st != GDN_OK) return st;
+  if (batch == 0) return ok();
+  if (sdims->head_dim > 1024) return fail(GDN_ERR_SHAPE, "%s: head_dim must be at most 1024", fn);
+  if (!slot_idx_dev) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: slot_idx_dev is null", fn);
+  if (slot_idx_host) {
+    st = check_slots(fn, slot_idx_host, batch, num_slots, true);
+    if (st != GDN_OK) return st;
+  }
+  p.Nseq = batch;
+  p.T = batch;
+  p.slots = slot_idx_dev;
+  return launched(fn, gdn::launch_mamba2_update(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_mamba2_workspace_size(const gdn_ssm_dims* sdims, int32_t num_seqs, int64_t total_tokens) {
+  if (sdims == nullptr || num_seqs < 0 || total_tokens < 0 || sdims->num_heads <= 0 || !mamba2_chunked_dims(sdims))
+    return 0;
+  return gdn::mamba2_workspace_bytes(sdims->num_heads, sdims->head_dim, sdims->state_dim, num_seqs, total_tokens);
+}
+
+gdn_status gdn_mamba2_chunk_scan(const gdn_ssm_dims* sdims, int32_t num_seqs, int64_t total_tokens,
+                                 const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* x,
+                                 const void* dt, const float* A, const void* B, const void* C, const float* D,
+                                 int32_t D_per_head_dim, const void* z, const gdn_ssm_dt* dtp,
+                                 gdn_dtype act_dtype, void* state_pool, gdn_dtype state_dtype, int32_t num_slots,
+                                 const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                                 const uint8_t* has_initial_state_dev, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_mamba2_chunk_scan";
+  gdn_status st = check_offsets(fn, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev);
+  if (st != GDN_OK) return st;
+  gdn::Mamba2Params p;
+  st = mamba2_common(fn, sdims, x, dt, A, B, C, D, D_per_head_dim, z, dtp, act_dtype, state_pool, state_dtype,
+                     num_slots, out, total_tokens > 0, p);
+  if (st != GDN_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!mamba2_chunked_dims(sdims))
+    return fail(GDN_ERR_SHAPE, "%s: head_dim and state_dim must be 32, 64 or 128, got %d and %d", fn,
+                sdims->head_dim, sdims->state_dim);
+  if ((slot_idx_host == nullptr) != (slot_idx_dev == nullptr))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: pass both slot index copies or neither", fn);
+  if (slot_idx_host) {
+    st = check_slots(fn, slot_idx_host, num_seqs, num_slots, false);
+    if (st != GDN_OK) return st;
+  } else if (num_seqs > num_slots) {
+    return fail(GDN_ERR_INDEX, "%s: %d sequences but only %d slots", fn, num_seqs, num_slots);
+  }
+  const size_t need = gdn::mamba2_workspace_bytes(sdims->num_heads, sdims->head_dim, sdims->state_dim, num_seqs,
+                                                  total_tokens);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  int64_t nchunks = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) nchunks += (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + 63) / 64;
+  p.Nseq = num_seqs;
+  p.T = total_tokens;
+  p.cu = cu_seqlens_dev;
+  p.slots = slot_idx_dev;
+  p.has_init = has_initial_state_dev;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.num_chunks = nchunks;
+  return launched(fn, gdn::launch_mamba2_chunk_scan(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,

@@ -161,6 +161,33 @@ struct KdaParams {
   int max_chunks_per_seq;
 };
 
+struct Mamba2Params {
+  int H, P, G, N;
+  int Nseq;               // sequences (prefill) or rows (decode)
+  int64_t T;
+  const int32_t* cu;      // device [Nseq+1] (prefill)
+  const void* x;          // [T, H, P] act
+  const void* dt;         // [T, H] act (raw)
+  const void* B;          // [T, G, N] act
+  const void* C;          // [T, G, N] act
+  const void* z;          // [T, H, P] act or null
+  const float* A;         // [H]
+  const float* dt_bias;   // [H] or null
+  const float* D;         // [H] or [H, P] or null
+  int D_per_p;
+  int dt_softplus;
+  float dt_min, dt_max;
+  void* ssm_pool;         // [S, H, P, N] state
+  int num_slots;
+  const int32_t* slots;   // device [Nseq] (decode: required; prefill: or null)
+  const uint8_t* has_init;  // device [Nseq] or null (prefill)
+  void* out;              // [T, H, P] act
+  gdn_dtype act, state;
+  void* workspace;        // prefill
+  size_t workspace_bytes;
+  int64_t num_chunks;
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the HIP status
 // of the launch.
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
@@ -172,6 +199,9 @@ hipError_t launch_kda_recurrent(const KdaParams& p, hipStream_t stream);
 hipError_t launch_kda_prefill(const KdaParams& p, hipStream_t stream);
 size_t kda_prefill_workspace_bytes(int Hv, int Dk, int Dv, int N, int64_t T, gdn_dtype qkv);
 bool kda_chunked_dims(int Dk, int Dv);
+hipError_t launch_mamba2_update(const Mamba2Params& p, hipStream_t stream);
+hipError_t launch_mamba2_chunk_scan(const Mamba2Params& p, hipStream_t stream);
+size_t mamba2_workspace_bytes(int H, int P, int N, int Ns, int64_t T);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
 

@@ -51,43 +51,10 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f16(const h8& a, const h8& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ h8 to_h8(const float* x) {
-  h8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
-  return r;
-}
-// x ~= hi + lo, both f16
-__device__ __forceinline__ void split8(const float* x, h8& hi, h8& lo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const _Float16 h = (_Float16)x[i];
-    hi[i] = h;
-    lo[i] = (_Float16)(x[i] - (float)h);
-  }
-}
-__device__ __forceinline__ h8 ld_h8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
-__device__ __forceinline__ h8 zero_h8() {
-  h8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (_Float16)0.0f;
-  return r;
-}
 
 // Eight consecutive input elements in their storage form (one 16-byte word
 // for bf16, two for f32).

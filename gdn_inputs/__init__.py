@@ -321,3 +321,56 @@ def kda_decode_workload() -> Dict[str, object]:
     the kernel, q/k L2 normalised."""
     return dict(name="kda_decode_b256_hk16_hv32_d128", dims=QWEN_DIMS, seqlens=(1,) * 256, num_slots=512,
                 qkv_dtype="bf16", state_dtype="f32", seed=1008, has_init=None)
+
+
+def mamba2_inputs(H: int, P: int, G: int, N: int, seqlens: Sequence[int], num_slots: int, act_dtype: str,
+                  state_dtype: str, seed: int, D_mode: str = "h", with_z: bool = True, init_std: float = 0.1,
+                  has_init: Optional[Sequence[int]] = None, null_rows: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of the Mamba2 / SSD layer (no page gives a workload; these
+    follow the layer's usual initialisation).  x, z [T, H, P] and B, C
+    [T, G, N] ~ N(0, 1) in ``act_dtype``; the raw step dt [T, H] ~ N(0, 0.5^2)
+    in ``act_dtype`` with dt_bias [H] = softplus^-1(u), u log-uniform in
+    [0.001, 0.1]; A = -exp(A_log), A_log ~ U(0, ln 16); D [H] (or [H, P]) ~
+    N(0, 1); the state pool ~ N(0, init_std^2).  Each sequence (or decode row,
+    one token each) gets a distinct slot; ``null_rows`` decode rows get -1."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(seqlens))
+    Ns = len(seqlens)
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = _normal(rng, (T, H, P), 1.0, act_dtype)
+    out["z"] = _normal(rng, (T, H, P), 1.0, act_dtype) if with_z else None
+    out["B"] = _normal(rng, (T, G, N), 1.0, act_dtype)
+    out["C"] = _normal(rng, (T, G, N), 1.0, act_dtype)
+    out["dt"] = _normal(rng, (T, H), 0.5, act_dtype)
+    u = np.exp(rng.uniform(math.log(0.001), math.log(0.1), size=H))
+    out["dt_bias"] = np.log(np.expm1(u)).astype(np.float32)
+    out["A"] = (-np.exp(rng.uniform(0.0, math.log(16.0), size=H))).astype(np.float32)
+    if D_mode == "h":
+        out["D"] = rng.standard_normal(H).astype(np.float32)
+    elif D_mode == "hp":
+        out["D"] = rng.standard_normal((H, P)).astype(np.float32)
+    else:
+        out["D"] = None
+    out["ssm_pool"] = _normal(rng, (num_slots, H, P, N), init_std, state_dtype)
+    out["cu"] = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    slots = rng.permutation(num_slots)[:Ns].astype(np.int32)
+    if null_rows:
+        slots[rng.choice(Ns, size=null_rows, replace=False)] = -1
+    out["slots"] = slots
+    out["has_init"] = np.ones(Ns, np.uint8) if has_init is None else np.asarray(has_init, np.uint8)
+    return out
+
+
+def mamba2_prefill_workload() -> Dict[str, object]:
+    """The Mamba2 prefill workload: one 4096-token sequence, H=64 heads of
+    P=64, G=8 groups, N=128; bf16 activations, f32 state from zero, z gate
+    and D per head."""
+    return dict(name="mamba2_prefill_T4096_h64_p64_g8_n128", H=64, P=64, G=8, N=128, seqlens=(4096,),
+                num_slots=1, act="bf16", state="f32", seed=1009, has_init=(0,))
+
+
+def mamba2_decode_workload() -> Dict[str, object]:
+    """The Mamba2 decode workload: 256 rows x 1 token at the same shapes
+    against a 512-slot f32 pool ~ N(0, 0.1^2)."""
+    return dict(name="mamba2_decode_b256_h64_p64_g8_n128", H=64, P=64, G=8, N=128, seqlens=(1,) * 256,
+                num_slots=512, act="bf16", state="f32", seed=1010, has_init=None)

@@ -73,6 +73,24 @@ typedef enum gdn_status {
   GDN_ERR_DEVICE = 6            /* HIP reported an error                     */
 } gdn_status;
 
+/* Mamba2 / SSD layer dimensions: H heads of head_dim P, G groups (H a
+ * multiple of G; head h uses group h / (H/G)), state_dim N. */
+typedef struct gdn_ssm_dims {
+  int32_t num_heads;  /* H */
+  int32_t head_dim;   /* P */
+  int32_t num_groups; /* G */
+  int32_t state_dim;  /* N */
+} gdn_ssm_dims;
+
+/* Mamba2 step-size processing: dt = clamp(softplus(dt_raw + dt_bias[h]),
+ * dt_min, dt_max), the softplus when `softplus` is non-zero (the identity
+ * above 20); dt_bias may be NULL. */
+typedef struct gdn_ssm_dt {
+  const float* dt_bias; /* device f32 [H] or NULL */
+  int32_t softplus;
+  float dt_min, dt_max;
+} gdn_ssm_dt;
+
 typedef struct gdn_dims {
   int32_t num_k_heads; /* Hk */
   int32_t num_v_heads; /* Hv, a multiple of Hk */
@@ -321,6 +339,64 @@ gdn_status gdn_kda_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_
  * invalid arguments). */
 size_t gdn_kda_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                                       int32_t chunk_size, gdn_dtype qkv_dtype);
+
+/*
+ * gdn_mamba2_state_update -- one Mamba2 / SSD step per row against the
+ * slot-indexed state pool [num_slots, H, P, N] ([P1] Mamba2StateUpdateKernel).
+ * Not the delta rule: for row b, head h, group g = h / (H/G):
+ *   dt = processed step (gdn_ssm_dt);  S <- exp(A[h] dt) S + dt x B^T
+ *   y[p] = sum_n S[p][n] C[n] + D x[p];  y *= silu(z[p]) when z is given
+ * S read at the pool dtype, computed in f32, stored back rounded.  A row whose
+ * slot is -1 gets a zero output and touches nothing.
+ *
+ * Arguments:
+ *   sdims                 H, P (1..1024), G, N in {16, 32, 64, 128, 256}.
+ *   batch                 B >= 0 rows.
+ *   x, z                  device [B, H, P] in act_dtype (z may be NULL).
+ *   dt                    device [B, H] in act_dtype, the raw step.
+ *   A                     device f32 [H], every entry < 0 (A = -exp(A_log)).
+ *   B, C                  device [B, G, N] in act_dtype.
+ *   D, D_per_head_dim     device f32 [H] (0) or [H, P] (1), or NULL.
+ *   dtp                   step processing (dt_bias device f32 [H] or NULL); dt_min >= 0.
+ *   act_dtype             GDN_F32 or GDN_BF16.
+ *   state_pool            device [num_slots, H, P, N] in state_dtype, in place.
+ *   slot_idx_dev/_host    int32 [B] as gdn_decode.
+ *   out                   device [B, H, P] in act_dtype.
+ * x, B, C, z, out and the pool must be 16-byte aligned.
+ */
+gdn_status gdn_mamba2_state_update(const gdn_ssm_dims* sdims, int32_t batch, const void* x, const void* dt,
+                                   const float* A, const void* B, const void* C, const float* D,
+                                   int32_t D_per_head_dim, const void* z, const gdn_ssm_dt* dtp,
+                                   gdn_dtype act_dtype, void* state_pool, gdn_dtype state_dtype,
+                                   int32_t num_slots, const int32_t* slot_idx_dev, const int32_t* slot_idx_host,
+                                   void* out, void* stream);
+
+/*
+ * gdn_mamba2_chunk_scan -- Mamba2 / SSD over varlen sequences (the same
+ * recurrence as gdn_mamba2_state_update, token by token), computed in chunks
+ * of 64 tokens in the dual form ([P1] Mamba2ChunkScanKernel, whose five
+ * stages compute it).  Sequence s starts from its slot's state (zero when
+ * has_initial_state[s] is 0) and its final state is written back.
+ *
+ * Arguments: those of gdn_mamba2_state_update over T tokens, plus
+ *   num_seqs, total_tokens, cu_seqlens_host/_dev: as gdn_prepare (no empty sequence).
+ *   sdims                 P in {32, 64, 128}, N in {32, 64, 128}.
+ *   slot_idx_host/_dev    int32 [N] (both NULL: slot s); -1 is refused.
+ *   has_initial_state_dev device uint8 [N] or NULL (= all 1).
+ *   workspace             device scratch of at least gdn_mamba2_workspace_size() bytes,
+ *                         256-byte aligned.
+ */
+gdn_status gdn_mamba2_chunk_scan(const gdn_ssm_dims* sdims, int32_t num_seqs, int64_t total_tokens,
+                                 const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* x,
+                                 const void* dt, const float* A, const void* B, const void* C, const float* D,
+                                 int32_t D_per_head_dim, const void* z, const gdn_ssm_dt* dtp,
+                                 gdn_dtype act_dtype, void* state_pool, gdn_dtype state_dtype, int32_t num_slots,
+                                 const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                                 const uint8_t* has_initial_state_dev, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes gdn_mamba2_chunk_scan needs (0 for invalid arguments). */
+size_t gdn_mamba2_workspace_size(const gdn_ssm_dims* sdims, int32_t num_seqs, int64_t total_tokens);
 
 /*
  * gdn_gated_rmsnorm -- the layer's output epilogue, for the output of

@@ -101,3 +101,19 @@ def kda_prefill(d, inp, qkv: str, state: str, scale: float, l2norm: bool, ssm_po
                                has_initial_state=dev(inp["has_init"]), use_qk_l2norm=l2norm)
     torch.cuda.synchronize()
     return host(out[:T]), host(sp)
+
+
+def mamba2(inp, act: str, state: str, decode: bool, ssm_pool=None, dt_min=0.0, dt_max=float("inf")):
+    T, H, P = inp["x"].shape
+    sp = dev(inp["ssm_pool"] if ssm_pool is None else ssm_pool, state)
+    out = torch.empty(T, H, P, device=DEV, dtype=TORCH_DTYPE[act])
+    opt = lambda a, dt="f32": None if a is None else dev(a, dt)
+    args = (dev(inp["x"], act), dev(inp["dt"], act), dev(inp["A"]), dev(inp["B"], act), dev(inp["C"], act))
+    kw = dict(D=opt(inp["D"]), z=opt(inp["z"], act), dt_bias=opt(inp["dt_bias"]), dt_min=dt_min, dt_max=dt_max)
+    if decode:
+        gdn.gdn_mamba2_state_update(*args, sp, dev(inp["slots"]), out, **kw)
+    else:
+        gdn.gdn_mamba2_chunk_scan(dev(inp["cu"]), *args, sp, out, slot_idx=dev(inp["slots"]),
+                                  has_initial_state=dev(inp["has_init"]), **kw)
+    torch.cuda.synchronize()
+    return host(out), host(sp)

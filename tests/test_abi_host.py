@@ -282,3 +282,89 @@ def test_kda_recurrent_rejects_bad_arguments(lib):
 
 def test_kda_recurrent_empty_is_a_no_op(lib):
     assert _kda(lib, N=0, T=0, cu=(0,), slots=()) == OK
+
+
+def _sdims(H=4, P=64, G=2, N=128):
+    return ctypes.byref(gdn._SsmDims(H, P, G, N))
+
+
+def _sdt(softplus=1, dt_min=0.0, dt_max=float("inf")):
+    return ctypes.byref(gdn._SsmDt(None, softplus, dt_min, dt_max))
+
+
+def _m2u(lib, sd=None, batch=2, act=1, state=0, dtp=None, slots=(1, 0), num_slots=2, Dp=0, x=FAKE, pool=FAKE,
+         A=FAKE):
+    sl_a, sl_p = _arr(slots)
+    return lib.gdn_mamba2_state_update(sd if sd is not None else _sdims(), batch, x, FAKE, A, FAKE, FAKE, None, Dp,
+                                       None, dtp if dtp is not None else _sdt(), act, pool, state, num_slots, FAKE,
+                                       sl_p, FAKE, None)
+
+
+def test_mamba2_state_update_rejects_bad_arguments(lib):
+    assert _m2u(lib, sd=_sdims(H=6, G=4)) == SHAPE
+    assert _m2u(lib, sd=_sdims(N=24)) == SHAPE and "state_dim" in _err(lib)
+    assert _m2u(lib, sd=_sdims(P=2048)) == SHAPE and "1024" in _err(lib)
+    assert _m2u(lib, act=2) == DTYPE
+    assert _m2u(lib, state=7) == DTYPE
+    assert _m2u(lib, x=None) == INVALID
+    assert _m2u(lib, A=None) == INVALID
+    assert _m2u(lib, x=FAKE + 8) == INVALID and "aligned" in _err(lib)
+    assert _m2u(lib, Dp=2) == INVALID
+    assert _m2u(lib, dtp=_sdt(softplus=3)) == INVALID
+    assert _m2u(lib, dtp=_sdt(dt_min=-1.0)) == INVALID
+    assert _m2u(lib, dtp=_sdt(dt_min=0.5, dt_max=0.1)) == INVALID
+    assert _m2u(lib, dtp=_sdt(dt_min=float("nan"))) == INVALID
+    assert _m2u(lib, slots=(0, 0)) == INDEX
+    assert _m2u(lib, slots=(0, 2)) == INDEX
+    assert _m2u(lib, num_slots=0) == SHAPE
+    assert _m2u(lib, batch=-1) == SHAPE
+    assert lib.gdn_mamba2_state_update(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, _sdt(), 1, FAKE, 0, 1,
+                                       FAKE, None, FAKE, None) == INVALID
+
+
+def test_mamba2_state_update_empty_is_a_no_op(lib):
+    assert _m2u(lib, batch=0, slots=(), x=None) == OK
+
+
+def _m2s(lib, sd=None, N=2, T=100, cu=(0, 36, 100), act=1, state=0, slots=(1, 0), num_slots=2, ws=FAKE,
+         ws_bytes=None, dtp=None, slots_dev=FAKE):
+    cu_a, cu_p = _arr(cu)
+    sl_a, sl_p = _arr(slots) if slots is not None else (None, None)
+    sd = sd if sd is not None else _sdims()
+    if ws_bytes is None:
+        ws_bytes = lib.gdn_mamba2_workspace_size(sd, N, T)
+    return lib.gdn_mamba2_chunk_scan(sd, N, T, cu_p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
+                                     dtp if dtp is not None else _sdt(), act, FAKE, state, num_slots, sl_p,
+                                     slots_dev if slots is not None else None, None, FAKE, ws, ws_bytes, None)
+
+
+def test_mamba2_workspace_size(lib):
+    # two sequences of 36 and 64 tokens: at most 100 / 64 + 2 = 3 chunk blocks per head
+    n = lib.gdn_mamba2_workspace_size(_sdims(H=4, P=64, N=128), 2, 100)
+    blk = (64 * 64 * 4 + 64 * 128 * 4 + 68 * 4 + 255) // 256 * 256
+    assert n == 256 + 2 * 256 + 3 * 4 * blk
+    assert lib.gdn_mamba2_workspace_size(_sdims(P=48), 2, 100) == 0
+    assert lib.gdn_mamba2_workspace_size(_sdims(), 0, 0) == 0
+    assert lib.gdn_mamba2_workspace_size(None, 1, 10) == 0
+
+
+def test_mamba2_chunk_scan_rejects_bad_arguments(lib):
+    assert _m2s(lib, sd=_sdims(P=48)) == SHAPE and "head_dim" in _err(lib)
+    assert _m2s(lib, sd=_sdims(N=256)) == SHAPE
+    assert _m2s(lib, sd=_sdims(N=16)) == SHAPE
+    assert _m2s(lib, cu=(0, 36, 36), T=36) == SHAPE and "empty" in _err(lib)
+    assert _m2s(lib, cu=(0, 36, 99)) == SHAPE
+    assert _m2s(lib, act=0, state=9) == DTYPE
+    assert _m2s(lib, slots=(0, 0)) == INDEX
+    assert _m2s(lib, slots=(-1, 0)) == INDEX
+    assert _m2s(lib, slots=(0, 5)) == INDEX
+    assert _m2s(lib, slots=None, num_slots=1) == INDEX
+    assert _m2s(lib, slots_dev=None) == INVALID and "both" in _err(lib)
+    assert _m2s(lib, ws=None) == WORKSPACE
+    assert _m2s(lib, ws_bytes=1024) == WORKSPACE
+    assert _m2s(lib, ws=FAKE + 16) == WORKSPACE and "aligned" in _err(lib)
+    assert _m2s(lib, dtp=_sdt(dt_max=-1.0)) == INVALID
+
+
+def test_mamba2_chunk_scan_empty_is_a_no_op(lib):
+    assert _m2s(lib, N=0, T=0, cu=(0,), slots=()) == OK
