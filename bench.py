@@ -48,6 +48,8 @@ def parse():
                     help="only run the speculative multi-token decode (gdn_decode_spec) workload")
     ap.add_argument("--kda-only", action="store_true",
                     help="only run the KDA workloads (chunked prefill, token-by-token decode)")
+    ap.add_argument("--mamba2-only", action="store_true",
+                    help="time only the Mamba2 prefill and decode workloads and print their record")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -457,6 +459,88 @@ def kda(torch, gdn, reps=20):
     return res
 
 
+def mamba2_prefill_flops(T, H, P, N, c=64):
+    """Algorithmic flops of the chunked Mamba2 / SSD prefill on full chunks of
+    c tokens, per token and head: C B^T (2 c N), the masked product with X
+    (2 c P), the inter-chunk term C S^T (2 P N) and the chunk's state
+    contribution X^T (w B) (2 P N).  Each product once, as dense c x c
+    blocks; the f16 hi/lo split is not counted."""
+    return T * H * (2 * c * N + 2 * c * P + 4 * P * N)
+
+
+def mamba2_prefill_bytes(T, H, P, G, N, act_bytes=2, state_bytes=4):
+    """Algorithmic HBM bytes of one Mamba2 prefill call from a zero state: x, z
+    and dt read, B and C read once per group, out and the final state written."""
+    return T * (2 * H * P + H + 2 * G * N) * act_bytes + T * H * P * act_bytes + H * P * N * state_bytes
+
+
+def mamba2_decode_bytes(Bn, H, P, G, N, act_bytes=2, state_bytes=4):
+    """Algorithmic HBM bytes of one Mamba2 single-step call over Bn rows: the
+    state read and written, x, z, dt, B, C and out, the slot index."""
+    return 2 * Bn * H * P * N * state_bytes + Bn * (3 * H * P + H + 2 * G * N) * act_bytes + Bn * 4
+
+
+def mamba2(torch, gdn, reps=20):
+    """The Mamba2 workloads (gdn_inputs.mamba2_prefill_workload,
+    mamba2_decode_workload): HIP events on the kernels' stream, median of
+    ``reps`` calls after 3 untimed ones."""
+    from gdn_inputs import mamba2_decode_workload, mamba2_inputs, mamba2_prefill_workload
+    dev = torch.device("cuda:0")
+    bf, f32 = torch.bfloat16, torch.float32
+    t = lambda a, dt=f32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for wl in (mamba2_prefill_workload(), mamba2_decode_workload()):
+        H, P, G, N = wl["H"], wl["P"], wl["G"], wl["N"]
+        inp = mamba2_inputs(H, P, G, N, wl["seqlens"], wl["num_slots"], wl["act"], wl["state"], wl["seed"],
+                            has_init=wl["has_init"])
+        x, z, dt, Bm, Cm = (t(inp[k], bf) for k in ("x", "z", "dt", "B", "C"))
+        A, D, dtb = t(inp["A"]), t(inp["D"]), t(inp["dt_bias"])
+        pool = t(inp["ssm_pool"])
+        cu_h, sl_h = inp["cu"], inp["slots"]
+        cu, sl, hi = t(cu_h, torch.int32), t(sl_h, torch.int32), t(inp["has_init"], torch.uint8)
+        T = int(cu_h[-1])
+        out = torch.empty(T, H, P, device=dev, dtype=bf)
+        chunked = wl["name"].startswith("mamba2_prefill")
+        ws = None
+        if chunked:
+            ws = torch.empty(max(gdn.gdn_mamba2_workspace_size(H, P, N, len(sl_h), T, G), 1), dtype=torch.uint8,
+                             device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps + 3):
+            e = ev[i - 3] if i >= 3 else None
+            if e:
+                e[0].record(stream)
+            if chunked:
+                gdn.gdn_mamba2_chunk_scan(cu, x, dt, A, Bm, Cm, pool, out, D=D, z=z, dt_bias=dtb, slot_idx=sl,
+                                          has_initial_state=hi, workspace=ws, cu_seqlens_host=cu_h,
+                                          slot_idx_host=sl_h, stream=stream)
+            else:
+                gdn.gdn_mamba2_state_update(x, dt, A, Bm, Cm, pool, sl, out, D=D, z=z, dt_bias=dtb,
+                                            slot_idx_host=sl_h, stream=stream)
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        sec = float(np.median(ms)) * 1e-3
+        if chunked:
+            fl = mamba2_prefill_flops(T, H, P, N)
+            nb = mamba2_prefill_bytes(T, H, P, G, N)
+            ws_b = 2 * gdn.gdn_mamba2_workspace_size(H, P, N, len(sl_h), T, G)
+            rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb,
+                  "workspace_bytes_per_launch": ws_b, "flops_per_launch": fl,
+                  "mfma_frac": fl / sec / 1e12 / F16_MFMA_PEAK_TFLOPS,
+                  "kernels": "ssd_table_kernel + ssd_chunk_kernel + ssd_scan_kernel"}
+        else:
+            nb = mamba2_decode_bytes(T, H, P, G, N)
+            rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb, "kernel": "mamba2_update_kernel"}
+        res[wl["name"]] = {"tokens_per_s": T / sec, **stats_us(ms), "roofline": rl}
+        del x, z, dt, Bm, Cm, pool, out, ws
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -484,6 +568,9 @@ def main():
         return
     if args.kda_only:
         print(json.dumps({"kda": kda(torch, gdn, reps=args.steps)}), flush=True)
+        return
+    if args.mamba2_only:
+        print(json.dumps({"mamba2": mamba2(torch, gdn, reps=args.steps)}), flush=True)
         return
     dev = torch.device("cuda:0")
     bf, f32 = torch.bfloat16, torch.float32
@@ -565,10 +652,11 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l, epi, spec, kda_r = None, None, None, None, None
+    copy_gbs, cold_l, epi, spec, kda_r, m2 = None, None, None, None, None, None
     if not args.no_extras:
         spec = speculative(torch, gdn)
         kda_r = kda(torch, gdn)
+        m2 = mamba2(torch, gdn)
         epi = epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dcfg.scale,
                        stream, T)
         copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
@@ -624,6 +712,7 @@ def main():
         "epilogue": epi,
         "decode_spec": spec,
         "kda": kda_r,
+        "mamba2": m2,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -9,14 +9,15 @@
 //   s' = da s + (dt x_p) B,   y_p = s' . C
 //
 // Prefill, in chunks of 64 tokens (the dual form; within a chunk, with
-// L_i = sum_{j<=i} A dt_j):
+// L_i = sum_{j<=i} A dt_j and S0 the state entering it):
 //   Y_intra = (M * C B^T) X,  M[i][j] = exp(L_i - L_j) dt_j  (j <= i)
 //   Y_inter[i] = exp(L_i) S0 C_i
 //   S_C = exp(L_C) S0 + sum_j exp(L_C - L_j) dt_j x_j B_j^T
-// ssd_chunk_kernel (one workgroup per chunk and head) forms Y_intra and the
-// chunk's state contribution on the f16 hi/lo MFMA; ssd_scan_kernel (one wave
-// per sequence, head and 16 state rows) carries S through the chunks in
-// registers, adds Y_inter (MFMA), D x and the gate, and writes the final state.
+// in three passes, each parallel over the whole chip: ssd_state_kernel (per
+// chunk and head) forms the chunk's state contribution on the f16 hi/lo MFMA;
+// ssd_pass_kernel (element-wise over the state) carries S across the chunks
+// and leaves each chunk's S0 in the workspace; ssd_out_kernel (per chunk and
+// head) forms both output terms on the MFMA and applies D x and the gate.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -133,15 +134,11 @@ __global__ __launch_bounds__(kUpdThreads) void mamba2_update_kernel(Mamba2Params
 // ---------------------------------------------------------------------------
 // Prefill: workspace
 // ---------------------------------------------------------------------------
-// Per (chunk, head) block: Y_intra [P/16][4][64 lanes][4] f32 (the scan's
-// accumulator order), the chunk's state contribution [P][N] f32, and
-// exp(L_i) [64] then exp(L_C).
-__host__ __device__ constexpr int64_t ssd_blk_y(int, int) { return 0; }
-__host__ __device__ constexpr int64_t ssd_blk_st(int P, int) { return (int64_t)kSsdChunk * P * 4; }
-__host__ __device__ constexpr int64_t ssd_blk_vec(int P, int N) { return ssd_blk_st(P, N) + (int64_t)P * N * 4; }
-__host__ __device__ constexpr int64_t ssd_blk_bytes(int P, int N) {
-  return (ssd_blk_vec(P, N) + (kSsdChunk + 4) * 4 + 255) / 256 * 256;
-}
+// Per (chunk, head) block: the chunk's state contribution St [P][N] f32,
+// which the state pass overwrites with the state entering the chunk, then
+// exp(L_C) (one float, padded to 256 bytes).
+__host__ __device__ constexpr int64_t ssd_blk_vec(int P, int N) { return (int64_t)P * N * 4; }
+__host__ __device__ constexpr int64_t ssd_blk_bytes(int P, int N) { return ssd_blk_vec(P, N) + 256; }
 
 struct SsdWs {
   int32_t* seq_chunk_off;  // [Nseq+1]
@@ -193,41 +190,95 @@ __global__ __launch_bounds__(64) void ssd_table_kernel(const int32_t* cu, int Ns
 }
 
 // [64 tokens][W] rows of an activation, transposed into LDS as f16 [W][kTS]
-// (hi, and lo for f32), rows past n zero.  Each thread moves 8 columns of
-// one token.
+// (hi, and lo for f32), rows past n zero.  Each of the 256 threads moves 8
+// columns of one token per item; all its loads are issued before the stores.
 template <typename ActT, int W>
 __device__ __forceinline__ void stage_transposed(const ActT* src, int64_t stride, int n, _Float16* hi,
                                                  _Float16* lo) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
-  for (int v = threadIdx.x; v < kSsdChunk * (W / 8); v += blockDim.x) {
+  constexpr int ITEMS = kSsdChunk * (W / 8) / 256;
+  static_assert(ITEMS >= 1 && kSsdChunk * (W / 8) % 256 == 0, "staging items");
+  float x[ITEMS][8];
+#pragma unroll
+  for (int u = 0; u < ITEMS; ++u) {
+    const int v = threadIdx.x + 256 * u;
     const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
-    float x[8];
-    if (t < n) load_n<ActT, 8>(src + (int64_t)t * stride + c0, x);
+    if (t < n) load_n<ActT, 8>(src + (int64_t)t * stride + c0, x[u]);
     else
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < ITEMS; ++u) {
+    const int v = threadIdx.x + 256 * u;
+    const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const _Float16 h = (_Float16)x[i];
+      const _Float16 h = (_Float16)x[u][i];
       hi[(c0 + i) * kTS + t] = h;
-      if constexpr (SPLIT) lo[(c0 + i) * kTS + t] = (_Float16)(x[i] - (float)h);
+      if constexpr (SPLIT) lo[(c0 + i) * kTS + t] = (_Float16)(x[u][i] - (float)h);
     }
   }
 }
 
+// [64 tokens][W] rows of an activation into LDS as f16 [64][W + 8] (hi, and
+// lo for f32), rows past n zero; loads first, as above.
+template <typename ActT, int W>
+__device__ __forceinline__ void stage_rows(const ActT* src, int64_t stride, int n, _Float16* hi, _Float16* lo) {
+  constexpr bool SPLIT = std::is_same<ActT, float>::value;
+  constexpr int RS = W + 8;
+  constexpr int ITEMS = kSsdChunk * (W / 8) / 256;
+  static_assert(ITEMS >= 1 && kSsdChunk * (W / 8) % 256 == 0, "staging items");
+  float x[ITEMS][8];
+#pragma unroll
+  for (int u = 0; u < ITEMS; ++u) {
+    const int v = threadIdx.x + 256 * u;
+    const int t = v / (W / 8), c0 = 8 * (v % (W / 8));
+    if (t < n) load_n<ActT, 8>(src + (int64_t)t * stride + c0, x[u]);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < ITEMS; ++u) {
+    const int v = threadIdx.x + 256 * u;
+    const int t = v / (W / 8), c0 = 8 * (v % (W / 8));
+    h8 xh, xl;
+    split8(x[u], xh, xl);
+    *reinterpret_cast<h8*>(hi + t * RS + c0) = xh;
+    if constexpr (SPLIT) *reinterpret_cast<h8*>(lo + t * RS + c0) = xl;
+  }
+}
+
+// Wave 0: the chunk's steps dt_j and cumulative log-decays L_i = sum_{j<=i}
+// A dt_j (f64 scan; tokens past n have dt = 0).  Returns L_i and dt_i of
+// lane i and L_C through lc.
+template <typename ActT>
+__device__ __forceinline__ double chunk_log_decay(const Mamba2Params& p, int64_t t0, int n, int h, int lane, float& d,
+                                                  double& lc) {
+  d = lane < n ? ssd_dt(p, Elem<ActT>::load(static_cast<const ActT*>(p.dt) + (t0 + lane) * p.H + h), h) : 0.0f;
+  double L = (double)p.A[h] * (double)d;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(L, off, 64);
+    if (lane >= off) L += o;
+  }
+  lc = __shfl(L, 63, 64);
+  return L;
+}
+
 // ---------------------------------------------------------------------------
-// Prefill: per (chunk, head)
+// Prefill pass 1, per (chunk, head): the chunk's state contribution
+//   St[p][n] = sum_j exp(L_C - L_j) dt_j x_j[p] B_j[n]
+// computed as St^T = B^T (w X) on the MFMA, and exp(L_C).
 // ---------------------------------------------------------------------------
 template <typename ActT, int P, int N>
-__global__ __launch_bounds__(256) void ssd_chunk_kernel(Mamba2Params p, SsdWs ws) {
+__global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
-  constexpr int MS = kSsdChunk + 4;   // f32 row stride of M
-  __shared__ __attribute__((aligned(16))) _Float16 CTh[N * kTS], BTh[N * kTS], XTh[P * kTS];
-  __shared__ __attribute__((aligned(16))) _Float16 CTl[SPLIT ? N * kTS : 8], BTl[SPLIT ? N * kTS : 8],
-      XTl[SPLIT ? P * kTS : 8];
-  __shared__ __attribute__((aligned(16))) float Ms[kSsdChunk * MS];
-  __shared__ double Ls[kSsdChunk];
-  __shared__ float dts[kSsdChunk], ws_[kSsdChunk];
+  constexpr int PT = P / 16, NT = N / 16, PER_WAVE = PT * NT / 4;
+  __shared__ __attribute__((aligned(16))) _Float16 BTh[N * kTS], XTh[P * kTS];
+  __shared__ __attribute__((aligned(16))) _Float16 BTl[SPLIT ? N * kTS : 8], XTl[SPLIT ? P * kTS : 8];
+  __shared__ __attribute__((aligned(16))) float ws_[kSsdChunk];
 
   const int cid = blockIdx.x, h = blockIdx.y;
   const int g = h / (p.H / p.G);
@@ -236,217 +287,329 @@ __global__ __launch_bounds__(256) void ssd_chunk_kernel(Mamba2Params p, SsdWs ws
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   char* blk = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
-  float* Yg = reinterpret_cast<float*>(blk + ssd_blk_y(P, N));
-  float* Stg = reinterpret_cast<float*>(blk + ssd_blk_st(P, N));
-  float* Vg = reinterpret_cast<float*>(blk + ssd_blk_vec(P, N));
+  float* Stg = reinterpret_cast<float*>(blk);
 
-  const ActT* Cp = static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N;
-  const ActT* Bp = static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N;
-  const ActT* Xp = static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P;
-  stage_transposed<ActT, N>(Cp, (int64_t)p.G * N, n, CTh, CTl);
-  stage_transposed<ActT, N>(Bp, (int64_t)p.G * N, n, BTh, BTl);
-  stage_transposed<ActT, P>(Xp, (int64_t)p.H * P, n, XTh, XTl);
+  stage_transposed<ActT, N>(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, BTh, BTl);
+  stage_transposed<ActT, P>(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n, XTh, XTl);
   if (wave == 0) {
-    const bool valid = lane < n;
-    const float d = valid ? ssd_dt(p, Elem<ActT>::load(static_cast<const ActT*>(p.dt) + (t0 + lane) * p.H + h), h)
-                          : 0.0f;
-    double L = (double)p.A[h] * (double)d;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(L, off, 64);
-      if (lane >= off) L += o;
-    }
-    const double Lc = __shfl(L, 63, 64);
-    Ls[lane] = L;
-    dts[lane] = d;
-    ws_[lane] = d * (float)exp(Lc - L);      // weight of token j in the chunk's state
-    Vg[lane] = (float)exp(L);                // exp(L_i) for the scan's inter-chunk term
-    if (lane == 0) Vg[kSsdChunk] = (float)exp(Lc);
+    float d;
+    double lc;
+    const double L = chunk_log_decay<ActT>(p, t0, n, h, lane, d, lc);
+    ws_[lane] = d * (float)exp(lc - L);
+    if (lane == 0) reinterpret_cast<float*>(blk + ssd_blk_vec(P, N))[0] = (float)exp(lc);
   }
   __syncthreads();
 
-  // C B^T, row block I = wave: lane holds rows i = 16I + 4lg + r, column j = 16J + li
-  {
-    constexpr int NK = N / 32;
+  // tiles in pt-major order, PER_WAVE consecutive tiles to a wave
+  int cur_pt = -1;
+  h8 bh[2], bl[2];
+#pragma unroll 1
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int tile = wave * PER_WAVE + q;
+    const int pt = tile / NT, nt = tile % NT;
+    if (pt != cur_pt) {  // B operand (w X)[j][p]: column p = 16 pt + li, rows j = 32 s + 8 lg ..
+      cur_pt = pt;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (J <= wave) {
+      for (int s = 0; s < 2; ++s) {
+        const int j0 = 32 * s + 8 * lg;
+        const h8 xh = ld_h8(XTh + (16 * pt + li) * kTS + j0);
+        h8 xl;
+        if constexpr (SPLIT) xl = ld_h8(XTl + (16 * pt + li) * kTS + j0);
+        const float4 w0 = *reinterpret_cast<const float4*>(ws_ + j0);
+        const float4 w1 = *reinterpret_cast<const float4*>(ws_ + j0 + 4);
+        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float v[8];
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          // A operand: C rows 16 wave + li over n = 32 s + 8 lg .. ; B operand: B rows 16 J + li
-          h8 ch, bh;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ch[e] = CTh[(32 * s + 8 * lg + e) * kTS + 16 * wave + li];
-            bh[e] = BTh[(32 * s + 8 * lg + e) * kTS + 16 * J + li];
-          }
-          acc = mfma_f16(ch, bh, acc);
-          if constexpr (SPLIT) {
-            h8 cl, bl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              cl[e] = CTl[(32 * s + 8 * lg + e) * kTS + 16 * wave + li];
-              bl[e] = BTl[(32 * s + 8 * lg + e) * kTS + 16 * J + li];
-            }
-            acc = mfma_f16(ch, bl, acc);
-            acc = mfma_f16(cl, bh, acc);
-          }
+        for (int e = 0; e < 8; ++e) {
+          float xv = (float)xh[e];
+          if constexpr (SPLIT) xv += (float)xl[e];
+          v[e] = xv * w[e];
         }
-      }
-      // D[4lg + r][li] = C_i . B_j with i = 16 wave + 4lg + r, j = 16J + li
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * wave + 4 * lg + r, j = 16 * J + li;
-        Ms[i * MS + j] = (j <= i && J <= wave) ? acc[r] * expf((float)(Ls[i] - Ls[j])) * dts[j] : 0.0f;
+        split8(v, bh[s], bl[s]);
       }
     }
-  }
-  __syncthreads();
-
-  // Y_intra = M X: row tile I = wave; column tiles pt over P
-#pragma unroll
-  for (int pt = 0; pt < P / 16; ++pt) {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (32 * s > 16 * wave + 15) break;
-      float m[8];
-#pragma unroll
-      for (int e4 = 0; e4 < 2; ++e4) {
-        const float4 v = *reinterpret_cast<const float4*>(Ms + (16 * wave + li) * MS + 32 * s + 8 * lg + 4 * e4);
-        m[4 * e4] = v.x; m[4 * e4 + 1] = v.y; m[4 * e4 + 2] = v.z; m[4 * e4 + 3] = v.w;
-      }
-      h8 mh, ml;
-      split8(m, mh, ml);
-      const h8 xh = ld_h8(XTh + (16 * pt + li) * kTS + 32 * s + 8 * lg);
-      acc = mfma_f16(mh, xh, acc);
-      acc = mfma_f16(ml, xh, acc);
-      if constexpr (SPLIT) acc = mfma_f16(mh, ld_h8(XTl + (16 * pt + li) * kTS + 32 * s + 8 * lg), acc);
+      // A operand B^T[n][j]: row n = 16 nt + li
+      const h8 ah = ld_h8(BTh + (16 * nt + li) * kTS + 32 * s + 8 * lg);
+      acc = mfma_f16(ah, bh[s], acc);
+      acc = mfma_f16(ah, bl[s], acc);
+      if constexpr (SPLIT) acc = mfma_f16(ld_h8(BTl + (16 * nt + li) * kTS + 32 * s + 8 * lg), bh[s], acc);
     }
-    // D[4lg + r][li] = Y[i = 16 wave + 4lg + r][p = 16 pt + li]: the scan's order
-    *reinterpret_cast<float4*>(Yg + (((int64_t)pt * 4 + wave) * 64 + lane) * 4) =
+    // D[4lg + r][li] = St^T[n = 16 nt + 4lg + r][p = 16 pt + li]
+    *reinterpret_cast<float4*>(Stg + (int64_t)(16 * pt + li) * N + 16 * nt + 4 * lg) =
         make_float4(acc[0], acc[1], acc[2], acc[3]);
-  }
-
-  // the chunk's state contribution St[p][n] = sum_j x_j[p] w_j B_j[n]:
-  // row tiles of P over the waves, column tiles of N
-  for (int pt = wave; pt < P / 16; pt += 4) {
-#pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        // A operand: x rows p = 16 pt + li over tokens j = 32 s + 8 lg .. scaled by w_j
-        float a[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 32 * s + 8 * lg + e;
-          float xv = (float)XTh[(16 * pt + li) * kTS + j];
-          if constexpr (SPLIT) xv += (float)XTl[(16 * pt + li) * kTS + j];
-          a[e] = xv * ws_[j];
-        }
-        h8 ah, al;
-        split8(a, ah, al);
-        const h8 bh = ld_h8(BTh + (16 * nt + li) * kTS + 32 * s + 8 * lg);
-        acc = mfma_f16(ah, bh, acc);
-        acc = mfma_f16(al, bh, acc);
-        if constexpr (SPLIT) acc = mfma_f16(ah, ld_h8(BTl + (16 * nt + li) * kTS + 32 * s + 8 * lg), acc);
-      }
-      // D[4lg + r][li] = St[p = 16 pt + 4lg + r][n = 16 nt + li]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Stg[(int64_t)(16 * pt + 4 * lg + r) * N + 16 * nt + li] = acc[r];
-    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: the sequential pass, one wave per (sequence, head, 16 state rows)
+// Prefill pass 2, element-wise over (sequence, head, 4 state entries): carry
+// S through the sequence's chunks, S <- exp(L_C) S + St, leaving in each
+// block the state that enters its chunk; the final S goes to the pool.
 // ---------------------------------------------------------------------------
-// The wave holds rows p = 16 pb + li of S as the B operand of S^T: lane
-// (li, lg) holds S[p][32 s + 8 lg + e] for s < N/32, e < 8.
-template <typename ActT, typename StT, int P, int N>
-__global__ __launch_bounds__(64) void ssd_scan_kernel(Mamba2Params p, SsdWs ws) {
-  constexpr bool SPLIT = std::is_same<ActT, float>::value;
-  constexpr int NK = N / 32;
-  const int pb = blockIdx.x, h = blockIdx.y, s_idx = blockIdx.z;
-  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
-  const int g = h / (p.H / p.G);
+constexpr int kPassAhead = 4;
+
+template <typename StT>
+__global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws) {
+  const int h = blockIdx.y, s_idx = blockIdx.z;
+  const int64_t PN = (int64_t)p.P * p.N;
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= PN) return;
   const int slot = p.slots ? p.slots[s_idx] : s_idx;
   const bool has = p.has_init == nullptr || p.has_init[s_idx] != 0;
-  const int prow = 16 * pb + li;
-  StT* Sg = static_cast<StT*>(p.ssm_pool) + (((int64_t)slot * p.H + h) * P + prow) * N;
-  float Sf[NK][8];
-#pragma unroll
-  for (int s = 0; s < NK; ++s) {
-    if (has) load_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf[s]);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Sf[s][e] = 0.0f;
-  }
+  StT* Sg = static_cast<StT*>(p.ssm_pool) + ((int64_t)slot * p.H + h) * PN + e0;
+  float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (has) load_n<StT, 4>(Sg, S);
   const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
-  const int64_t seq_start = p.cu[s_idx], seq_end = p.cu[s_idx + 1];
-  const ActT* xg = static_cast<const ActT*>(p.x);
-  const ActT* zg = static_cast<const ActT*>(p.z);
-  ActT* og = static_cast<ActT*>(p.out);
-  const float dcoef = p.D ? (p.D_per_p ? p.D[h * P + prow] : p.D[h]) : 0.0f;
-  for (int cid = c_begin; cid < c_end; ++cid) {
-    const char* blk = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
-    const float* Yg = reinterpret_cast<const float*>(blk + ssd_blk_y(P, N));
-    const float* Stg = reinterpret_cast<const float*>(blk + ssd_blk_st(P, N));
-    const float* Vg = reinterpret_cast<const float*>(blk + ssd_blk_vec(P, N));
-    const int64_t t0 = seq_start + (int64_t)kSsdChunk * (cid - c_begin);
-    const int n = (int)min((int64_t)kSsdChunk, seq_end - t0);
-    // S split into f16 halves as the B operand
-    h8 Sh[NK], Sl[NK];
+  const int64_t bb = ssd_blk_bytes(p.P, p.N), vo = ssd_blk_vec(p.P, p.N);
+  for (int c = c_begin; c < c_end; c += kPassAhead) {
+    float4 v[kPassAhead];
+    float eL[kPassAhead];
 #pragma unroll
-    for (int s = 0; s < NK; ++s) split8(Sf[s], Sh[s], Sl[s]);
+    for (int u = 0; u < kPassAhead; ++u) {
+      if (c + u < c_end) {
+        const char* blk = ws.blocks + ((int64_t)(c + u) * p.H + h) * bb;
+        v[u] = *reinterpret_cast<const float4*>(blk + e0 * 4);
+        eL[u] = *reinterpret_cast<const float*>(blk + vo);
+      }
+    }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if (16 * it >= n) break;
-      // A operand: C rows t0 + 16 it + li over n = 32 s + 8 lg ..
-      const int crow = min(16 * it + li, n - 1);
-      const ActT* cr = static_cast<const ActT*>(p.C) + ((t0 + crow) * p.G + g) * N;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < kPassAhead; ++u) {
+      if (c + u < c_end) {
+        char* blk = ws.blocks + ((int64_t)(c + u) * p.H + h) * bb;
+        *reinterpret_cast<float4*>(blk + e0 * 4) = make_float4(S[0], S[1], S[2], S[3]);
+        S[0] = eL[u] * S[0] + v[u].x;
+        S[1] = eL[u] * S[1] + v[u].y;
+        S[2] = eL[u] * S[2] + v[u].z;
+        S[3] = eL[u] * S[3] + v[u].w;
+      }
+    }
+  }
+  store_n<StT, 4>(Sg, S);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill pass 3, per (chunk, head): outputs
+//   Y = (M * C B^T) X + diag(exp(L)) C S0^T,  y = (Y + D x) silu(z)
+// with S0 the state entering the chunk.  C and B are staged row-major (the
+// k index of both products is n), X transposed (k = token).
+// ---------------------------------------------------------------------------
+template <int P, int N, bool SPLIT>
+struct SsdOutLds {
+  static constexpr int RS = N + 8;            // halves per C/B row
+  static constexpr int MS = kSsdChunk + 4;    // floats per M row
+  static constexpr int YS = P + 4;            // floats per Y row
+  static constexpr int kRowHalves = kSsdChunk * RS;
+  static constexpr int kXHalves = P * kTS;
+  static constexpr int kParts = SPLIT ? 2 : 1;
+  static constexpr int kC = kRowHalves * kParts * 2;    // C (hi, lo) at 0, B (hi, lo) after it
+  static constexpr int kMBytes = kSsdChunk * MS * 4;    // M, over B once C B^T is in registers
+  static constexpr int kYBytes = kSsdChunk * YS * 4;    // Y, over everything above at the end
+  static constexpr int kU0 = 2 * kC > kC + kMBytes ? 2 * kC : kC + kMBytes;
+  static constexpr int kUnion = kU0 > kYBytes ? kU0 : kYBytes;
+  static constexpr int kX = kUnion;                     // X^T (hi, lo)
+  static constexpr int kL = kX + kXHalves * kParts * 2; // double L[64]
+  static constexpr int kDt = kL + kSsdChunk * 8;
+  static constexpr int kE = kDt + kSsdChunk * 4;
+  static constexpr int kBytes = kE + kSsdChunk * 4;
+};
+
+template <typename ActT, int P, int N>
+__global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
+  constexpr bool SPLIT = std::is_same<ActT, float>::value;
+  using Lay = SsdOutLds<P, N, SPLIT>;
+  constexpr int RS = Lay::RS, MS = Lay::MS, YS = Lay::YS;
+  constexpr int NK = N / 32;
+  constexpr int NPT = P / 64 > 0 ? P / 64 : 1;  // column tiles of 16 per wave
+  __shared__ __attribute__((aligned(16))) char smem[Lay::kBytes];
+  _Float16* Ch = reinterpret_cast<_Float16*>(smem);
+  _Float16* Cl = Ch + Lay::kRowHalves;   // f32 activations only
+  _Float16* Bh = reinterpret_cast<_Float16*>(smem + Lay::kC);
+  _Float16* Bl = Bh + Lay::kRowHalves;
+  float* Ms = reinterpret_cast<float*>(smem + Lay::kC);  // over B
+  float* Ys = reinterpret_cast<float*>(smem);            // over C, B and M at the end
+  _Float16* XTh = reinterpret_cast<_Float16*>(smem + Lay::kX);
+  _Float16* XTl = XTh + Lay::kXHalves;
+  double* Ls = reinterpret_cast<double*>(smem + Lay::kL);
+  float* dts = reinterpret_cast<float*>(smem + Lay::kDt);
+  float* eLs = reinterpret_cast<float*>(smem + Lay::kE);
+
+  const int cid = blockIdx.x, h = blockIdx.y;
+  const int g = h / (p.H / p.G);
+  const int seq = ws.chunk_seq[cid];
+  const int64_t t0 = ws.chunk_start[cid];
+  const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const float* S0 = reinterpret_cast<const float*>(ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N));
+
+  // the wave's column tiles pt = wave + 4 q (P = 32: waves 2, 3 have none);
+  // their S0 rows as the B operand S0^T[n][p], loaded before the staging
+  const bool has_cols = 16 * wave < P;
+  float sv[NPT][NK][8];
+  if (has_cols) {
+#pragma unroll
+    for (int q = 0; q < NPT; ++q)
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        float c8[8];
-        load_n<ActT, 8>(cr + 32 * s + 8 * lg, c8);
-        h8 chh, cl;
-        split8(c8, chh, cl);
-        acc = mfma_f16(chh, Sh[s], acc);
-        acc = mfma_f16(chh, Sl[s], acc);
-        if constexpr (SPLIT) acc = mfma_f16(cl, Sh[s], acc);
+        const float* sp = S0 + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
+        const float4 a = *reinterpret_cast<const float4*>(sp);
+        const float4 b = *reinterpret_cast<const float4*>(sp + 4);
+        sv[q][s][0] = a.x; sv[q][s][1] = a.y; sv[q][s][2] = a.z; sv[q][s][3] = a.w;
+        sv[q][s][4] = b.x; sv[q][s][5] = b.y; sv[q][s][6] = b.z; sv[q][s][7] = b.w;
       }
-      // D[4lg + r][li] = (C S^T)[i = 16 it + 4lg + r][p = 16 pb + li]
-      const float4 yv = *reinterpret_cast<const float4*>(Yg + (((int64_t)pb * 4 + it) * 64 + lane) * 4);
-      const float4 ev = *reinterpret_cast<const float4*>(Vg + 16 * it + 4 * lg);
-      const float ya[4] = {yv.x, yv.y, yv.z, yv.w}, ea[4] = {ev.x, ev.y, ev.z, ev.w};
+  }
+
+  stage_rows<ActT, N>(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Ch, Cl);
+  stage_rows<ActT, N>(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Bh, Bl);
+  stage_transposed<ActT, P>(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n, XTh, XTl);
+
+  // the epilogue's x and z (8 consecutive p of one token per item), loaded
+  // now and kept packed so that their latency overlaps the products
+  constexpr int EPI = (kSsdChunk * (P / 8) + 255) / 256;
+  constexpr int NV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
+  const ActT* xg = static_cast<const ActT*>(p.x);
+  const ActT* zg = static_cast<const ActT*>(p.z);
+  uint4 xr[EPI][NV], zr[EPI][NV];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * lg + r;
-        if (i < n) {
-          const int64_t off = ((t0 + i) * p.H + h) * P + prow;
-          float y = ea[r] * acc[r] + ya[r];
-          if (p.D) y += dcoef * Elem<ActT>::load(xg + off);
-          if (p.z) y *= silu_f(Elem<ActT>::load(zg + off));
-          Elem<ActT>::store(og + off, y);
-        }
+  for (int u = 0; u < EPI; ++u) {
+    const int v = tid + 256 * u;
+    const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
+    if (v < kSsdChunk * (P / 8) && i < n) {
+      const int64_t off = ((t0 + i) * p.H + h) * P + p0;
+#pragma unroll
+      for (int w = 0; w < NV; ++w) {
+        if (p.D) xr[u][w] = ld16(xg + off + w * Elem<ActT>::kVec);
+        if (zg) zr[u][w] = ld16(zg + off + w * Elem<ActT>::kVec);
       }
-    }
-    // S <- exp(L_C) S + St
-    const float eL = Vg[kSsdChunk];
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      const float4 a = *reinterpret_cast<const float4*>(Stg + (int64_t)prow * N + 32 * s + 8 * lg);
-      const float4 b = *reinterpret_cast<const float4*>(Stg + (int64_t)prow * N + 32 * s + 8 * lg + 4);
-      const float add[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Sf[s][e] = eL * Sf[s][e] + add[e];
     }
   }
+  if (wave == 0) {
+    float d;
+    double lc;
+    const double L = chunk_log_decay<ActT>(p, t0, n, h, lane, d, lc);
+    Ls[lane] = L;
+    dts[lane] = d;
+    eLs[lane] = (float)exp(L);
+  }
+  __syncthreads();
+
+  // M = (C B^T) masked and weighted; row block I = wave, column blocks J <= I
+  f32x4 cb[4];
 #pragma unroll
-  for (int s = 0; s < NK; ++s) store_n<StT, 8>(Sg + 32 * s + 8 * lg, Sf[s]);
+  for (int J = 0; J < 4; ++J) {
+    cb[J] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (J > wave) continue;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int k0 = 32 * s + 8 * lg;
+      const h8 ch = ld_h8(Ch + (16 * wave + li) * RS + k0);
+      const h8 bh = ld_h8(Bh + (16 * J + li) * RS + k0);
+      cb[J] = mfma_f16(ch, bh, cb[J]);
+      if constexpr (SPLIT) {
+        cb[J] = mfma_f16(ch, ld_h8(Bl + (16 * J + li) * RS + k0), cb[J]);
+        cb[J] = mfma_f16(ld_h8(Cl + (16 * wave + li) * RS + k0), bh, cb[J]);
+      }
+    }
+  }
+  __syncthreads();  // B is done with; M goes over it
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * wave + 4 * lg + r, j = 16 * J + li;
+      Ms[i * MS + j] = (J <= wave && j <= i) ? cb[J][r] * expf((float)(Ls[i] - Ls[j])) * dts[j] : 0.0f;
+    }
+  __syncthreads();
+
+  // Y[16 it + .., 16 pt + ..] = (M X) + exp(L_i) (C S0^T), pt = the wave's tiles
+  float yv[NPT][4][4];
+  if (has_cols) {
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+      const int pt = wave + 4 * q;
+      h8 sh[NK], sl[NK];
+#pragma unroll
+      for (int s = 0; s < NK; ++s) split8(sv[q][s], sh[s], sl[s]);
+      h8 xh[2], xl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        xh[s] = ld_h8(XTh + (16 * pt + li) * kTS + 32 * s + 8 * lg);
+        if constexpr (SPLIT) xl[s] = ld_h8(XTl + (16 * pt + li) * kTS + 32 * s + 8 * lg);
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (32 * s > 16 * it + 15) break;
+          float m[8];
+#pragma unroll
+          for (int e4 = 0; e4 < 2; ++e4) {
+            const float4 v = *reinterpret_cast<const float4*>(Ms + (16 * it + li) * MS + 32 * s + 8 * lg + 4 * e4);
+            m[4 * e4] = v.x; m[4 * e4 + 1] = v.y; m[4 * e4 + 2] = v.z; m[4 * e4 + 3] = v.w;
+          }
+          h8 mh, ml;
+          split8(m, mh, ml);
+          acc = mfma_f16(mh, xh[s], acc);
+          acc = mfma_f16(ml, xh[s], acc);
+          if constexpr (SPLIT) acc = mfma_f16(mh, xl[s], acc);
+        }
+        f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const int k0 = 32 * s + 8 * lg;
+          const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
+          acc2 = mfma_f16(ch, sh[s], acc2);
+          acc2 = mfma_f16(ch, sl[s], acc2);
+          if constexpr (SPLIT) acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
+        }
+        const float4 ev = *reinterpret_cast<const float4*>(eLs + 16 * it + 4 * lg);
+        yv[q][it][0] = acc[0] + ev.x * acc2[0];
+        yv[q][it][1] = acc[1] + ev.y * acc2[1];
+        yv[q][it][2] = acc[2] + ev.z * acc2[2];
+        yv[q][it][3] = acc[3] + ev.w * acc2[3];
+      }
+    }
+  }
+  __syncthreads();  // C and M are done with; Y goes over them
+  if (has_cols) {
+#pragma unroll
+    for (int q = 0; q < NPT; ++q)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ys[(16 * it + 4 * lg + r) * YS + 16 * (wave + 4 * q) + li] = yv[q][it][r];
+  }
+  __syncthreads();
+
+  // epilogue, 8 consecutive p of one token per item: + D x, * silu(z)
+  ActT* og = static_cast<ActT*>(p.out);
+#pragma unroll
+  for (int u = 0; u < EPI; ++u) {
+    const int v = tid + 256 * u;
+    const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
+    if (v >= kSsdChunk * (P / 8) || i >= n) continue;
+    const int64_t off = ((t0 + i) * p.H + h) * P + p0;
+    const float4 y0 = *reinterpret_cast<const float4*>(Ys + i * YS + p0);
+    const float4 y1 = *reinterpret_cast<const float4*>(Ys + i * YS + p0 + 4);
+    float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    if (p.D) {
+      float xv[8];
+#pragma unroll
+      for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(xr[u][w], xv + w * Elem<ActT>::kVec);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] += (p.D_per_p ? p.D[h * P + p0 + e] : p.D[h]) * xv[e];
+    }
+    if (zg) {
+      float zv[8];
+#pragma unroll
+      for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(zr[u][w], zv + w * Elem<ActT>::kVec);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= silu_f(zv[e]);
+    }
+    store_n<ActT, 8>(og + off, y);
+  }
 }
 
 template <typename ActT, typename StT, int N>
@@ -466,39 +629,47 @@ hipError_t launch_update(const Mamba2Params& p, hipStream_t stream) {
   }
 }
 
-template <typename ActT, typename StT, int P, int N>
+template <typename ActT, int P, int N>
 hipError_t launch_chunked_pn(const Mamba2Params& p, const SsdWs& ws, hipStream_t stream) {
-  if (p.num_chunks > 0) ssd_chunk_kernel<ActT, P, N><<<dim3((unsigned)p.num_chunks, p.H), 256, 0, stream>>>(p, ws);
-  ssd_scan_kernel<ActT, StT, P, N><<<dim3(P / 16, p.H, p.Nseq), 64, 0, stream>>>(p, ws);
+  if (p.num_chunks > 0) {
+    const dim3 grid((unsigned)p.num_chunks, p.H);
+    ssd_state_kernel<ActT, P, N><<<grid, 256, 0, stream>>>(p, ws);
+    switch (p.state) {
+      case GDN_F32: ssd_pass_kernel<float><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
+      case GDN_BF16: ssd_pass_kernel<bf16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
+      default: ssd_pass_kernel<f16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
+    }
+    ssd_out_kernel<ActT, P, N><<<grid, 256, 0, stream>>>(p, ws);
+  }
   return hipGetLastError();
 }
 
-template <typename ActT, typename StT, int P>
+template <typename ActT, int P>
 hipError_t launch_chunked_p(const Mamba2Params& p, const SsdWs& ws, hipStream_t stream) {
   switch (p.N) {
-    case 32: return launch_chunked_pn<ActT, StT, P, 32>(p, ws, stream);
-    case 64: return launch_chunked_pn<ActT, StT, P, 64>(p, ws, stream);
-    default: return launch_chunked_pn<ActT, StT, P, 128>(p, ws, stream);
-  }
-}
-
-template <typename ActT, typename StT>
-hipError_t launch_chunked(const Mamba2Params& p, hipStream_t stream) {
-  const SsdWs ws = ssd_carve(p.workspace, p.Nseq, p.T);
-  ssd_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.Nseq, ws);
-  switch (p.P) {
-    case 32: return launch_chunked_p<ActT, StT, 32>(p, ws, stream);
-    case 64: return launch_chunked_p<ActT, StT, 64>(p, ws, stream);
-    default: return launch_chunked_p<ActT, StT, 128>(p, ws, stream);
+    case 32: return launch_chunked_pn<ActT, P, 32>(p, ws, stream);
+    case 64: return launch_chunked_pn<ActT, P, 64>(p, ws, stream);
+    default: return launch_chunked_pn<ActT, P, 128>(p, ws, stream);
   }
 }
 
 template <typename ActT>
-hipError_t dispatch_state(const Mamba2Params& p, bool chunked, hipStream_t stream) {
+hipError_t launch_chunked(const Mamba2Params& p, hipStream_t stream) {
+  const SsdWs ws = ssd_carve(p.workspace, p.Nseq, p.T);
+  ssd_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.Nseq, ws);
+  switch (p.P) {
+    case 32: return launch_chunked_p<ActT, 32>(p, ws, stream);
+    case 64: return launch_chunked_p<ActT, 64>(p, ws, stream);
+    default: return launch_chunked_p<ActT, 128>(p, ws, stream);
+  }
+}
+
+template <typename ActT>
+hipError_t dispatch_update(const Mamba2Params& p, hipStream_t stream) {
   switch (p.state) {
-    case GDN_F32: return chunked ? launch_chunked<ActT, float>(p, stream) : launch_update<ActT, float>(p, stream);
-    case GDN_BF16: return chunked ? launch_chunked<ActT, bf16>(p, stream) : launch_update<ActT, bf16>(p, stream);
-    default: return chunked ? launch_chunked<ActT, f16>(p, stream) : launch_update<ActT, f16>(p, stream);
+    case GDN_F32: return launch_update<ActT, float>(p, stream);
+    case GDN_BF16: return launch_update<ActT, bf16>(p, stream);
+    default: return launch_update<ActT, f16>(p, stream);
   }
 }
 
@@ -511,11 +682,11 @@ size_t mamba2_workspace_bytes(int H, int P, int N, int Ns, int64_t T) {
 }
 
 hipError_t launch_mamba2_update(const Mamba2Params& p, hipStream_t stream) {
-  return p.act == GDN_F32 ? dispatch_state<float>(p, false, stream) : dispatch_state<bf16>(p, false, stream);
+  return p.act == GDN_F32 ? dispatch_update<float>(p, stream) : dispatch_update<bf16>(p, stream);
 }
 
 hipError_t launch_mamba2_chunk_scan(const Mamba2Params& p, hipStream_t stream) {
-  return p.act == GDN_F32 ? dispatch_state<float>(p, true, stream) : dispatch_state<bf16>(p, true, stream);
+  return p.act == GDN_F32 ? launch_chunked<float>(p, stream) : launch_chunked<bf16>(p, stream);
 }
 
 }  // namespace gdn
