@@ -531,7 +531,7 @@ def mamba2(torch, gdn, reps=20):
                   "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb,
                   "workspace_bytes_per_launch": ws_b, "flops_per_launch": fl,
                   "mfma_frac": fl / sec / 1e12 / F16_MFMA_PEAK_TFLOPS,
-                  "kernels": "ssd_table_kernel + ssd_chunk_kernel + ssd_scan_kernel"}
+                  "kernels": "ssd_table_kernel + ssd_state_kernel + ssd_pass_kernel + ssd_out_kernel"}
         else:
             nb = mamba2_decode_bytes(T, H, P, G, N)
             rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -376,7 +376,9 @@ gdn_status gdn_mamba2_state_update(const gdn_ssm_dims* sdims, int32_t batch, con
  * recurrence as gdn_mamba2_state_update, token by token), computed in chunks
  * of 64 tokens in the dual form ([P1] Mamba2ChunkScanKernel, whose five
  * stages compute it).  Sequence s starts from its slot's state (zero when
- * has_initial_state[s] is 0) and its final state is written back.
+ * has_initial_state[s] is 0) and its final state is written back, rounded
+ * once to the pool dtype; the states passed between chunks stay f32 (the
+ * pages round them to the pool dtype as well).
  *
  * Arguments: those of gdn_mamba2_state_update over T tokens, plus
  *   num_seqs, total_tokens, cu_seqlens_host/_dev: as gdn_prepare (no empty sequence).
