@@ -76,6 +76,21 @@ struct Elem16 {
   }
 };
 
+// Eight f32 -> bf16 with the gfx950 conversion instruction (two values per
+// instruction, round to nearest even): finite values round exactly as
+// f32_to_bf16 does; a NaN stays a NaN (its payload may differ).
+__device__ __forceinline__ uint4 pack_bf16x8_hw(const float* v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t a = {v[2 * i], v[2 * i + 1]};
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 struct BF16Conv {
   __device__ __forceinline__ static float to_f32(uint16_t b) { return bf16_to_f32(b); }
   __device__ __forceinline__ static uint16_t from_f32(float f) { return f32_to_bf16(f); }

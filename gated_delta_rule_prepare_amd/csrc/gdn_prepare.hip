@@ -17,6 +17,8 @@
 // sequence's last K-1 raw inputs into its conv history row.  It runs after
 // kernel 1 on the same stream, so every read of an old history row happens
 // before that row is overwritten.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -25,7 +27,7 @@ namespace {
 
 constexpr int kConvWaves = 4;   // waves per workgroup (one channel block each)
 constexpr int kStrip = 32;      // tokens per wave
-constexpr int kAhead = 8;       // token rows loaded before they are used
+constexpr int kAhead = 4;       // token rows loaded before they are used
 
 // Largest s in [0, N) with cu[s] <= t, found by the whole wave (t is
 // wave-uniform and cu[0] = 0 <= t).  Each round splits the candidate range
@@ -189,13 +191,59 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
     QkvT* dst = out_base + t * out_row + out_col;
     if constexpr (OW >= 1) {
 #pragma unroll
-      for (int o = 0; o < OW; ++o)
-        store_stream(dst + o * Elem<QkvT>::kVec, Elem<QkvT>::pack(y + o * Elem<QkvT>::kVec));
+      for (int o = 0; o < OW; ++o) {
+        const float* yo = y + o * Elem<QkvT>::kVec;
+        if constexpr (std::is_same<QkvT, bf16>::value) store_stream(dst + o * Elem<QkvT>::kVec, pack_bf16x8_hw(yo));
+        else store_stream(dst + o * Elem<QkvT>::kVec, Elem<QkvT>::pack(yo));
+      }
     } else {
       store_n<QkvT, V>(dst, y);
     }
   };
+  // conv + SiLU of one token from its input xv and the K-1 inputs before it
+  // (prev(j) = the input j+1 tokens back), then the q/k L2 norm; stores.
+  auto finish_token = [&](int64_t t, const float* xv, auto prev) {
+    float y[V];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float acc = wt[K - 1][i] * xv[i];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) acc += wt[K - 2 - j][i] * prev(j, i);
+      y[i] = silu_f(acc);
+      ss += y[i] * y[i];
+    }
+    if (p.l2norm && region < 2) {
+      const float inv = __builtin_amdgcn_rsqf(head_sum(ss) + 1e-6f);
+#pragma unroll
+      for (int i = 0; i < V; ++i) y[i] *= inv;
+    }
+    store_row(t, y);
+  };
   auto process = [&](const uint4* buf, int64_t tb) {
+    if (tb + kAhead <= t1 && tb + kAhead <= seq_end) {
+      // the whole block lies in the current sequence: every earlier input
+      // comes from this block's rows or the window, at fixed positions
+      float xs[kAhead][V];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) Elem<ActT>::unpack(buf[u], xs[u]);
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        finish_token(tb + u, xs[u], [&](int j, int i) { return u - 1 - j >= 0 ? xs[u - 1 - j][i] : win[j - u][i]; });
+      if constexpr (K > 1) {
+        // new window: input j+1 tokens before the next block
+        float nw[H][V];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+          for (int i = 0; i < V; ++i) nw[j][i] = kAhead - 1 - j >= 0 ? xs[kAhead - 1 - j][i] : win[j - kAhead][i];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+          for (int i = 0; i < V; ++i) win[j][i] = nw[j][i];
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
       const int64_t t = tb + u;
@@ -208,22 +256,7 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
       }
       float xv[V];
       Elem<ActT>::unpack(buf[u], xv);
-      float y[V];
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        float acc = wt[K - 1][i] * xv[i];
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j) acc += wt[K - 2 - j][i] * win[j][i];
-        y[i] = silu_f(acc);
-        ss += y[i] * y[i];
-      }
-      if (p.l2norm && region < 2) {
-        const float inv = __builtin_amdgcn_rsqf(head_sum(ss) + 1e-6f);
-#pragma unroll
-        for (int i = 0; i < V; ++i) y[i] *= inv;
-      }
-      store_row(t, y);
+      finish_token(t, xv, [&](int j, int i) { return win[j][i]; });
       if constexpr (K > 1) {
 #pragma unroll
         for (int j = K - 2; j > 0; --j)

@@ -138,6 +138,24 @@ def test_prepare_full_size_sampled_heads(which):
         np.testing.assert_array_equal(got["conv_pool"][:, ch], want["conv_pool"])
 
 
+def test_prepare_bf16_outputs_are_rne_of_f32_outputs():
+    """The bf16 q/k/v of the prepare are the f32 results rounded to nearest
+    even, bit for bit: the same inputs through the f32-output and the
+    bf16-output kernels (the bf16 store uses the hardware conversion).
+    Several sequences, so that blocks inside a sequence and blocks that
+    straddle a sequence start both run."""
+    cfg = Config("p_rne", "prefill", Dims(4, 8, 128, 128, 4), seqlens=(300, 5, 77, 130), num_slots=6,
+                 act_dtype="bf16", qkv_dtype="bf16", conv_state_std=1.0, init_state_std=0.05, seed=18)
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    _say(f"[prepare rne] T={cfg.T}")
+    got32 = R.prepare(d, inp, "bf16", "f32", True)
+    got16 = R.prepare(d, inp, "bf16", "bf16", True)
+    for key in ("q", "k", "v"):
+        np.testing.assert_array_equal(got16[key], oracle.round_to(got32[key], "bf16"), err_msg=key)
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
