@@ -13,7 +13,8 @@
 //
 // Phase B (the recurrence, vllm.cpp cpu_ops.cpp GdnHeadTokenStep): state rows
 // stream through registers.  A lane holds 16 bytes of a row (Dk/lanes-per-row
-// columns); a wave load covers 1 KiB of consecutive rows.  Per row the two
+// columns); a wave load covers 1 KiB of consecutive rows; a lane has eight
+// such loads per batch and two batches in flight.  Per row the two
 // dot products S.k and S.q are formed in one pass and summed across the
 // lanes of the row; then, with d = exp(g):
 //   u = d (S.k);  delta = beta (v - u);  o = d (S.q) + delta (k.q);
@@ -47,7 +48,7 @@ __device__ __forceinline__ void store_stream(void* p, const uint4& u) {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kLoads = 4;  // 16-byte state loads per lane per batch (two batches in flight)
+constexpr int kLoads = 8;  // 16-byte state loads per lane per batch (two batches in flight)
 
 // value as stored in ActT and read back
 template <typename ActT>
@@ -84,7 +85,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
 
   const int sub = lane / LPR;          // row within this wave's load
   const int col = (lane % LPR) * SV;   // first state column of this lane
-  auto row_of = [&](int it, int u) { return it * ROWS_PER_ITER + (u * kDecWaves + wave) * RPL + sub; };
+  // Workgroups start their stream at different batches of their rows (a
+  // rotation by block index; every batch is still visited once), so the
+  // workgroups in flight do not all open the same offsets of their regions
+  // at the same moment.
+  const int iters = (R + ROWS_PER_ITER - 1) / ROWS_PER_ITER;
+  const int rot = (int)((blockIdx.x * 5u + blockIdx.y * 3u) % (unsigned)iters);
+  auto row_of = [&](int it, int u) {
+    return ((it + rot) % iters) * ROWS_PER_ITER + (u * kDecWaves + wave) * RPL + sub;
+  };
 
   // issue the first batch of state loads before the prepare work
   uint4 raw[kLoads];
@@ -167,7 +176,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
 
   // ---- phase B: stream the R state rows, the next batch of loads in flight
   // while the current one computes (rows past R re-read row R-1, unused)
-  const int iters = (R + ROWS_PER_ITER - 1) / ROWS_PER_ITER;
   auto load_batch = [&](uint4* buf, int it) {
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) buf[u] = load_stream(S + (int64_t)min(row_of(it, u), R - 1) * DK + col);
@@ -201,9 +209,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
   };
   uint4 raw2[kLoads];
   for (int it = 0; it < iters; it += 2) {
-    load_batch(raw2, min(it + 1, iters - 1));
+    if (it + 1 < iters) load_batch(raw2, it + 1);  // workgroup-uniform branches: no batch is loaded twice
     compute_batch(raw, it);
-    load_batch(raw, min(it + 2, iters - 1));
+    if (it + 2 < iters) load_batch(raw, it + 2);
     if (it + 1 < iters) compute_batch(raw2, it + 1);
   }
 
