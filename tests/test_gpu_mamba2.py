@@ -70,6 +70,11 @@ SCAN_CASES = [
     ("f32_f32_h2_p32_n32_Dhp", 2, 32, 1, 32, (100, 7), "f32", "f32", dict(D_mode="hp")),
     ("f32_bf16_h3_p128_n64_noz", 3, 128, 3, 64, (129,), "f32", "bf16", dict(with_z=False)),
     ("bf16_f16_h8_p64_n64_long", 8, 64, 4, 64, (700,), "bf16", "f16", dict(init_std=0.05)),
+    # the largest instantiation (f32 activations, P = N = 128)
+    ("f32_f32_h2_p128_n128_Dhp", 2, 128, 2, 128, (150, 70), "f32", "f32", dict(D_mode="hp")),
+    ("bf16_f32_h2_p32_n128", 2, 32, 1, 128, (90, 64), "bf16", "f32", {}),
+    # more sequences than the chunk-table wave has lanes
+    ("bf16_f32_h2_p64_n64_70seqs", 2, 64, 1, 64, tuple(1 + (i * 37) % 150 for i in range(70)), "bf16", "f32", {}),
 ]
 
 

@@ -285,6 +285,10 @@ PF_CASES += [
                       act_dtype="bf16", qkv_dtype="f32", init_state_std=0.1, conv_state_std=1.0, seed=37)),
     ("d64_r3_f16", Config("pf_d64b", "prefill", Dims(1, 3, 64, 64, 2), seqlens=(129, 300), num_slots=4,
                           act_dtype="bf16", qkv_dtype="bf16", state_dtype="f16", init_state_std=0.1, seed=38)),
+    # more sequences than the chunk-table wave has lanes: each lane takes two
+    ("over_64_seqs", Config("pf_70", "prefill", Dims(1, 2, 64, 64, 4),
+                            seqlens=tuple(1 + (i * 37) % 150 for i in range(70)), num_slots=72, act_dtype="bf16",
+                            qkv_dtype="bf16", state_dtype="f32", init_state_std=0.05, conv_state_std=1.0, seed=40)),
     ("many_short_seqs", Config("pf_many", "prefill", Dims(2, 4, 128, 128, 4),
                                seqlens=tuple([1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 63, 64, 65, 127, 128]),
                                num_slots=20, act_dtype="bf16", qkv_dtype="bf16", state_dtype="f32",
