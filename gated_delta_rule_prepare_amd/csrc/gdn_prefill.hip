@@ -31,18 +31,25 @@
 //  2. chunk_prep_kernel, one workgroup per (chunk, value head), no state
 //     dependence: K K^T and Q K^T with operands read straight from memory,
 //     T = (I + A)^-1 (16x16 diagonal blocks by substitution in registers,
-//     off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ on MFMA), then W and U
-//     against K^T / V^T staged in LDS.  Writes W and P (f16 hi/lo), U^T
-//     (f32), the row-scaled K^T (f16), gamma, exp(G_C - G_j) and the q/k row
-//     scales to the workspace.
+//     off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ on MFMA).  Writes P
+//     (f16), the row-scaled K^T (f16), gamma, exp(G_C - G_j) and the q/k row
+//     scales to the workspace, and then
+//       - with bf16 q/k/v (the "T form"): T diag(beta) (f16 hi/lo) and the
+//         row-scaled K rows in the scan's contraction order;
+//       - with f32 q/k/v (the "W form"): W (f16 hi/lo) and U^T (f32), formed
+//         against K^T / V^T staged in LDS.
 //  3. chunk_scan_kernel, one workgroup (8 waves) per (sequence, value head,
 //     block of 16 value rows), placed so that the row blocks and value heads
 //     of one key head share an XCD's L2: walks the sequence's chunks in order.
 //     Four waves carry the 16 x Dk state block in registers and run only the
 //     serial part (Delta and the state update); four more do the bulk loads,
-//     staging W and K^T into LDS, and form the output of each chunk from the
-//     state and Delta published in LDS.  One barrier per chunk.  Value rows of
-//     the state are independent, so row blocks never communicate.
+//     staging the chunk operands and K^T into LDS, and form the output of
+//     each chunk from the state and Delta published in LDS.  One barrier per
+//     chunk.  Value rows of the state are independent, so row blocks never
+//     communicate.  Delta = U - W S0^T in the W form; in the T form
+//     Delta = T diag(beta) (V - diag(gamma) K S0^T), the same quantity by
+//     (I + A) Delta = diag(beta) V - diag(beta gamma) K S0^T, which moves the
+//     two [c, c] x [c, D] products W and U out of the per-chunk work.
 //
 // Shapes the chunked kernels do not cover (Dk != Dv, or head dims 16 or
 // 256) run a token-sequential kernel: one wave per sequence, value head and
@@ -101,6 +108,13 @@ __host__ __device__ constexpr int64_t blk_kt_hi(int D) { return blk_p_hi(D) + kC
 __host__ __device__ constexpr int64_t blk_kt_lo(int D) { return blk_kt_hi(D) + (int64_t)D * kChunk * 2; }
 __host__ __device__ constexpr int64_t blk_vec(int D) { return blk_kt_hi(D) + (int64_t)D * kChunk * 4; }
 __host__ __device__ constexpr int64_t blk_bytes(int D) { return blk_vec(D) + 4 * kChunk * 4; }
+
+// With bf16 q/k/v the block holds T diag(beta) (f16 hi [64][64], then lo)
+// in place of W and U^T, and the scan forms Delta = T diag(beta) (V -
+// diag(gamma) K S0^T) itself.  The first 16 KiB of a block always lie inside
+// the W / U^T region (blk_p_hi(D) = 512 D >= 16 KiB for D >= 32).
+__host__ __device__ constexpr int64_t blk_tb_hi() { return 0; }
+__host__ __device__ constexpr int64_t blk_tb_lo() { return (int64_t)kChunk * kChunk * 2; }
 
 struct ChunkWs {
   int32_t* seq_chunk_off;  // [N+1] first chunk id of each sequence
@@ -374,14 +388,40 @@ __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, c
   }
 }
 
+// T diag(beta) as f16 hi/lo [64][64] rows for the scan (bf16 q/k/v), the
+// columns of each group of 32 in the scan's contraction order (position
+// 8b + 4a + c holds column 16a + 4b + c).  Entries above the diagonal are
+// zero.  Thread t writes positions 16 (t % 4) .. +15 of row t / 4.
+template <int TS>
+__device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _Float16* hi, _Float16* lo) {
+  const int i = threadIdx.x >> 2, q = threadIdx.x & 3;
+  float v[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int pos = 16 * q + m, w = pos & 31;
+    const int j = (pos & ~31) + 16 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
+    v[m] = j <= i ? Ts[i * TS + j] * bs[j] : 0.0f;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    h8 vh, vl;
+    split8(v + 8 * h, vh, vl);
+    *reinterpret_cast<h8*>(hi + i * kChunk + 16 * q + 8 * h) = vh;
+    *reinterpret_cast<h8*>(lo + i * kChunk + 16 * q + 8 * h) = vl;
+  }
+}
+
+// Three workgroups per CU (measured 64 -> 56 us at 4096 tokens against two;
+// four would spill heavily).
 template <typename QkvT, int D>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
   constexpr int NKS = D / 32;      // 32-wide k steps over the head dim
   constexpr int NCT = D / 16;      // 16-column tiles of W (and of U)
   constexpr int TS = kChunk + 4;   // f32 row stride of A and T
-  __shared__ __attribute__((aligned(16))) _Float16 KTh[D * KTS];
-  __shared__ __attribute__((aligned(16))) _Float16 VTh[D * KTS];
+  // the transposed K and V tiles feed W and U, which only f32 inputs form here
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[SPLIT ? D * KTS : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 VTh[SPLIT ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 KTl[SPLIT ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 VTl[SPLIT ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) float As[kChunk * TS];
@@ -422,23 +462,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
   constexpr int RS = D + 8;  // row stride (elements) of the staged rows
   static_assert(!STAGE || kChunk * RS * 2 <= kChunk * TS * 4, "staged rows fit the A / T buffers");
   QkvT* Ks = reinterpret_cast<QkvT*>(Ts);
-  QkvT* Vs = reinterpret_cast<QkvT*>(As);
   TransposedTile<QkvT, D> ktile, vtile;
   Raw8<QkvT> kf[4][NKS], qf[NKS];
   if constexpr (STAGE) {
     constexpr int VPR = D / 8, NV = kChunk * VPR / 256;
-    u32x4 kr[NV], vr[NV];
+    u32x4 kr[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
       kr[j] = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
-      vr[j] = *reinterpret_cast<const u32x4*>(vp + rr * v_stride + 8 * c);
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int v = tid + 256 * j, r = v / VPR, c = v % VPR;
       *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = kr[j];
-      *reinterpret_cast<u32x4*>(Vs + r * RS + 8 * c) = vr[j];
     }
   } else {
     ktile.load(kp, qk_stride, n);
@@ -527,13 +564,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     dc_g[lane] = expf((float)(Glast - G));
   }
   __syncthreads();
-  if constexpr (STAGE) {
-    ktile.load(Ks, RS, n);
-    vtile.load(Vs, RS, n);
+  if constexpr (!STAGE) {
+    ktile.store(KTh, KTl, kn, n);
+    vtile.store(VTh, VTl, nullptr, n);
   }
-  ktile.store(KTh, KTl, kn, n);
-  vtile.store(VTh, VTl, nullptr, n);
-  if constexpr (STAGE) __syncthreads();  // V rows are read before A overwrites them
 
   // (K_J K_w^T) and (K_J Q_w^T): lane holds row i = 16w + li, columns j = 16J + 4lg + r
   {
@@ -599,9 +633,38 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
     }
   }
   __syncthreads();
-  // the scaled K^T tile for the scan, without the LDS row padding
+  if constexpr (STAGE) {
+    // the scaled K^T tile for the scan (f16, rows past the end zero), read
+    // column-wise from the staged rows
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
+    for (int j = 0; j < D / 32; ++j) {
+      const int v = tid + 256 * j, r = v >> 3, c8 = v & 7;
+      h8 o;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] = (_Float16)(Elem<QkvT>::load(Ks + (8 * c8 + t) * RS + r) * kn[8 * c8 + t]);
+      *reinterpret_cast<h8*>(blk + blk_kt_hi(D) + (r * kChunk + 8 * c8) * 2) = o;
+    }
+    // T form: the scaled K rows for the scan, each group of 32 columns in the
+    // contraction order (position 8b + 4a + c holds column 16a + 4b + c), in
+    // the K^T lo slot (unused with bf16 q/k/v); the same f16 values as K^T
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const int v = tid + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
+      const float sc = kn[r];
+      h8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = 8 * c8 + e, w = pos & 31;
+        const int col = (pos & ~31) + 16 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
+        o[e] = (_Float16)(Elem<QkvT>::load(Ks + r * RS + col) * sc);
+      }
+      *reinterpret_cast<h8*>(blk + blk_kt_lo(D) + (r * D + 8 * c8) * 2) = o;
+    }
+    __syncthreads();  // the staged rows live in Ts, which the inverse overwrites
+  }
+  // f32 inputs: the scaled K^T tile for the scan, without the LDS row padding
+#pragma unroll
+  for (int j = 0; j < (STAGE ? 0 : D / 32); ++j) {
     const int v = tid + 256 * j, r = v >> 3, c8 = v & 7;
     *reinterpret_cast<uint4*>(blk + blk_kt_hi(D) + (r * kChunk + 8 * c8) * 2) =
         *reinterpret_cast<const uint4*>(KTh + r * KTS + 8 * c8);
@@ -612,7 +675,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillParams p, ChunkW
 
   unit_lower_inverse<TS>(As, Ts, Ms);
 
-  w_u_products<SPLIT, SPLIT, TS, D>(Ts, bg, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+  if constexpr (SPLIT)
+    w_u_products<SPLIT, SPLIT, TS, D>(Ts, bg, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+  else
+    store_t_beta<TS>(Ts, bs, reinterpret_cast<_Float16*>(blk + blk_tb_hi()), reinterpret_cast<_Float16*>(blk + blk_tb_lo()));
 }
 
 // ---------------------------------------------------------------------------
@@ -1155,23 +1221,28 @@ template <typename QkvT, typename StT, int D, bool KDA>
 __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
   constexpr bool KT_LO = SPLIT || KDA;  // K^T lo tiles
-  constexpr bool STAGE_W = !KT_LO;      // LDS room for W next to K^T lo tiles is lacking
+  // bf16 q/k/v (GDN): the block holds T diag(beta) rather than W and U^T
+  // (T form); the state waves form Delta = T diag(beta) (V - diag(gamma) K S0^T)
+  constexpr bool TF = !KT_LO;
   using QT = typename std::conditional<KDA, KdaQ<QkvT>, QkvT>::type;  // q rows as the scan reads them
   constexpr int NKS = D / 32;     // 32-wide k steps
   constexpr int NCT = D / 16;     // 16-column tiles of the state
   constexpr int WS = D + 8;       // f16 row stride of W and of the published state
   constexpr int KTV = D / 32;     // 16-byte K^T vectors per output-wave lane (per hi / lo)
-  constexpr int WV = D / 16;      // 16-byte W vectors per output-wave lane (hi and lo)
+  constexpr int TSS = kChunk + 8; // f16 row stride of T diag(beta) in LDS
+  constexpr int KRS = D + 8;      // f16 row stride of the K rows in LDS
+  constexpr int TBV = 4;          // 16-byte T diag(beta) vectors per output-wave lane (hi and lo)
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][D * KTS];  // K^T [column][token]
   __shared__ __attribute__((aligned(16))) _Float16 KTl[2][KT_LO ? D * KTS : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 Wsh[2][STAGE_W ? 2 * kChunk * WS : 8];  // W hi rows, then lo rows
+  __shared__ __attribute__((aligned(16))) _Float16 Tsh[2][TF ? 2 * kChunk * TSS : 8];  // T diag(beta) hi rows, then lo rows
+  __shared__ __attribute__((aligned(16))) _Float16 Krow[2][TF ? kChunk * KRS : 8];     // K rows, contraction order
   __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
   __shared__ __attribute__((aligned(16))) _Float16 DTl[2][SPLIT ? 16 * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 ETh[2][16 * KTS];  // (exp(G_C - G_j) Delta)^T
   __shared__ __attribute__((aligned(16))) _Float16 ETl[2][16 * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
-  __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T rows e0 .. e0+15
+  __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T (T form: V^T) rows e0 .. e0+15
   __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk];        // exp(G_C - G_j), then gamma
   __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
   constexpr int QEV = 16 / (int)sizeof(QT);     // q elements per 16-byte vector
@@ -1218,9 +1289,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 
   // ---- state-wave operands
   float Sf[8 * NKS];
-  h8 Wgh[STAGE_W ? 1 : NKS], Wgl[STAGE_W ? 1 : NKS];  // W fragments when they come straight from memory
+  h8 Wgh[TF ? 1 : NKS], Wgl[TF ? 1 : NKS];  // W fragments (W form), straight from memory
   auto load_wg = [&](int cid) {
-    if constexpr (!STAGE_W) {
+    if constexpr (!TF) {
       const char* b = blk_of(cid);
       const int row = 16 * w4 + li;
 #pragma unroll
@@ -1236,7 +1307,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
   u32x4 KTr[KTV], KTrl[KT_LO ? KTV : 1];
-  u32x4 Wr[STAGE_W ? WV : 1];
+  u32x4 Tr[TF ? TBV : 1], Kr[TF ? KTV : 1];
   const int ot = tid - 256;      // output-wave thread index
   // a wave's q rows move whole 16-byte vectors (contiguous per row) and are
   // read back in the contraction order from its own LDS slice
@@ -1289,38 +1360,62 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       if constexpr (KT_LO) *reinterpret_cast<u32x4*>(KTl[bb] + r * KTS + 8 * c8) = KTrl[j];
     }
   };
-  // W hi then W lo as 2 * 64 rows of D halves; vector v covers row v / (D/8)
+  // T form: T diag(beta) hi then lo as 2 * 64 rows of 64 halves (vector v
+  // covers row v / 8), and the K rows in the contraction order
   auto load_wst = [&](int cid) {
-    if constexpr (STAGE_W) {
-      const char* b = blk_of(cid) + blk_w_hi(D);
+    if constexpr (TF) {
+      const char* b = blk_of(cid) + blk_tb_hi();
 #pragma unroll
-      for (int j = 0; j < WV; ++j) Wr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
+      for (int j = 0; j < TBV; ++j) Tr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
+      const char* kb = blk_of(cid) + blk_kt_lo(D);
+#pragma unroll
+      for (int j = 0; j < KTV; ++j) Kr[j] = *reinterpret_cast<const u32x4*>(kb + (ot + 256 * j) * 16);
     }
   };
   // U^T rows e0 .. e0+15 (one float4 per lane), exp(G_C - G_j) and gamma
   // (and with KDA exp(G_C) per column)
   float4 Ur, Vr, Gr;
+  uint2 Vt;  // T form: four bf16 values of V, token ot / 4, rows e0 + 4 (ot % 4) .. +3
   auto load_uv = [&](int cid) {
     const char* b = blk_of(cid);
-    Ur = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + (ot >> 4)) * kChunk +
-                                          4 * (ot & 15));
+    if constexpr (TF) {
+      const int tk = min(ot >> 2, ntok(cid) - 1);  // rows past the end re-read the last row (beta = 0 there)
+      Vt = *reinterpret_cast<const uint2*>(static_cast<const QkvT*>(p.v) + (tok0(cid) + tk) * (int64_t)p.Hv * D +
+                                           (int64_t)h * D + e0 + 4 * (ot & 3));
+    } else {
+      Ur = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + (ot >> 4)) * kChunk +
+                                            4 * (ot & 15));
+    }
     const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
     Vr = *reinterpret_cast<const float4*>(v + (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)));
     if constexpr (KDA)
       Gr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_kda_gam<QT>(D)) + 4 * (ot % (D / 4)));
   };
   auto stage_uv = [&](int bb) {
-    *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
+    if constexpr (TF) {
+      const int tk = ot >> 2, e = 4 * (ot & 3);
+      Us[bb][e * 68 + tk] = __uint_as_float(Vt.x << 16);
+      Us[bb][(e + 1) * 68 + tk] = __uint_as_float(Vt.x & 0xffff0000u);
+      Us[bb][(e + 2) * 68 + tk] = __uint_as_float(Vt.y << 16);
+      Us[bb][(e + 3) * 68 + tk] = __uint_as_float(Vt.y & 0xffff0000u);
+    } else {
+      *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
+    }
     if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
     if constexpr (KDA)
       if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
   };
   auto stage_w = [&](int bb) {
-    if constexpr (STAGE_W) {
+    if constexpr (TF) {
 #pragma unroll
-      for (int j = 0; j < WV; ++j) {
+      for (int j = 0; j < TBV; ++j) {
+        const int v = ot + 256 * j, r = v >> 3, c8 = v & 7;
+        *reinterpret_cast<u32x4*>(Tsh[bb] + r * TSS + 8 * c8) = Tr[j];
+      }
+#pragma unroll
+      for (int j = 0; j < KTV; ++j) {
         const int v = ot + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
-        *reinterpret_cast<u32x4*>(Wsh[bb] + r * WS + 8 * c8) = Wr[j];
+        *reinterpret_cast<u32x4*>(Krow[bb] + r * KRS + 8 * c8) = Kr[j];
       }
     }
   };
@@ -1369,34 +1464,76 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
           *reinterpret_cast<h8*>(SSh[b] + li * WS + 32 * s + 8 * lg) = Sh[s];
           if constexpr (SPLIT) *reinterpret_cast<h8*>(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
         }
-      // Delta rows of this wave's 16 tokens: U - W S0^T, three independent chains
-      f32x4 ahh = {0.0f, 0.0f, 0.0f, 0.0f}, ahl = ahh, alh = ahh;
+      // Delta rows of this wave's 16 tokens
+      float dl[4];
+      if constexpr (TF) {
+        // Y_J = V_J - diag(gamma) K_J S0^T for the token blocks J <= w4 (zero
+        // beyond), then Delta = T diag(beta) Y over the lower-triangular row
+        // block; the accumulator rows of Y_J, Y_J+1 are exactly this lane's
+        // B operand in the contraction order of T diag(beta)'s columns
+        f32x4 dhh = {0.0f, 0.0f, 0.0f, 0.0f}, dhl = dhh, dlh = dhh;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        h8 wh, wl;
-        if constexpr (STAGE_W) {
-          wh = ld_h8(Wsh[b] + (16 * w4 + li) * WS + 32 * s + 8 * lg);
-          wl = ld_h8(Wsh[b] + (kChunk + 16 * w4 + li) * WS + 32 * s + 8 * lg);
-        } else {
-          wh = Wgh[s];
-          wl = Wgl[s];
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (2 * s2 > w4) break;
+          float yy[8];
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int J = 2 * s2 + a;
+            if (J > w4) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) yy[4 * a + r] = 0.0f;
+              continue;
+            }
+            f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+              const h8 kf = ld_h8(Krow[b] + (16 * J + li) * KRS + 32 * s + 8 * lg);
+              xh = mfma_f16(kf, Sh[s], xh);
+              xl = mfma_f16(kf, Sl[s], xl);
+            }
+            const float4 vt = *reinterpret_cast<const float4*>(Us[b] + li * 68 + 16 * J + 4 * lg);
+            const float4 gm = *reinterpret_cast<const float4*>(Vs[b] + kChunk + 16 * J + 4 * lg);
+            yy[4 * a + 0] = vt.x - gm.x * (xh[0] + xl[0]);
+            yy[4 * a + 1] = vt.y - gm.y * (xh[1] + xl[1]);
+            yy[4 * a + 2] = vt.z - gm.z * (xh[2] + xl[2]);
+            yy[4 * a + 3] = vt.w - gm.w * (xh[3] + xl[3]);
+          }
+          h8 yh, yl;
+          split8(yy, yh, yl);
+          const h8 th = ld_h8(Tsh[b] + (16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
+          const h8 tl = ld_h8(Tsh[b] + (kChunk + 16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
+          dhh = mfma_f16(th, yh, dhh);
+          dhl = mfma_f16(th, yl, dhl);
+          dlh = mfma_f16(tl, yh, dlh);
         }
-        ahh = mfma_f16(wh, Sh[s], ahh);
-        ahl = mfma_f16(wh, Sl[s], ahl);
-        alh = mfma_f16(wl, Sh[s], alh);
+        const f32x4 dd = dhh + (dhl + dlh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dl[r] = dd[r];
+      } else {
+        // U - W S0^T, three independent chains
+        f32x4 ahh = {0.0f, 0.0f, 0.0f, 0.0f}, ahl = ahh, alh = ahh;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          ahh = mfma_f16(Wgh[s], Sh[s], ahh);
+          ahl = mfma_f16(Wgh[s], Sl[s], ahl);
+          alh = mfma_f16(Wgl[s], Sh[s], alh);
+        }
+        const f32x4 acc = ahh + (ahl + alh);
+        const float4 utv = *reinterpret_cast<const float4*>(Us[b] + li * 68 + 16 * w4 + 4 * lg);
+        const float us[4] = {utv.x, utv.y, utv.z, utv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dl[r] = us[r] - acc[r];
       }
-      const f32x4 acc = ahh + (ahl + alh);
-      const float4 utv = *reinterpret_cast<const float4*>(Us[b] + li * 68 + 16 * w4 + 4 * lg);
       const float4 dcv = *reinterpret_cast<const float4*>(Vs[b] + 16 * w4 + 4 * lg);
       const float gc = Vs[b][kChunk + kChunk - 1];
-      const float us[4] = {utv.x, utv.y, utv.z, utv.w}, dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
+      const float dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
       load_wg(cn);
       {
         // Delta^T and E^T (f16 hi/lo), 4 consecutive tokens per lane
         uint32_t w[4][2];
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
-          const float d0 = us[2 * r2] - acc[2 * r2], d1 = us[2 * r2 + 1] - acc[2 * r2 + 1];
+          const float d0 = dl[2 * r2], d1 = dl[2 * r2 + 1];
           const float x0 = d0 * dcs[2 * r2], x1 = d1 * dcs[2 * r2 + 1];
           const _Float16 a0 = (_Float16)d0, a1 = (_Float16)d1;
           const _Float16 b0 = (_Float16)(d0 - (float)a0), b1 = (_Float16)(d1 - (float)a1);
@@ -1443,7 +1580,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int r = 0; r < 4; ++r) sc[r] = a2[r];
       }
     } else {
-      // next chunk's W into the other buffer, then start loading the one after
+      // next chunk's W (T form: T diag(beta), V^T and the K rows) into the
+      // other buffer, then start loading the one after
       stage_w(b ^ 1);
       stage_uv(b ^ 1);
       load_wst(min(cid + 2, c_end - 1));
