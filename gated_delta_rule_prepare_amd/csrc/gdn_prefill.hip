@@ -594,13 +594,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
         for (int J2 = 0; J2 < 4; ++J2)
           if (J2 == wave) kf[J2][s].get(bk);
         qf[s].get(bq);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[e] *= sj;
-          bk[e] *= ksc;
-          bq[e] *= qsc;
-        }
         if constexpr (SPLIT) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            a[e] *= sj;
+            bk[e] *= ksc;
+            bq[e] *= qsc;
+          }
           h8 ah, al, kh8, kl8, qh8, ql8;
           split8(a, ah, al);
           split8(bk, kh8, kl8);
@@ -612,9 +612,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
           aqk = mfma_f16(ah, ql8, aqk);
           aqk = mfma_f16(al, qh8, aqk);
         } else {
+          // bf16 rows are exact in f16; the row scales go on the f32 products
           const h8 ah = to_h8(a);
           akk = mfma_f16(ah, to_h8(bk), akk);
           aqk = mfma_f16(ah, to_h8(bq), aqk);
+        }
+      }
+      if constexpr (!SPLIT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sk = kn[16 * J + 4 * lg + r];
+          akk[r] *= ksc * sk;
+          aqk[r] *= qsc * sk;
         }
       }
       float av[4], pv[4];
@@ -634,29 +643,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   }
   __syncthreads();
   if constexpr (STAGE) {
-    // the scaled K^T tile for the scan (f16, rows past the end zero), read
-    // column-wise from the staged rows
+    // the K^T tile for the scan, read column-wise from the staged rows: f16
+    // holds bf16 rows exactly, so the rows stay unscaled (the scan applies the
+    // k scale, which is zero past the end, to E and to K S0^T)
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int v = tid + 256 * j, r = v >> 3, c8 = v & 7;
       h8 o;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] = (_Float16)(Elem<QkvT>::load(Ks + (8 * c8 + t) * RS + r) * kn[8 * c8 + t]);
+      for (int t = 0; t < 8; ++t) o[t] = (_Float16)Elem<QkvT>::load(Ks + (8 * c8 + t) * RS + r);
       *reinterpret_cast<h8*>(blk + blk_kt_hi(D) + (r * kChunk + 8 * c8) * 2) = o;
     }
-    // T form: the scaled K rows for the scan, each group of 32 columns in the
+    // T form: the K rows for the scan, each group of 32 columns in the
     // contraction order (position 8b + 4a + c holds column 16a + 4b + c), in
     // the K^T lo slot (unused with bf16 q/k/v); the same f16 values as K^T
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int v = tid + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
-      const float sc = kn[r];
       h8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int pos = 8 * c8 + e, w = pos & 31;
         const int col = (pos & ~31) + 16 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
-        o[e] = (_Float16)(Elem<QkvT>::load(Ks + r * RS + col) * sc);
+        o[e] = (_Float16)Elem<QkvT>::load(Ks + r * RS + col);
       }
       *reinterpret_cast<h8*>(blk + blk_kt_lo(D) + (r * D + 8 * c8) * 2) = o;
     }
@@ -1243,7 +1252,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
   __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T (T form: V^T) rows e0 .. e0+15
-  __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk];        // exp(G_C - G_j), then gamma
+  // exp(G_C - G_j), then gamma (T form: both times the k row scale), then gamma_C
+  __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk + 4];
   __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
   constexpr int QEV = 16 / (int)sizeof(QT);     // q elements per 16-byte vector
   constexpr int QVPR = D / QEV;                  // vectors per q row
@@ -1374,7 +1384,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   };
   // U^T rows e0 .. e0+15 (one float4 per lane), exp(G_C - G_j) and gamma
   // (and with KDA exp(G_C) per column)
-  float4 Ur, Vr, Gr;
+  float4 Ur, Vr, Gr, Kv;
   uint2 Vt;  // T form: four bf16 values of V, token ot / 4, rows e0 + 4 (ot % 4) .. +3
   auto load_uv = [&](int cid) {
     const char* b = blk_of(cid);
@@ -1388,6 +1398,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     }
     const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
     Vr = *reinterpret_cast<const float4*>(v + (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)));
+    if constexpr (TF) Kv = *reinterpret_cast<const float4*>(v + 2 * kChunk + 4 * (ot & 15));
     if constexpr (KDA)
       Gr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_kda_gam<QT>(D)) + 4 * (ot % (D / 4)));
   };
@@ -1401,7 +1412,16 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     } else {
       *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
     }
-    if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
+    if constexpr (TF) {
+      // K^T and the K rows are unscaled in the T form: the k row scale goes
+      // on E (with exp(G_C - G_j)) and on K S0^T (with gamma)
+      if (ot < 32)
+        *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = make_float4(Vr.x * Kv.x, Vr.y * Kv.y, Vr.z * Kv.z, Vr.w * Kv.w);
+      if (ot == 31) Vs[bb][2 * kChunk] = Vr.w;  // gamma_C
+    } else {
+      if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
+      if (ot == 31) Vs[bb][2 * kChunk] = Vr.w;
+    }
     if constexpr (KDA)
       if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
   };
@@ -1525,7 +1545,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int r = 0; r < 4; ++r) dl[r] = us[r] - acc[r];
       }
       const float4 dcv = *reinterpret_cast<const float4*>(Vs[b] + 16 * w4 + 4 * lg);
-      const float gc = Vs[b][kChunk + kChunk - 1];
+      const float gc = Vs[b][2 * kChunk];
       const float dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
       load_wg(cn);
       {

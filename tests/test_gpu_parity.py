@@ -283,6 +283,8 @@ PF_CASES += [
                             act_dtype="bf16", qkv_dtype="bf16", state_dtype="bf16", init_state_std=0.1, seed=35)),
     ("d32_r2", Config("pf_d32b", "prefill", Dims(2, 4, 32, 32, 4), seqlens=(200, 1, 64), num_slots=3,
                       act_dtype="bf16", qkv_dtype="f32", init_state_std=0.1, conv_state_std=1.0, seed=37)),
+    ("d32_r2_bf16", Config("pf_d32c", "prefill", Dims(2, 4, 32, 32, 4), seqlens=(200, 1, 64), num_slots=3,
+                           act_dtype="bf16", qkv_dtype="bf16", init_state_std=0.1, conv_state_std=1.0, seed=41)),
     ("d64_r3_f16", Config("pf_d64b", "prefill", Dims(1, 3, 64, 64, 2), seqlens=(129, 300), num_slots=4,
                           act_dtype="bf16", qkv_dtype="bf16", state_dtype="f16", init_state_std=0.1, seed=38)),
     # more sequences than the chunk-table wave has lanes: each lane takes two
@@ -313,19 +315,20 @@ def test_prefill_parity(name, cfg):
     assert_close(sp, s_ref, cfg.state_dtype, f"{name} state")
 
 
-def test_prefill_l2norm_inside():
-    cfg = Config("pf_l2", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(20, 90), num_slots=2, act_dtype="bf16",
-                 qkv_dtype="f32", init_state_std=0.05, seed=36)
+@pytest.mark.parametrize("qkv,D", [("f32", 128), ("bf16", 128), ("bf16", 32)])
+def test_prefill_l2norm_inside(qkv, D):
+    cfg = Config("pf_l2", "prefill", Dims(2, 4, D, D, 4), seqlens=(20, 90), num_slots=2, act_dtype="bf16",
+                 qkv_dtype=qkv, init_state_std=0.05, seed=36)
     R = _runner()
     d = cfg.dims
     inp = make_inputs(cfg)
     pre = _oracle_prepared(cfg, inp, l2norm=False)
-    _say("[prefill] l2norm inside")
+    _say(f"[prefill] l2norm inside, {qkv} q/k/v, D={D}")
     out, sp = R.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
-                        inp["slots"], inp["has_init"], "f32", "f32", cfg.scale, l2norm=True)
+                        inp["slots"], inp["has_init"], qkv, "f32", cfg.scale, l2norm=True)
     o_ref, s_ref = oracle.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
-                                  inp["slots"], inp["has_init"], cfg.scale, True, "f32", "f32")
-    assert_close(out, o_ref, "f32", "out")
+                                  inp["slots"], inp["has_init"], cfg.scale, True, "f32", qkv)
+    assert_close(out, o_ref, qkv, "out")
     assert_close(sp, s_ref, "f32", "state")
 
 
