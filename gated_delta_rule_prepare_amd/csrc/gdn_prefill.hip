@@ -1252,8 +1252,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
   __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T (T form: V^T) rows e0 .. e0+15
-  // exp(G_C - G_j), then gamma (T form: both times the k row scale), then gamma_C
-  __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk + 4];
+  // exp(G_C - G_j), then gamma (T form: both times the k row scale, then gamma_C)
+  __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk + (TF ? 4 : 0)];
   __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
   constexpr int QEV = 16 / (int)sizeof(QT);     // q elements per 16-byte vector
   constexpr int QVPR = D / QEV;                  // vectors per q row
@@ -1420,7 +1420,6 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       if (ot == 31) Vs[bb][2 * kChunk] = Vr.w;  // gamma_C
     } else {
       if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
-      if (ot == 31) Vs[bb][2 * kChunk] = Vr.w;
     }
     if constexpr (KDA)
       if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
@@ -1545,7 +1544,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int r = 0; r < 4; ++r) dl[r] = us[r] - acc[r];
       }
       const float4 dcv = *reinterpret_cast<const float4*>(Vs[b] + 16 * w4 + 4 * lg);
-      const float gc = Vs[b][2 * kChunk];
+      const float gc = Vs[b][TF ? 2 * kChunk : 2 * kChunk - 1];
       const float dcs[4] = {dcv.x, dcv.y, dcv.z, dcv.w};
       load_wg(cn);
       {
