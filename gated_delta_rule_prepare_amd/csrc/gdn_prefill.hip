@@ -411,8 +411,9 @@ __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _
   }
 }
 
-// Three workgroups per CU (measured 64 -> 56 us at 4096 tokens against two;
-// four would spill heavily).
+// With bf16 q/k/v the kernel needs 40 KB of LDS and under 128 VGPRs (the
+// other blocks' K rows are read from LDS where they are used), so four
+// workgroups share a CU.
 template <typename QkvT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
@@ -500,13 +501,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   const float braw = p.beta[(t0 + gt) * p.Hv + h];
   if constexpr (STAGE) {
     __syncthreads();
-    // rows past the end hold the last row again (their scale is 0)
+    // this wave's own K rows (rows past the end hold the last row again, their
+    // scale is 0); the other blocks' rows are read from LDS where they are used
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      if (J > wave) break;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) kf[J][s].load(Ks + (16 * J + li) * RS + 32 * s + 8 * lg);
-    }
+    for (int s = 0; s < NKS; ++s) kf[0][s].load(Ks + (16 * wave + li) * RS + 32 * s + 8 * lg);
   }
 
   // row scales of this wave's block: 1/sqrt(|row|^2 + 1e-6) with the L2 norm, else 1; zero past the end
@@ -521,10 +519,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 #pragma unroll
       for (int i = 0; i < 8; ++i) sq += xq[i] * xq[i];
     }
-    // K rows of this block are kf[wave]
+    // K rows of this block are kf[wave] (kf[0] with staged rows)
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-      if (J != wave) continue;
+      if (J != (STAGE ? 0 : wave)) continue;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         float xk[8];
@@ -589,10 +587,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         float a[8], bk[8], bq[8];
-        kf[J][s].get(a);
+        if constexpr (STAGE) {
+          Raw8<QkvT> kj;
+          kj.load(Ks + (16 * J + li) * RS + 32 * s + 8 * lg);
+          kj.get(a);
+          kf[0][s].get(bk);
+        } else {
+          kf[J][s].get(a);
 #pragma unroll
-        for (int J2 = 0; J2 < 4; ++J2)
-          if (J2 == wave) kf[J2][s].get(bk);
+          for (int J2 = 0; J2 < 4; ++J2)
+            if (J2 == wave) kf[J2][s].get(bk);
+        }
         qf[s].get(bq);
         if constexpr (SPLIT) {
 #pragma unroll
