@@ -545,7 +545,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer shards "
-              "without communication by batch or by key-head group; see DESIGN.md)", file=sys.stderr)
+              "without communication by batch or by key-head group, and one long sequence needs one exchange of "
+              "per-segment state transitions)", file=sys.stderr)
         sys.exit(2)
     import torch
 
