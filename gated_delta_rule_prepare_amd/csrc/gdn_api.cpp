@@ -211,7 +211,7 @@ gdn_status gdn_prepare(const gdn_dims* dims, int32_t num_seqs, int64_t total_tok
   p.b = b_raw; p.b_stride = b_row_stride; p.w = conv_weight; p.A_log = A_log; p.dt_bias = dt_bias;
   p.conv_pool = conv_state_pool; p.W = conv_row_len(dims); p.num_slots = num_slots; p.slots = slot_idx_dev;
   p.has_init = has_initial_state_dev; p.l2norm = apply_qk_l2norm; p.q = q_out; p.k = k_out; p.v = v_out;
-  p.g = g_out; p.beta = beta_out; p.act = act_dtype; p.qkv = qkv_dtype;
+  p.g = g_out; p.beta = beta_out; p.act = act_dtype; p.qkv = qkv_dtype; p.cu_host = cu_seqlens_host;
   return launched(fn, gdn::launch_prepare(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -38,6 +38,7 @@ struct PrepareParams {
   float* g;               // [T, Hv]
   float* beta;            // [T, Hv]
   gdn_dtype act, qkv;
+  const int32_t* cu_host;  // host [N+1]: read by the launcher only
 };
 
 struct DecodeParams {

@@ -12,11 +12,16 @@
 // Conv semantics: vllm.cpp cpu_ops.cpp, CausalConv1dFwdKernel; split and
 // norm: GdnPostConvKernel, L2NormKernel.
 //
-// Kernel 2 (finish): the per-(token, value head) gates g and beta
-// (vllm.cpp cpu_ops.cpp, GdnGBetaKernel) and the write-back of each
-// sequence's last K-1 raw inputs into its conv history row.  It runs after
-// kernel 1 on the same stream, so every read of an old history row happens
-// before that row is overwritten.
+// The workgroups of a strip also form the per-(token, value head) gates g and
+// beta of its tokens (vllm.cpp cpu_ops.cpp, GdnGBetaKernel), after their
+// stream.
+//
+// The new conv history row of a sequence (its last K-1 raw inputs) is
+// written by the workgroup whose strip holds the sequence's first token,
+// after that workgroup has read the old row, when the first K-1 tokens of
+// every sequence lie in the strip of its first token (the host checks the
+// offsets): then no other workgroup reads that old row.  Otherwise kernel 2
+// (finish) writes every history row after kernel 1 on the same stream.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -57,15 +62,34 @@ __device__ __forceinline__ void store_stream(void* p, const uint4& u) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
 }
 
-template <typename ActT, typename QkvT, int K>
+// g and beta of one (token, value head) item i = t * Hv + h
+template <typename ActT>
+__device__ __forceinline__ void gate_item(const PrepareParams& p, int64_t i) {
+  const int64_t t = i / p.Hv;
+  const int h = (int)(i % p.Hv);
+  const float a = Elem<ActT>::load(static_cast<const ActT*>(p.a) + t * p.a_stride + h);
+  const float b = Elem<ActT>::load(static_cast<const ActT*>(p.b) + t * p.b_stride + h);
+  p.g[i] = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
+  p.beta[i] = sigmoid_f(b);
+}
+
+template <typename ActT, typename QkvT, int K, bool HIST>
 __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PrepareParams p) {
+  // the gates of this strip's tokens, spread over the strip's workgroups
+  // (one item per thread at the usual shapes)
+  const int64_t g_end = min(p.T, (int64_t)(blockIdx.y + 1) * kStrip) * p.Hv;
+  const int64_t g_first = (int64_t)blockIdx.y * kStrip * p.Hv + (int64_t)blockIdx.x * (kConvWaves * 64) + threadIdx.x;
+  const int64_t g_step = (int64_t)gridDim.x * (kConvWaves * 64);
   constexpr int V = Elem<ActT>::kVec;
   constexpr int H = K > 1 ? K - 1 : 1;  // history length (storage for K = 1 unused)
   constexpr int OW = (int)sizeof(QkvT) * V / 16;  // 16-byte words per lane of output
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c0 = (blockIdx.x * kConvWaves + wave) * 64 * V;
-  if (c0 >= p.Cc) return;  // wave-uniform; the kernel uses no block barrier
+  if (c0 >= p.Cc) {  // wave-uniform; the kernel uses no block barrier
+    for (int64_t i = g_first; i < g_end; i += g_step) gate_item<ActT>(p, i);
+    return;
+  }
   const int c = c0 + lane * V;
   const bool active = c < p.Cc;  // Cc is a multiple of 16, so lanes are all-in or all-out
   const int cl = active ? c : 0;  // in-bounds column for lanes past the end
@@ -109,6 +133,7 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   // win[j][i]: raw input j+1 tokens back
   float win[H][V];
   int s = find_sequence(p.cu, p.N, t0);
+  const int s_first = s;
   int64_t seq_start = p.cu[s];
   int64_t seq_end = p.cu[s + 1];
 
@@ -275,23 +300,45 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
     load_block(bufA, tb + 2 * kAhead);
     process(bufB, tb + kAhead);
   }
+  for (int64_t i = g_first; i < g_end; i += g_step) gate_item<ActT>(p, i);
+
+  if constexpr (HIST && K > 1) {
+    // new history rows of the sequences that start in this strip, after this
+    // lane's reads of their old rows (above, in program order): column j
+    // holds the input K-1-j tokens before the sequence end, or for a
+    // sequence shorter than K-1 an entry of the old row (zero without one)
+    if (!active) return;
+    ActT* __restrict__ hw = static_cast<ActT*>(p.conv_pool);
+    for (int sq = (p.cu[s_first] == t0 ? s_first : s_first + 1); sq < p.N && p.cu[sq] < t1; ++sq) {
+      const int64_t start = p.cu[sq];
+      const int64_t len = p.cu[sq + 1] - start;
+      const int slot = p.slots ? p.slots[sq] : sq;
+      const bool has = p.has_init == nullptr || p.has_init[sq] != 0;
+      ActT* row = hw + ((int64_t)slot * p.Cc + c) * p.W;
+      float nv[K - 1][V];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        const int64_t tp = len - (K - 1) + j;  // position of the input column j holds
+        if (tp >= 0) {
+          load_vec<ActT>(x + (start + tp) * p.x_stride + c, nv[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            nv[j][i] = has ? Elem<ActT>::load(row + (int64_t)i * p.W + (K - 1) + tp) : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) Elem<ActT>::store(row + (int64_t)i * p.W + j, nv[j][i]);
+    }
+  }
 }
 
 template <typename ActT, int K>
-__global__ __launch_bounds__(256) void prepare_finish_kernel(PrepareParams p, int gate_blocks) {
-  if ((int)blockIdx.x < gate_blocks) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= p.T * p.Hv) return;
-    const int64_t t = i / p.Hv;
-    const int h = (int)(i % p.Hv);
-    const float a = Elem<ActT>::load(static_cast<const ActT*>(p.a) + t * p.a_stride + h);
-    const float b = Elem<ActT>::load(static_cast<const ActT*>(p.b) + t * p.b_stride + h);
-    p.g[i] = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
-    p.beta[i] = sigmoid_f(b);
-    return;
-  }
+__global__ __launch_bounds__(256) void prepare_finish_kernel(PrepareParams p) {
   if constexpr (K > 1) {
-    const int64_t i = (int64_t)(blockIdx.x - gate_blocks) * 256 + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)p.N * p.Cc) return;
     const int s = (int)(i / p.Cc);
     const int c = (int)(i % p.Cc);
@@ -314,15 +361,30 @@ __global__ __launch_bounds__(256) void prepare_finish_kernel(PrepareParams p, in
   }
 }
 
+// True when the first K-1 tokens of every sequence lie in the strip of its
+// first token, so that the strip's workgroups are the only readers of the
+// sequence's old history row.
+bool history_in_conv(const PrepareParams& p) {
+  if (p.K <= 1 || p.cu_host == nullptr) return false;
+  for (int s = 0; s < p.N; ++s)
+    if (p.cu_host[s] % kStrip > kStrip - (p.K - 1)) return false;
+  return true;
+}
+
 template <typename ActT, typename QkvT, int K>
 hipError_t launch_typed(const PrepareParams& p, hipStream_t stream) {
   constexpr int V = Elem<ActT>::kVec;
   const int chans_per_block = kConvWaves * 64 * V;
   dim3 grid((p.Cc + chans_per_block - 1) / chans_per_block, (unsigned)((p.T + kStrip - 1) / kStrip));
-  prepare_conv_kernel<ActT, QkvT, K><<<grid, kConvWaves * 64, 0, stream>>>(p);
-  const int gate_blocks = (int)((p.T * p.Hv + 255) / 256);
-  const int hist_blocks = K > 1 ? (int)(((int64_t)p.N * p.Cc + 255) / 256) : 0;
-  prepare_finish_kernel<ActT, K><<<gate_blocks + hist_blocks, 256, 0, stream>>>(p, gate_blocks);
+  if (history_in_conv(p)) {
+    prepare_conv_kernel<ActT, QkvT, K, true><<<grid, kConvWaves * 64, 0, stream>>>(p);
+    return hipGetLastError();
+  }
+  prepare_conv_kernel<ActT, QkvT, K, false><<<grid, kConvWaves * 64, 0, stream>>>(p);
+  if (K > 1) {
+    const int hist_blocks = (int)(((int64_t)p.N * p.Cc + 255) / 256);
+    prepare_finish_kernel<ActT, K><<<hist_blocks, 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -93,6 +93,16 @@ PREP_CASES = [
     ("f32_act_to_bf16", Config("p7", "prefill", Dims(2, 4, 64, 64, 4), seqlens=(33, 1, 2), num_slots=5,
                                act_dtype="f32", qkv_dtype="bf16", conv_state_std=1.0, init_state_std=0.1,
                                seed=17)),
+    # sequences that start in the last K-2 tokens of a 32-token strip: their
+    # first tokens read the old history from two strips, so the history rows
+    # are written by a second kernel
+    ("starts_at_strip_end", Config("p8", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(30, 1, 33, 2, 40),
+                                   num_slots=6, act_dtype="bf16", qkv_dtype="bf16", conv_state_std=1.0,
+                                   init_state_std=0.05, seed=18)),
+    # every sequence's first K-1 tokens in one strip, one of them ending it
+    ("starts_before_strip_end", Config("p9", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(29, 3, 27, 1, 2),
+                                       num_slots=6, act_dtype="bf16", qkv_dtype="bf16", conv_state_std=1.0,
+                                       init_state_std=0.05, seed=19)),
 ]
 
 
