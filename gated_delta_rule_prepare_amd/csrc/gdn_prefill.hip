@@ -27,7 +27,8 @@
 //
 // Kernels (all on the caller's stream):
 //  1. chunk_table_kernel: chunk ids -> (sequence, first token); chunks never
-//     cross sequences and a sequence's last chunk may be short.
+//     cross sequences and a sequence's last chunk may be short.  A single
+//     sequence needs no table (chunk c starts at token 64 c).
 //  2. chunk_prep_kernel, one workgroup per (chunk, value head), no state
 //     dependence: K K^T and Q K^T with operands read straight from memory,
 //     T = (I + A)^-1 (16x16 diagonal blocks by substitution in registers,
@@ -121,6 +122,7 @@ struct ChunkWs {
   int32_t* chunk_seq;      // [NC]
   int32_t* chunk_start;    // [NC] first token (global index)
   char* blocks;            // [NC, Hv] blocks of blk_bytes(D)
+  int single;              // one sequence: chunk c starts at token 64 c, and no table is built
 };
 
 inline int64_t max_chunks(int N, int64_t T) { return T / kChunk + N; }
@@ -136,6 +138,7 @@ ChunkWs carve(void* base, int N, int64_t T) {
   w.chunk_start = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)nc * 4);
   w.blocks = p;
+  w.single = N == 1;
   return w;
 }
 
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 
   const int cid = blockIdx.x, h = blockIdx.y;
   const int kh = h / (p.Hv / p.Hk);
-  const int seq = ws.chunk_seq[cid];
-  const int64_t t0 = ws.chunk_start[cid];
+  const int seq = ws.single ? 0 : ws.chunk_seq[cid];
+  const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D);
@@ -778,8 +781,8 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
 
   const int cid = blockIdx.x, h = blockIdx.y;
   const int kh = h / (p.Hv / p.Hk);
-  const int seq = ws.chunk_seq[cid];
-  const int64_t t0 = ws.chunk_start[cid];
+  const int seq = ws.single ? 0 : ws.chunk_seq[cid];
+  const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_kda_bytes<QT>(D);
@@ -1287,7 +1290,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   StT* Sg = static_cast<StT*>(p.ssm_pool) + (((int64_t)slot * p.Hv + h) * D + e0 + li) * D;
   const QkvT* qbase = static_cast<const QkvT*>(p.q) + (int64_t)kh * D;
   QkvT* obase = static_cast<QkvT*>(p.out) + (int64_t)h * D + e0;
-  const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
+  const int c_begin = ws.single ? 0 : ws.seq_chunk_off[s_idx];
+  const int c_end = ws.single ? (int)((p.T + kChunk - 1) / kChunk) : ws.seq_chunk_off[s_idx + 1];
   constexpr int64_t kBlk = KDA ? blk_kda_bytes<QT>(D) : blk_bytes(D);
   auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * kBlk; };
   if (c_begin == c_end) {
@@ -1801,7 +1805,7 @@ template <typename QkvT, typename StT>
 hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
   if (!chunked_dims(p.Dk, p.Dv)) return launch_seq<QkvT, StT>(p, stream);
   const ChunkWs ws = carve(p.workspace, p.N, p.T);
-  chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
+  if (!ws.single) chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
   switch (p.Dk) {
     case 32: return launch_chunked_d<QkvT, StT, 32>(p, ws, stream);
     case 64: return launch_chunked_d<QkvT, StT, 64>(p, ws, stream);
@@ -1837,7 +1841,7 @@ hipError_t launch_kda_chunked_d(const KdaParams& p, const ChunkWs& ws, hipStream
 template <typename QkvT, typename StT>
 hipError_t launch_kda_typed(const KdaParams& p, hipStream_t stream) {
   const ChunkWs ws = carve(p.workspace, p.N, p.T);
-  chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
+  if (!ws.single) chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
   switch (p.Dk) {
     case 32: return launch_kda_chunked_d<QkvT, StT, 32>(p, ws, stream);
     case 64: return launch_kda_chunked_d<QkvT, StT, 64>(p, ws, stream);
