@@ -145,6 +145,7 @@ struct SsdWs {
   int32_t* chunk_seq;      // [NC]
   int32_t* chunk_start;    // [NC]
   char* blocks;            // [NC, H] blocks
+  int single;              // one sequence: chunk c starts at token 64 c, and no table is built
 };
 
 __host__ __device__ inline size_t ssd_align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -161,6 +162,7 @@ SsdWs ssd_carve(void* base, int Ns, int64_t T) {
   w.chunk_start = reinterpret_cast<int32_t*>(q);
   q += ssd_align256((size_t)nc * 4);
   w.blocks = q;
+  w.single = Ns == 1;
   return w;
 }
 
@@ -282,8 +284,8 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
 
   const int cid = blockIdx.x, h = blockIdx.y;
   const int g = h / (p.H / p.G);
-  const int seq = ws.chunk_seq[cid];
-  const int64_t t0 = ws.chunk_start[cid];
+  const int seq = ws.single ? 0 : ws.chunk_seq[cid];
+  const int64_t t0 = ws.single ? (int64_t)kSsdChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   char* blk = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
@@ -361,7 +363,8 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
   StT* Sg = static_cast<StT*>(p.ssm_pool) + ((int64_t)slot * p.H + h) * PN + e0;
   float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (has) load_n<StT, 4>(Sg, S);
-  const int c_begin = ws.seq_chunk_off[s_idx], c_end = ws.seq_chunk_off[s_idx + 1];
+  const int c_begin = ws.single ? 0 : ws.seq_chunk_off[s_idx];
+  const int c_end = ws.single ? (int)((p.T + kSsdChunk - 1) / kSsdChunk) : ws.seq_chunk_off[s_idx + 1];
   const int64_t bb = ssd_blk_bytes(p.P, p.N), vo = ssd_blk_vec(p.P, p.N);
   for (int c = c_begin; c < c_end; c += kPassAhead) {
     float4 v[kPassAhead];
@@ -437,8 +440,8 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
 
   const int cid = blockIdx.x, h = blockIdx.y;
   const int g = h / (p.H / p.G);
-  const int seq = ws.chunk_seq[cid];
-  const int64_t t0 = ws.chunk_start[cid];
+  const int seq = ws.single ? 0 : ws.chunk_seq[cid];
+  const int64_t t0 = ws.single ? (int64_t)kSsdChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   const float* S0 = reinterpret_cast<const float*>(ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N));
@@ -656,7 +659,7 @@ hipError_t launch_chunked_p(const Mamba2Params& p, const SsdWs& ws, hipStream_t 
 template <typename ActT>
 hipError_t launch_chunked(const Mamba2Params& p, hipStream_t stream) {
   const SsdWs ws = ssd_carve(p.workspace, p.Nseq, p.T);
-  ssd_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.Nseq, ws);
+  if (!ws.single) ssd_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.Nseq, ws);
   switch (p.P) {
     case 32: return launch_chunked_p<ActT, 32>(p, ws, stream);
     case 64: return launch_chunked_p<ActT, 64>(p, ws, stream);
