@@ -449,7 +449,7 @@ def kda(torch, gdn, reps=20):
             rl = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": fl / sec / 1e12 / F16_MFMA_PEAK_TFLOPS, "flops_per_launch": fl, "bytes_per_launch": nb,
                   "hbm_frac": nb / sec / 1e9 / HBM_PEAK_GBS,
-                  "kernels": "chunk_table_kernel + kda_prep_kernel + chunk_scan_kernel (KDA)"}
+                  "kernels": "kda_prep_kernel + chunk_scan_kernel (KDA; one sequence: no chunk_table_kernel)"}
         else:
             nb = kda_decode_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv)
             rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -531,7 +531,7 @@ def mamba2(torch, gdn, reps=20):
                   "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb,
                   "workspace_bytes_per_launch": ws_b, "flops_per_launch": fl,
                   "mfma_frac": fl / sec / 1e12 / F16_MFMA_PEAK_TFLOPS,
-                  "kernels": "ssd_table_kernel + ssd_state_kernel + ssd_pass_kernel + ssd_out_kernel"}
+                  "kernels": "ssd_state_kernel + ssd_pass_kernel + ssd_out_kernel (one sequence: no ssd_table_kernel)"}
         else:
             nb = mamba2_decode_bytes(T, H, P, G, N)
             rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -685,7 +685,7 @@ def main():
                                  "bytes_per_launch": prep_b}},
         "prefill": {"avg_ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3), **stats_us(pre_l),
                     "mfma_counters": mfma,
-                    "kernels": "chunk_table_kernel + chunk_prep_kernel + chunk_scan_kernel",
+                    "kernels": "chunk_prep_kernel + chunk_scan_kernel (one sequence: no chunk_table_kernel)",
                     "roofline": {"bound": "mfma", "achieved": pre_flops / (pre_ms * 1e-3) / 1e12,
                                  "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": pre_flops / (pre_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
