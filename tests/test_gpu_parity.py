@@ -295,6 +295,13 @@ PF_CASES += [
                       act_dtype="bf16", qkv_dtype="f32", init_state_std=0.1, conv_state_std=1.0, seed=37)),
     ("d32_r2_bf16", Config("pf_d32c", "prefill", Dims(2, 4, 32, 32, 4), seqlens=(200, 1, 64), num_slots=3,
                            act_dtype="bf16", qkv_dtype="bf16", init_state_std=0.1, conv_state_std=1.0, seed=41)),
+    # one sequence (no chunk table) continuing from a nonzero state, both block forms
+    ("single_seq_init_bf16", Config("pf_1b", "prefill", Dims(2, 4, 128, 128, 4), seqlens=(150,), num_slots=2,
+                                    act_dtype="bf16", qkv_dtype="bf16", init_state_std=0.05, conv_state_std=1.0,
+                                    seed=42)),
+    ("single_seq_init_f32", Config("pf_1f", "prefill", Dims(2, 4, 64, 64, 4), seqlens=(97,), num_slots=2,
+                                   act_dtype="bf16", qkv_dtype="f32", init_state_std=0.05, conv_state_std=1.0,
+                                   seed=43)),
     ("d64_r3_f16", Config("pf_d64b", "prefill", Dims(1, 3, 64, 64, 2), seqlens=(129, 300), num_slots=4,
                           act_dtype="bf16", qkv_dtype="bf16", state_dtype="f16", init_state_std=0.1, seed=38)),
     # more sequences than the chunk-table wave has lanes: each lane takes two
