@@ -137,7 +137,16 @@ __global__ __launch_bounds__(64 * kKdaWaves) void kda_recurrent_kernel(KdaParams
   // the final state (an empty sequence writes back its initial state)
 #pragma unroll
   for (int j = 0; j < NS; ++j)
-    if (rows[j] < Dv) store_n<StT, 4>(Sg + (int64_t)rows[j] * DK + col, st[j]);
+    if (rows[j] < Dv) {
+      // f32 rows are written once and not read again here: nontemporal stores
+      if constexpr (std::is_same<StT, float>::value) {
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        const v4f x = {st[j][0], st[j][1], st[j][2], st[j][3]};
+        __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(Sg + (int64_t)rows[j] * DK + col));
+      } else {
+        store_n<StT, 4>(Sg + (int64_t)rows[j] * DK + col, st[j]);
+      }
+    }
 }
 
 template <typename QkvT, typename StT>
