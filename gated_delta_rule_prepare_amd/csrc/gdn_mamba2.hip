@@ -411,15 +411,18 @@ struct SsdOutLds {
   static constexpr int kYBytes = kSsdChunk * YS * 4;    // Y, over everything above at the end
   static constexpr int kU0 = 2 * kC > kC + kMBytes ? 2 * kC : kC + kMBytes;
   static constexpr int kUnion = kU0 > kYBytes ? kU0 : kYBytes;
-  static constexpr int kX = kUnion;                     // X^T (hi, lo)
-  static constexpr int kL = kX + kXHalves * kParts * 2; // double L[64]
+  // X^T (hi, lo), written once C S0^T is formed: over C where it fits, else
+  // after the union
+  static constexpr bool kXOverC = kXHalves * kParts * 2 <= kC;
+  static constexpr int kX = kXOverC ? 0 : kUnion;
+  static constexpr int kL = kXOverC ? kUnion : kUnion + kXHalves * kParts * 2;  // double L[64]
   static constexpr int kDt = kL + kSsdChunk * 8;
   static constexpr int kE = kDt + kSsdChunk * 4;
   static constexpr int kBytes = kE + kSsdChunk * 4;
 };
 
 template <typename ActT, int P, int N>
-__global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
   using Lay = SsdOutLds<P, N, SPLIT>;
   constexpr int RS = Lay::RS, MS = Lay::MS, YS = Lay::YS;
@@ -465,7 +468,21 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
 
   stage_rows<ActT, N>(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Ch, Cl);
   stage_rows<ActT, N>(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Bh, Bl);
-  stage_transposed<ActT, P>(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n, XTh, XTl);
+  // the chunk's x rows, held in registers until C is done with and X^T goes
+  // over it (item (token, 8 consecutive p), token fastest; rows past n zero)
+  constexpr int XIT = kSsdChunk * (P / 8) / 256;
+  static_assert(XIT >= 1 && kSsdChunk * (P / 8) % 256 == 0, "x staging items");
+  constexpr int XNV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
+  uint4 xs[XIT][XNV];
+#pragma unroll
+  for (int u = 0; u < XIT; ++u) {
+    const int v = tid + 256 * u;
+    const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
+#pragma unroll
+    for (int w = 0; w < XNV; ++w)
+      xs[u][w] = t < n ? ld16(static_cast<const ActT*>(p.x) + ((t0 + t) * p.H + h) * P + c0 + w * Elem<ActT>::kVec)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // the epilogue's x and z (8 consecutive p of one token per item), loaded
   // now and kept packed so that their latency overlaps the products
@@ -515,7 +532,32 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
       }
     }
   }
-  __syncthreads();  // B is done with; M goes over it
+  // C S0^T for the wave's column tiles, while C is staged (S0 leaves the
+  // registers here)
+  float cs[NPT][4][4];
+  if (has_cols) {
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+      h8 sh[NK], sl[NK];
+#pragma unroll
+      for (int s = 0; s < NK; ++s) split8(sv[q][s], sh[s], sl[s]);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const int k0 = 32 * s + 8 * lg;
+          const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
+          acc2 = mfma_f16(ch, sh[s], acc2);
+          acc2 = mfma_f16(ch, sl[s], acc2);
+          if constexpr (SPLIT) acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cs[q][it][r] = acc2[r];
+      }
+    }
+  }
+  __syncthreads();  // B and C are done with; M goes over B, X^T over C
 #pragma unroll
   for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -523,6 +565,20 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
       const int i = 16 * wave + 4 * lg + r, j = 16 * J + li;
       Ms[i * MS + j] = (J <= wave && j <= i) ? cb[J][r] * expf((float)(Ls[i] - Ls[j])) * dts[j] : 0.0f;
     }
+#pragma unroll
+  for (int u = 0; u < XIT; ++u) {
+    const int v = tid + 256 * u;
+    const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
+    float xv[8];
+#pragma unroll
+    for (int w = 0; w < XNV; ++w) Elem<ActT>::unpack(xs[u][w], xv + w * Elem<ActT>::kVec);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const _Float16 hx = (_Float16)xv[i];
+      XTh[(c0 + i) * kTS + t] = hx;
+      if constexpr (SPLIT) XTl[(c0 + i) * kTS + t] = (_Float16)(xv[i] - (float)hx);
+    }
+  }
   __syncthreads();
 
   // Y[16 it + .., 16 pt + ..] = (M X) + exp(L_i) (C S0^T), pt = the wave's tiles
@@ -531,9 +587,6 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
 #pragma unroll
     for (int q = 0; q < NPT; ++q) {
       const int pt = wave + 4 * q;
-      h8 sh[NK], sl[NK];
-#pragma unroll
-      for (int s = 0; s < NK; ++s) split8(sv[q][s], sh[s], sl[s]);
       h8 xh[2], xl[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -558,24 +611,15 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(Mamba2Params p, SsdWs ws) 
           acc = mfma_f16(ml, xh[s], acc);
           if constexpr (SPLIT) acc = mfma_f16(mh, xl[s], acc);
         }
-        f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          const int k0 = 32 * s + 8 * lg;
-          const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
-          acc2 = mfma_f16(ch, sh[s], acc2);
-          acc2 = mfma_f16(ch, sl[s], acc2);
-          if constexpr (SPLIT) acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
-        }
         const float4 ev = *reinterpret_cast<const float4*>(eLs + 16 * it + 4 * lg);
-        yv[q][it][0] = acc[0] + ev.x * acc2[0];
-        yv[q][it][1] = acc[1] + ev.y * acc2[1];
-        yv[q][it][2] = acc[2] + ev.z * acc2[2];
-        yv[q][it][3] = acc[3] + ev.w * acc2[3];
+        yv[q][it][0] = acc[0] + ev.x * cs[q][it][0];
+        yv[q][it][1] = acc[1] + ev.y * cs[q][it][1];
+        yv[q][it][2] = acc[2] + ev.z * cs[q][it][2];
+        yv[q][it][3] = acc[3] + ev.w * cs[q][it][3];
       }
     }
   }
-  __syncthreads();  // C and M are done with; Y goes over them
+  __syncthreads();  // M and X^T are done with; Y goes over them
   if (has_cols) {
 #pragma unroll
     for (int q = 0; q < NPT; ++q)
