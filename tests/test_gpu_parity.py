@@ -127,6 +127,26 @@ def test_prepare_parity(name, cfg, l2norm):
     _check_prepare(d, inp, cfg, got, want, name)
 
 
+@pytest.mark.parametrize("seqlens", [(1, 2, 40, 1, 3, 20), (30, 1, 2, 33, 1)],
+                         ids=["history_in_conv", "history_kernel"])
+def test_prepare_mixed_initial_history(seqlens):
+    """Sequences with and without a conv history in one call, short ones
+    among them (new rows mixing old taps, zeros and inputs), for both ways
+    the new history rows are written: by the conv kernel (every sequence's
+    first K-1 tokens in one 32-token strip) and by the second kernel."""
+    cfg = Config("pmix", "prefill", Dims(2, 4, 128, 128, 4), seqlens=seqlens, num_slots=len(seqlens) + 2,
+                 act_dtype="bf16", qkv_dtype="bf16", conv_state_std=1.0, seed=20)
+    R = _runner()
+    d = cfg.dims
+    inp = make_inputs(cfg)
+    inp["has_init"] = np.array([i % 2 for i in range(len(seqlens))], np.uint8)
+    _say(f"[prepare] mixed initial history {seqlens}")
+    got = R.prepare(d, inp, cfg.act_dtype, cfg.qkv_dtype, True)
+    want = oracle.prepare(d, inp["cu"], inp["x"], inp["w"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                          inp["conv_pool"], inp["slots"], inp["has_init"], True, cfg.qkv_dtype)
+    _check_prepare(d, inp, cfg, got, want, "mixed initial history")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("which", ["prefill_single", "varlen", "long"])
 def test_prepare_full_size_sampled_heads(which):
