@@ -341,7 +341,8 @@ def test_prefill_parity(name, cfg):
     d = cfg.dims
     inp = make_inputs(cfg)
     has = inp["has_init"].copy()
-    has[::2] = 0  # mix continuing and fresh sequences
+    if has.size > 1:
+        has[::2] = 0  # mix continuing and fresh sequences
     pre = _oracle_prepared(cfg, {**inp, "has_init": has})
     _say(f"[prefill] {name} T={cfg.T}")
     out, sp = R.prefill(d, inp["cu"], pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["ssm_pool"],
