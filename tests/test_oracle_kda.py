@@ -129,3 +129,61 @@ def test_pool_composition_with_gate():
     np.testing.assert_array_equal(newp[slots], oracle.round_to(s2, "bf16"))
     for sl in (0, 2, 4):
         np.testing.assert_array_equal(newp[sl], pool[sl])
+
+
+def _l2n(x):
+    """q / sqrt(sum q^2 + 1e-6) per (token, key head): the plain sum, eps
+    inside the root (ferrum-kernels cpu.rs, recurrent_gated_delta_rule_f32's
+    in-loop normalisation; the same form as the GDN prepare's L2 norm)."""
+    return x / np.sqrt((x ** 2).sum(-1, keepdims=True) + 1e-6)
+
+
+def test_l2norm_inside_equals_prenormalised():
+    """kda_recurrence(l2norm=True) equals kda_recurrence on q and k
+    normalised beforehand in numpy, with per-channel decays and Hv != Hk."""
+    q, k, v, g, beta, S0 = _problem(T=11, N=2, seed=9)
+    cu = np.array([0, 4, 11], np.int32)
+    has = np.array([1, 0], np.uint8)
+    o1, s1 = oracle.kda_recurrence(q, k, v, g, beta, cu, S0, has, 0.55, l2norm=True)
+    o2, s2 = oracle.kda_recurrence(_l2n(q), _l2n(k), v, g, beta, cu, S0, has, 0.55, l2norm=False)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s1, s2, rtol=1e-13, atol=1e-14)
+
+
+def test_l2norm_brute_force_matrix_algebra():
+    """With the in-loop norm, S_t = S_{t-1} diag(exp(g_t)) (I - beta_t kh kh^T)
+    + beta_t v_t kh^T and o_t = S_t (scale qh), kh and qh the normalised key
+    and query, written out with explicit Dk x Dk matrices."""
+    q, k, v, g, beta, S0 = _problem(T=6, seed=10)
+    k *= 3.0  # norms well away from 1, so a skipped normalisation shows
+    scale = 0.8
+    out, st = oracle.kda_recurrence(q, k, v, g, beta, [0, 6], S0, [1], scale, l2norm=True)
+    Hk, Hv, Dk = q.shape[1], v.shape[1], q.shape[2]
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        S = S0[0, h].copy()
+        for t in range(6):
+            kt = k[t, kh] / np.linalg.norm(np.append(k[t, kh], 1e-3))   # sqrt(|k|^2 + 1e-6)
+            qt = q[t, kh] / np.linalg.norm(np.append(q[t, kh], 1e-3))
+            S = S @ np.diag(np.exp(g[t, h])) @ (np.eye(Dk) - beta[t, h] * np.outer(kt, kt)) \
+                + beta[t, h] * np.outer(v[t, h], kt)
+            np.testing.assert_allclose(out[t, h], S @ (scale * qt), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(st[0, h], S, rtol=1e-12, atol=1e-13)
+
+
+def test_l2norm_eps_inside_the_root_small_vectors():
+    """One token from a zero state with q = k = c e_0, beta = 1, scale = 1:
+    o = v (kh . qh) with kh . qh = c^2 / (c^2 + 1e-6).  At c = 1e-3 that is
+    exactly 1/2; eps outside the root (c / (|c| + 1e-6)) would give 0.998."""
+    Dk, Dv = 4, 3
+    c = 1e-3
+    q = np.zeros((1, 1, Dk)); q[0, 0, 0] = c
+    k = q.copy()
+    v = np.array([[[1.0, -2.0, 0.5]]])
+    g = np.zeros((1, 1, Dk))
+    beta = np.ones((1, 1))
+    out, st = oracle.kda_recurrence(q, k, v, g, beta, [0, 1], np.zeros((1, 1, Dv, Dk)), [0], 1.0, l2norm=True)
+    np.testing.assert_allclose(out[0, 0], v[0, 0] * 0.5, rtol=1e-12)
+    # S = beta v kh^T with kh = e_0 / sqrt(2)
+    want = np.zeros((Dv, Dk)); want[:, 0] = v[0, 0] / np.sqrt(2.0)
+    np.testing.assert_allclose(st[0, 0], want, rtol=1e-12)
