@@ -157,6 +157,18 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _workspace(nbytes: int, device, stream):
+    """A uint8 scratch tensor owned by the stream the kernels run on: torch's
+    caching allocator hands a freed block back only to later work on the
+    stream it was allocated on, so the block is not reused while the kernels
+    enqueued on ``stream`` may still read it."""
+    import torch
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def gdn_prepare(dims: Dims, cu_seqlens, mixed_qkv, a_raw, b_raw, conv_weight, A_log, dt_bias, conv_state_pool,
                 q_out, k_out, v_out, g_out, beta_out, slot_idx=None, has_initial_state=None,
                 apply_qk_l2norm: bool = True, cu_seqlens_host=None, slot_idx_host=None, stream=None) -> None:
@@ -278,8 +290,7 @@ def gdn_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool,
     T = int(cu_h[-1]) if n > 0 else 0
     need = gdn_prefill_workspace_size(dims, n, T, chunk_size)
     if workspace is None and need > 0:
-        import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_prefill_varlen(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(q), _ptr(k),
                                 _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(ssm_state_pool),
@@ -329,8 +340,7 @@ def gdn_kda_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_p
     T = int(cu_h[-1]) if n > 0 else 0
     need = gdn_kda_prefill_workspace_size(dims, n, T, _dtype_code(q), chunk_size)
     if workspace is None and need > 0:
-        import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_kda_prefill_varlen(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(q), _ptr(k),
                                     _ptr(v), _dtype_code(q), _ptr(g), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
@@ -386,8 +396,7 @@ def gdn_mamba2_chunk_scan(cu_seqlens, x, dt, A, B, C, state_pool, out, D=None, z
     d, t = _ssm(x, B, dt_bias, dt_softplus, dt_min, dt_max)
     need = int(lib.gdn_mamba2_workspace_size(ctypes.byref(d), n, T))
     if workspace is None and need > 0:
-        import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _workspace(need, x.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_mamba2_chunk_scan(ctypes.byref(d), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A),
                                    _ptr(B), _ptr(C), _ptr(D), int(D is not None and D.dim() == 2), _ptr(z),

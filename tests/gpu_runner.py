@@ -53,13 +53,20 @@ def decode(d, inp, act: str, state: str, scale: float, conv_pool=None, ssm_pool=
 
 
 def prefill(d, cu, q, k, v, g, beta, ssm_pool, slots, has_init, qkv: str, state: str, scale: float,
-            l2norm: bool = False):
+            l2norm: bool = False, stream=None):
+    """The prefill through the binding; with ``stream`` (a torch.cuda.Stream)
+    the inputs are made on the current stream, which the side stream then
+    waits for, and the binding allocates its workspace itself."""
     T = int(cu[-1])
     sp = dev(ssm_pool, state)
     out = torch.empty(T, d.Hv, d.Dv, device=DEV, dtype=TORCH_DTYPE[qkv])
-    gdn.gdn_prefill_varlen(gdims(d), dev(np.asarray(cu, np.int32)), dev(q, qkv), dev(k, qkv), dev(v, qkv),
-                           dev(g), dev(beta), sp, out, scale, slot_idx=dev(np.asarray(slots, np.int32)),
-                           has_initial_state=dev(np.asarray(has_init, np.uint8)), use_qk_l2norm=l2norm)
+    args = (gdims(d), dev(np.asarray(cu, np.int32)), dev(q, qkv), dev(k, qkv), dev(v, qkv), dev(g), dev(beta), sp,
+            out, scale)
+    kw = dict(slot_idx=dev(np.asarray(slots, np.int32)), has_initial_state=dev(np.asarray(has_init, np.uint8)),
+              use_qk_l2norm=l2norm)
+    if stream is not None:
+        stream.wait_stream(torch.cuda.current_stream())
+    gdn.gdn_prefill_varlen(*args, **kw, stream=stream)
     torch.cuda.synchronize()
     return host(out), host(sp)
 

@@ -104,12 +104,9 @@ def test_kda_prefill_parity(name, d, lens, qkv, sdt, opts):
 @pytest.mark.parametrize("which", ["prefill", "decode"])
 def test_kda_full_size(which):
     """The benchmarked KDA workloads in the launch configuration the bench
-    times; the prefill's oracle runs two sampled key-head groups (heads are
-    independent), the decode's all heads."""
-    import torch
+    times, every head checked against the oracle."""
     from gdn_inputs import kda_decode_workload, kda_prefill_workload
     from tests import gpu_runner as R
-    from tests.test_gpu_parity import slice_key_head
     wl = kda_prefill_workload() if which == "prefill" else kda_decode_workload()
     d = wl["dims"]
     inp = kda_inputs(d, wl["seqlens"], wl["num_slots"], wl["qkv_dtype"], wl["state_dtype"], wl["seed"],
@@ -118,14 +115,6 @@ def test_kda_full_size(which):
     _say(f"[kda full] {wl['name']}")
     run = R.kda_prefill if which == "prefill" else R.kda_recurrent
     out, sp = run(d, inp, "bf16", "f32", scale, True)
-    heads = (0, 9) if which == "prefill" else tuple(range(d.Hk))
-    for kh in heads:
-        _, hs, sd = slice_key_head(d, kh)
-        sub = dict(inp)
-        sub["q"], sub["k"] = inp["q"][:, kh:kh + 1], inp["k"][:, kh:kh + 1]
-        sub["v"], sub["g"], sub["beta"] = inp["v"][:, hs], inp["g"][:, hs], inp["beta"][:, hs]
-        sub["A_log"], sub["dt_bias"] = inp["A_log"][hs], inp["dt_bias"][hs]
-        sub["ssm_pool"] = inp["ssm_pool"][:, hs]
-        o_ref, s_ref = _oracle(sd, sub, scale, True, "bf16", "f32")
-        assert_close(out[:, hs], o_ref, "bf16", f"key head {kh} out")
-        assert_close(sp[:, hs], s_ref, "f32", f"key head {kh} state pool")
+    o_ref, s_ref = _oracle(d, inp, scale, True, "bf16", "f32")
+    assert_close(out, o_ref, "bf16", "out, every head")
+    assert_close(sp, s_ref, "f32", "state pool, every head")
