@@ -9,7 +9,7 @@ Function names follow the C ABI: :func:`gdn_prepare`, :func:`gdn_decode`, :func:
 :func:`gdn_decode_spec`, :func:`gdn_gated_rmsnorm`, :func:`gdn_kda_recurrent`,
 :func:`gdn_kda_prefill_varlen`, :func:`gdn_kda_prefill_workspace_size`, :func:`gdn_mamba2_state_update`,
 :func:`gdn_mamba2_chunk_scan`, :func:`gdn_mamba2_workspace_size`,
-:func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`.
+:func:`gdn_prefill_varlen`, :func:`gdn_prefill_workspace_size`, :func:`gdn_prefill_varlen_noalloc`.
 """
 from __future__ import annotations
 
@@ -72,7 +72,7 @@ class Dims:
 
 _lib = None
 EXPORTS = ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
-           "gdn_prefill_workspace_size", "gdn_gated_rmsnorm", "gdn_kda_recurrent",
+           "gdn_prefill_workspace_size", "gdn_prefill_varlen_noalloc", "gdn_gated_rmsnorm", "gdn_kda_recurrent",
            "gdn_kda_prefill_varlen", "gdn_kda_prefill_workspace_size", "gdn_mamba2_state_update",
            "gdn_mamba2_chunk_scan", "gdn_mamba2_workspace_size", "gdn_status_string", "gdn_last_error", "gdn_version")
 
@@ -112,7 +112,10 @@ def load_library():
                                        i32, P, P, sz, P]
     lib.gdn_prefill_workspace_size.argtypes = [D, i32, i64, i32]
     lib.gdn_prefill_workspace_size.restype = sz
+    lib.gdn_prefill_varlen_noalloc.argtypes = [D, i32, i64, P, P, P, P, P, i32, P, P, P, i32, i32, P, P, P, f32,
+                                               i32, i32, P, P]
     for fn in ("gdn_prepare", "gdn_decode", "gdn_decode_gated", "gdn_decode_spec", "gdn_prefill_varlen",
+               "gdn_prefill_varlen_noalloc",
                "gdn_gated_rmsnorm", "gdn_kda_recurrent", "gdn_kda_prefill_varlen", "gdn_mamba2_state_update",
                "gdn_mamba2_chunk_scan"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -298,6 +301,25 @@ def gdn_prefill_varlen(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool,
                                 _ptr(has_initial_state), float(scale), int(use_qk_l2norm), int(chunk_size),
                                 _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_prefill_varlen", st)
+
+
+def gdn_prefill_varlen_noalloc(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool, out, scale: float,
+                               slot_idx=None, has_initial_state=None, use_qk_l2norm: bool = False,
+                               chunk_size: int = 64, cu_seqlens_host=None, slot_idx_host=None, stream=None) -> None:
+    """:func:`gdn_prefill_varlen` on the library's static device scratch: no
+    device memory is allocated, here or in the library.  Pass the host copies
+    of ``cu_seqlens`` and ``slot_idx`` to avoid a device-to-host copy."""
+    lib = load_library()
+    cu_h = _host_i32(cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens)
+    sl_h = _host_i32(slot_idx_host if slot_idx_host is not None else slot_idx)
+    n = int(cu_h.size - 1)
+    T = int(cu_h[-1]) if n > 0 else 0
+    st = lib.gdn_prefill_varlen_noalloc(ctypes.byref(dims.c()), n, T, _hptr(cu_h), _ptr(cu_seqlens), _ptr(q),
+                                        _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(ssm_state_pool),
+                                        _dtype_code(ssm_state_pool), ssm_state_pool.shape[0], _hptr(sl_h),
+                                        _ptr(slot_idx), _ptr(has_initial_state), float(scale), int(use_qk_l2norm),
+                                        int(chunk_size), _ptr(out), _stream(stream))
+    _check("gdn_prefill_varlen_noalloc", st)
 
 
 def gdn_kda_recurrent(dims: Dims, cu_seqlens, q, k, v, g, beta, ssm_state_pool, out, scale: float, A_log=None,

@@ -665,16 +665,21 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_
                                       dims->head_v_dim, num_seqs, total_tokens, chunk_size);
 }
 
-gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
-                              const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
-                              const void* q, const void* k, const void* v, gdn_dtype qkv_dtype,
-                              const float* g, const float* beta, void* ssm_state_pool,
-                              gdn_dtype state_dtype, int32_t num_slots,
-                              const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
-                              const uint8_t* has_initial_state_dev, float scale,
-                              int32_t use_qk_l2norm, int32_t chunk_size, void* out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "gdn_prefill_varlen";
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill_varlen and its allocation-free variant: the same checks, then
+// the launch on the caller's workspace or on the library's static scratch.
+gdn_status prefill_entry(const char* fn, const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                         const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, const void* q,
+                         const void* k, const void* v, gdn_dtype qkv_dtype, const float* g, const float* beta,
+                         void* ssm_state_pool, gdn_dtype state_dtype, int32_t num_slots,
+                         const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                         const uint8_t* has_initial_state_dev, float scale, int32_t use_qk_l2norm,
+                         int32_t chunk_size, void* out, void* workspace, size_t workspace_bytes, bool noalloc,
+                         void* stream) {
+
   gdn_status st = check_dims(fn, dims);
   if (st != GDN_OK) return st;
   st = check_offsets(fn, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev);
@@ -702,13 +707,23 @@ gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t to
   if (use_qk_l2norm != 0 && use_qk_l2norm != 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: use_qk_l2norm must be 0 or 1", fn);
   if (!(scale == scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
-  const size_t need = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_k_dim,
-                                                   dims->head_v_dim, num_seqs, total_tokens, chunk_size);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if (noalloc) {
+    const size_t one = gdn::prefill_workspace_bytes_per_head(dims->head_k_dim, dims->head_v_dim, num_seqs,
+                                                             total_tokens);
+    if (one > gdn::kNoAllocScratchBytes)
+      return fail(GDN_ERR_WORKSPACE,
+                  "%s: %d sequences of %lld tokens need %zu bytes of scratch per value head; the static scratch "
+                  "holds %zu",
+                  fn, num_seqs, (long long)total_tokens, one, gdn::kNoAllocScratchBytes);
+  } else {
+    const size_t need = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_k_dim,
+                                                     dims->head_v_dim, num_seqs, total_tokens, chunk_size);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
 
   int64_t nchunks = 0;
   int max_chunks = 0;
@@ -724,7 +739,42 @@ gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t to
   p.has_init = has_initial_state_dev; p.scale = scale; p.l2norm = use_qk_l2norm; p.chunk = chunk_size;
   p.out = out; p.workspace = workspace; p.workspace_bytes = workspace_bytes; p.num_chunks = nchunks;
   p.max_chunks_per_seq = max_chunks; p.qkv = qkv_dtype; p.state = state_dtype;
+  p.h0 = 0; p.hg = dims->num_v_heads;
+  if (noalloc) return launched(fn, gdn::launch_prefill_noalloc(p, static_cast<hipStream_t>(stream)));
   return launched(fn, gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                              const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                              const void* q, const void* k, const void* v, gdn_dtype qkv_dtype,
+                              const float* g, const float* beta, void* ssm_state_pool,
+                              gdn_dtype state_dtype, int32_t num_slots,
+                              const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                              const uint8_t* has_initial_state_dev, float scale,
+                              int32_t use_qk_l2norm, int32_t chunk_size, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_entry("gdn_prefill_varlen", dims, num_seqs, total_tokens, cu_seqlens_host, cu_seqlens_dev, q, k,
+                       v, qkv_dtype, g, beta, ssm_state_pool, state_dtype, num_slots, slot_idx_host, slot_idx_dev,
+                       has_initial_state_dev, scale, use_qk_l2norm, chunk_size, out, workspace, workspace_bytes,
+                       false, stream);
+}
+
+gdn_status gdn_prefill_varlen_noalloc(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                      const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                                      const void* q, const void* k, const void* v, gdn_dtype qkv_dtype,
+                                      const float* g, const float* beta, void* ssm_state_pool,
+                                      gdn_dtype state_dtype, int32_t num_slots,
+                                      const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                                      const uint8_t* has_initial_state_dev, float scale,
+                                      int32_t use_qk_l2norm, int32_t chunk_size, void* out, void* stream) {
+  return prefill_entry("gdn_prefill_varlen_noalloc", dims, num_seqs, total_tokens, cu_seqlens_host,
+                       cu_seqlens_dev, q, k, v, qkv_dtype, g, beta, ssm_state_pool, state_dtype, num_slots,
+                       slot_idx_host, slot_idx_dev, has_initial_state_dev, scale, use_qk_l2norm, chunk_size, out,
+                       nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -133,6 +133,9 @@ struct PrefillParams {
   int64_t num_chunks;     // sum over sequences of ceil(L / chunk)
   int max_chunks_per_seq;
   gdn_dtype qkv, state;
+  // value heads h0 .. h0+hg-1 run in this launch; the workspace holds blocks
+  // for those heads only ([chunk][hg]); h0 = 0, hg = Hv for the whole layer
+  int h0, hg;
 };
 
 struct KdaParams {
@@ -205,5 +208,13 @@ hipError_t launch_mamba2_chunk_scan(const Mamba2Params& p, hipStream_t stream);
 size_t mamba2_workspace_bytes(int H, int P, int N, int Ns, int64_t T);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T, int chunk);
+// Scratch bytes the chunked prefill needs for ONE value head (0 when the
+// shape runs the token-sequential kernel, which needs none).
+size_t prefill_workspace_bytes_per_head(int Dk, int Dv, int N, int64_t T);
+// The prefill on the library's static scratch (no allocation), value heads in
+// groups that fit it; p.workspace is ignored.  The caller has checked that
+// one head fits (prefill_workspace_bytes_per_head <= kNoAllocScratchBytes).
+hipError_t launch_prefill_noalloc(const PrefillParams& p, hipStream_t stream);
+constexpr size_t kNoAllocScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
 
 }  // namespace gdn

@@ -55,6 +55,8 @@
 // Shapes the chunked kernels do not cover (Dk != Dv, or head dims 16 or
 // 256) run a token-sequential kernel: one wave per sequence, value head and
 // 16 value rows, with the state rows in registers.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -434,13 +436,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   __shared__ double Gs[kChunk];
   __shared__ float bs[kChunk], bg[kChunk], kn[kChunk];
 
-  const int cid = blockIdx.x, h = blockIdx.y;
+  const int cid = blockIdx.x, h = p.h0 + (int)blockIdx.y;
   const int kh = h / (p.Hv / p.Hk);
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
   const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_bytes(D);
+  char* blk = ws.blocks + ((int64_t)cid * p.hg + blockIdx.y) * blk_bytes(D);
   _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
   _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
   _Float16* Ph = reinterpret_cast<_Float16*>(blk + blk_p_hi(D));
@@ -1272,13 +1274,14 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
   // same XCD and share its L2 (they read the same W, P, K and Q blocks).
-  const int nwg = (D / 16) * p.Hv * p.N;
+  const int nwg = (D / 16) * p.hg * p.N;
   const int per_xcd = (int)gridDim.x / 8;
   const int logical = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
   if (logical >= nwg) return;
   const int e0 = 16 * (logical % (D / 16));
-  const int h = (logical / (D / 16)) % p.Hv;
-  const int s_idx = logical / ((D / 16) * p.Hv);
+  const int hl = (logical / (D / 16)) % p.hg;  // head within this launch's group
+  const int h = p.h0 + hl;
+  const int s_idx = logical / ((D / 16) * p.hg);
   const int kh = h / (p.Hv / p.Hk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   const int w4 = wave & 3;
@@ -1293,7 +1296,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   const int c_begin = ws.single ? 0 : ws.seq_chunk_off[s_idx];
   const int c_end = ws.single ? (int)((p.T + kChunk - 1) / kChunk) : ws.seq_chunk_off[s_idx + 1];
   constexpr int64_t kBlk = KDA ? blk_kda_bytes<QT>(D) : blk_bytes(D);
-  auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.Hv + h) * kBlk; };
+  auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.hg + hl) * kBlk; };
   if (c_begin == c_end) {
     // an empty sequence (KDA allows them): its final state is its initial
     // state, zero without one
@@ -1795,17 +1798,17 @@ hipError_t launch_seq(const PrefillParams& p, hipStream_t stream) {
 
 template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
-  chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
-  const int nwg = (D / 16) * p.Hv * p.N;
+  chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.hg), 256, 0, stream>>>(p, ws);
+  const int nwg = (D / 16) * p.hg * p.N;
   chunk_scan_kernel<QkvT, StT, D, false><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
   return hipGetLastError();
 }
 
 template <typename QkvT, typename StT>
-hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
+hipError_t launch_typed(const PrefillParams& p, hipStream_t stream, bool build_table = true) {
   if (!chunked_dims(p.Dk, p.Dv)) return launch_seq<QkvT, StT>(p, stream);
   const ChunkWs ws = carve(p.workspace, p.N, p.T);
-  if (!ws.single) chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
+  if (!ws.single && build_table) chunk_table_kernel<<<1, 64, 0, stream>>>(p.cu, p.N, ws);
   switch (p.Dk) {
     case 32: return launch_chunked_d<QkvT, StT, 32>(p, ws, stream);
     case 64: return launch_chunked_d<QkvT, StT, 64>(p, ws, stream);
@@ -1814,11 +1817,11 @@ hipError_t launch_typed(const PrefillParams& p, hipStream_t stream) {
 }
 
 template <typename QkvT>
-hipError_t launch_state(const PrefillParams& p, hipStream_t stream) {
+hipError_t launch_state(const PrefillParams& p, hipStream_t stream, bool build_table = true) {
   switch (p.state) {
-    case GDN_F32: return launch_typed<QkvT, float>(p, stream);
-    case GDN_BF16: return launch_typed<QkvT, bf16>(p, stream);
-    default: return launch_typed<QkvT, f16>(p, stream);
+    case GDN_F32: return launch_typed<QkvT, float>(p, stream, build_table);
+    case GDN_BF16: return launch_typed<QkvT, bf16>(p, stream, build_table);
+    default: return launch_typed<QkvT, f16>(p, stream, build_table);
   }
 }
 
@@ -1833,6 +1836,7 @@ hipError_t launch_kda_chunked_d(const KdaParams& p, const ChunkWs& ws, hipStream
   pp.slots = p.slots; pp.has_init = p.has_init; pp.scale = p.scale; pp.l2norm = p.l2norm; pp.chunk = kChunk;
   pp.out = p.out; pp.workspace = p.workspace; pp.workspace_bytes = p.workspace_bytes; pp.num_chunks = p.num_chunks;
   pp.max_chunks_per_seq = p.max_chunks_per_seq; pp.qkv = p.qkv; pp.state = p.state;
+  pp.h0 = 0; pp.hg = p.Hv;
   const int nwg = (D / 16) * p.Hv * p.N;
   chunk_scan_kernel<QkvT, StT, D, true><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(pp, ws);
   return hipGetLastError();
@@ -1882,8 +1886,82 @@ size_t prefill_workspace_bytes(int Hk, int Hv, int Dk, int Dv, int N, int64_t T,
   return align256((size_t)(N + 1) * 4) + 2 * align256((size_t)nc * 4) + (size_t)nc * Hv * blk_bytes(Dk);
 }
 
+size_t prefill_workspace_bytes_per_head(int Dk, int Dv, int N, int64_t T) {
+  return prefill_workspace_bytes(0, 1, Dk, Dv, N, T, kChunk);
+}
+
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  return p.qkv == GDN_F32 ? launch_state<float>(p, stream) : launch_state<bf16>(p, stream);
+  PrefillParams q = p;
+  q.h0 = 0;
+  q.hg = p.Hv;
+  return q.qkv == GDN_F32 ? launch_state<float>(q, stream) : launch_state<bf16>(q, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The prefill without allocation: a static scratch array in device memory.
+// Its name is a host-side stand-in in host code; the device address comes
+// from hipGetSymbolAddress, once per device, and only that address reaches
+// the kernels.  Every call on a device shares the array (calls that overlap
+// on one device race); the prefill needs no part of it cleared.
+// ---------------------------------------------------------------------------
+}  // namespace gdn
+
+static __device__ __align__(256) char scratch[gdn::kNoAllocScratchBytes];
+
+namespace gdn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on its first use there).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_noalloc(const PrefillParams& p, hipStream_t stream) {
+  void* base = nullptr;
+  hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  PrefillParams q = p;
+  q.workspace = base;
+  q.workspace_bytes = kNoAllocScratchBytes;
+  const size_t one = prefill_workspace_bytes_per_head(p.Dk, p.Dv, p.N, p.T);
+  if (one == 0) {  // the token-sequential kernel: no scratch at all
+    q.h0 = 0;
+    q.hg = p.Hv;
+    return q.qkv == GDN_F32 ? launch_state<float>(q, stream) : launch_state<bf16>(q, stream);
+  }
+  // value heads per launch: as many as the scratch holds, whole key-head
+  // groups where more than one fits (they share the L2 of one XCD)
+  const size_t table = one - (size_t)max_chunks(p.N, p.T) * blk_bytes(p.Dk);
+  const size_t per_head = one - table;
+  int hg = (int)std::min<size_t>((size_t)p.Hv, (kNoAllocScratchBytes - table) / per_head);
+  const int r = p.Hv / p.Hk;
+  if (hg >= r) hg -= hg % r;
+  for (int h0 = 0; h0 < p.Hv; h0 += hg) {
+    q.h0 = h0;
+    q.hg = std::min(hg, p.Hv - h0);
+    // the chunk table depends on the offsets only: built by the first launch
+    e = q.qkv == GDN_F32 ? launch_state<float>(q, stream, h0 == 0) : launch_state<bf16>(q, stream, h0 == 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn

@@ -466,6 +466,39 @@ gdn_status gdn_prefill_varlen(const gdn_dims* dims, int32_t num_seqs, int64_t to
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
                                   int32_t chunk_size);
 
+/* Bytes of device memory the library holds, on every device it runs on, for
+ * gdn_prefill_varlen_noalloc: a static array, resident until the process ends. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * gdn_prefill_varlen_noalloc -- gdn_prefill_varlen for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation): it takes no workspace and allocates
+ * nothing.  Its scratch is a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * per device (its address is looked up once per device, on the first call
+ * made with that device current).  When the batch needs more scratch than
+ * that, the value heads run in groups that fit, one group after another on
+ * the stream; each head is computed exactly as gdn_prefill_varlen computes
+ * it, so the results are the same.
+ *
+ * Arguments: those of gdn_prefill_varlen without workspace / workspace_bytes.
+ * Errors: those of gdn_prefill_varlen; GDN_ERR_WORKSPACE when a single value
+ *   head's scratch, gdn_prefill_workspace_size() with Hv = 1, exceeds
+ *   GDN_NOALLOC_SCRATCH_BYTES (about 74 k tokens with Dk = Dv = 128).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (the prefill reads nothing of it that it has not written in
+ * the same call): calls that overlap on one device, on different streams or
+ * from different threads, race and must be ordered by the caller.
+ */
+gdn_status gdn_prefill_varlen_noalloc(const gdn_dims* dims, int32_t num_seqs, int64_t total_tokens,
+                                      const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                                      const void* q, const void* k, const void* v, gdn_dtype qkv_dtype,
+                                      const float* g, const float* beta, void* ssm_state_pool,
+                                      gdn_dtype state_dtype, int32_t num_slots,
+                                      const int32_t* slot_idx_host, const int32_t* slot_idx_dev,
+                                      const uint8_t* has_initial_state_dev, float scale,
+                                      int32_t use_qk_l2norm, int32_t chunk_size, void* out, void* stream);
+
 /* Static English name of a status code. */
 const char* gdn_status_string(gdn_status status);
 

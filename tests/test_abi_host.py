@@ -368,3 +368,20 @@ def test_mamba2_chunk_scan_rejects_bad_arguments(lib):
 
 def test_mamba2_chunk_scan_empty_is_a_no_op(lib):
     assert _m2s(lib, N=0, T=0, cu=(0,), slots=()) == OK
+
+
+def test_prefill_noalloc_refuses_batches_beyond_its_scratch(lib):
+    """The allocation-free prefill refuses, before any device work, a batch
+    whose one value head needs more scratch than the static array holds."""
+    d = _dims(Hk=1, Hv=1)
+    T = 80000
+    per_head = lib.gdn_prefill_workspace_size(d, 1, T, 64)
+    assert per_head > (128 << 20)
+    cu_a, cu_p = _arr((0, T))
+    st = lib.gdn_prefill_varlen_noalloc(d, 1, T, cu_p, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, 1, None, None,
+                                        None, 0.1, 0, 64, FAKE, None)
+    assert st == WORKSPACE and "static scratch" in _err(lib)
+    # the ordinary checks come first, as in gdn_prefill_varlen
+    st = lib.gdn_prefill_varlen_noalloc(d, 1, T, cu_p, FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, 1, None, None,
+                                        None, 0.1, 0, 64, FAKE, None)
+    assert st == INVALID
