@@ -13,7 +13,9 @@ events recorded on the stream the kernels run on.  A bounded sample of the
 same work is also run through the f64 CPU oracle on the host cores
 (cpu_baseline).  After the timed region the output epilogue and the
 speculative multi-token decode (256 requests x 4 tokens) are timed on their
-own and reported beside the step, and so are the KDA variant's chunked
+own and reported beside the step, and so are the two other prefill
+workloads (16 varlen sequences with bf16 state carried in; 32768 tokens with
+Hv=48 and f16 state, one call and 8 chained calls), the KDA variant's chunked
 prefill (4096 tokens) and token-by-token decode (256 sequences).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -50,6 +52,8 @@ def parse():
                     help="only run the KDA workloads (chunked prefill, token-by-token decode)")
     ap.add_argument("--mamba2-only", action="store_true",
                     help="time only the Mamba2 prefill and decode workloads and print their record")
+    ap.add_argument("--prefill-configs-only", action="store_true",
+                    help="only time the varlen (16 sequences) and long (32768 tokens, Hv=48) prefill workloads")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
@@ -459,6 +463,120 @@ def kda(torch, gdn, reps=20):
     return res
 
 
+def varlen_prefill_bytes(T, N, Hk, Hv, Dk, Dv, qkv_bytes=2, state_bytes=4, has_init=True):
+    """Algorithmic HBM bytes of one gdn_prefill_varlen call over N sequences
+    of T tokens in all: q, k, v, g, beta read and out written once, and each
+    sequence's state read (when it continues its slot) and written once."""
+    return (T * (2 * Hk * Dk + Hv * Dv) * qkv_bytes + 2 * T * Hv * 4 + T * Hv * Dv * qkv_bytes
+            + N * (2 if has_init else 1) * Hv * Dv * Dk * state_bytes)
+
+
+def varlen_prepare_bytes(T, N, Hk, Hv, Dk, Dv, K, act_bytes=2, qkv_bytes=2, has_init=True):
+    """prepare_bytes plus each sequence's conv-history row read (when it
+    continues its slot) and written."""
+    Cc = 2 * Hk * Dk + Hv * Dv
+    return (prepare_bytes(T, Hk, Hv, Dk, Dv, K, act_bytes, qkv_bytes)
+            + N * (2 if has_init else 1) * Cc * (K - 1) * act_bytes)
+
+
+def prefill_configs(torch, gdn, reps=10):
+    """The two other prefill workloads, timed after the timed region, each as
+    gdn_prepare + gdn_prefill_varlen per call (HIP events on the kernels'
+    stream, median of ``reps`` calls after 2 untimed ones):
+      * varlen: 16 sequences, lengths ~U[128, 8192] (73,145 tokens), bf16
+        state pool and conv histories carried in (has_initial_state = 1): the
+        general path, whose chunk table chunk_table_kernel builds;
+      * long: one 32,768-token sequence, Hv = 48, f16 state from zero, as one
+        call and as 8 chained 4096-token calls (conv history and state carried).
+    The prefill is reported against the f16 MFMA peak (algorithmic flops of
+    the chunked form) with its HBM fraction beside it, the prepare against the
+    HBM peak."""
+    from gdn_inputs import make_inputs, prefill_long, prefill_varlen
+    dev = torch.device("cuda:0")
+    bf, f32 = torch.bfloat16, torch.float32
+    sdt = {"f32": f32, "bf16": bf, "f16": torch.float16}
+    sbytes = {"f32": 4, "bf16": 2, "f16": 2}
+    t = lambda a, dt=f32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for cfg in (prefill_varlen(), prefill_long()):
+        d = cfg.dims
+        gd = gdn.Dims(d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+        inp = make_inputs(cfg)
+        x, w, a, b = t(inp["x"], bf), t(inp["w"], bf), t(inp["a"], bf), t(inp["b"], bf)
+        A, dtb = t(inp["A_log"]), t(inp["dt_bias"])
+        conv = t(inp["conv_pool"], bf)
+        pool = t(inp["ssm_pool"], sdt[cfg.state_dtype])
+        del inp["x"]
+        T, N = cfg.T, cfg.N
+        q = torch.empty(T, d.Hk, d.Dk, device=dev, dtype=bf)
+        k = torch.empty_like(q)
+        v = torch.empty(T, d.Hv, d.Dv, device=dev, dtype=bf)
+        g = torch.empty(T, d.Hv, device=dev)
+        beta = torch.empty_like(g)
+        out = torch.empty(T, d.Hv, d.Dv, device=dev, dtype=bf)
+        ws = torch.empty(max(gdn.gdn_prefill_workspace_size(gd, N, T, 64), 1), dtype=torch.uint8, device=dev)
+        has_init = bool(inp["has_init"][0])
+        # (first token, token count, cu host, has_init host) per call of one pass
+        modes = {"one_call": [(0, T, inp["cu"], inp["has_init"])]}
+        if cfg.name.startswith("long"):
+            L = 4096
+            modes["eight_calls"] = [(L * i, L, np.array([0, L], np.int32), np.array([1 if i else 0], np.uint8))
+                                    for i in range(T // L)]
+        rec = {"tokens": T, "sequences": N, "state_dtype": cfg.state_dtype, "Hv": d.Hv,
+               "has_initial_state": has_init}
+        for mode, calls in modes.items():
+            dcalls = [(t0, n, cu_h, t(cu_h, torch.int32), hi_h, t(hi_h, torch.uint8)) for t0, n, cu_h, hi_h in calls]
+            sl_h = inp["slots"]
+            sl = t(sl_h, torch.int32)
+            evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in dcalls] for _ in range(reps)]
+            for it in range(reps + 2):
+                for j, (t0, n, cu_h, cu_d, hi_h, hi_d) in enumerate(dcalls):
+                    e = evs[it - 2][j] if it >= 2 else None
+                    sl_ = slice(t0, t0 + n)
+                    if e:
+                        e[0].record(stream)
+                    gdn.gdn_prepare(gd, cu_d, x[sl_], a[sl_], b[sl_], w, A, dtb, conv, q[sl_], k[sl_], v[sl_], g[sl_],
+                                    beta[sl_], slot_idx=sl, has_initial_state=hi_d, cu_seqlens_host=cu_h,
+                                    slot_idx_host=sl_h, stream=stream)
+                    if e:
+                        e[1].record(stream)
+                    gdn.gdn_prefill_varlen(gd, cu_d, q[sl_], k[sl_], v[sl_], g[sl_], beta[sl_], pool, out[sl_],
+                                           cfg.scale, slot_idx=sl, has_initial_state=hi_d, workspace=ws,
+                                           cu_seqlens_host=cu_h, slot_idx_host=sl_h, stream=stream)
+                    if e:
+                        e[2].record(stream)
+            torch.cuda.synchronize()
+            prep_ms = [sum(e[0].elapsed_time(e[1]) for e in calls_e) for calls_e in evs]
+            pre_ms = [sum(e[1].elapsed_time(e[2]) for e in calls_e) for calls_e in evs]
+            sp, sq = float(np.median(prep_ms)) * 1e-3, float(np.median(pre_ms)) * 1e-3
+            ncalls = len(dcalls)
+            fl = prefill_chunked_flops(T, d.Hk, d.Hv, d.Dk, d.Dv)
+            # state traffic per call: read when the call continues a slot, always written
+            nb = varlen_prefill_bytes(T, N, d.Hk, d.Hv, d.Dk, d.Dv, 2, sbytes[cfg.state_dtype], has_init)
+            nb += (ncalls - 1) * N * d.Hv * d.Dv * d.Dk * sbytes[cfg.state_dtype] * 2
+            pb = varlen_prepare_bytes(T, N, d.Hk, d.Hv, d.Dk, d.Dv, d.K, has_init=has_init)
+            pb += (ncalls - 1) * (2 * N * d.Cc * (d.K - 1) * 2 + d.Cc * d.K * 2)
+            rec[mode] = {
+                "calls": ncalls, "tokens_per_s": T / (sp + sq),
+                "prepare": {**stats_us(prep_ms),
+                            "roofline": {"bound": "hbm", "achieved": pb / sp / 1e9, "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": pb / sp / 1e9 / HBM_PEAK_GBS,
+                                         "bytes_per_launch": pb}},
+                "prefill": {**stats_us(pre_ms),
+                            "kernels": "chunk_prep_kernel + chunk_scan_kernel" +
+                                       (" + chunk_table_kernel" if N > 1 else " (one sequence: no chunk table)"),
+                            "roofline": {"bound": "mfma", "achieved": fl / sq / 1e12, "peak": F16_MFMA_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": fl / sq / 1e12 / F16_MFMA_PEAK_TFLOPS,
+                                         "flops_per_launch": fl, "bytes_per_launch": nb,
+                                         "hbm_frac": nb / sq / 1e9 / HBM_PEAK_GBS}},
+            }
+        res[cfg.name] = rec
+        del x, w, a, b, conv, pool, q, k, v, g, beta, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def mamba2_prefill_flops(T, H, P, N, c=64):
     """Algorithmic flops of the chunked Mamba2 / SSD prefill on full chunks of
     c tokens, per token and head: C B^T (2 c N), the masked product with X
@@ -573,6 +691,9 @@ def main():
     if args.mamba2_only:
         print(json.dumps({"mamba2": mamba2(torch, gdn, reps=args.steps)}), flush=True)
         return
+    if args.prefill_configs_only:
+        print(json.dumps({"prefill_configs": prefill_configs(torch, gdn, reps=args.steps)}), flush=True)
+        return
     dev = torch.device("cuda:0")
     bf, f32 = torch.bfloat16, torch.float32
 
@@ -653,8 +774,9 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l, epi, spec, kda_r, m2 = None, None, None, None, None, None
+    copy_gbs, cold_l, epi, spec, kda_r, m2, pcfgs = None, None, None, None, None, None, None
     if not args.no_extras:
+        pcfgs = prefill_configs(torch, gdn)
         spec = speculative(torch, gdn)
         kda_r = kda(torch, gdn)
         m2 = mamba2(torch, gdn)
@@ -701,7 +823,10 @@ def main():
     line = {
         "metric": METRIC, "value": (B + T) / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 vector arithmetic and state; matrix products on the f16 MFMA with f32 operands split into f16 "
+                 "hi + lo (about 22 bits), hi only for Q S^T and P Delta into bf16 outputs; bf16 io",
+        "data": "synthetic",
         "config": {"workload": "GDN step: decode 256 rows (512-slot f32 state pool) + prefill of one 4096-token "
                                "sequence; Hk=16 Hv=32 Dk=Dv=128 K=4; bf16 activations",
                    "decode_rows": B, "prefill_tokens": T, "chunk": 64, "state_dtype": "f32",
@@ -711,6 +836,7 @@ def main():
         "roofline": rl,
         "copy_GBps": copy_gbs,
         "epilogue": epi,
+        "prefill_configs": pcfgs,
         "decode_spec": spec,
         "kda": kda_r,
         "mamba2": m2,
