@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the device-copy and cold-cache decode runs after the timed region (for profiling)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpu count))")
+    ap.add_argument("--rmw-probe", action="store_true",
+                    help="only time the decode's state stream alone (in-place update of 256 random 2 MB slots "
+                         "of a 512-slot f32 pool, trivial arithmetic) under several launch shapes, beside gdn_decode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -659,6 +662,72 @@ def mamba2(torch, gdn, reps=20):
     return res
 
 
+def rmw_probe(torch, gdn, reps=20):
+    """The ceiling of the decode's memory access pattern: libgdn_probe.so's
+    in-place read-modify-write of 256 random 2 MB slots out of a 512-slot f32
+    pool (1 GiB; the slot subset re-drawn per call as in the decode bench),
+    with a trivial update and none of the decode's other work, timed with HIP
+    events (median of ``reps`` calls after 3), beside gdn_decode on the same
+    slot sets.  Rates count the state bytes read and written (1 GiB per call)
+    for the probe and the decode's algorithmic bytes for the decode."""
+    import ctypes
+    from gdn_inputs import decode_batch, decode_slot_sets, make_inputs
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_prepare_amd", "libgdn_probe.so"))
+    lib.gdn_probe_slot_rmw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p]
+    lib.gdn_probe_slot_rmw.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    cfg = decode_batch("f32")
+    d = cfg.dims
+    slot_floats = d.Hv * d.Dv * d.Dk
+    pool = torch.zeros(cfg.num_slots * slot_floats, dtype=torch.float32, device=dev)
+    n = reps + 3
+    sets_h = decode_slot_sets(cfg, n, seed=4242)
+    sets = torch.from_numpy(sets_h).to(dev)
+    contiguous = torch.arange(cfg.batch, dtype=torch.int32, device=dev)
+    state_bytes = 2 * cfg.batch * slot_floats * 4
+
+    def timed(call):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            call(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev[3:]])) * 1e-3
+
+    res = {"pool_slots": cfg.num_slots, "rows": cfg.batch, "slot_bytes": slot_floats * 4,
+           "state_bytes_per_call": state_bytes}
+    shapes = [("decode_shape_128KB_per_wg_nt_stores", 16, 0, False), ("128KB_per_wg_plain_stores", 16, 1, False),
+              ("whole_2MB_slot_per_wg_1024_threads", 1, 2, False),
+              ("decode_shape_contiguous_slots", 16, 0, True)]
+    for name, regions, mode, contig in shapes:
+        def call(i, regions=regions, mode=mode, contig=contig):
+            sl = contiguous if contig else sets[i]
+            rc = lib.gdn_probe_slot_rmw(ctypes.c_void_p(pool.data_ptr()), ctypes.c_void_p(sl.data_ptr()), cfg.batch,
+                                        slot_floats, regions, mode, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        sec = timed(call)
+        res[name] = {"median_us": sec * 1e6, "GBps": state_bytes / sec / 1e9,
+                     "frac_of_hbm_peak": state_bytes / sec / 1e9 / HBM_PEAK_GBS}
+    del pool
+    inp = make_inputs(cfg)
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    bf = torch.bfloat16
+    gd = gdn.Dims(d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    x, w, a, b = t(inp["x"], bf), t(inp["w"], bf), t(inp["a"], bf), t(inp["b"], bf)
+    A, dtb, conv, ssm = t(inp["A_log"]), t(inp["dt_bias"]), t(inp["conv_pool"], bf), t(inp["ssm_pool"])
+    out = torch.empty(cfg.batch, d.Hv, d.Dv, device=dev, dtype=bf)
+    sec = timed(lambda i: gdn.gdn_decode(gd, x, a, b, w, A, dtb, conv, ssm, sets[i], out, cfg.scale,
+                                         slot_idx_host=sets_h[i], stream=stream))
+    nb = decode_bytes(cfg.batch, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
+    res["gdn_decode"] = {"median_us": sec * 1e6, "GBps": nb / sec / 1e9, "frac_of_hbm_peak": nb / sec / 1e9 / HBM_PEAK_GBS,
+                         "frac_of_probe": (nb / sec) / (state_bytes / (res["decode_shape_128KB_per_wg_nt_stores"]["median_us"] * 1e-6))}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -690,6 +759,9 @@ def main():
         return
     if args.mamba2_only:
         print(json.dumps({"mamba2": mamba2(torch, gdn, reps=args.steps)}), flush=True)
+        return
+    if args.rmw_probe:
+        print(json.dumps({"rmw_probe": rmw_probe(torch, gdn, reps=args.steps)}), flush=True)
         return
     if args.prefill_configs_only:
         print(json.dumps({"prefill_configs": prefill_configs(torch, gdn, reps=args.steps)}), flush=True)
