@@ -421,8 +421,14 @@ struct SsdOutLds {
   static constexpr int kBytes = kE + kSsdChunk * 4;
 };
 
+// Four workgroups per CU where the register budget of 128 allows it (bf16
+// activations with P <= 64, f32 with P = 32 and N <= 64); the other shapes
+// need more registers and take what they need.
 template <typename ActT, int P, int N>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
+constexpr int kSsdOutWaves = (std::is_same<ActT, float>::value ? (P == 32 && N <= 64) : (P <= 64)) ? 4 : 1;
+
+template <typename ActT, int P, int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWaves<ActT, P, N>))) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
   using Lay = SsdOutLds<P, N, SPLIT>;
   constexpr int RS = Lay::RS, MS = Lay::MS, YS = Lay::YS;

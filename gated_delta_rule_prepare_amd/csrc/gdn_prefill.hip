@@ -1261,7 +1261,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) _Float16 ETl[2][16 * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
   __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
-  __shared__ __attribute__((aligned(16))) float Us[2][16 * 68];           // U^T (T form: V^T) rows e0 .. e0+15
+  __shared__ __attribute__((aligned(16))) float Us[2][TF ? 4 : 16 * 68];  // U^T rows e0 .. e0+15 (W form)
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[2][TF ? 16 * 68 : 8];  // T form: V^T rows e0 .. e0+15 (bf16)
+  // T form: each state wave's Y (its 16 tokens, f16 hi then lo), per lane
+  __shared__ __attribute__((aligned(16))) uint32_t Yx[TF ? 4 * 64 * 4 : 4];
   // exp(G_C - G_j), then gamma (T form: both times the k row scale, then gamma_C)
   __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk + (TF ? 4 : 0)];
   __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
@@ -1417,10 +1420,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   auto stage_uv = [&](int bb) {
     if constexpr (TF) {
       const int tk = ot >> 2, e = 4 * (ot & 3);
-      Us[bb][e * 68 + tk] = __uint_as_float(Vt.x << 16);
-      Us[bb][(e + 1) * 68 + tk] = __uint_as_float(Vt.x & 0xffff0000u);
-      Us[bb][(e + 2) * 68 + tk] = __uint_as_float(Vt.y << 16);
-      Us[bb][(e + 3) * 68 + tk] = __uint_as_float(Vt.y & 0xffff0000u);
+      Vb[bb][e * 68 + tk] = (uint16_t)(Vt.x & 0xffffu);
+      Vb[bb][(e + 1) * 68 + tk] = (uint16_t)(Vt.x >> 16);
+      Vb[bb][(e + 2) * 68 + tk] = (uint16_t)(Vt.y & 0xffffu);
+      Vb[bb][(e + 3) * 68 + tk] = (uint16_t)(Vt.y >> 16);
     } else {
       *reinterpret_cast<float4*>(Us[bb] + (ot >> 4) * 68 + 4 * (ot & 15)) = Ur;
     }
@@ -1498,39 +1501,47 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       // Delta rows of this wave's 16 tokens
       float dl[4];
       if constexpr (TF) {
-        // Y_J = V_J - diag(gamma) K_J S0^T for the token blocks J <= w4 (zero
-        // beyond), then Delta = T diag(beta) Y over the lower-triangular row
-        // block; the accumulator rows of Y_J, Y_J+1 are exactly this lane's
-        // B operand in the contraction order of T diag(beta)'s columns
+        // Y_J = V_J - diag(gamma) K_J S0^T for this wave's token block J = w4,
+        // published (f16 hi/lo) for every state wave; then Delta =
+        // T diag(beta) Y over the lower-triangular row block.  Lane (li, lg)
+        // holds tokens 16 J + 4 lg + r of row li, and in the contraction order
+        // of T diag(beta)'s columns the B operand of step s2 is the Y of
+        // blocks 2 s2 and 2 s2 + 1 at this same lane.  Blocks past w4 meet
+        // zero columns of T diag(beta).
+        {
+          f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            const h8 kf = ld_h8(Krow[b] + (16 * w4 + li) * KRS + 32 * s + 8 * lg);
+            xh = mfma_f16(kf, Sh[s], xh);
+            xl = mfma_f16(kf, Sl[s], xl);
+          }
+          const uint2 vv = *reinterpret_cast<const uint2*>(Vb[b] + li * 68 + 16 * w4 + 4 * lg);
+          const float vt[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                               __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+          const float4 gm = *reinterpret_cast<const float4*>(Vs[b] + kChunk + 16 * w4 + 4 * lg);
+          const float g4[4] = {gm.x, gm.y, gm.z, gm.w};
+          uint32_t hw[2], lw[2];
+#pragma unroll
+          for (int r2 = 0; r2 < 2; ++r2) {
+            const float y0 = vt[2 * r2] - g4[2 * r2] * (xh[2 * r2] + xl[2 * r2]);
+            const float y1 = vt[2 * r2 + 1] - g4[2 * r2 + 1] * (xh[2 * r2 + 1] + xl[2 * r2 + 1]);
+            const _Float16 a0 = (_Float16)y0, a1 = (_Float16)y1;
+            const _Float16 b0 = (_Float16)(y0 - (float)a0), b1 = (_Float16)(y1 - (float)a1);
+            hw[r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+            lw[r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          }
+          *reinterpret_cast<u32x4*>(Yx + (w4 * 64 + lane) * 4) = u32x4{hw[0], hw[1], lw[0], lw[1]};
+        }
+        __syncthreads();  // every state wave's Y is published
         f32x4 dhh = {0.0f, 0.0f, 0.0f, 0.0f}, dhl = dhh, dlh = dhh;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (2 * s2 > w4) break;
-          float yy[8];
-#pragma unroll
-          for (int a = 0; a < 2; ++a) {
-            const int J = 2 * s2 + a;
-            if (J > w4) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) yy[4 * a + r] = 0.0f;
-              continue;
-            }
-            f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-              const h8 kf = ld_h8(Krow[b] + (16 * J + li) * KRS + 32 * s + 8 * lg);
-              xh = mfma_f16(kf, Sh[s], xh);
-              xl = mfma_f16(kf, Sl[s], xl);
-            }
-            const float4 vt = *reinterpret_cast<const float4*>(Us[b] + li * 68 + 16 * J + 4 * lg);
-            const float4 gm = *reinterpret_cast<const float4*>(Vs[b] + kChunk + 16 * J + 4 * lg);
-            yy[4 * a + 0] = vt.x - gm.x * (xh[0] + xl[0]);
-            yy[4 * a + 1] = vt.y - gm.y * (xh[1] + xl[1]);
-            yy[4 * a + 2] = vt.z - gm.z * (xh[2] + xl[2]);
-            yy[4 * a + 3] = vt.w - gm.w * (xh[3] + xl[3]);
-          }
-          h8 yh, yl;
-          split8(yy, yh, yl);
+          const u32x4 y0 = *reinterpret_cast<const u32x4*>(Yx + ((2 * s2) * 64 + lane) * 4);
+          const u32x4 y1 = *reinterpret_cast<const u32x4*>(Yx + ((2 * s2 + 1) * 64 + lane) * 4);
+          const h8 yh = __builtin_bit_cast(h8, u32x4{y0.x, y0.y, y1.x, y1.y});
+          const h8 yl = __builtin_bit_cast(h8, u32x4{y0.z, y0.w, y1.z, y1.w});
           const h8 th = ld_h8(Tsh[b] + (16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
           const h8 tl = ld_h8(Tsh[b] + (kChunk + 16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
           dhh = mfma_f16(th, yh, dhh);
@@ -1617,6 +1628,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       stage_uv(b ^ 1);
       load_wst(min(cid + 2, c_end - 1));
       load_uv(min(cid + 2, c_end - 1));
+      // T form: this is the barrier behind which the state waves publish Y
+      // (and, before it, this chunk's split state), so Q S0^T runs while
+      // they form Delta; a second barrier below publishes Delta.  Other
+      // forms: the one barrier of the chunk.
       __syncthreads();
       // O of this chunk: diag(scale gamma) Q S0^T with Q's row scale, + P Delta
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
@@ -1644,6 +1659,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       const float qs[4] = {qsv.x, qsv.y, qsv.z, qsv.w}, gm[4] = {gmv.x, gmv.y, gmv.z, gmv.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] *= qs[r] * p.scale * gm[r];
+      if constexpr (TF) __syncthreads();  // Delta is published
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s > (w4 >> 1)) break;
