@@ -119,6 +119,15 @@ __host__ __device__ constexpr int64_t blk_bytes(int D) { return blk_vec(D) + 4 *
 __host__ __device__ constexpr int64_t blk_tb_hi() { return 0; }
 __host__ __device__ constexpr int64_t blk_tb_lo() { return (int64_t)kChunk * kChunk * 2; }
 
+// The first value head of h's key head within the launch's head range
+// [h0, h0 + hg): with bf16 q/k/v its block holds the key head's K^T and K
+// rows for every value head of the key head in the launch.
+__host__ __device__ inline int kv_first(const PrefillParams& p, int h) {
+  const int r = p.Hv / p.Hk;
+  const int f = h - h % r;
+  return f > p.h0 ? f : p.h0;
+}
+
 struct ChunkWs {
   int32_t* seq_chunk_off;  // [N+1] first chunk id of each sequence
   int32_t* chunk_seq;      // [NC]
@@ -652,7 +661,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     }
   }
   __syncthreads();
-  if constexpr (STAGE) {
+  // K^T and the K rows depend on the key head only: the first value head of
+  // the key head in this launch writes them, and the scan reads them from
+  // that head's block
+  if (STAGE && h == kv_first(p, h)) {
     // the K^T tile for the scan, read column-wise from the staged rows: f16
     // holds bf16 rows exactly, so the rows stay unscaled (the scan applies the
     // k scale, which is zero past the end, to E and to K S0^T)
@@ -679,8 +691,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
       }
       *reinterpret_cast<h8*>(blk + blk_kt_lo(D) + (r * D + 8 * c8) * 2) = o;
     }
-    __syncthreads();  // the staged rows live in Ts, which the inverse overwrites
   }
+  if constexpr (STAGE) __syncthreads();  // the staged rows live in Ts, which the inverse overwrites
   // f32 inputs: the scaled K^T tile for the scan, without the LDS row padding
 #pragma unroll
   for (int j = 0; j < (STAGE ? 0 : D / 32); ++j) {
@@ -1300,6 +1312,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   const int c_end = ws.single ? (int)((p.T + kChunk - 1) / kChunk) : ws.seq_chunk_off[s_idx + 1];
   constexpr int64_t kBlk = KDA ? blk_kda_bytes<QT>(D) : blk_bytes(D);
   auto blk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.hg + hl) * kBlk; };
+  // T form: the key head's K^T and K rows sit in the block of its first value head
+  const int hk_blk = TF ? kv_first(p, h) - p.h0 : hl;
+  auto kblk_of = [&](int cid) { return ws.blocks + ((int64_t)cid * p.hg + hk_blk) * kBlk; };
   if (c_begin == c_end) {
     // an empty sequence (KDA allows them): its final state is its initial
     // state, zero without one
@@ -1369,7 +1384,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     qsv = *reinterpret_cast<const float4*>(v + 3 * kChunk + 16 * w4 + 4 * lg);
   };
   auto load_kt = [&](int cid) {
-    const char* b = blk_of(cid);
+    const char* b = kblk_of(cid);
 #pragma unroll
     for (int j = 0; j < KTV; ++j) {
       const int v = ot + 256 * j;
@@ -1392,7 +1407,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       const char* b = blk_of(cid) + blk_tb_hi();
 #pragma unroll
       for (int j = 0; j < TBV; ++j) Tr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
-      const char* kb = blk_of(cid) + blk_kt_lo(D);
+      const char* kb = kblk_of(cid) + blk_kt_lo(D);
 #pragma unroll
       for (int j = 0; j < KTV; ++j) Kr[j] = *reinterpret_cast<const u32x4*>(kb + (ot + 256 * j) * 16);
     }
