@@ -665,20 +665,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   // the key head in this launch writes them, and the scan reads them from
   // that head's block
   if (STAGE && h == kv_first(p, h)) {
-    // the K^T tile for the scan, read column-wise from the staged rows: f16
-    // holds bf16 rows exactly, so the rows stay unscaled (the scan applies the
-    // k scale, which is zero past the end, to E and to K S0^T)
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      const int v = tid + 256 * j, r = v >> 3, c8 = v & 7;
-      h8 o;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] = (_Float16)Elem<QkvT>::load(Ks + (8 * c8 + t) * RS + r);
-      *reinterpret_cast<h8*>(blk + blk_kt_hi(D) + (r * kChunk + 8 * c8) * 2) = o;
-    }
     // T form: the K rows for the scan, each group of 32 columns in the
     // contraction order (position 8b + 4a + c holds column 16a + 4b + c), in
-    // the K^T lo slot (unused with bf16 q/k/v); the same f16 values as K^T
+    // the K^T lo slot (unused with bf16 q/k/v).  f16 holds bf16 rows
+    // exactly, so the rows stay unscaled (the scan applies the k scale, which
+    // is zero past the end, to E and to K S0^T).  The scan reads the K^T
+    // tiles of the state update from these rows with transposing LDS reads.
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int v = tid + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
@@ -1263,7 +1255,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   constexpr int TSS = kChunk + 8; // f16 row stride of T diag(beta) in LDS
   constexpr int KRS = D + 8;      // f16 row stride of the K rows in LDS
   constexpr int TBV = 4;          // 16-byte T diag(beta) vectors per output-wave lane (hi and lo)
-  __shared__ __attribute__((aligned(16))) _Float16 KTh[2][D * KTS];  // K^T [column][token]
+  // K^T [column][token]; the T form reads the update's K^T tiles from the K
+  // rows instead, with transposing LDS reads
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[2][TF ? 8 : D * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 KTl[2][KT_LO ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 Tsh[2][TF ? 2 * kChunk * TSS : 8];  // T diag(beta) hi rows, then lo rows
   __shared__ __attribute__((aligned(16))) _Float16 Krow[2][TF ? kChunk * KRS : 8];     // K rows, contraction order
@@ -1353,15 +1347,14 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   // read back in the contraction order from its own LDS slice
   auto load_q = [&](int cid) {
     const int n = ntok(cid);
+    const auto r16 = KDA ? buf_rsrc(blk_of(cid) + blk_kda_q<QT>(D), kChunk * D * (int)sizeof(QT))
+                         : buf_rsrc(qbase + tok0(cid) * qk_stride, (uint32_t)(n * qk_stride * (int64_t)sizeof(QkvT)));
 #pragma unroll
     for (int j = 0; j < NQV; ++j) {
       const int v = lane + 64 * j, r = v / QVPR, c = v % QVPR;
       const int rr = min(16 * w4 + r, n - 1);  // rows past the end re-read the last row; their scale is 0
-      if constexpr (KDA)
-        Qraw[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const QT*>(blk_of(cid) + blk_kda_q<QT>(D)) +
-                                                  rr * D + c * QEV);
-      else
-        Qraw[j] = *reinterpret_cast<const u32x4*>(qbase + (tok0(cid) + rr) * qk_stride + c * QEV);
+      const int64_t el = KDA ? (int64_t)rr * D + c * QEV : rr * qk_stride + c * QEV;
+      Qraw[j] = buf_ld16(r16, (uint32_t)(el * (int64_t)sizeof(QT)));
     }
   };
   auto stage_q = [&]() {
@@ -1372,24 +1365,23 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     }
   };
   auto load_pv = [&](int cid) {
-    const char* b = blk_of(cid);
+    const auto rb = buf_rsrc(blk_of(cid), (uint32_t)kBlk);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      Pfh[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_hi(D)) + ((2 * w4 + s) * 64 + lane) * 8);
-      if constexpr (SPLIT)
-        Pfl[s] = ld_h8(reinterpret_cast<const _Float16*>(b + blk_p_lo(D)) + ((2 * w4 + s) * 64 + lane) * 8);
+      const uint32_t o = (uint32_t)(((2 * w4 + s) * 64 + lane) * 16);
+      Pfh[s] = __builtin_bit_cast(h8, buf_ld16(rb, (uint32_t)blk_p_hi(D) + o));
+      if constexpr (SPLIT) Pfl[s] = __builtin_bit_cast(h8, buf_ld16(rb, (uint32_t)blk_p_lo(D) + o));
     }
-    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
-    gmv = *reinterpret_cast<const float4*>(v + 16 * w4 + 4 * lg);
-    qsv = *reinterpret_cast<const float4*>(v + 3 * kChunk + 16 * w4 + 4 * lg);
+    gmv = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (16 * w4 + 4 * lg))));
+    qsv = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (3 * kChunk + 16 * w4 + 4 * lg))));
   };
   auto load_kt = [&](int cid) {
-    const char* b = kblk_of(cid);
+    const auto rk = buf_rsrc(kblk_of(cid), (uint32_t)kBlk);
 #pragma unroll
     for (int j = 0; j < KTV; ++j) {
-      const int v = ot + 256 * j;
-      KTr[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_hi(D) + v * 16);
-      if constexpr (KT_LO) KTrl[j] = *reinterpret_cast<const u32x4*>(b + blk_kt_lo(D) + v * 16);
+      const uint32_t o = (uint32_t)((ot + 256 * j) * 16);
+      KTr[j] = buf_ld16(rk, (uint32_t)blk_kt_hi(D) + o);
+      if constexpr (KT_LO) KTrl[j] = buf_ld16(rk, (uint32_t)blk_kt_lo(D) + o);
     }
   };
   auto stage_kt = [&](int bb) {
@@ -1402,14 +1394,18 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   };
   // T form: T diag(beta) hi then lo as 2 * 64 rows of 64 halves (vector v
   // covers row v / 8), and the K rows in the contraction order
-  auto load_wst = [&](int cid) {
+  auto load_tb = [&](int cid) {
     if constexpr (TF) {
-      const char* b = blk_of(cid) + blk_tb_hi();
+      const auto rb = buf_rsrc(blk_of(cid), (uint32_t)kBlk);
 #pragma unroll
-      for (int j = 0; j < TBV; ++j) Tr[j] = *reinterpret_cast<const u32x4*>(b + (ot + 256 * j) * 16);
-      const char* kb = kblk_of(cid) + blk_kt_lo(D);
+      for (int j = 0; j < TBV; ++j) Tr[j] = buf_ld16(rb, (uint32_t)(blk_tb_hi() + (ot + 256 * j) * 16));
+    }
+  };
+  auto load_kr = [&](int cid) {
+    if constexpr (TF) {
+      const auto rk = buf_rsrc(kblk_of(cid), (uint32_t)kBlk);
 #pragma unroll
-      for (int j = 0; j < KTV; ++j) Kr[j] = *reinterpret_cast<const u32x4*>(kb + (ot + 256 * j) * 16);
+      for (int j = 0; j < KTV; ++j) Kr[j] = buf_ld16(rk, (uint32_t)(blk_kt_lo(D) + (ot + 256 * j) * 16));
     }
   };
   // U^T rows e0 .. e0+15 (one float4 per lane), exp(G_C - G_j) and gamma
@@ -1417,20 +1413,21 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   float4 Ur, Vr, Gr, Kv;
   uint2 Vt;  // T form: four bf16 values of V, token ot / 4, rows e0 + 4 (ot % 4) .. +3
   auto load_uv = [&](int cid) {
-    const char* b = blk_of(cid);
+    const auto rb = buf_rsrc(blk_of(cid), (uint32_t)kBlk);
     if constexpr (TF) {
-      const int tk = min(ot >> 2, ntok(cid) - 1);  // rows past the end re-read the last row (beta = 0 there)
-      Vt = *reinterpret_cast<const uint2*>(static_cast<const QkvT*>(p.v) + (tok0(cid) + tk) * (int64_t)p.Hv * D +
-                                           (int64_t)h * D + e0 + 4 * (ot & 3));
+      const int n = ntok(cid);
+      const int tk = min(ot >> 2, n - 1);  // rows past the end re-read the last row (beta = 0 there)
+      const int64_t vrow = (int64_t)p.Hv * D;
+      const auto rv = buf_rsrc(static_cast<const QkvT*>(p.v) + tok0(cid) * vrow + (int64_t)h * D + e0,
+                               (uint32_t)(((n - 1) * vrow + 16) * (int64_t)sizeof(QkvT)));
+      Vt = buf_ld8(rv, (uint32_t)((tk * vrow + 4 * (ot & 3)) * (int64_t)sizeof(QkvT)));
     } else {
-      Ur = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_ut(D)) + (e0 + (ot >> 4)) * kChunk +
-                                            4 * (ot & 15));
+      Ur = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_ut(D) + 4 * ((e0 + (ot >> 4)) * kChunk + 4 * (ot & 15)))));
     }
-    const float* v = reinterpret_cast<const float*>(b + blk_vec(D));
-    Vr = *reinterpret_cast<const float4*>(v + (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)));
-    if constexpr (TF) Kv = *reinterpret_cast<const float4*>(v + 2 * kChunk + 4 * (ot & 15));
+    Vr = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (ot < 16 ? kChunk + 4 * ot : 4 * (ot & 15)))));
+    if constexpr (TF) Kv = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (2 * kChunk + 4 * (ot & 15)))));
     if constexpr (KDA)
-      Gr = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(b + blk_kda_gam<QT>(D)) + 4 * (ot % (D / 4)));
+      Gr = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_kda_gam<QT>(D) + 4 * (4 * (ot % (D / 4))))));
   };
   auto stage_uv = [&](int bb) {
     if constexpr (TF) {
@@ -1454,13 +1451,17 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     if constexpr (KDA)
       if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
   };
-  auto stage_w = [&](int bb) {
+  auto stage_tb = [&](int bb) {
     if constexpr (TF) {
 #pragma unroll
       for (int j = 0; j < TBV; ++j) {
         const int v = ot + 256 * j, r = v >> 3, c8 = v & 7;
         *reinterpret_cast<u32x4*>(Tsh[bb] + r * TSS + 8 * c8) = Tr[j];
       }
+    }
+  };
+  auto stage_kr = [&](int bb) {
+    if constexpr (TF) {
 #pragma unroll
       for (int j = 0; j < KTV; ++j) {
         const int v = ot + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
@@ -1483,18 +1484,21 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     }
     load_wg(c_begin);
   } else {
-    load_wst(c_begin);
+    load_tb(c_begin);
+    load_kr(c_begin);
     load_uv(c_begin);
-    load_kt(c_begin);
+    if constexpr (!TF) load_kt(c_begin);
     load_q(c_begin);
     load_pv(c_begin);
-    stage_w(0);
+    stage_tb(0);
+    stage_kr(0);
     stage_uv(0);
-    stage_kt(0);
+    if constexpr (!TF) stage_kt(0);
     stage_q();
-    load_wst(min(c_begin + 1, c_end - 1));
+    load_tb(min(c_begin + 1, c_end - 1));
+    load_kr(min(c_begin + 1, c_end - 1));
     load_uv(min(c_begin + 1, c_end - 1));
-    load_kt(min(c_begin + 1, c_end - 1));
+    if constexpr (!TF) load_kt(min(c_begin + 1, c_end - 1));
     load_q(min(c_begin + 1, c_end - 1));
   }
   __syncthreads();
@@ -1541,10 +1545,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
           for (int r2 = 0; r2 < 2; ++r2) {
             const float y0 = vt[2 * r2] - g4[2 * r2] * (xh[2 * r2] + xl[2 * r2]);
             const float y1 = vt[2 * r2 + 1] - g4[2 * r2 + 1] * (xh[2 * r2 + 1] + xl[2 * r2 + 1]);
-            const _Float16 a0 = (_Float16)y0, a1 = (_Float16)y1;
-            const _Float16 b0 = (_Float16)(y0 - (float)a0), b1 = (_Float16)(y1 - (float)a1);
-            hw[r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-            lw[r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+            split2(y0, y1, hw[r2], lw[r2]);
           }
           *reinterpret_cast<u32x4*>(Yx + (w4 * 64 + lane) * 4) = u32x4{hw[0], hw[1], lw[0], lw[1]};
         }
@@ -1591,15 +1592,13 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
           const float d0 = dl[2 * r2], d1 = dl[2 * r2 + 1];
-          const float x0 = d0 * dcs[2 * r2], x1 = d1 * dcs[2 * r2 + 1];
-          const _Float16 a0 = (_Float16)d0, a1 = (_Float16)d1;
-          const _Float16 b0 = (_Float16)(d0 - (float)a0), b1 = (_Float16)(d1 - (float)a1);
-          const _Float16 c0 = (_Float16)x0, c1 = (_Float16)x1;
-          const _Float16 f0 = (_Float16)(x0 - (float)c0), f1 = (_Float16)(x1 - (float)c1);
-          w[0][r2] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-          w[1][r2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-          w[2][r2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) | ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
-          w[3][r2] = (uint32_t)__builtin_bit_cast(uint16_t, f0) | ((uint32_t)__builtin_bit_cast(uint16_t, f1) << 16);
+          if constexpr (SPLIT) {
+            split2(d0, d1, w[0][r2], w[1][r2]);
+          } else {
+            w[0][r2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)d0) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)d1) << 16);
+          }
+          split2(d0 * dcs[2 * r2], d1 * dcs[2 * r2 + 1], w[2][r2], w[3][r2]);
         }
         const int off = li * KTS + 16 * w4 + 4 * lg;
         *reinterpret_cast<uint2*>(DTh[b] + off) = make_uint2(w[0][0], w[0][1]);
@@ -1628,7 +1627,21 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const h8 kk = ld_h8(KTh[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg);
+          h8 kk;
+          if constexpr (TF) {
+            // K^T rows 16 ct .. 16 ct + 15 at tokens 32 s + 8 lg .. +7 from
+            // the K rows: in each 16-lane group a transposing read hands
+            // lane 4a + c element c of the 8-byte reads of lanes a, a+4, a+8,
+            // a+12, so lane li reads token 32 s + 8 lg + 4 h + li / 4 at the
+            // four columns 16 ct + 4 (li % 4) .. +3, which sit together in
+            // the contraction order
+            const _Float16* kp = Krow[b] + (32 * s + 8 * lg + (li >> 2)) * KRS + 32 * (ct >> 1) + 8 * (li & 3) +
+                                 4 * (ct & 1);
+            const uint2 k0 = lds_read_tr16(kp), k1 = lds_read_tr16(kp + 4 * KRS);
+            kk = __builtin_bit_cast(h8, u32x4{k0.x, k0.y, k1.x, k1.y});
+          } else {
+            kk = ld_h8(KTh[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg);
+          }
           a2 = mfma_f16(kk, eh[s], a2);
           a2 = mfma_f16(kk, el[s], a2);
           if constexpr (KT_LO) a2 = mfma_f16(ld_h8(KTl[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg), eh[s], a2);
@@ -1637,17 +1650,22 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int r = 0; r < 4; ++r) sc[r] = a2[r];
       }
     } else {
-      // next chunk's W (T form: T diag(beta), V^T and the K rows) into the
-      // other buffer, then start loading the one after
-      stage_w(b ^ 1);
+      // next chunk's T diag(beta) and V^T (W form: U^T) into the other
+      // buffer, then start loading the one after
+      stage_tb(b ^ 1);
       stage_uv(b ^ 1);
-      load_wst(min(cid + 2, c_end - 1));
+      load_tb(min(cid + 2, c_end - 1));
       load_uv(min(cid + 2, c_end - 1));
       // T form: this is the barrier behind which the state waves publish Y
       // (and, before it, this chunk's split state), so Q S0^T runs while
       // they form Delta; a second barrier below publishes Delta.  Other
       // forms: the one barrier of the chunk.
       __syncthreads();
+      // T form: the next chunk's K rows.  The state waves read the other
+      // buffer's rows until their update of the previous chunk, which ends
+      // before the barrier above; they read these after the next one.
+      stage_kr(b ^ 1);
+      load_kr(min(cid + 2, c_end - 1));
       // O of this chunk: diag(scale gamma) Q S0^T with Q's row scale, + P Delta
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
 #pragma unroll
@@ -1701,11 +1719,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         store4(obase + (tok0(cid) + i) * (int64_t)p.Hv * D + ec, vals);
       }
       // next chunk's K^T and q rows; operands of the chunks ahead
-      stage_kt(b ^ 1);
+      if constexpr (!TF) stage_kt(b ^ 1);
       stage_q();
       load_pv(cn);
       load_q(min(cid + 2, c_end - 1));
-      load_kt(min(cid + 2, c_end - 1));
+      if constexpr (!TF) load_kt(min(cid + 2, c_end - 1));
     }
   }
   if (wave == 0)
