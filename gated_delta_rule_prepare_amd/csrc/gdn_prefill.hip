@@ -1253,14 +1253,20 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   constexpr int WS = D + 8;       // f16 row stride of W and of the published state
   constexpr int KTV = D / 32;     // 16-byte K^T vectors per output-wave lane (per hi / lo)
   constexpr int TSS = kChunk + 8; // f16 row stride of T diag(beta) in LDS
-  constexpr int KRS = D + 8;      // f16 row stride of the K rows in LDS
+  // K rows in LDS: D halves per row, the 16-byte units of row r XOR-permuted
+  // by ((r & 3) << 2 | (r >> 2) & 3) (within the row's D / 8 units), which
+  // keeps the row reads of K S0^T, the transposing reads of the update and
+  // the staging writes free of bank conflicts without padding
+  auto krow_at = [](int r, int unit) {
+    return r * D + 8 * (unit ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (D / 8 - 1)));
+  };
   constexpr int TBV = 4;          // 16-byte T diag(beta) vectors per output-wave lane (hi and lo)
   // K^T [column][token]; the T form reads the update's K^T tiles from the K
   // rows instead, with transposing LDS reads
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][TF ? 8 : D * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 KTl[2][KT_LO ? D * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 Tsh[2][TF ? 2 * kChunk * TSS : 8];  // T diag(beta) hi rows, then lo rows
-  __shared__ __attribute__((aligned(16))) _Float16 Krow[2][TF ? kChunk * KRS : 8];     // K rows, contraction order
+  __shared__ __attribute__((aligned(16))) _Float16 Krow[2][TF ? kChunk * D : 8];     // K rows, contraction order
   __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
   __shared__ __attribute__((aligned(16))) _Float16 DTl[2][SPLIT ? 16 * KTS : 8];
   __shared__ __attribute__((aligned(16))) _Float16 ETh[2][16 * KTS];  // (exp(G_C - G_j) Delta)^T
@@ -1465,7 +1471,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 #pragma unroll
       for (int j = 0; j < KTV; ++j) {
         const int v = ot + 256 * j, r = v / (D / 8), c8 = v % (D / 8);
-        *reinterpret_cast<u32x4*>(Krow[bb] + r * KRS + 8 * c8) = Kr[j];
+        *reinterpret_cast<u32x4*>(Krow[bb] + krow_at(r, c8)) = Kr[j];
       }
     }
   };
@@ -1531,7 +1537,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
           f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
 #pragma unroll
           for (int s = 0; s < NKS; ++s) {
-            const h8 kf = ld_h8(Krow[b] + (16 * w4 + li) * KRS + 32 * s + 8 * lg);
+            const h8 kf = ld_h8(Krow[b] + krow_at(16 * w4 + li, 4 * s + lg));
             xh = mfma_f16(kf, Sh[s], xh);
             xl = mfma_f16(kf, Sl[s], xl);
           }
@@ -1635,9 +1641,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
             // a+12, so lane li reads token 32 s + 8 lg + 4 h + li / 4 at the
             // four columns 16 ct + 4 (li % 4) .. +3, which sit together in
             // the contraction order
-            const _Float16* kp = Krow[b] + (32 * s + 8 * lg + (li >> 2)) * KRS + 32 * (ct >> 1) + 8 * (li & 3) +
-                                 4 * (ct & 1);
-            const uint2 k0 = lds_read_tr16(kp), k1 = lds_read_tr16(kp + 4 * KRS);
+            const int kr = 32 * s + 8 * lg + (li >> 2), ku = 4 * (ct >> 1) + (li & 3);
+            const uint2 k0 = lds_read_tr16(Krow[b] + krow_at(kr, ku) + 4 * (ct & 1));
+            const uint2 k1 = lds_read_tr16(Krow[b] + krow_at(kr + 4, ku) + 4 * (ct & 1));
             kk = __builtin_bit_cast(h8, u32x4{k0.x, k0.y, k1.x, k1.y});
           } else {
             kk = ld_h8(KTh[b] + (16 * ct + li) * KTS + 32 * s + 8 * lg);
