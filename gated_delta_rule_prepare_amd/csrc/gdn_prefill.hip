@@ -1228,9 +1228,11 @@ __device__ __forceinline__ void store4(bf16* p, const float* v) {
 // Waves 4-7 (the output waves) do all the loading: they stage the next
 // chunk's W, U^T rows and decay factors (before the barrier) and K^T (after
 // it) into LDS for the state waves, and after the barrier form O = diag(scale gamma) Q S^T + P Delta for
-// 16 tokens each from the published state and Delta, writing it out through
-// a small LDS transpose.  With f32 q/k/v the LDS holds no W; the state waves
-// then load W themselves.
+// 16 tokens each from the published state and Delta.  They form it
+// transposed, O^T = S Q^T + Delta^T P^T (the same register fragments with the
+// operand roles swapped), so each lane ends with four consecutive value rows
+// of one token and stores them as one vector.  With f32 q/k/v the LDS holds
+// no W; the state waves then load W themselves.
 //
 // One barrier per chunk.  Every LDS buffer is double-buffered by chunk parity
 // and written and read in phases that a barrier separates.  Loads run one to
@@ -1272,7 +1274,6 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) _Float16 ETh[2][16 * KTS];  // (exp(G_C - G_j) Delta)^T
   __shared__ __attribute__((aligned(16))) _Float16 ETl[2][16 * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 SSh[2][(SPLIT ? 2 : 1) * 16 * WS];  // state hi rows (then lo rows)
-  __shared__ __attribute__((aligned(16))) float Os[4][16 * 20];          // output transpose, per wave
   __shared__ __attribute__((aligned(16))) float Us[2][TF ? 4 : 16 * 68];  // U^T rows e0 .. e0+15 (W form)
   __shared__ __attribute__((aligned(16))) uint16_t Vb[2][TF ? 16 * 68 : 8];  // T form: V^T rows e0 .. e0+15 (bf16)
   // T form: each state wave's Y (its 16 tokens, f16 hi then lo), per lane
@@ -1345,7 +1346,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   // ---- output-wave operands
   u32x4 Qraw[NQV];               // q rows 16 w4 .. 16 w4 + 15 of a chunk ahead, as stored
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
-  float4 qsv, gmv;               // q row scale and gamma at tokens 16 w4 + 4 lg + r
+  float qsv, gmv;                // q row scale and gamma at token 16 w4 + li
   u32x4 KTr[KTV], KTrl[KT_LO ? KTV : 1];
   u32x4 Tr[TF ? TBV : 1], Kr[TF ? KTV : 1];
   const int ot = tid - 256;      // output-wave thread index
@@ -1378,8 +1379,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       Pfh[s] = __builtin_bit_cast(h8, buf_ld16(rb, (uint32_t)blk_p_hi(D) + o));
       if constexpr (SPLIT) Pfl[s] = __builtin_bit_cast(h8, buf_ld16(rb, (uint32_t)blk_p_lo(D) + o));
     }
-    gmv = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (16 * w4 + 4 * lg))));
-    qsv = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_vec(D) + 4 * (3 * kChunk + 16 * w4 + 4 * lg))));
+    gmv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(blk_vec(D) + 4 * (16 * w4 + li)), 0, 0));
+    qsv = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(blk_vec(D) + 4 * (3 * kChunk + 16 * w4 + li)), 0, 0));
   };
   auto load_kt = [&](int cid) {
     const auto rk = buf_rsrc(kblk_of(cid), (uint32_t)kBlk);
@@ -1687,42 +1689,33 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
           const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
           h8 qh, ql;
           split8(qx, qh, ql);
-          o = mfma_f16(qh, sh, o);
-          o2 = mfma_f16(qh, sl, o2);
-          o2 = mfma_f16(ql, sh, o2);
+          o = mfma_f16(sh, qh, o);
+          o2 = mfma_f16(sl, qh, o2);
+          o2 = mfma_f16(sh, ql, o2);
         } else {
-          o = mfma_f16(to_h8(qx), sh, o);
+          o = mfma_f16(sh, to_h8(qx), o);
         }
       }
       o += o2;
-      const float qs[4] = {qsv.x, qsv.y, qsv.z, qsv.w}, gm[4] = {gmv.x, gmv.y, gmv.z, gmv.w};
+      const float osc = qsv * p.scale * gmv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] *= qs[r] * p.scale * gm[r];
+      for (int r = 0; r < 4; ++r) o[r] *= osc;
       if constexpr (TF) __syncthreads();  // Delta is published
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s > (w4 >> 1)) break;
         const h8 dh = ld_h8(DTh[b] + li * KTS + 32 * s + 8 * lg);
-        o = mfma_f16(Pfh[s], dh, o);
+        o = mfma_f16(dh, Pfh[s], o);
         if constexpr (SPLIT) {
-          o = mfma_f16(Pfh[s], ld_h8(DTl[b] + li * KTS + 32 * s + 8 * lg), o);
-          o = mfma_f16(Pfl[s], dh, o);
+          o = mfma_f16(ld_h8(DTl[b] + li * KTS + 32 * s + 8 * lg), Pfh[s], o);
+          o = mfma_f16(dh, Pfl[s], o);
         }
       }
-      // lane holds O[token 16 w4 + 4 lg + r][e0 + li]; transpose so that each
-      // lane writes four consecutive e of one token
-      float* os = Os[w4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) os[(4 * lg + r) * 20 + li] = o[r];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int tt = lane >> 2, ec = 4 * (lane & 3);
-      const float4 ov = *reinterpret_cast<const float4*>(os + tt * 20 + ec);
-      const int i = 16 * w4 + tt;
+      // lane holds O[token 16 w4 + li][e0 + 4 lg + r], r = 0..3
+      const int i = 16 * w4 + li;
       if (i < ntok(cid)) {
-        const float vals[4] = {ov.x, ov.y, ov.z, ov.w};
-        store4(obase + (tok0(cid) + i) * (int64_t)p.Hv * D + ec, vals);
+        const float vals[4] = {o[0], o[1], o[2], o[3]};
+        store4(obase + (tok0(cid) + i) * (int64_t)p.Hv * D + 4 * lg, vals);
       }
       // next chunk's K^T and q rows; operands of the chunks ahead
       if constexpr (!TF) stage_kt(b ^ 1);
