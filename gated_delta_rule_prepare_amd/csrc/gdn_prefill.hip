@@ -1497,17 +1497,22 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     load_uv(c_begin);
     if constexpr (!TF) load_kt(c_begin);
     load_q(c_begin);
-    load_pv(c_begin);
     stage_tb(0);
     stage_kr(0);
     stage_uv(0);
     if constexpr (!TF) stage_kt(0);
     stage_q();
-    load_tb(min(c_begin + 1, c_end - 1));
-    load_kr(min(c_begin + 1, c_end - 1));
-    load_uv(min(c_begin + 1, c_end - 1));
-    if constexpr (!TF) load_kt(min(c_begin + 1, c_end - 1));
-    load_q(min(c_begin + 1, c_end - 1));
+    // the loads in flight at the loop's head, issued in the order one pass of
+    // the loop issues them, so that the waits the compiler places at the
+    // head (which must hold for both ways in) wait for no more than the
+    // loop's own order needs
+    const int n1 = min(c_begin + 1, c_end - 1);
+    load_tb(n1);
+    load_uv(n1);
+    load_kr(n1);
+    load_pv(c_begin);
+    load_q(n1);
+    if constexpr (!TF) load_kt(n1);
   }
   __syncthreads();
 
