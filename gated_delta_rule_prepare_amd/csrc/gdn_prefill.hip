@@ -188,11 +188,11 @@ __global__ __launch_bounds__(64) void chunk_table_kernel(const int32_t* cu, int 
 // Transposed staging of a [64 tokens][D] tile into LDS as [D][KTS] f16 (hi
 // and, for f32 inputs, lo).  Lane l of a wave takes tokens 2(l%32), 2(l%32)+1
 // of one 8-column segment, so each 32-lane half writes 32 consecutive words.
-template <typename T, int D>
+template <typename T, int D, int NW = 4>
 struct TransposedTile {
   static constexpr bool kSplit = std::is_same<T, float>::value;
   static constexpr int kSegs = D / 8;
-  static constexpr int kPasses = (kSegs + 7) / 8;
+  static constexpr int kPasses = (kSegs + 2 * NW - 1) / (2 * NW);
   Raw8<T> r0[kPasses], r1[kPasses];
   // Loads are unconditional (rows past the chunk end re-read row n-1, and
   // segments past D re-read segment 0) so that no load sits under a branch;
@@ -203,7 +203,7 @@ struct TransposedTile {
     const int ta = min(t, n - 1), tb = min(t + 1, n - 1);
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int seg = seg0 + 8 * ps < kSegs ? seg0 + 8 * ps : 0;
+      const int seg = seg0 + 2 * NW * ps < kSegs ? seg0 + 2 * NW * ps : 0;
       r0[ps].load(src + (int64_t)ta * stride + seg * 8);
       r1[ps].load(src + (int64_t)tb * stride + seg * 8);
     }
@@ -221,7 +221,7 @@ struct TransposedTile {
     if (t + 1 >= n) s1 = 0.0f;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int seg = seg0 + 8 * ps;
+      const int seg = seg0 + 2 * NW * ps;
       if (seg >= kSegs) continue;
       float x0[8], x1[8];
       r0[ps].get(x0);
@@ -283,11 +283,12 @@ __device__ __forceinline__ int p_frag(int I, int li, int J, int q) {
 // T = (I + A)^-1 of the 64 x 64 strictly lower A (row stride TS) into Ts;
 // Ms is 4 x 16 x 17 floats of scratch.  Diagonal block w by wave w, lane li
 // solving column li by substitution; off-diagonal blocks by distance on the
-// f32 MFMA: T_IJ = -T_II sum_K A_IK T_KJ.  Ends with a barrier.
+// f32 MFMA: T_IJ = -T_II sum_K A_IK T_KJ.  Waves 0-3 do the work (every
+// wave of the workgroup takes the barriers).  Ends with a barrier.
 template <int TS>
 __device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, float* Ms) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  {
+  if (wave < 4) {
     const int B0 = 16 * wave, j = li;
     float tc[16];
 #pragma unroll
@@ -311,7 +312,8 @@ __device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, f
   // off-diagonal blocks, by distance: wave I computes T_{I, I-dist}
   for (int dist = 1; dist < 4; ++dist) {
     const int I = wave, J = wave - dist;
-    if (J >= 0) {
+    const bool act = wave < 4 && J >= 0;
+    if (act) {
       f32x4 M = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int K = J; K < I; ++K)
 #pragma unroll
@@ -321,7 +323,7 @@ __device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, f
       for (int r = 0; r < 4; ++r) Ms[wave * 272 + (4 * lg + r) * 17 + li] = M[r];
     }
     __syncthreads();
-    if (J >= 0) {
+    if (act) {
       f32x4 X = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -338,13 +340,13 @@ __device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, f
 // columns of a row of W / U; column tiles over the waves.  K^T and V^T are
 // [D][KTS] f16 tiles (with lo halves when K_LO / V_LO).  W is written f16 hi/lo
 // in the scan's contraction order, U^T as f32 [D][64].
-template <bool K_LO, bool V_LO, int TS, int D>
+template <bool K_LO, bool V_LO, int TS, int D, int NW = 4>
 __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, const float* bu, const _Float16* KTh,
                                              const _Float16* KTl, const _Float16* VTh, const _Float16* VTl,
                                              _Float16* Wh, _Float16* Wl, float* UTg) {
   constexpr int NCT = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  constexpr int NT = (2 * NCT + 3) / 4;  // tiles per wave
+  constexpr int NT = (2 * NCT + NW - 1) / NW;  // tiles per wave
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
     const int i = 16 * I + li;
@@ -371,7 +373,7 @@ __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, c
       split8(tu, tuh, tul);
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int ct = wave + 4 * m;
+        const int ct = wave + NW * m;
         if (ct >= 2 * NCT) break;
         const bool isW = ct < NCT;
         const int col0 = 16 * (isW ? ct : ct - NCT);
@@ -386,7 +388,7 @@ __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, c
     }
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
-      const int ct = wave + 4 * m;
+      const int ct = wave + NW * m;
       if (ct >= 2 * NCT) break;
       const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
       if (ct < NCT) {
@@ -428,8 +430,13 @@ __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _
 // With bf16 q/k/v the kernel needs 40 KB of LDS and under 128 VGPRs (the
 // other blocks' K rows are read from LDS where they are used), so four
 // workgroups share a CU.
+// occupancy the register allocation aims at: three waves per SIMD with bf16
+// q/k/v (four workgroups share a CU); f32 q/k/v keep the compiler's choice
+template <typename QkvT>
+constexpr int kPrepWaves = std::is_same<QkvT, float>::value ? 1 : 3;
+
 template <typename QkvT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<QkvT>))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
   constexpr int NKS = D / 32;      // 32-wide k steps over the head dim
   constexpr int NCT = D / 16;      // 16-column tiles of W (and of U)
@@ -753,7 +760,8 @@ __device__ __forceinline__ void load4(const bf16* p, float* o) {
 }
 
 template <typename QkvT, int D>
-__global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) {
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) {
+  constexpr int NW = 8;                 // waves: 0-3 own token blocks, 4-7 help
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
   using QT = KdaQ<QkvT>;
   constexpr int NKS = D / 32;
@@ -773,6 +781,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   __shared__ __attribute__((aligned(16))) float Ec[4][D];   // exp(rho_4 - rho_{I+1})
   __shared__ __attribute__((aligned(16))) float Em[3][D];   // exp(rho_I - rho_{J+1}): (2,0), (3,1), (3,0)
   __shared__ float bs[kChunk], kn[kChunk], qn[kChunk];
+  __shared__ double Bt[4][D];           // per-channel block totals of the log-decays
   // with bf16 q/k/v the chunk's K and Q rows are staged once (the diagonal
   // blocks and the element-wise tiles read them many times)
   constexpr bool STAGE = !SPLIT;
@@ -808,48 +817,53 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
   const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
 
-  // ---- loads: V tile, the K / Q fragments of this wave's blocks
-  TransposedTile<QkvT, D> vtile;
+  // Waves 0-3 (row waves) each own token block I = wave: its row scales,
+  // its diagonal block of A and P.  Waves 4-7 (helpers) form the element-wise
+  // tiles and the six off-diagonal blocks of A and P.  The W / U products run
+  // on all eight.
+  const bool roww = wave < 4;
+  const int ht = tid - 256;             // helper thread index
+  // ---- loads: V tile, the K / Q fragments of a row wave's own block
+  TransposedTile<QkvT, D, NW> vtile;
   vtile.load(vp, v_stride, n);
-  Raw8<QkvT> kf[4][NKS], qf[NKS];
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    if (J > wave) break;
-    const int rr = min(16 * J + li, n - 1);
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
-  }
+  Raw8<QkvT> kfo[NKS], qf[NKS];
   {
-    const int rr = min(16 * wave + li, n - 1);
+    const int rr = min(16 * (wave & 3) + li, n - 1);
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
+    for (int s = 0; s < NKS; ++s) {
+      kfo[s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
+      qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
+    }
   }
   if (tid < kChunk) bs[tid] = tid < n ? p.beta[(t0 + tid) * p.Hv + h] : 0.0f;
   if constexpr (STAGE) {
-    constexpr int VPR = D / 8, NV = kChunk * VPR / 256;
+    constexpr int VPR = D / 8, NV = (kChunk * VPR + 64 * NW - 1) / (64 * NW);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
-      *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
-      *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+      const int v = tid + 64 * NW * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      if (v < kChunk * VPR) {
+        *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
+        *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+      }
     }
   }
   // the chunk's log-decays, gate applied, all threads, 4 channels each: every
   // load is issued before any is used
   {
-    constexpr int NG = kChunk * (D / 4) / 256;
+    constexpr int NG = (kChunk * (D / 4) + 64 * NW - 1) / (64 * NW);
     const float a = p.A_log ? -expf(p.A_log[h]) : 0.0f;
     float4 raw[NG], bias[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const int v = tid + 256 * j, t = v / (D / 4), c = 4 * (v % (D / 4));
+      const int v = min(tid + 64 * NW * j, kChunk * (D / 4) - 1), t = v / (D / 4), c = 4 * (v % (D / 4));
       raw[j] = *reinterpret_cast<const float4*>(p.g + ((t0 + min(t, n - 1)) * p.Hv + h) * D + c);
       bias[j] = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + c)
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const int v = tid + 256 * j, t = v / (D / 4), c = 4 * (v % (D / 4));
+      const int v = tid + 64 * NW * j, t = v / (D / 4), c = 4 * (v % (D / 4));
+      if (v >= kChunk * (D / 4)) break;
       float x[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
       const float bb[4] = {bias[j].x, bias[j].y, bias[j].z, bias[j].w};
 #pragma unroll
@@ -873,45 +887,44 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   }
   __syncthreads();
 
-  // ---- per-channel running sums (f64), one thread per channel, in place
-  if (tid < D) {
-    const int d = tid;
-    double G = 0.0, rho[5];
+  // ---- per-channel running sums (f64), one thread per (channel, token
+  // block), in place: the sums within the block, then the block totals
+  const int sd = tid % D, sI = tid / D;
+  if (sI < 4) {
+    double G = 0.0;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      rho[I] = G;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = 16 * I + j;
-        G += (double)Gb[t * GS + d];
-        Gb[t * GS + d] = (float)((G - rho[I]) * kLog2e);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int t = 16 * sI + j;
+      G += (double)Gb[t * GS + sd];
+      Gb[t * GS + sd] = (float)(G * kLog2e);
     }
-    rho[4] = G;
+    Bt[sI][sd] = G;
+  }
+  __syncthreads();
+  if (sI < 4) {
+    double rho[5];
+    rho[0] = 0.0;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      Bk[I][d] = (float)((rho[I + 1] - rho[I]) * kLog2e);
-      Er[I][d] = (float)exp(rho[I]);
-      Ec[I][d] = (float)exp(rho[4] - rho[I + 1]);
-    }
-    Em[0][d] = (float)exp(rho[2] - rho[1]);
-    Em[1][d] = (float)exp(rho[3] - rho[2]);
-    Em[2][d] = (float)exp(rho[3] - rho[1]);
-    gam_g[d] = (float)exp(rho[4]);
+    for (int I = 0; I < 4; ++I) rho[I + 1] = rho[I] + Bt[I][sd];
+    Bk[sI][sd] = (float)(Bt[sI][sd] * kLog2e);
+    Er[sI][sd] = (float)exp(rho[sI]);
+    Ec[sI][sd] = (float)exp(rho[4] - rho[sI + 1]);
+    if (sI < 3)
+      Em[sI][sd] = (float)exp(sI == 0 ? rho[2] - rho[1] : sI == 1 ? rho[3] - rho[2] : rho[3] - rho[1]);
+    else
+      gam_g[sd] = (float)exp(rho[4]);
   }
 
-  // ---- row scales of this wave's block (L2 norm, else 1; zero past the end)
-  const int row = 16 * wave + li;
-  float ksc, qsc;
-  {
+  // ---- row scales of a row wave's block (L2 norm, else 1; zero past the end)
+  const int row = 16 * (wave & 3) + li;
+  float ksc = 0.0f, qsc = 0.0f;
+  if (roww) {
     float sk = 0.0f, sq = 0.0f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       float xq[8], xk[8];
       qf[s].get(xq);
-#pragma unroll
-      for (int J = 0; J < 4; ++J)
-        if (J == wave) kf[J][s].get(xk);
+      kfo[s].get(xk);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         sq += xq[i] * xq[i];
@@ -937,9 +950,10 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   __syncthreads();
 
   // ---- element-wise tiles: (k exp(G))^T into LDS, (k exp(G_C - G))^T and
-  // q exp(G) into the block.  Item (t, 8 channels), t fastest.
+  // q exp(G) into the block.  Item (t, 8 channels), t fastest; V^T by all
+  // eight waves, the rest by the helpers.
   vtile.store(VTh, VTl, nullptr, n);
-  for (int item = tid; item < kChunk * (D / 8); item += 256) {
+  for (int item = roww ? kChunk * (D / 8) : ht; item < kChunk * (D / 8); item += 256) {
     const int t = item & (kChunk - 1), c0 = 8 * (item / kChunk), I = t >> 4;
     const int rr = min(t, n - 1);
     Raw8<QkvT> kr, qr;
@@ -980,52 +994,69 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     }
   }
 
-  // ---- A and P of row block I = wave: lane holds row t = 16I + li,
-  // columns 16J + 4lg + r of each block J <= I
-  float av[4][4], pv[4][4];
-  {
-    const int t = row;
-    const float bt = bs[t];
-    // off-diagonal blocks on the MFMA: A operand = rows i of block J scaled by
-    // exp(rho_{J+1} - G_i) exp(rho_I - rho_{J+1}), B operand = this wave's rows
-    // scaled by exp(G_t - rho_I)
-    float lk[NKS][8], lq[NKS][8];
+  // Rows of the chunk as MFMA fragments: lane (li, lg) of row r, k step s
+  auto kfrag = [&](Raw8<QkvT>& f, int r, int s) {
+    if constexpr (STAGE)
+      f.load(Ks + r * RS + 32 * s + 8 * lg);
+    else
+      f.load(kp + min(r, n - 1) * qk_stride + 32 * s + 8 * lg);
+  };
+  auto qfrag = [&](Raw8<QkvT>& f, int r, int s) {
+    if constexpr (STAGE)
+      f.load(Qs + r * RS + 32 * s + 8 * lg);
+    else
+      f.load(qp + min(r, n - 1) * qk_stride + 32 * s + 8 * lg);
+  };
+
+  // ---- off-diagonal blocks (I, J), J < I, on the helpers: lane holds row
+  // t = 16I + li, columns 16J + 4lg + r.  Helper 0 takes (3,2) and (1,0),
+  // helper 1 (3,1) and (2,1), helper 2 (3,0), helper 3 (2,0).  A operand =
+  // rows i of block J scaled by exp(rho_{J+1} - G_i) exp(rho_I - rho_{J+1}),
+  // B operand = rows t scaled by exp(G_t - rho_I).
+  float avh[2][4];
+  int nblk = 0, bI[2] = {0, 0}, bJ[2] = {0, 0};
+  if (!roww) {
+    const int hw = wave - 4;
+    nblk = hw < 2 ? 2 : 1;
+    bI[0] = 3;
+    bJ[0] = hw == 0 ? 2 : hw == 1 ? 1 : 0;
+    if (hw == 3) bI[0] = 2;
+    bI[1] = hw == 0 ? 1 : 2;
+    bJ[1] = hw == 0 ? 0 : 1;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      float xk[8], xq[8];
-#pragma unroll
-      for (int J = 0; J < 4; ++J)
-        if (J == wave) kf[J][s].get(xk);
-      qf[s].get(xq);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ea = exp2_f(Gb[t * GS + 32 * s + 8 * lg + e]);
-        lk[s][e] = xk[e] * ksc * ea;
-        lq[s][e] = xq[e] * qsc * ea;
-      }
-    }
-#pragma unroll
-    for (int J = 0; J < 3; ++J) {
-      if (J >= wave) break;
+    for (int u = 0; u < 2; ++u) {
+      if (u >= nblk) break;
+      const int I = bI[u], J = bJ[u];
+      const int t = 16 * I + li;
+      const float bt = bs[t], tk = kn[t], tq = qn[t];
       const int i = 16 * J + li;  // the A-operand row this lane feeds
       const float si = kn[i];
-      const float* em = (wave - J >= 2) ? Em[wave == 2 ? 0 : (J == 1 ? 1 : 2)] : nullptr;
+      const float* em = (I - J >= 2) ? Em[I == 2 ? 0 : (J == 1 ? 1 : 2)] : nullptr;
       f32x4 akk = {0.0f, 0.0f, 0.0f, 0.0f}, aqk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        float a[8];
-        kf[J][s].get(a);
+        Raw8<QkvT> fa, fk, fq;
+        kfrag(fa, i, s);
+        kfrag(fk, t, s);
+        qfrag(fq, t, s);
+        float a[8], lk[8], lq[8];
+        fa.get(a);
+        fk.get(lk);
+        fq.get(lq);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * s + 8 * lg + e;
           float f = exp2_f(Bk[J][d] - Gb[i * GS + d]);
           if (em) f *= em[d];
           a[e] *= si * f;
+          const float ea = exp2_f(Gb[t * GS + d]);
+          lk[e] *= tk * ea;
+          lq[e] *= tq * ea;
         }
         h8 ah, al, kh8, kl8, qh8, ql8;
         split8(a, ah, al);
-        split8(lk[s], kh8, kl8);
-        split8(lq[s], qh8, ql8);
+        split8(lk, kh8, kl8);
+        split8(lq, qh8, ql8);
         akk = mfma_f16(ah, kh8, akk);
         akk = mfma_f16(ah, kl8, akk);
         akk = mfma_f16(al, kh8, akk);
@@ -1035,14 +1066,20 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
           aqk = mfma_f16(al, qh8, aqk);
         }
       }
+      float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        av[J][r] = bt * akk[r];
-        pv[J][r] = p.scale * aqk[r];
+        avh[u][r] = bt * akk[r];
+        pv[r] = p.scale * aqk[r];
       }
+      if constexpr (SPLIT)
+        store_h4_split(Ph + p_frag(I, li, J, lg), Pl + p_frag(I, li, J, lg), pv);
+      else
+        store_h4(Ph + p_frag(I, li, J, lg), pv);
     }
   }
-  {
+  float avd[4];
+  if (roww) {
     // diagonal block I = wave, in sub-blocks of 4 tokens.  With sigma_b the
     // running sum at the token before sub-block b, a pair in different
     // sub-blocks (i in b' < b, t in b) factors as
@@ -1061,9 +1098,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         float xk[8], xq[8], r8[8], l8[8], m8[8];
-#pragma unroll
-        for (int J = 0; J < 4; ++J)
-          if (J == wave) kf[J][s].get(xk);
+        kfo[s].get(xk);
         qf[s].get(xq);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1131,35 +1166,44 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     // lane (li, lg) holds row t = 16 wave + li, columns 4 lg + r of the block
     const bool same = lg == (li >> 2);
     const float bt = bs[row];
+    float pvd[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
-      if (J == wave)
+    for (int r = 0; r < 4; ++r) {
+      avd[r] = same ? Ms[wave * 272 + li * 17 + 4 * lg + r] : bt * ck[r];
+      pvd[r] = same ? Px[wave * 272 + li * 17 + 4 * lg + r] : p.scale * cq[r];
+    }
+    // P fragments go straight to the block; blocks above the diagonal are zero
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          av[J][r] = same ? Ms[wave * 272 + li * 17 + 4 * lg + r] : bt * ck[r];
-          pv[J][r] = same ? Px[wave * 272 + li * 17 + 4 * lg + r] : p.scale * cq[r];
-        }
-  }
-  // P fragments go straight to the block; blocks above the diagonal are zero
-#pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* v = J <= wave ? pv[J] : z;
-    if constexpr (SPLIT)
-      store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), v);
-    else
-      store_h4(Ph + p_frag(wave, li, J, lg), v);
+    for (int J = 0; J < 4; ++J) {
+      if (J < wave) continue;
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float* v = J == wave ? pvd : z;
+      if constexpr (SPLIT)
+        store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), v);
+      else
+        store_h4(Ph + p_frag(wave, li, J, lg), v);
+    }
   }
   __syncthreads();  // every read of the decay rows is done: A may overwrite them
+  if (roww) {
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* v = J <= wave ? av[J] : z;
-    *reinterpret_cast<float4*>(As + row * TS + 16 * J + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+    for (int J = 0; J < 4; ++J) {
+      if (J < wave) continue;
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float* v = J == wave ? avd : z;
+      *reinterpret_cast<float4*>(As + row * TS + 16 * J + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u >= nblk) break;
+      *reinterpret_cast<float4*>(As + (16 * bI[u] + li) * TS + 16 * bJ[u] + 4 * lg) =
+          make_float4(avh[u][0], avh[u][1], avh[u][2], avh[u][3]);
+    }
   }
   __syncthreads();
   unit_lower_inverse<TS>(As, Ts, Ms);
-  w_u_products<true, SPLIT, TS, D>(Ts, bs, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+  w_u_products<true, SPLIT, TS, D, NW>(Ts, bs, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
 }
 
 // ---------------------------------------------------------------------------
@@ -1881,7 +1925,7 @@ hipError_t launch_state(const PrefillParams& p, hipStream_t stream, bool build_t
 // ---- KDA
 template <typename QkvT, typename StT, int D>
 hipError_t launch_kda_chunked_d(const KdaParams& p, const ChunkWs& ws, hipStream_t stream) {
-  if (p.num_chunks > 0) kda_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 256, 0, stream>>>(p, ws);
+  if (p.num_chunks > 0) kda_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 512, 0, stream>>>(p, ws);
   // the scan reads what it needs of the layer through the GDN parameter block
   PrefillParams pp{};
   pp.Hk = p.Hk; pp.Hv = p.Hv; pp.Dk = p.Dk; pp.Dv = p.Dv; pp.N = p.N; pp.T = p.T; pp.cu = p.cu;
