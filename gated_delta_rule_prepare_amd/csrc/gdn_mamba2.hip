@@ -135,10 +135,15 @@ __global__ __launch_bounds__(kUpdThreads) void mamba2_update_kernel(Mamba2Params
 // Prefill: workspace
 // ---------------------------------------------------------------------------
 // Per (chunk, head) block: the chunk's state contribution St [P][N] f32,
-// which the state pass overwrites with the state entering the chunk, then
-// exp(L_C) (one float, padded to 256 bytes).
+// then exp(L_C) (one float, padded to 256 bytes), then the state entering
+// the chunk as f16 [P][N].  With f32 activations the state pass overwrites
+// St with the entering state in f32 (the output kernel splits it into f16
+// hi/lo); with 16-bit activations it writes the f16 copy, which the output
+// kernel's product C S0^T takes as is (its outputs round to 16 bits), and
+// the f32 St is read once and never written back.
 __host__ __device__ constexpr int64_t ssd_blk_vec(int P, int N) { return (int64_t)P * N * 4; }
-__host__ __device__ constexpr int64_t ssd_blk_bytes(int P, int N) { return ssd_blk_vec(P, N) + 256; }
+__host__ __device__ constexpr int64_t ssd_blk_s0h(int P, int N) { return ssd_blk_vec(P, N) + 256; }
+__host__ __device__ constexpr int64_t ssd_blk_bytes(int P, int N) { return ssd_blk_s0h(P, N) + (int64_t)P * N * 2; }
 
 struct SsdWs {
   int32_t* seq_chunk_off;  // [Nseq+1]
@@ -252,6 +257,63 @@ __device__ __forceinline__ void stage_rows(const ActT* src, int64_t stride, int 
   }
 }
 
+// The same two stagings split in two: load() issues the loads (16-byte
+// vectors kept in their storage form, rows past n zero), store() converts
+// and writes LDS, so that a kernel can issue every load it needs before it
+// waits on the first.
+template <typename ActT, int W, bool ROWS>
+struct Staged {
+  static constexpr bool kSplit = std::is_same<ActT, float>::value;
+  static constexpr int kItems = kSsdChunk * (W / 8) / 256;
+  static constexpr int kVecs = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
+  static_assert(kItems >= 1 && kSsdChunk * (W / 8) % 256 == 0, "staging items");
+  uint4 r[kItems][kVecs];
+  __device__ __forceinline__ static void item(int u, int& t, int& c0) {
+    const int v = threadIdx.x + 256 * u;
+    if (ROWS) {
+      t = v / (W / 8);
+      c0 = 8 * (v % (W / 8));
+    } else {
+      t = v % kSsdChunk;
+      c0 = 8 * (v / kSsdChunk);
+    }
+  }
+  __device__ __forceinline__ void load(const ActT* src, int64_t stride, int n) {
+#pragma unroll
+    for (int u = 0; u < kItems; ++u) {
+      int t, c0;
+      item(u, t, c0);
+#pragma unroll
+      for (int w = 0; w < kVecs; ++w)
+        r[u][w] = t < n ? *reinterpret_cast<const uint4*>(src + (int64_t)t * stride + c0 + w * Elem<ActT>::kVec)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* hi, _Float16* lo) const {
+#pragma unroll
+    for (int u = 0; u < kItems; ++u) {
+      int t, c0;
+      item(u, t, c0);
+      float x[8];
+#pragma unroll
+      for (int w = 0; w < kVecs; ++w) Elem<ActT>::unpack(r[u][w], x + w * Elem<ActT>::kVec);
+      if (ROWS) {
+        h8 xh, xl;
+        split8(x, xh, xl);
+        *reinterpret_cast<h8*>(hi + t * (W + 8) + c0) = xh;
+        if constexpr (kSplit) *reinterpret_cast<h8*>(lo + t * (W + 8) + c0) = xl;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const _Float16 h = (_Float16)x[i];
+          hi[(c0 + i) * kTS + t] = h;
+          if constexpr (kSplit) lo[(c0 + i) * kTS + t] = (_Float16)(x[i] - (float)h);
+        }
+      }
+    }
+  }
+};
+
 // Wave 0: the chunk's steps dt_j and cumulative log-decays L_i = sum_{j<=i}
 // A dt_j (f64 scan; tokens past n have dt = 0).  Returns L_i and dt_i of
 // lane i and L_C through lc.
@@ -291,8 +353,14 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
   char* blk = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
   float* Stg = reinterpret_cast<float*>(blk);
 
-  stage_transposed<ActT, N>(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, BTh, BTl);
-  stage_transposed<ActT, P>(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n, XTh, XTl);
+  {
+    Staged<ActT, N, false> bt;
+    Staged<ActT, P, false> xt;
+    bt.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
+    xt.load(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n);
+    bt.store(BTh, BTl);
+    xt.store(XTh, XTl);
+  }
   if (wave == 0) {
     float d;
     double lc;
@@ -348,7 +416,8 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
 // ---------------------------------------------------------------------------
 // Prefill pass 2, element-wise over (sequence, head, 4 state entries): carry
 // S through the sequence's chunks, S <- exp(L_C) S + St, leaving in each
-// block the state that enters its chunk; the final S goes to the pool.
+// block the state that enters its chunk (f32 in place with f32 activations,
+// else the f16 copy); the final S goes to the pool.
 // ---------------------------------------------------------------------------
 constexpr int kPassAhead = 4;
 
@@ -365,7 +434,8 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
   if (has) load_n<StT, 4>(Sg, S);
   const int c_begin = ws.single ? 0 : ws.seq_chunk_off[s_idx];
   const int c_end = ws.single ? (int)((p.T + kSsdChunk - 1) / kSsdChunk) : ws.seq_chunk_off[s_idx + 1];
-  const int64_t bb = ssd_blk_bytes(p.P, p.N), vo = ssd_blk_vec(p.P, p.N);
+  const int64_t bb = ssd_blk_bytes(p.P, p.N), vo = ssd_blk_vec(p.P, p.N), ho = ssd_blk_s0h(p.P, p.N);
+  const bool f16_s0 = p.act != GDN_F32;
   for (int c = c_begin; c < c_end; c += kPassAhead) {
     float4 v[kPassAhead];
     float eL[kPassAhead];
@@ -381,7 +451,13 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
     for (int u = 0; u < kPassAhead; ++u) {
       if (c + u < c_end) {
         char* blk = ws.blocks + ((int64_t)(c + u) * p.H + h) * bb;
-        *reinterpret_cast<float4*>(blk + e0 * 4) = make_float4(S[0], S[1], S[2], S[3]);
+        if (f16_s0) {
+          const uint2 w = make_uint2((uint32_t)f32_to_f16(S[0]) | ((uint32_t)f32_to_f16(S[1]) << 16),
+                                     (uint32_t)f32_to_f16(S[2]) | ((uint32_t)f32_to_f16(S[3]) << 16));
+          *reinterpret_cast<uint2*>(blk + ho + e0 * 2) = w;
+        } else {
+          *reinterpret_cast<float4*>(blk + e0 * 4) = make_float4(S[0], S[1], S[2], S[3]);
+        }
         S[0] = eL[u] * S[0] + v[u].x;
         S[1] = eL[u] * S[1] + v[u].y;
         S[2] = eL[u] * S[2] + v[u].z;
@@ -453,27 +529,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   const int64_t t0 = ws.single ? (int64_t)kSsdChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  const float* S0 = reinterpret_cast<const float*>(ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N));
+  const char* blk0 = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
+  const float* S0 = reinterpret_cast<const float*>(blk0);
+  const _Float16* S0h = reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N));
 
   // the wave's column tiles pt = wave + 4 q (P = 32: waves 2, 3 have none);
   // their S0 rows as the B operand S0^T[n][p], loaded before the staging
+  // (f32 activations: f32, split below; else the f16 copy)
   const bool has_cols = 16 * wave < P;
-  float sv[NPT][NK][8];
+  float sv[SPLIT ? NPT : 1][SPLIT ? NK : 1][8];
+  h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
   if (has_cols) {
 #pragma unroll
     for (int q = 0; q < NPT; ++q)
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        const float* sp = S0 + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
-        const float4 a = *reinterpret_cast<const float4*>(sp);
-        const float4 b = *reinterpret_cast<const float4*>(sp + 4);
-        sv[q][s][0] = a.x; sv[q][s][1] = a.y; sv[q][s][2] = a.z; sv[q][s][3] = a.w;
-        sv[q][s][4] = b.x; sv[q][s][5] = b.y; sv[q][s][6] = b.z; sv[q][s][7] = b.w;
+        if constexpr (SPLIT) {
+          const float* sp = S0 + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
+          const float4 a = *reinterpret_cast<const float4*>(sp);
+          const float4 b = *reinterpret_cast<const float4*>(sp + 4);
+          sv[q][s][0] = a.x; sv[q][s][1] = a.y; sv[q][s][2] = a.z; sv[q][s][3] = a.w;
+          sv[q][s][4] = b.x; sv[q][s][5] = b.y; sv[q][s][6] = b.z; sv[q][s][7] = b.w;
+        } else {
+          svh[q][s] = ld_h8(S0h + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg);
+        }
       }
   }
 
-  stage_rows<ActT, N>(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Ch, Cl);
-  stage_rows<ActT, N>(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, Bh, Bl);
+  Staged<ActT, N, true> crow, brow;
+  crow.load(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
+  brow.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
   // the chunk's x rows, held in registers until C is done with and X^T goes
   // over it (item (token, 8 consecutive p), token fastest; rows past n zero)
   constexpr int XIT = kSsdChunk * (P / 8) / 256;
@@ -510,6 +595,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       }
     }
   }
+  crow.store(Ch, Cl);
+  brow.store(Bh, Bl);
   if (wave == 0) {
     float d;
     double lc;
@@ -546,7 +633,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
     for (int q = 0; q < NPT; ++q) {
       h8 sh[NK], sl[NK];
 #pragma unroll
-      for (int s = 0; s < NK; ++s) split8(sv[q][s], sh[s], sl[s]);
+      for (int s = 0; s < NK; ++s) {
+        if constexpr (SPLIT)
+          split8(sv[q][s], sh[s], sl[s]);
+        else
+          sh[s] = svh[q][s];
+      }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -555,8 +647,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
           const int k0 = 32 * s + 8 * lg;
           const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
           acc2 = mfma_f16(ch, sh[s], acc2);
-          acc2 = mfma_f16(ch, sl[s], acc2);
-          if constexpr (SPLIT) acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
+          if constexpr (SPLIT) {
+            acc2 = mfma_f16(ch, sl[s], acc2);
+            acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) cs[q][it][r] = acc2[r];
