@@ -135,14 +135,16 @@ __global__ __launch_bounds__(kUpdThreads) void mamba2_update_kernel(Mamba2Params
 // Prefill: workspace
 // ---------------------------------------------------------------------------
 // Per (chunk, head) block: the chunk's state contribution St [P][N] f32,
-// then exp(L_C) (one float, padded to 256 bytes), then the state entering
-// the chunk as f16 [P][N].  With f32 activations the state pass overwrites
+// then the chunk's decay vector (exp(L_C), then per token dt_j, exp(L_j) f32
+// and L_j f64; 1280 bytes), then the state entering the chunk as f16 [P][N].  With f32 activations the state pass overwrites
 // St with the entering state in f32 (the output kernel splits it into f16
 // hi/lo); with 16-bit activations it writes the f16 copy, which the output
 // kernel's product C S0^T takes as is (its outputs round to 16 bits), and
 // the f32 St is read once and never written back.
 __host__ __device__ constexpr int64_t ssd_blk_vec(int P, int N) { return (int64_t)P * N * 4; }
-__host__ __device__ constexpr int64_t ssd_blk_s0h(int P, int N) { return ssd_blk_vec(P, N) + 256; }
+__host__ __device__ constexpr int64_t ssd_blk_s0h(int P, int N) { return ssd_blk_vec(P, N) + 1280; }
+// offsets within the decay vector
+constexpr int kVecDt = 16, kVecEL = 16 + 4 * 64, kVecL = 16 + 8 * 64;
 __host__ __device__ constexpr int64_t ssd_blk_bytes(int P, int N) { return ssd_blk_s0h(P, N) + (int64_t)P * N * 2; }
 
 struct SsdWs {
@@ -361,12 +363,11 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
     bt.store(BTh, BTl);
     xt.store(XTh, XTl);
   }
+  float dec_dt = 0.0f;
+  double dec_L = 0.0, dec_lc = 0.0;
   if (wave == 0) {
-    float d;
-    double lc;
-    const double L = chunk_log_decay<ActT>(p, t0, n, h, lane, d, lc);
-    ws_[lane] = d * (float)exp(lc - L);
-    if (lane == 0) reinterpret_cast<float*>(blk + ssd_blk_vec(P, N))[0] = (float)exp(lc);
+    dec_L = chunk_log_decay<ActT>(p, t0, n, h, lane, dec_dt, dec_lc);
+    ws_[lane] = dec_dt * (float)exp(dec_lc - dec_L);
   }
   __syncthreads();
 
@@ -410,6 +411,14 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
     // D[4lg + r][li] = St^T[n = 16 nt + 4lg + r][p = 16 pt + li]
     *reinterpret_cast<float4*>(Stg + (int64_t)(16 * pt + li) * N + 16 * nt + 4 * lg) =
         make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+  if (wave == 0) {
+    // the decay vector, which the output kernel reads instead of forming it again
+    char* vec = blk + ssd_blk_vec(P, N);
+    if (lane == 0) reinterpret_cast<float*>(vec)[0] = (float)exp(dec_lc);
+    reinterpret_cast<float*>(vec + kVecDt)[lane] = dec_dt;
+    reinterpret_cast<float*>(vec + kVecEL)[lane] = (float)exp(dec_L);
+    reinterpret_cast<double*>(vec + kVecL)[lane] = dec_L;
   }
 }
 
@@ -533,6 +542,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   const float* S0 = reinterpret_cast<const float*>(blk0);
   const _Float16* S0h = reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N));
 
+  // the chunk's decay vector, written by the state kernel (wave 0 puts it in LDS)
+  double dec_L = 0.0;
+  float dec_dt = 0.0f, dec_eL = 0.0f;
+  if (wave == 0) {
+    const char* vec = blk0 + ssd_blk_vec(P, N);
+    dec_L = reinterpret_cast<const double*>(vec + kVecL)[lane];
+    dec_dt = reinterpret_cast<const float*>(vec + kVecDt)[lane];
+    dec_eL = reinterpret_cast<const float*>(vec + kVecEL)[lane];
+  }
   // the wave's column tiles pt = wave + 4 q (P = 32: waves 2, 3 have none);
   // their S0 rows as the B operand S0^T[n][p], loaded before the staging
   // (f32 activations: f32, split below; else the f16 copy)
@@ -598,12 +616,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   crow.store(Ch, Cl);
   brow.store(Bh, Bl);
   if (wave == 0) {
-    float d;
-    double lc;
-    const double L = chunk_log_decay<ActT>(p, t0, n, h, lane, d, lc);
-    Ls[lane] = L;
-    dts[lane] = d;
-    eLs[lane] = (float)exp(L);
+    Ls[lane] = dec_L;
+    dts[lane] = dec_dt;
+    eLs[lane] = dec_eL;
   }
   __syncthreads();
 
