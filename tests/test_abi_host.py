@@ -341,7 +341,9 @@ def _m2s(lib, sd=None, N=2, T=100, cu=(0, 36, 100), act=1, state=0, slots=(1, 0)
 def test_mamba2_workspace_size(lib):
     # two sequences of 36 and 64 tokens: at most 100 / 64 + 2 = 3 chunk blocks per head
     n = lib.gdn_mamba2_workspace_size(_sdims(H=4, P=64, N=128), 2, 100)
-    blk = 64 * 128 * 4 + 256
+    # per (chunk, head): the f32 state contribution, the 1280-byte decay
+    # vector, the f16 state entering the chunk
+    blk = 64 * 128 * 4 + 1280 + 64 * 128 * 2
     assert n == 256 + 2 * 256 + 3 * 4 * blk
     assert lib.gdn_mamba2_workspace_size(_sdims(P=48), 2, 100) == 0
     assert lib.gdn_mamba2_workspace_size(_sdims(), 0, 0) == 0
