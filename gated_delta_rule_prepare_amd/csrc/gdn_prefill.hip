@@ -185,6 +185,19 @@ __global__ __launch_bounds__(64) void chunk_table_kernel(const int32_t* cu, int 
   if (lane == 63) ws.seq_chunk_off[N] = incl;
 }
 
+// four consecutive elements (one 8-byte read for bf16, 16 for f32)
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* o) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
 // Transposed staging of a [64 tokens][D] tile into LDS as [D][KTS] f16 (hi
 // and, for f32 inputs, lo).  Lane l of a wave takes tokens 2(l%32), 2(l%32)+1
 // of one 8-column segment, so each 32-lane half writes 32 consecutive words.
@@ -690,6 +703,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
       }
       *reinterpret_cast<h8*>(blk + blk_kt_lo(D) + (r * D + 8 * c8) * 2) = o;
     }
+    // the q rows as the scan's MFMA fragments (f16, exact for bf16), in the
+    // K^T hi slot: for token block I and k step s a 1 KiB run in which lane
+    // (li, lg) holds row 16 I + li at the contraction positions 32 s + 8 lg
+    // .. +7, i.e. columns 32 s + 4 lg .. +3 and 32 s + 16 + 4 lg .. +3
+    // (unscaled: the scan applies the q row scale, zero past the end)
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const int f = tid + 256 * j, I = f / (NKS * 64), s = (f / 64) % NKS, ln = f % 64;
+      const int rq = min(16 * I + (ln & 15), n - 1), c0 = 32 * s + 4 * (ln >> 4);
+      float a[4], b[4];
+      load4(qp + rq * qk_stride + c0, a);
+      load4(qp + rq * qk_stride + c0 + 16, b);
+      h8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (_Float16)a[e];
+        o[4 + e] = (_Float16)b[e];
+      }
+      *reinterpret_cast<h8*>(blk + blk_kt_hi(D) + f * 16) = o;
+    }
   }
   if constexpr (STAGE) __syncthreads();  // the staged rows live in Ts, which the inverse overwrites
   // f32 inputs: the scaled K^T tile for the scan, without the LDS row padding
@@ -746,18 +779,6 @@ using KdaQ = typename std::conditional<std::is_same<QkvT, float>::value, float, 
 constexpr double kLog2e = 1.4426950408889634;
 // 2^x with the hardware exponential (about 1 ulp; 0 far below the f32 range)
 __device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
-// four consecutive elements (one 8-byte read for bf16, 16 for f32)
-__device__ __forceinline__ void load4(const float* p, float* o) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-}
-__device__ __forceinline__ void load4(const bf16* p, float* o) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  o[0] = __uint_as_float(v.x << 16);
-  o[1] = __uint_as_float(v.x & 0xffff0000u);
-  o[2] = __uint_as_float(v.y << 16);
-  o[3] = __uint_as_float(v.y & 0xffff0000u);
-}
 
 template <typename QkvT, int D>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) {
@@ -1329,7 +1350,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   constexpr int QVPR = D / QEV;                  // vectors per q row
   constexpr int NQV = 16 * QVPR / 64;            // vectors per lane for a wave's 16 rows
   constexpr int QS = D + QEV;                    // row stride (elements) of the staged rows
-  __shared__ __attribute__((aligned(16))) QT Qsm[4][16 * QS];         // each output wave's 16 q rows
+  // each output wave's 16 q rows (the T form reads q as MFMA fragments the prep wrote instead)
+  __shared__ __attribute__((aligned(16))) QT Qsm[4][TF ? 8 : 16 * QS];
 
   // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that the
   // row blocks of one head, and the value heads of one key head, run on the
@@ -1388,7 +1410,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   };
 
   // ---- output-wave operands
-  u32x4 Qraw[NQV];               // q rows 16 w4 .. 16 w4 + 15 of a chunk ahead, as stored
+  u32x4 Qraw[TF ? 1 : NQV];      // q rows 16 w4 .. 16 w4 + 15 of a chunk ahead, as stored
+  h8 Qf[TF ? NKS : 1];           // T form: this chunk's q fragments (contraction order, f16)
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float qsv, gmv;                // q row scale and gamma at token 16 w4 + li
   u32x4 KTr[KTV], KTrl[KT_LO ? KTV : 1];
@@ -1406,6 +1429,15 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       const int rr = min(16 * w4 + r, n - 1);  // rows past the end re-read the last row; their scale is 0
       const int64_t el = KDA ? (int64_t)rr * D + c * QEV : rr * qk_stride + c * QEV;
       Qraw[j] = buf_ld16(r16, (uint32_t)(el * (int64_t)sizeof(QT)));
+    }
+  };
+  // T form: the q fragments the prep wrote in the key head's block (K^T hi slot)
+  auto load_qf = [&](int cid) {
+    if constexpr (TF) {
+      const auto rk = buf_rsrc(kblk_of(cid), (uint32_t)kBlk);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        Qf[s] = __builtin_bit_cast(h8, buf_ld16(rk, (uint32_t)(blk_kt_hi(D) + ((w4 * NKS + s) * 64 + lane) * 16)));
     }
   };
   auto stage_q = [&]() {
@@ -1540,12 +1572,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     load_kr(c_begin);
     load_uv(c_begin);
     if constexpr (!TF) load_kt(c_begin);
-    load_q(c_begin);
+    if constexpr (!TF) load_q(c_begin);
     stage_tb(0);
     stage_kr(0);
     stage_uv(0);
     if constexpr (!TF) stage_kt(0);
-    stage_q();
+    if constexpr (!TF) stage_q();
     // the loads in flight at the loop's head, issued in the order one pass of
     // the loop issues them, so that the waits the compiler places at the
     // head (which must hold for both ways in) wait for no more than the
@@ -1555,7 +1587,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     load_uv(n1);
     load_kr(n1);
     load_pv(c_begin);
-    load_q(n1);
+    if constexpr (TF)
+      load_qf(c_begin);
+    else
+      load_q(n1);
     if constexpr (!TF) load_kt(n1);
   }
   __syncthreads();
@@ -1727,13 +1762,17 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = o;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
+        const h8 sh = ld_h8(SSh[b] + li * WS + 32 * s + 8 * lg);
+        if constexpr (TF) {
+          o = mfma_f16(sh, Qf[s], o);
+          continue;
+        }
         Raw4<QT> qa, qb;
         qa.load(Qsm[w4] + li * QS + 32 * s + 4 * lg);
         qb.load(Qsm[w4] + li * QS + 32 * s + 16 + 4 * lg);
         float qx[8];
         qa.get(qx);
         qb.get(qx + 4);
-        const h8 sh = ld_h8(SSh[b] + li * WS + 32 * s + 8 * lg);
         if constexpr (SPLIT) {
           const h8 sl = ld_h8(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg);
           h8 qh, ql;
@@ -1768,9 +1807,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       }
       // next chunk's K^T and q rows; operands of the chunks ahead
       if constexpr (!TF) stage_kt(b ^ 1);
-      stage_q();
+      if constexpr (!TF) stage_q();
       load_pv(cn);
-      load_q(min(cid + 2, c_end - 1));
+      if constexpr (TF)
+        load_qf(cn);
+      else
+        load_q(min(cid + 2, c_end - 1));
       if constexpr (!TF) load_kt(min(cid + 2, c_end - 1));
     }
   }
