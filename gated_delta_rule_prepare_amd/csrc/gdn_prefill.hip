@@ -33,20 +33,21 @@
 //     dependence: K K^T and Q K^T with operands read straight from memory,
 //     T = (I + A)^-1 (16x16 diagonal blocks by substitution in registers,
 //     off-diagonal blocks T_IJ = -T_II sum_K A_IK T_KJ on MFMA).  Writes P
-//     (f16), the row-scaled K^T (f16), gamma, exp(G_C - G_j) and the q/k row
-//     scales to the workspace, and then
-//       - with bf16 q/k/v (the "T form"): T diag(beta) (f16 hi/lo) and the
-//         row-scaled K rows in the scan's contraction order;
-//       - with f32 q/k/v (the "W form"): W (f16 hi/lo) and U^T (f32), formed
-//         against K^T / V^T staged in LDS.
+//     (f16), gamma, exp(G_C - G_j) and the q/k row scales to the workspace,
+//     and then
+//       - with bf16 q/k/v (the "T form"): T diag(beta) (f16 hi/lo, MFMA
+//         fragment order) and, once per key head, the K rows in the scan's
+//         contraction order and the q rows as MFMA fragments (unscaled);
+//       - with f32 q/k/v (the "W form"): the row-scaled K^T (f16 hi/lo), W
+//         (f16 hi/lo) and U^T (f32), formed against K^T / V^T staged in LDS.
 //  3. chunk_scan_kernel, one workgroup (8 waves) per (sequence, value head,
 //     block of 16 value rows), placed so that the row blocks and value heads
 //     of one key head share an XCD's L2: walks the sequence's chunks in order.
 //     Four waves carry the 16 x Dk state block in registers and run only the
 //     serial part (Delta and the state update); four more do the bulk loads,
-//     staging the chunk operands and K^T into LDS, and form the output of
-//     each chunk from the state and Delta published in LDS.  One barrier per
-//     chunk.  Value rows of the state are independent, so row blocks never
+//     staging the chunk operands into LDS, and form the output of each chunk
+//     from the state and Delta published in LDS.  One barrier per chunk (two
+//     in the T form).  Value rows of the state are independent, so row blocks never
 //     communicate.  Delta = U - W S0^T in the W form; in the T form
 //     Delta = T diag(beta) (V - diag(gamma) K S0^T), the same quantity by
 //     (I + A) Delta = diag(beta) V - diag(beta gamma) K S0^T, which moves the
@@ -112,9 +113,11 @@ __host__ __device__ constexpr int64_t blk_kt_lo(int D) { return blk_kt_hi(D) + (
 __host__ __device__ constexpr int64_t blk_vec(int D) { return blk_kt_hi(D) + (int64_t)D * kChunk * 4; }
 __host__ __device__ constexpr int64_t blk_bytes(int D) { return blk_vec(D) + 4 * kChunk * 4; }
 
-// With bf16 q/k/v the block holds T diag(beta) (f16 hi [64][64], then lo)
-// in place of W and U^T, and the scan forms Delta = T diag(beta) (V -
-// diag(gamma) K S0^T) itself.  The first 16 KiB of a block always lie inside
+// With bf16 q/k/v the block holds T diag(beta) (f16 hi [64 x 64], then lo,
+// each in MFMA fragment order) in place of W and U^T, and the scan forms
+// Delta = T diag(beta) (V - diag(gamma) K S0^T) itself; the block of a key
+// head's first value head also holds the key head's K rows (K^T lo slot)
+// and q fragments (K^T hi slot).  The first 16 KiB of a block always lie inside
 // the W / U^T region (blk_p_hi(D) = 512 D >= 16 KiB for D >= 32).
 __host__ __device__ constexpr int64_t blk_tb_hi() { return 0; }
 __host__ __device__ constexpr int64_t blk_tb_lo() { return (int64_t)kChunk * kChunk * 2; }
@@ -417,10 +420,12 @@ __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, c
   }
 }
 
-// T diag(beta) as f16 hi/lo [64][64] rows for the scan (bf16 q/k/v), the
+// T diag(beta) as f16 hi/lo for the scan (bf16 q/k/v), each in MFMA
+// fragment order: for row block I and 32-column step s a 1 KiB run in which
+// lane li + 16 g holds row 16 I + li at positions 32 s + 8 g .. +7, the
 // columns of each group of 32 in the scan's contraction order (position
 // 8b + 4a + c holds column 16a + 4b + c).  Entries above the diagonal are
-// zero.  Thread t writes positions 16 (t % 4) .. +15 of row t / 4.
+// zero.  Thread t forms positions 16 (t % 4) .. +15 of row t / 4.
 template <int TS>
 __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _Float16* hi, _Float16* lo) {
   const int i = threadIdx.x >> 2, q = threadIdx.x & 3;
@@ -435,8 +440,10 @@ __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _
   for (int h = 0; h < 2; ++h) {
     h8 vh, vl;
     split8(v + 8 * h, vh, vl);
-    *reinterpret_cast<h8*>(hi + i * kChunk + 16 * q + 8 * h) = vh;
-    *reinterpret_cast<h8*>(lo + i * kChunk + 16 * q + 8 * h) = vl;
+    // positions 16 q + 8 h .. +7: step s = q / 2, lane group g = 2 (q % 2) + h
+    const int f = ((2 * (i >> 4) + (q >> 1)) * 64 + (i & 15) + 16 * (2 * (q & 1) + h)) * 8;
+    *reinterpret_cast<h8*>(hi + f) = vh;
+    *reinterpret_cast<h8*>(lo + f) = vl;
   }
 }
 
@@ -1319,7 +1326,6 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   constexpr int NCT = D / 16;     // 16-column tiles of the state
   constexpr int WS = D + 8;       // f16 row stride of W and of the published state
   constexpr int KTV = D / 32;     // 16-byte K^T vectors per output-wave lane (per hi / lo)
-  constexpr int TSS = kChunk + 8; // f16 row stride of T diag(beta) in LDS
   // K rows in LDS: D halves per row, the 16-byte units of row r XOR-permuted
   // by ((r & 3) << 2 | (r >> 2) & 3) (within the row's D / 8 units), which
   // keeps the row reads of K S0^T, the transposing reads of the update and
@@ -1327,12 +1333,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   auto krow_at = [](int r, int unit) {
     return r * D + 8 * (unit ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (D / 8 - 1)));
   };
-  constexpr int TBV = 4;          // 16-byte T diag(beta) vectors per output-wave lane (hi and lo)
   // K^T [column][token]; the T form reads the update's K^T tiles from the K
   // rows instead, with transposing LDS reads
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][TF ? 8 : D * KTS];
   __shared__ __attribute__((aligned(16))) _Float16 KTl[2][KT_LO ? D * KTS : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 Tsh[2][TF ? 2 * kChunk * TSS : 8];  // T diag(beta) hi rows, then lo rows
   __shared__ __attribute__((aligned(16))) _Float16 Krow[2][TF ? kChunk * D : 8];     // K rows, contraction order
   __shared__ __attribute__((aligned(16))) _Float16 DTh[2][16 * KTS];  // Delta^T [e][token]
   __shared__ __attribute__((aligned(16))) _Float16 DTl[2][SPLIT ? 16 * KTS : 8];
@@ -1396,6 +1400,20 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
 
   // ---- state-wave operands
   float Sf[8 * NKS];
+  // T form: this wave's T diag(beta) fragments (row block w4; hi then lo of
+  // k steps 0 and 1), loaded a chunk ahead straight from the block
+  u32x4 Tf[TF ? 4 : 1];
+  auto load_tf = [&](int cid) {
+    if constexpr (TF) {
+      const auto rb = buf_rsrc(blk_of(cid), (uint32_t)kBlk);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint32_t o = (uint32_t)(((2 * w4 + s2) * 64 + lane) * 16);
+        Tf[2 * s2] = buf_ld16(rb, (uint32_t)blk_tb_hi() + o);
+        Tf[2 * s2 + 1] = buf_ld16(rb, (uint32_t)blk_tb_lo() + o);
+      }
+    }
+  };
   h8 Wgh[TF ? 1 : NKS], Wgl[TF ? 1 : NKS];  // W fragments (W form), straight from memory
   auto load_wg = [&](int cid) {
     if constexpr (!TF) {
@@ -1415,7 +1433,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   h8 Pfh[2], Pfl[SPLIT ? 2 : 1];
   float qsv, gmv;                // q row scale and gamma at token 16 w4 + li
   u32x4 KTr[KTV], KTrl[KT_LO ? KTV : 1];
-  u32x4 Tr[TF ? TBV : 1], Kr[TF ? KTV : 1];
+  u32x4 Kr[TF ? KTV : 1];
   const int ot = tid - 256;      // output-wave thread index
   // a wave's q rows move whole 16-byte vectors (contiguous per row) and are
   // read back in the contraction order from its own LDS slice
@@ -1476,15 +1494,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       if constexpr (KT_LO) *reinterpret_cast<u32x4*>(KTl[bb] + r * KTS + 8 * c8) = KTrl[j];
     }
   };
-  // T form: T diag(beta) hi then lo as 2 * 64 rows of 64 halves (vector v
-  // covers row v / 8), and the K rows in the contraction order
-  auto load_tb = [&](int cid) {
-    if constexpr (TF) {
-      const auto rb = buf_rsrc(blk_of(cid), (uint32_t)kBlk);
-#pragma unroll
-      for (int j = 0; j < TBV; ++j) Tr[j] = buf_ld16(rb, (uint32_t)(blk_tb_hi() + (ot + 256 * j) * 16));
-    }
-  };
+  // T form: the K rows in the contraction order
   auto load_kr = [&](int cid) {
     if constexpr (TF) {
       const auto rk = buf_rsrc(kblk_of(cid), (uint32_t)kBlk);
@@ -1535,15 +1545,6 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     if constexpr (KDA)
       if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
   };
-  auto stage_tb = [&](int bb) {
-    if constexpr (TF) {
-#pragma unroll
-      for (int j = 0; j < TBV; ++j) {
-        const int v = ot + 256 * j, r = v >> 3, c8 = v & 7;
-        *reinterpret_cast<u32x4*>(Tsh[bb] + r * TSS + 8 * c8) = Tr[j];
-      }
-    }
-  };
   auto stage_kr = [&](int bb) {
     if constexpr (TF) {
 #pragma unroll
@@ -1567,13 +1568,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       }
     }
     load_wg(c_begin);
+    load_tf(c_begin);
   } else {
-    load_tb(c_begin);
     load_kr(c_begin);
     load_uv(c_begin);
     if constexpr (!TF) load_kt(c_begin);
     if constexpr (!TF) load_q(c_begin);
-    stage_tb(0);
     stage_kr(0);
     stage_uv(0);
     if constexpr (!TF) stage_kt(0);
@@ -1583,7 +1583,6 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     // head (which must hold for both ways in) wait for no more than the
     // loop's own order needs
     const int n1 = min(c_begin + 1, c_end - 1);
-    load_tb(n1);
     load_uv(n1);
     load_kr(n1);
     load_pv(c_begin);
@@ -1650,13 +1649,14 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
           const u32x4 y1 = *reinterpret_cast<const u32x4*>(Yx + ((2 * s2 + 1) * 64 + lane) * 4);
           const h8 yh = __builtin_bit_cast(h8, u32x4{y0.x, y0.y, y1.x, y1.y});
           const h8 yl = __builtin_bit_cast(h8, u32x4{y0.z, y0.w, y1.z, y1.w});
-          const h8 th = ld_h8(Tsh[b] + (16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
-          const h8 tl = ld_h8(Tsh[b] + (kChunk + 16 * w4 + li) * TSS + 32 * s2 + 8 * lg);
+          const h8 th = __builtin_bit_cast(h8, Tf[2 * s2]);
+          const h8 tl = __builtin_bit_cast(h8, Tf[2 * s2 + 1]);
           dhh = mfma_f16(th, yh, dhh);
           dhl = mfma_f16(th, yl, dhl);
           dlh = mfma_f16(tl, yh, dlh);
         }
         const f32x4 dd = dhh + (dhl + dlh);
+        load_tf(cn);  // the next chunk's fragments; this chunk's are consumed
 #pragma unroll
         for (int r = 0; r < 4; ++r) dl[r] = dd[r];
       } else {
@@ -1742,11 +1742,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         for (int r = 0; r < 4; ++r) sc[r] = a2[r];
       }
     } else {
-      // next chunk's T diag(beta) and V^T (W form: U^T) into the other
+      // next chunk's V^T (W form: U^T) and decay factors into the other
       // buffer, then start loading the one after
-      stage_tb(b ^ 1);
       stage_uv(b ^ 1);
-      load_tb(min(cid + 2, c_end - 1));
       load_uv(min(cid + 2, c_end - 1));
       // T form: this is the barrier behind which the state waves publish Y
       // (and, before it, this chunk's split state), so Q S0^T runs while
