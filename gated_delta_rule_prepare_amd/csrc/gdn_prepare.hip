@@ -62,15 +62,25 @@ __device__ __forceinline__ void store_stream(void* p, const uint4& u) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
 }
 
-// g and beta of one (token, value head) item i = t * Hv + h
+// g and beta of one (token, value head) item i = t * Hv + h: its inputs,
+// then the two outputs
+struct GateIn {
+  float a, b, A_log, dt_bias;
+};
 template <typename ActT>
-__device__ __forceinline__ void gate_item(const PrepareParams& p, int64_t i) {
+__device__ __forceinline__ GateIn gate_load(const PrepareParams& p, int64_t i) {
   const int64_t t = i / p.Hv;
   const int h = (int)(i % p.Hv);
-  const float a = Elem<ActT>::load(static_cast<const ActT*>(p.a) + t * p.a_stride + h);
-  const float b = Elem<ActT>::load(static_cast<const ActT*>(p.b) + t * p.b_stride + h);
-  p.g[i] = -expf(p.A_log[h]) * softplus_f(a + p.dt_bias[h]);
-  p.beta[i] = sigmoid_f(b);
+  return {Elem<ActT>::load(static_cast<const ActT*>(p.a) + t * p.a_stride + h),
+          Elem<ActT>::load(static_cast<const ActT*>(p.b) + t * p.b_stride + h), p.A_log[h], p.dt_bias[h]};
+}
+__device__ __forceinline__ void gate_store(const PrepareParams& p, int64_t i, const GateIn& in) {
+  p.g[i] = -expf(in.A_log) * softplus_f(in.a + in.dt_bias);
+  p.beta[i] = sigmoid_f(in.b);
+}
+template <typename ActT>
+__device__ __forceinline__ void gate_item(const PrepareParams& p, int64_t i) {
+  gate_store(p, i, gate_load<ActT>(p, i));
 }
 
 template <typename ActT, typename QkvT, int K, bool HIST>
@@ -97,6 +107,11 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   const int64_t t1 = min(p.T, t0 + kStrip);
 
   const ActT* __restrict__ x = static_cast<const ActT*>(p.x);
+  // the inputs of this thread's first gate item, loaded before the stream
+  // so that the gates after it wait on no load
+  const bool g_has = g_first < g_end;
+  GateIn gin{};
+  if (g_has) gin = gate_load<ActT>(p, g_first);
   const ActT* __restrict__ w = static_cast<const ActT*>(p.w);
   const ActT* __restrict__ hist = static_cast<const ActT*>(p.conv_pool);
   const int key_dim = p.Hk * p.Dk;
@@ -202,8 +217,23 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
   }
 
   // sum over the lanes of one q/k head (head_lanes a power of two <= 32):
-  // a fixed butterfly whose steps wider than the head add nothing
+  // a fixed butterfly whose steps wider than the head add nothing.  With 16
+  // lanes per head (the usual Dk = 128) the steps run as row rotations of
+  // the data-parallel primitives (DPP): after the step of distance 8 every
+  // partial sum is the same for lanes i and i ^ 8, so a rotation by 4 within
+  // the 16-lane row reads the same value as lane i ^ 4, and so on down to 1;
+  // the sums are bit for bit those of the butterfly.
   auto head_sum = [&](float v) {
+    if (head_lanes == 16) {
+      auto ror_add = [](float x, auto ctrl) {
+        return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+      };
+      v = ror_add(v, std::integral_constant<int, 0x128>{});  // row_ror:8
+      v = ror_add(v, std::integral_constant<int, 0x124>{});  // row_ror:4
+      v = ror_add(v, std::integral_constant<int, 0x122>{});  // row_ror:2
+      v = ror_add(v, std::integral_constant<int, 0x121>{});  // row_ror:1
+      return v;
+    }
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) {
       const float o = __shfl_xor(v, off, 64);
@@ -300,7 +330,8 @@ __global__ __launch_bounds__(kConvWaves * 64) void prepare_conv_kernel(PreparePa
     load_block(bufA, tb + 2 * kAhead);
     process(bufB, tb + kAhead);
   }
-  for (int64_t i = g_first; i < g_end; i += g_step) gate_item<ActT>(p, i);
+  if (g_has) gate_store(p, g_first, gin);
+  for (int64_t i = g_first + g_step; i < g_end; i += g_step) gate_item<ActT>(p, i);
 
   if constexpr (HIST && K > 1) {
     // new history rows of the sequences that start in this strip, after this
