@@ -14,10 +14,13 @@
 //   Y_inter[i] = exp(L_i) S0 C_i
 //   S_C = exp(L_C) S0 + sum_j exp(L_C - L_j) dt_j x_j B_j^T
 // in three passes, each parallel over the whole chip: ssd_state_kernel (per
-// chunk and head) forms the chunk's state contribution on the f16 hi/lo MFMA;
-// ssd_pass_kernel (element-wise over the state) carries S across the chunks
-// and leaves each chunk's S0 in the workspace; ssd_out_kernel (per chunk and
-// head) forms both output terms on the MFMA and applies D x and the gate.
+// pair of consecutive chunks and head) forms both chunks' state contributions
+// on the f16 hi/lo MFMA and the pair's; ssd_pass_kernel (element-wise over
+// the state) carries S across the pairs and leaves each pair's S0 in the
+// workspace; ssd_out_kernel (per chunk and head) forms the second chunk's S0
+// of a pair from the first's, forms both output terms on the MFMA and applies
+// D x and the gate.  Carrying the state per pair halves the state traffic of
+// the pass; the second chunk's S0 costs one more [P, N] read.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -134,13 +137,15 @@ __global__ __launch_bounds__(kUpdThreads) void mamba2_update_kernel(Mamba2Params
 // ---------------------------------------------------------------------------
 // Prefill: workspace
 // ---------------------------------------------------------------------------
-// Per (chunk, head) block: the chunk's state contribution St [P][N] f32,
-// then the chunk's decay vector (exp(L_C), then per token dt_j, exp(L_j) f32
-// and L_j f64; 1280 bytes), then the state entering the chunk as f16 [P][N].  With f32 activations the state pass overwrites
-// St with the entering state in f32 (the output kernel splits it into f16
-// hi/lo); with 16-bit activations it writes the f16 copy, which the output
-// kernel's product C S0^T takes as is (its outputs round to 16 bits), and
-// the f32 St is read once and never written back.
+// Per (chunk, head) block: a [P][N] f32 state, then the chunk's decay
+// vector (exp(L_C), for a pair's first chunk exp(L_C + L_C') of the pair,
+// then per token dt_j, exp(L_j) f32 and L_j f64; 1280 bytes), then a [P][N]
+// f16 state.  A pair's first block holds the pair's contribution St_pair in
+// f32; the state pass overwrites it with the state entering the pair in f32
+// with f32 activations (the output kernel splits it into f16 hi/lo), else
+// writes the f16 copy, which the output kernel's product C S0^T takes as is
+// (its outputs round to 16 bits).  A pair's second block holds the first
+// chunk's St: in f32 with f32 activations, else in the f16 slot.
 __host__ __device__ constexpr int64_t ssd_blk_vec(int P, int N) { return (int64_t)P * N * 4; }
 __host__ __device__ constexpr int64_t ssd_blk_s0h(int P, int N) { return ssd_blk_vec(P, N) + 1280; }
 // offsets within the decay vector
@@ -262,7 +267,8 @@ __device__ __forceinline__ void stage_rows(const ActT* src, int64_t stride, int 
 // The same two stagings split in two: load() issues the loads (16-byte
 // vectors kept in their storage form, rows past n zero), store() converts
 // and writes LDS, so that a kernel can issue every load it needs before it
-// waits on the first.
+// waits on the first.  tx is the thread's index among the 256 that share the
+// tile.
 template <typename ActT, int W, bool ROWS>
 struct Staged {
   static constexpr bool kSplit = std::is_same<ActT, float>::value;
@@ -270,8 +276,8 @@ struct Staged {
   static constexpr int kVecs = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
   static_assert(kItems >= 1 && kSsdChunk * (W / 8) % 256 == 0, "staging items");
   uint4 r[kItems][kVecs];
-  __device__ __forceinline__ static void item(int u, int& t, int& c0) {
-    const int v = threadIdx.x + 256 * u;
+  __device__ __forceinline__ static void item(int tx, int u, int& t, int& c0) {
+    const int v = tx + 256 * u;
     if (ROWS) {
       t = v / (W / 8);
       c0 = 8 * (v % (W / 8));
@@ -280,22 +286,22 @@ struct Staged {
       c0 = 8 * (v / kSsdChunk);
     }
   }
-  __device__ __forceinline__ void load(const ActT* src, int64_t stride, int n) {
+  __device__ __forceinline__ void load(const ActT* src, int64_t stride, int n, int tx) {
 #pragma unroll
     for (int u = 0; u < kItems; ++u) {
       int t, c0;
-      item(u, t, c0);
+      item(tx, u, t, c0);
 #pragma unroll
       for (int w = 0; w < kVecs; ++w)
         r[u][w] = t < n ? *reinterpret_cast<const uint4*>(src + (int64_t)t * stride + c0 + w * Elem<ActT>::kVec)
                         : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  __device__ __forceinline__ void store(_Float16* hi, _Float16* lo) const {
+  __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, int tx) const {
 #pragma unroll
     for (int u = 0; u < kItems; ++u) {
       int t, c0;
-      item(u, t, c0);
+      item(tx, u, t, c0);
       float x[8];
 #pragma unroll
       for (int w = 0; w < kVecs; ++w) Elem<ActT>::unpack(r[u][w], x + w * Elem<ActT>::kVec);
@@ -316,9 +322,9 @@ struct Staged {
   }
 };
 
-// Wave 0: the chunk's steps dt_j and cumulative log-decays L_i = sum_{j<=i}
-// A dt_j (f64 scan; tokens past n have dt = 0).  Returns L_i and dt_i of
-// lane i and L_C through lc.
+// One wave: the chunk's steps dt_j and cumulative log-decays L_i =
+// sum_{j<=i} A dt_j (f64 scan; tokens past n have dt = 0).  Returns L_i and
+// dt_i of lane i and L_C through lc.
 template <typename ActT>
 __device__ __forceinline__ double chunk_log_decay(const Mamba2Params& p, int64_t t0, int n, int h, int lane, float& d,
                                                   double& lc) {
@@ -334,72 +340,117 @@ __device__ __forceinline__ double chunk_log_decay(const Mamba2Params& p, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Prefill pass 1, per (chunk, head): the chunk's state contribution
-//   St[p][n] = sum_j exp(L_C - L_j) dt_j x_j[p] B_j[n]
-// computed as St^T = B^T (w X) on the MFMA, and exp(L_C).
+// Prefill pass 1, per (pair of consecutive chunks of a sequence, head): the
+// contribution of each chunk to the state after it,
+//   St[p][n] = sum_j exp(L_C - L_j) dt_j x_j[p] B_j[n],
+// computed as St^T = B^T (w X) on the MFMA, and the pair's
+//   St_pair = exp(L_C') St + St'   (' marks the second chunk).
+// The state pass then steps from pair to pair, and the output kernel of a
+// pair's second chunk forms the state entering it, exp(L_C) S0 + St, from
+// the pair's entering state S0 and the first chunk's St, which this kernel
+// leaves in the second chunk's block.  Pairs start at even chunk offsets
+// within a sequence; the last chunk of a sequence with an odd chunk count
+// is a pair of one.  Each half of the workgroup loads one chunk; the first
+// is staged, its tiles formed, then the second staged over it.  The
+// workgroup of a pair's second chunk has nothing to do.  The grid is one
+// dimensional, head fastest: workgroups are dealt to the XCDs in turn, so
+// with the chunk fastest every busy workgroup would land on every other XCD.
+// With H a multiple of 8 the heads are permuted so that one XCD takes whole
+// groups of heads, which share B.
 // ---------------------------------------------------------------------------
+// Three workgroups of eight waves per CU where 80 registers suffice (16-bit
+// activations up to P * N = 64 * 128); the other shapes take what they need.
 template <typename ActT, int P, int N>
-__global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws) {
+constexpr int kSsdStateWaves = (!std::is_same<ActT, float>::value && P * N <= 64 * 128) ? 6 : 1;
+
+template <typename ActT, int P, int N>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWaves<ActT, P, N>))) void ssd_state_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
-  constexpr int PT = P / 16, NT = N / 16, PER_WAVE = PT * NT / 4;
+  constexpr int PT = P / 16, NT = N / 16, TILES = PT * NT, TPW = (TILES + 7) / 8;
   __shared__ __attribute__((aligned(16))) _Float16 BTh[N * kTS], XTh[P * kTS];
   __shared__ __attribute__((aligned(16))) _Float16 BTl[SPLIT ? N * kTS : 8], XTl[SPLIT ? P * kTS : 8];
-  __shared__ __attribute__((aligned(16))) float ws_[kSsdChunk];
+  __shared__ __attribute__((aligned(16))) float ws_[2][kSsdChunk];
+  __shared__ double lc_s[2];
+  __shared__ float elc_s[2];
 
-  const int cid = blockIdx.x, h = blockIdx.y;
-  const int g = h / (p.H / p.G);
+  const int hx = (int)(blockIdx.x % (unsigned)p.H), cid = (int)(blockIdx.x / (unsigned)p.H);
+  const int h = p.H % 8 == 0 ? (hx % 8) * (p.H / 8) + hx / 8 : hx;
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
+  const int c_first = ws.single ? 0 : ws.seq_chunk_off[seq];
+  if ((cid - c_first) & 1) return;  // the second chunk of a pair: its first chunk's workgroup does it
+  const int c_end = ws.single ? (int)p.num_chunks : ws.seq_chunk_off[seq + 1];
+  const bool two = cid + 1 < c_end;
+  const int g = h / (p.H / p.G);
   const int64_t t0 = ws.single ? (int64_t)kSsdChunk * cid : ws.chunk_start[cid];
-  const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  char* blk = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
-  float* Stg = reinterpret_cast<float*>(blk);
+  const int tid = threadIdx.x, half = tid >> 8, ht = tid & 255, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  // half k loads chunk cid + k (nothing for the second half of a pair of one)
+  const int64_t tk = t0 + (int64_t)kSsdChunk * half;
+  const int nk = (half == 0 || two) ? (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - tk) : 0;
+  const int64_t bb = ssd_blk_bytes(P, N);
+  char* blk = ws.blocks + ((int64_t)cid * p.H + h) * bb;
+  char* blk2 = blk + (int64_t)p.H * bb;  // the second chunk's block (same head)
 
-  {
-    Staged<ActT, N, false> bt;
-    Staged<ActT, P, false> xt;
-    bt.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
-    xt.load(static_cast<const ActT*>(p.x) + (t0 * p.H + h) * P, (int64_t)p.H * P, n);
-    bt.store(BTh, BTl);
-    xt.store(XTh, XTl);
+  // both chunks' loads first; the second chunk is staged once the first is
+  // done with
+  Staged<ActT, N, false> bt;
+  Staged<ActT, P, false> xt;
+  bt.load(static_cast<const ActT*>(p.B) + (tk * p.G + g) * N, (int64_t)p.G * N, nk, ht);
+  xt.load(static_cast<const ActT*>(p.x) + (tk * p.H + h) * P, (int64_t)p.H * P, nk, ht);
+  if ((wave & 3) == 0 && nk > 0) {  // the first wave of each half with a chunk
+    float dec_dt;
+    double dec_lc;
+    const double dec_L = chunk_log_decay<ActT>(p, tk, nk, h, lane, dec_dt, dec_lc);
+    ws_[half][lane] = dec_dt * (float)exp(dec_lc - dec_L);
+    const float elc = (float)exp(dec_lc);
+    if (lane == 0) {
+      lc_s[half] = dec_lc;
+      elc_s[half] = elc;
+    }
+    // each chunk's decay vector, which the output kernel reads instead of
+    // forming it again (the first chunk's also holds the pair's
+    // exp(L_C + L_C'), written below)
+    char* vec = (half ? blk2 : blk) + ssd_blk_vec(P, N);
+    if (lane == 0) reinterpret_cast<float*>(vec)[0] = elc;
+    reinterpret_cast<float*>(vec + kVecDt)[lane] = dec_dt;
+    reinterpret_cast<float*>(vec + kVecEL)[lane] = (float)exp(dec_L);
+    reinterpret_cast<double*>(vec + kVecL)[lane] = dec_L;
   }
-  float dec_dt = 0.0f;
-  double dec_L = 0.0, dec_lc = 0.0;
-  if (wave == 0) {
-    dec_L = chunk_log_decay<ActT>(p, t0, n, h, lane, dec_dt, dec_lc);
-    ws_[lane] = dec_dt * (float)exp(dec_lc - dec_L);
+  if (half == 0) {
+    bt.store(BTh, BTl, ht);
+    xt.store(XTh, XTl, ht);
   }
   __syncthreads();
 
-  // tiles in pt-major order, PER_WAVE consecutive tiles to a wave
-  int cur_pt = -1;
+  if (tid == 0)
+    reinterpret_cast<float*>(blk + ssd_blk_vec(P, N))[1] = (float)exp(lc_s[0] + (two ? lc_s[1] : 0.0));
+  // tiles in pt-major order, TPW consecutive tiles to a wave
+  const float e2 = two ? elc_s[1] : 1.0f;  // exp(L_C') scales the first chunk's St
+  float* Stg = reinterpret_cast<float*>(blk);
   h8 bh[2], bl[2];
-#pragma unroll 1
-  for (int q = 0; q < PER_WAVE; ++q) {
-    const int tile = wave * PER_WAVE + q;
-    const int pt = tile / NT, nt = tile % NT;
-    if (pt != cur_pt) {  // B operand (w X)[j][p]: column p = 16 pt + li, rows j = 32 s + 8 lg ..
-      cur_pt = pt;
+  // B operand (w X)[j][p] of chunk k: column p = 16 pt + li, rows j = 32 s + 8 lg ..
+  auto operand = [&](int k, int pt) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int j0 = 32 * s + 8 * lg;
-        const h8 xh = ld_h8(XTh + (16 * pt + li) * kTS + j0);
-        h8 xl;
-        if constexpr (SPLIT) xl = ld_h8(XTl + (16 * pt + li) * kTS + j0);
-        const float4 w0 = *reinterpret_cast<const float4*>(ws_ + j0);
-        const float4 w1 = *reinterpret_cast<const float4*>(ws_ + j0 + 4);
-        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float v[8];
+    for (int s = 0; s < 2; ++s) {
+      const int j0 = 32 * s + 8 * lg;
+      const h8 xh = ld_h8(XTh + (16 * pt + li) * kTS + j0);
+      h8 xl;
+      if constexpr (SPLIT) xl = ld_h8(XTl + (16 * pt + li) * kTS + j0);
+      const float4 w0 = *reinterpret_cast<const float4*>(&ws_[k][j0]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&ws_[k][j0 + 4]);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float xv = (float)xh[e];
-          if constexpr (SPLIT) xv += (float)xl[e];
-          v[e] = xv * w[e];
-        }
-        split8(v, bh[s], bl[s]);
+      for (int e = 0; e < 8; ++e) {
+        float xv = (float)xh[e];
+        if constexpr (SPLIT) xv += (float)xl[e];
+        v[e] = xv * w[e];
       }
+      split8(v, bh[s], bl[s]);
     }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  // D[4lg + r][li] = St^T[n = 16 nt + 4lg + r][p = 16 pt + li]
+  auto product = [&](int nt, f32x4 acc) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // A operand B^T[n][j]: row n = 16 nt + li
@@ -408,25 +459,70 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(Mamba2Params p, SsdWs ws
       acc = mfma_f16(ah, bl[s], acc);
       if constexpr (SPLIT) acc = mfma_f16(ld_h8(BTl + (16 * nt + li) * kTS + 32 * s + 8 * lg), bh[s], acc);
     }
-    // D[4lg + r][li] = St^T[n = 16 nt + 4lg + r][p = 16 pt + li]
-    *reinterpret_cast<float4*>(Stg + (int64_t)(16 * pt + li) * N + 16 * nt + 4 * lg) =
-        make_float4(acc[0], acc[1], acc[2], acc[3]);
+    return acc;
+  };
+  auto offset = [&](int pt, int nt) { return (int64_t)(16 * pt + li) * N + 16 * nt + 4 * lg; };
+
+  // the first chunk's St: the pair's St_pair for a pair of one, else kept
+  // (scaled by exp(L_C')) for the second chunk's products and stored for
+  // the second chunk's entering state (f32 with f32 activations, else f16
+  // in the entering-state slot)
+  f32x4 acc1[TPW];
+  int cur_pt = -1;
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int tile = wave * TPW + q;
+    if (tile >= TILES) break;  // wave-uniform
+    const int pt = tile / NT, nt = tile % NT;
+    if (pt != cur_pt) {
+      cur_pt = pt;
+      operand(0, pt);
+    }
+    f32x4 acc = product(nt, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+    const int64_t o = offset(pt, nt);
+    if (!two) {
+      *reinterpret_cast<float4*>(Stg + o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      continue;
+    }
+    if constexpr (SPLIT) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk2) + o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(blk2 + ssd_blk_s0h(P, N)) + o) =
+          make_uint2((uint32_t)f32_to_f16(acc[0]) | ((uint32_t)f32_to_f16(acc[1]) << 16),
+                     (uint32_t)f32_to_f16(acc[2]) | ((uint32_t)f32_to_f16(acc[3]) << 16));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc1[q][r] = acc[r] * e2;
   }
-  if (wave == 0) {
-    // the decay vector, which the output kernel reads instead of forming it again
-    char* vec = blk + ssd_blk_vec(P, N);
-    if (lane == 0) reinterpret_cast<float*>(vec)[0] = (float)exp(dec_lc);
-    reinterpret_cast<float*>(vec + kVecDt)[lane] = dec_dt;
-    reinterpret_cast<float*>(vec + kVecEL)[lane] = (float)exp(dec_L);
-    reinterpret_cast<double*>(vec + kVecL)[lane] = dec_L;
+  if (two) {
+    __syncthreads();  // the first chunk's tiles are done with
+    if (half == 1) {
+      bt.store(BTh, BTl, ht);
+      xt.store(XTh, XTl, ht);
+    }
+    __syncthreads();
+    cur_pt = -1;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int tile = wave * TPW + q;
+      if (tile >= TILES) break;
+      const int pt = tile / NT, nt = tile % NT;
+      if (pt != cur_pt) {
+        cur_pt = pt;
+        operand(1, pt);
+      }
+      const f32x4 acc = product(nt, acc1[q]);
+      *reinterpret_cast<float4*>(Stg + offset(pt, nt)) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Prefill pass 2, element-wise over (sequence, head, 4 state entries): carry
-// S through the sequence's chunks, S <- exp(L_C) S + St, leaving in each
-// block the state that enters its chunk (f32 in place with f32 activations,
-// else the f16 copy); the final S goes to the pool.
+// S through the sequence's chunk pairs, S <- exp(L_C + L_C') S + St_pair,
+// leaving in each pair's first block the state that enters the pair (f32 in
+// place with f32 activations, else the f16 copy); the final S goes to the
+// pool.
 // ---------------------------------------------------------------------------
 constexpr int kPassAhead = 4;
 
@@ -445,21 +541,21 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
   const int c_end = ws.single ? (int)((p.T + kSsdChunk - 1) / kSsdChunk) : ws.seq_chunk_off[s_idx + 1];
   const int64_t bb = ssd_blk_bytes(p.P, p.N), vo = ssd_blk_vec(p.P, p.N), ho = ssd_blk_s0h(p.P, p.N);
   const bool f16_s0 = p.act != GDN_F32;
-  for (int c = c_begin; c < c_end; c += kPassAhead) {
+  for (int c = c_begin; c < c_end; c += 2 * kPassAhead) {
     float4 v[kPassAhead];
     float eL[kPassAhead];
 #pragma unroll
     for (int u = 0; u < kPassAhead; ++u) {
-      if (c + u < c_end) {
-        const char* blk = ws.blocks + ((int64_t)(c + u) * p.H + h) * bb;
+      if (c + 2 * u < c_end) {
+        const char* blk = ws.blocks + ((int64_t)(c + 2 * u) * p.H + h) * bb;
         v[u] = *reinterpret_cast<const float4*>(blk + e0 * 4);
-        eL[u] = *reinterpret_cast<const float*>(blk + vo);
+        eL[u] = reinterpret_cast<const float*>(blk + vo)[1];
       }
     }
 #pragma unroll
     for (int u = 0; u < kPassAhead; ++u) {
-      if (c + u < c_end) {
-        char* blk = ws.blocks + ((int64_t)(c + u) * p.H + h) * bb;
+      if (c + 2 * u < c_end) {
+        char* blk = ws.blocks + ((int64_t)(c + 2 * u) * p.H + h) * bb;
         if (f16_s0) {
           const uint2 w = make_uint2((uint32_t)f32_to_f16(S[0]) | ((uint32_t)f32_to_f16(S[1]) << 16),
                                      (uint32_t)f32_to_f16(S[2]) | ((uint32_t)f32_to_f16(S[3]) << 16));
@@ -480,8 +576,10 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
 // ---------------------------------------------------------------------------
 // Prefill pass 3, per (chunk, head): outputs
 //   Y = (M * C B^T) X + diag(exp(L)) C S0^T,  y = (Y + D x) silu(z)
-// with S0 the state entering the chunk.  C and B are staged row-major (the
-// k index of both products is n), X transposed (k = token).
+// with S0 the state entering the chunk: the pair's entering state for the
+// first chunk of a pair, exp(L_C) S0 + St of the first chunk for the second.
+// C and B are staged row-major (the k index of both products is n), X
+// transposed (k = token).
 // ---------------------------------------------------------------------------
 template <int P, int N, bool SPLIT>
 struct SsdOutLds {
@@ -539,8 +637,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   const char* blk0 = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
-  const float* S0 = reinterpret_cast<const float*>(blk0);
-  const _Float16* S0h = reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N));
+  // the second chunk of a pair takes the pair's entering state from the
+  // first chunk's block and the first chunk's St from its own
+  const int c_first = ws.single ? 0 : ws.seq_chunk_off[seq];
+  const bool second = ((cid - c_first) & 1) != 0;
+  const char* blkS = second ? blk0 - (int64_t)p.H * ssd_blk_bytes(P, N) : blk0;
+  const float* S0 = reinterpret_cast<const float*>(blkS);
+  const _Float16* S0h = reinterpret_cast<const _Float16*>(blkS + ssd_blk_s0h(P, N));
+  const float* St1 = reinterpret_cast<const float*>(blk0);
+  const _Float16* St1h = reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N));
+  const float e1 = second ? reinterpret_cast<const float*>(blkS + ssd_blk_vec(P, N))[0] : 0.0f;  // exp(L_C), first chunk
 
   // the chunk's decay vector, written by the state kernel (wave 0 puts it in LDS)
   double dec_L = 0.0;
@@ -556,27 +662,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   // (f32 activations: f32, split below; else the f16 copy)
   const bool has_cols = 16 * wave < P;
   float sv[SPLIT ? NPT : 1][SPLIT ? NK : 1][8];
-  h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
+  h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK], sth[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
   if (has_cols) {
 #pragma unroll
     for (int q = 0; q < NPT; ++q)
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
+        const int64_t o = (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
         if constexpr (SPLIT) {
-          const float* sp = S0 + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
-          const float4 a = *reinterpret_cast<const float4*>(sp);
-          const float4 b = *reinterpret_cast<const float4*>(sp + 4);
+          const float4 a = *reinterpret_cast<const float4*>(S0 + o);
+          const float4 b = *reinterpret_cast<const float4*>(S0 + o + 4);
           sv[q][s][0] = a.x; sv[q][s][1] = a.y; sv[q][s][2] = a.z; sv[q][s][3] = a.w;
           sv[q][s][4] = b.x; sv[q][s][5] = b.y; sv[q][s][6] = b.z; sv[q][s][7] = b.w;
+          if (second) {
+            const float4 c = *reinterpret_cast<const float4*>(St1 + o);
+            const float4 d = *reinterpret_cast<const float4*>(St1 + o + 4);
+            const float t[8] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[q][s][e] = e1 * sv[q][s][e] + t[e];
+          }
         } else {
-          svh[q][s] = ld_h8(S0h + (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg);
+          svh[q][s] = ld_h8(S0h + o);
+          if (second) sth[q][s] = ld_h8(St1h + o);
         }
       }
   }
 
   Staged<ActT, N, true> crow, brow;
-  crow.load(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
-  brow.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n);
+  crow.load(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
+  brow.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
   // the chunk's x rows, held in registers until C is done with and X^T goes
   // over it (item (token, 8 consecutive p), token fastest; rows past n zero)
   constexpr int XIT = kSsdChunk * (P / 8) / 256;
@@ -613,8 +727,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       }
     }
   }
-  crow.store(Ch, Cl);
-  brow.store(Bh, Bl);
+  crow.store(Ch, Cl, tid);
+  brow.store(Bh, Bl, tid);
   if (wave == 0) {
     Ls[lane] = dec_L;
     dts[lane] = dec_dt;
@@ -649,10 +763,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       h8 sh[NK], sl[NK];
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        if constexpr (SPLIT)
+        if constexpr (SPLIT) {
           split8(sv[q][s], sh[s], sl[s]);
-        else
+        } else if (second) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sh[s][e] = (_Float16)(e1 * (float)svh[q][s][e] + (float)sth[q][s][e]);
+        } else {
           sh[s] = svh[q][s];
+        }
       }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -795,7 +913,7 @@ template <typename ActT, int P, int N>
 hipError_t launch_chunked_pn(const Mamba2Params& p, const SsdWs& ws, hipStream_t stream) {
   if (p.num_chunks > 0) {
     const dim3 grid((unsigned)p.num_chunks, p.H);
-    ssd_state_kernel<ActT, P, N><<<grid, 256, 0, stream>>>(p, ws);
+    ssd_state_kernel<ActT, P, N><<<dim3((unsigned)(p.num_chunks * p.H)), 512, 0, stream>>>(p, ws);
     switch (p.state) {
       case GDN_F32: ssd_pass_kernel<float><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
       case GDN_BF16: ssd_pass_kernel<bf16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
