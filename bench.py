@@ -647,7 +647,13 @@ def mamba2(torch, gdn, reps=20):
         if chunked:
             fl = mamba2_prefill_flops(T, H, P, N)
             nb = mamba2_prefill_bytes(T, H, P, G, N)
-            ws_b = 2 * gdn.gdn_mamba2_workspace_size(H, P, N, len(sl_h), T, G)
+            # workspace traffic of one sequence: per (chunk pair, head) the
+            # pair's f32 contribution written and read, the first chunk's f16
+            # contribution written and read, the pair's f16 entering state
+            # written and read twice, and each chunk's decay vector written
+            # and read
+            npairs = ((T + 127) // 128) * H
+            ws_b = npairs * (2 * P * N * 4 + 2 * P * N * 2 + 3 * P * N * 2 + 2 * 2 * 1280)
             rl = {"bound": "hbm", "achieved": nb / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": nb / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nb,
                   "workspace_bytes_per_launch": ws_b, "flops_per_launch": fl,
