@@ -574,12 +574,15 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
 }
 
 // ---------------------------------------------------------------------------
-// Prefill pass 3, per (chunk, head): outputs
+// Prefill pass 3, per (chunk, group of heads that share B and C): outputs
 //   Y = (M * C B^T) X + diag(exp(L)) C S0^T,  y = (Y + D x) silu(z)
 // with S0 the state entering the chunk: the pair's entering state for the
 // first chunk of a pair, exp(L_C) S0 + St of the first chunk for the second.
-// C and B are staged row-major (the k index of both products is n), X
-// transposed (k = token).
+// C B^T does not depend on the head: the workgroup stages C and B once,
+// keeps C B^T in registers and C in LDS, and walks the group's heads; each
+// head's loads are issued while the head before it is formed.  C and B are
+// staged row-major (the k index of both products is n), X transposed
+// (k = token).
 // ---------------------------------------------------------------------------
 template <int P, int N, bool SPLIT>
 struct SsdOutLds {
@@ -589,26 +592,28 @@ struct SsdOutLds {
   static constexpr int kRowHalves = kSsdChunk * RS;
   static constexpr int kXHalves = P * kTS;
   static constexpr int kParts = SPLIT ? 2 : 1;
-  static constexpr int kC = kRowHalves * kParts * 2;    // C (hi, lo) at 0, B (hi, lo) after it
-  static constexpr int kMBytes = kSsdChunk * MS * 4;    // M, over B once C B^T is in registers
-  static constexpr int kYBytes = kSsdChunk * YS * 4;    // Y, over everything above at the end
-  static constexpr int kU0 = 2 * kC > kC + kMBytes ? 2 * kC : kC + kMBytes;
-  static constexpr int kUnion = kU0 > kYBytes ? kU0 : kYBytes;
-  // X^T (hi, lo), written once C S0^T is formed: over C where it fits, else
-  // after the union
-  static constexpr bool kXOverC = kXHalves * kParts * 2 <= kC;
-  static constexpr int kX = kXOverC ? 0 : kUnion;
-  static constexpr int kL = kXOverC ? kUnion : kUnion + kXHalves * kParts * 2;  // double L[64]
+  static constexpr int kRowsBytes = kRowHalves * kParts * 2;
+  static constexpr int kMBytes = kSsdChunk * MS * 4;
+  static constexpr int kYBytes = kSsdChunk * YS * 4;
+  // C (hi, lo) at 0 for the whole workgroup; then B (hi, lo), which M goes
+  // over once C B^T is in registers, and each head's Y over its M
+  static constexpr int kU = kRowsBytes;
+  static constexpr int kUBytes = kRowsBytes > kMBytes ? (kRowsBytes > kYBytes ? kRowsBytes : kYBytes)
+                                                      : (kMBytes > kYBytes ? kMBytes : kYBytes);
+  static constexpr int kX = kU + kUBytes;                    // X^T (hi, lo) of the current head
+  static constexpr int kL = kX + kXHalves * kParts * 2;      // double L[64]
   static constexpr int kDt = kL + kSsdChunk * 8;
   static constexpr int kE = kDt + kSsdChunk * 4;
-  static constexpr int kBytes = kE + kSsdChunk * 4;
+  static constexpr int kD = kE + kSsdChunk * 4;              // the head's D per column
+  static constexpr int kBytes = kD + P * 4;
 };
 
-// Four workgroups per CU where the register budget of 128 allows it (bf16
-// activations with P <= 64, f32 with P = 32 and N <= 64); the other shapes
-// need more registers and take what they need.
+// Two workgroups per CU (one per (chunk, group) fills the chip twice at the
+// usual shapes) where 256 registers hold two heads' loads (16-bit
+// activations with P <= 64); the other shapes hold one head's loads and take
+// the registers they need.
 template <typename ActT, int P, int N>
-constexpr int kSsdOutWaves = (std::is_same<ActT, float>::value ? (P == 32 && N <= 64) : (P <= 64)) ? 4 : 1;
+constexpr int kSsdOutWaves = (!std::is_same<ActT, float>::value && P <= 64) ? 2 : 1;
 
 template <typename ActT, int P, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWaves<ActT, P, N>))) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
@@ -620,123 +625,135 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   __shared__ __attribute__((aligned(16))) char smem[Lay::kBytes];
   _Float16* Ch = reinterpret_cast<_Float16*>(smem);
   _Float16* Cl = Ch + Lay::kRowHalves;   // f32 activations only
-  _Float16* Bh = reinterpret_cast<_Float16*>(smem + Lay::kC);
+  _Float16* Bh = reinterpret_cast<_Float16*>(smem + Lay::kU);
   _Float16* Bl = Bh + Lay::kRowHalves;
-  float* Ms = reinterpret_cast<float*>(smem + Lay::kC);  // over B
-  float* Ys = reinterpret_cast<float*>(smem);            // over C, B and M at the end
+  float* Ms = reinterpret_cast<float*>(smem + Lay::kU);  // over B
+  float* Ys = reinterpret_cast<float*>(smem + Lay::kU);  // over M
   _Float16* XTh = reinterpret_cast<_Float16*>(smem + Lay::kX);
   _Float16* XTl = XTh + Lay::kXHalves;
   double* Ls = reinterpret_cast<double*>(smem + Lay::kL);
   float* dts = reinterpret_cast<float*>(smem + Lay::kDt);
   float* eLs = reinterpret_cast<float*>(smem + Lay::kE);
+  float* Ds = reinterpret_cast<float*>(smem + Lay::kD);
 
-  const int cid = blockIdx.x, h = blockIdx.y;
-  const int g = h / (p.H / p.G);
+  const int cid = blockIdx.x, g = blockIdx.y;
+  const int hpg = p.H / p.G;  // heads per group
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
   const int64_t t0 = ws.single ? (int64_t)kSsdChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kSsdChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  const char* blk0 = ws.blocks + ((int64_t)cid * p.H + h) * ssd_blk_bytes(P, N);
+  const int64_t bb = ssd_blk_bytes(P, N);
   // the second chunk of a pair takes the pair's entering state from the
   // first chunk's block and the first chunk's St from its own
   const int c_first = ws.single ? 0 : ws.seq_chunk_off[seq];
   const bool second = ((cid - c_first) & 1) != 0;
-  const char* blkS = second ? blk0 - (int64_t)p.H * ssd_blk_bytes(P, N) : blk0;
-  const float* S0 = reinterpret_cast<const float*>(blkS);
-  const _Float16* S0h = reinterpret_cast<const _Float16*>(blkS + ssd_blk_s0h(P, N));
-  const float* St1 = reinterpret_cast<const float*>(blk0);
-  const _Float16* St1h = reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N));
-  const float e1 = second ? reinterpret_cast<const float*>(blkS + ssd_blk_vec(P, N))[0] : 0.0f;  // exp(L_C), first chunk
+  auto block = [&](int h) { return ws.blocks + ((int64_t)cid * p.H + h) * bb; };
+  const bool has_cols = 16 * wave < P;  // the wave's column tiles pt = wave + 4 q (P = 32: waves 2, 3 have none)
 
-  // the chunk's decay vector, written by the state kernel (wave 0 puts it in LDS)
-  double dec_L = 0.0;
-  float dec_dt = 0.0f, dec_eL = 0.0f;
-  if (wave == 0) {
-    const char* vec = blk0 + ssd_blk_vec(P, N);
-    dec_L = reinterpret_cast<const double*>(vec + kVecL)[lane];
-    dec_dt = reinterpret_cast<const float*>(vec + kVecDt)[lane];
-    dec_eL = reinterpret_cast<const float*>(vec + kVecEL)[lane];
-  }
-  // the wave's column tiles pt = wave + 4 q (P = 32: waves 2, 3 have none);
-  // their S0 rows as the B operand S0^T[n][p], loaded before the staging
-  // (f32 activations: f32, split below; else the f16 copy)
-  const bool has_cols = 16 * wave < P;
-  float sv[SPLIT ? NPT : 1][SPLIT ? NK : 1][8];
-  h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK], sth[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
-  if (has_cols) {
-#pragma unroll
-    for (int q = 0; q < NPT; ++q)
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const int64_t o = (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
-        if constexpr (SPLIT) {
-          const float4 a = *reinterpret_cast<const float4*>(S0 + o);
-          const float4 b = *reinterpret_cast<const float4*>(S0 + o + 4);
-          sv[q][s][0] = a.x; sv[q][s][1] = a.y; sv[q][s][2] = a.z; sv[q][s][3] = a.w;
-          sv[q][s][4] = b.x; sv[q][s][5] = b.y; sv[q][s][6] = b.z; sv[q][s][7] = b.w;
-          if (second) {
-            const float4 c = *reinterpret_cast<const float4*>(St1 + o);
-            const float4 d = *reinterpret_cast<const float4*>(St1 + o + 4);
-            const float t[8] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sv[q][s][e] = e1 * sv[q][s][e] + t[e];
-          }
-        } else {
-          svh[q][s] = ld_h8(S0h + o);
-          if (second) sth[q][s] = ld_h8(St1h + o);
-        }
-      }
-  }
-
-  Staged<ActT, N, true> crow, brow;
-  crow.load(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
-  brow.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
-  // the chunk's x rows, held in registers until C is done with and X^T goes
-  // over it (item (token, 8 consecutive p), token fastest; rows past n zero)
+  // per head, loaded while the head before it is formed (two register sets,
+  // used in turn): the wave's S0 rows as the B operand S0^T[n][p] (f32
+  // activations: f32, with a pair's second chunk's exp(L_C) S0 + St formed
+  // as they arrive, split where used; else the f16 copy, and for a pair's
+  // second chunk the first chunk's St); the chunk's x rows (item (token,
+  // 8 consecutive p), token fastest; rows past n zero); the epilogue's x and
+  // z (8 consecutive p of one token per item, kept packed); the decay
+  // vector the state kernel wrote (wave 0), the head's D (thread p holds
+  // column p's) and for a second chunk the first chunk's exp(L_C)
   constexpr int XIT = kSsdChunk * (P / 8) / 256;
   static_assert(XIT >= 1 && kSsdChunk * (P / 8) % 256 == 0, "x staging items");
   constexpr int XNV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
-  uint4 xs[XIT][XNV];
+  constexpr int EPI = (kSsdChunk * (P / 8) + 255) / 256;
+  constexpr int NV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
+  struct HeadRegs {
+    float sv[SPLIT ? NPT : 1][SPLIT ? NK : 1][8];
+    h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK], sth[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
+    uint4 xs[XIT][XNV];
+    uint4 xr[EPI][NV], zr[EPI][NV];
+    double dec_L;
+    float dec_dt, dec_eL, e1, d;
+  };
+  const ActT* xg = static_cast<const ActT*>(p.x);
+  const ActT* zg = static_cast<const ActT*>(p.z);
+  // per-thread element offsets of head 0 (a head adds h * P): the x rows
+  // staged as X^T and the epilogue's items; rows past n re-read row n - 1
+  // (their X^T columns meet zero rows of M, their outputs are not stored)
+  int64_t xs_off[XIT], epi_off[EPI];
 #pragma unroll
   for (int u = 0; u < XIT; ++u) {
     const int v = tid + 256 * u;
     const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
-#pragma unroll
-    for (int w = 0; w < XNV; ++w)
-      xs[u][w] = t < n ? ld16(static_cast<const ActT*>(p.x) + ((t0 + t) * p.H + h) * P + c0 + w * Elem<ActT>::kVec)
-                       : make_uint4(0u, 0u, 0u, 0u);
+    xs_off[u] = (t0 + min(t, n - 1)) * p.H * P + c0;
   }
-
-  // the epilogue's x and z (8 consecutive p of one token per item), loaded
-  // now and kept packed so that their latency overlaps the products
-  constexpr int EPI = (kSsdChunk * (P / 8) + 255) / 256;
-  constexpr int NV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
-  const ActT* xg = static_cast<const ActT*>(p.x);
-  const ActT* zg = static_cast<const ActT*>(p.z);
-  uint4 xr[EPI][NV], zr[EPI][NV];
 #pragma unroll
   for (int u = 0; u < EPI; ++u) {
-    const int v = tid + 256 * u;
+    const int v = min(tid + 256 * u, kSsdChunk * (P / 8) - 1);
     const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
-    if (v < kSsdChunk * (P / 8) && i < n) {
-      const int64_t off = ((t0 + i) * p.H + h) * P + p0;
+    epi_off[u] = (t0 + min(i, n - 1)) * p.H * P + p0;
+  }
+  auto load_head = [&](HeadRegs& R, int h) __attribute__((always_inline)) {
+    const char* blk0 = block(h);
+    const char* blkS = second ? blk0 - (int64_t)p.H * bb : blk0;
+    R.e1 = second ? reinterpret_cast<const float*>(blkS + ssd_blk_vec(P, N))[0] : 0.0f;
+    if (has_cols) {
+#pragma unroll
+      for (int q = 0; q < NPT; ++q)
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const int64_t o = (int64_t)(16 * (wave + 4 * q) + li) * N + 32 * s + 8 * lg;
+          if constexpr (SPLIT) {
+            const float* S0 = reinterpret_cast<const float*>(blkS);
+            const float* St1 = reinterpret_cast<const float*>(blk0);
+            const float4 a = *reinterpret_cast<const float4*>(S0 + o);
+            const float4 b = *reinterpret_cast<const float4*>(S0 + o + 4);
+            float* sv = R.sv[q][s];
+            sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
+            sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
+            if (second) {
+              const float4 c = *reinterpret_cast<const float4*>(St1 + o);
+              const float4 d = *reinterpret_cast<const float4*>(St1 + o + 4);
+              const float t[8] = {c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sv[e] = R.e1 * sv[e] + t[e];
+            }
+          } else {
+            R.svh[q][s] = ld_h8(reinterpret_cast<const _Float16*>(blkS + ssd_blk_s0h(P, N)) + o);
+            if (second) R.sth[q][s] = ld_h8(reinterpret_cast<const _Float16*>(blk0 + ssd_blk_s0h(P, N)) + o);
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < XIT; ++u)
+#pragma unroll
+      for (int w = 0; w < XNV; ++w) R.xs[u][w] = ld16(xg + xs_off[u] + h * P + w * Elem<ActT>::kVec);
+    if (wave == 0) {
+      const char* vec = blk0 + ssd_blk_vec(P, N);
+      R.dec_L = reinterpret_cast<const double*>(vec + kVecL)[lane];
+      R.dec_dt = reinterpret_cast<const float*>(vec + kVecDt)[lane];
+      R.dec_eL = reinterpret_cast<const float*>(vec + kVecEL)[lane];
+    }
+    if (p.D && tid < P) R.d = p.D_per_p ? p.D[h * P + tid] : p.D[h];
+#pragma unroll
+    for (int u = 0; u < EPI; ++u)
 #pragma unroll
       for (int w = 0; w < NV; ++w) {
-        if (p.D) xr[u][w] = ld16(xg + off + w * Elem<ActT>::kVec);
-        if (zg) zr[u][w] = ld16(zg + off + w * Elem<ActT>::kVec);
+        if (p.D) R.xr[u][w] = ld16(xg + epi_off[u] + h * P + w * Elem<ActT>::kVec);
+        if (zg) R.zr[u][w] = ld16(zg + epi_off[u] + h * P + w * Elem<ActT>::kVec);
       }
-    }
-  }
-  crow.store(Ch, Cl, tid);
-  brow.store(Bh, Bl, tid);
-  if (wave == 0) {
-    Ls[lane] = dec_L;
-    dts[lane] = dec_dt;
-    eLs[lane] = dec_eL;
+  };
+
+  const int h_first = g * hpg;
+  HeadRegs RA, RB;
+  {
+    Staged<ActT, N, true> crow, brow;
+    crow.load(static_cast<const ActT*>(p.C) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
+    brow.load(static_cast<const ActT*>(p.B) + (t0 * p.G + g) * N, (int64_t)p.G * N, n, tid);
+    load_head(RA, h_first);
+    crow.store(Ch, Cl, tid);
+    brow.store(Bh, Bl, tid);
   }
   __syncthreads();
 
-  // M = (C B^T) masked and weighted; row block I = wave, column blocks J <= I
+  // C B^T, row block I = wave, column blocks J <= I, kept for every head
   f32x4 cb[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
@@ -754,141 +771,206 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       }
     }
   }
-  // C S0^T for the wave's column tiles, while C is staged (S0 leaves the
-  // registers here)
-  float cs[NPT][4][4];
-  if (has_cols) {
-#pragma unroll
-    for (int q = 0; q < NPT; ++q) {
-      h8 sh[NK], sl[NK];
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        if constexpr (SPLIT) {
-          split8(sv[q][s], sh[s], sl[s]);
-        } else if (second) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sh[s][e] = (_Float16)(e1 * (float)svh[q][s][e] + (float)sth[q][s][e]);
-        } else {
-          sh[s] = svh[q][s];
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          const int k0 = 32 * s + 8 * lg;
-          const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
-          acc2 = mfma_f16(ch, sh[s], acc2);
-          if constexpr (SPLIT) {
-            acc2 = mfma_f16(ch, sl[s], acc2);
-            acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cs[q][it][r] = acc2[r];
-      }
-    }
-  }
-  __syncthreads();  // B and C are done with; M goes over B, X^T over C
-#pragma unroll
-  for (int J = 0; J < 4; ++J)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * wave + 4 * lg + r, j = 16 * J + li;
-      Ms[i * MS + j] = (J <= wave && j <= i) ? cb[J][r] * expf((float)(Ls[i] - Ls[j])) * dts[j] : 0.0f;
-    }
-#pragma unroll
-  for (int u = 0; u < XIT; ++u) {
-    const int v = tid + 256 * u;
-    const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
-    float xv[8];
-#pragma unroll
-    for (int w = 0; w < XNV; ++w) Elem<ActT>::unpack(xs[u][w], xv + w * Elem<ActT>::kVec);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const _Float16 hx = (_Float16)xv[i];
-      XTh[(c0 + i) * kTS + t] = hx;
-      if constexpr (SPLIT) XTl[(c0 + i) * kTS + t] = (_Float16)(xv[i] - (float)hx);
-    }
-  }
-  __syncthreads();
+  __syncthreads();  // B is done with: each head's M and Y go over it
 
-  // Y[16 it + .., 16 pt + ..] = (M X) + exp(L_i) (C S0^T), pt = the wave's tiles
-  float yv[NPT][4][4];
-  if (has_cols) {
-#pragma unroll
-    for (int q = 0; q < NPT; ++q) {
-      const int pt = wave + 4 * q;
-      h8 xh[2], xl[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        xh[s] = ld_h8(XTh + (16 * pt + li) * kTS + 32 * s + 8 * lg);
-        if constexpr (SPLIT) xl[s] = ld_h8(XTl + (16 * pt + li) * kTS + 32 * s + 8 * lg);
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s > 16 * it + 15) break;
-          float m[8];
-#pragma unroll
-          for (int e4 = 0; e4 < 2; ++e4) {
-            const float4 v = *reinterpret_cast<const float4*>(Ms + (16 * it + li) * MS + 32 * s + 8 * lg + 4 * e4);
-            m[4 * e4] = v.x; m[4 * e4 + 1] = v.y; m[4 * e4 + 2] = v.z; m[4 * e4 + 3] = v.w;
-          }
-          h8 mh, ml;
-          split8(m, mh, ml);
-          acc = mfma_f16(mh, xh[s], acc);
-          acc = mfma_f16(ml, xh[s], acc);
-          if constexpr (SPLIT) acc = mfma_f16(mh, xl[s], acc);
-        }
-        const float4 ev = *reinterpret_cast<const float4*>(eLs + 16 * it + 4 * lg);
-        yv[q][it][0] = acc[0] + ev.x * cs[q][it][0];
-        yv[q][it][1] = acc[1] + ev.y * cs[q][it][1];
-        yv[q][it][2] = acc[2] + ev.z * cs[q][it][2];
-        yv[q][it][3] = acc[3] + ev.w * cs[q][it][3];
-      }
-    }
-  }
-  __syncthreads();  // M and X^T are done with; Y goes over them
-  if (has_cols) {
-#pragma unroll
-    for (int q = 0; q < NPT; ++q)
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ys[(16 * it + 4 * lg + r) * YS + 16 * (wave + 4 * q) + li] = yv[q][it][r];
-  }
-  __syncthreads();
-
-  // epilogue, 8 consecutive p of one token per item: + D x, * silu(z)
   ActT* og = static_cast<ActT*>(p.out);
+  auto process = [&](const HeadRegs& R, int h) __attribute__((always_inline)) {
+    // X^T and the decay vector of head h into LDS (columns past n hold row
+    // n - 1 again; M is zero there, as B is)
 #pragma unroll
-  for (int u = 0; u < EPI; ++u) {
-    const int v = tid + 256 * u;
-    const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
-    if (v >= kSsdChunk * (P / 8) || i >= n) continue;
-    const int64_t off = ((t0 + i) * p.H + h) * P + p0;
-    const float4 y0 = *reinterpret_cast<const float4*>(Ys + i * YS + p0);
-    const float4 y1 = *reinterpret_cast<const float4*>(Ys + i * YS + p0 + 4);
-    float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-    if (p.D) {
+    for (int u = 0; u < XIT; ++u) {
+      const int v = tid + 256 * u;
+      const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
       float xv[8];
 #pragma unroll
-      for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(xr[u][w], xv + w * Elem<ActT>::kVec);
+      for (int w = 0; w < XNV; ++w) Elem<ActT>::unpack(R.xs[u][w], xv + w * Elem<ActT>::kVec);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] += (p.D_per_p ? p.D[h * P + p0 + e] : p.D[h]) * xv[e];
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 hx = (_Float16)xv[i];
+        XTh[(c0 + i) * kTS + t] = hx;
+        if constexpr (SPLIT) XTl[(c0 + i) * kTS + t] = (_Float16)(xv[i] - (float)hx);
+      }
     }
-    if (zg) {
-      float zv[8];
-#pragma unroll
-      for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(zr[u][w], zv + w * Elem<ActT>::kVec);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] *= silu_f(zv[e]);
+    if (wave == 0) {
+      Ls[lane] = R.dec_L;
+      dts[lane] = R.dec_dt;
+      eLs[lane] = R.dec_eL;
     }
-    store_n<ActT, 8>(og + off, y);
+    if (p.D && tid < P) Ds[tid] = R.d;
+    // C S0^T for the wave's column tiles (C stays staged for every head)
+    float cs[NPT][4][4];
+    if (has_cols) {
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        h8 sh[NK], sl[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          if constexpr (SPLIT) {
+            split8(R.sv[q][s], sh[s], sl[s]);
+          } else if (second) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sh[s][e] = (_Float16)(R.e1 * (float)R.svh[q][s][e] + (float)R.sth[q][s][e]);
+          } else {
+            sh[s] = R.svh[q][s];
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          f32x4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < NK; ++s) {
+            const int k0 = 32 * s + 8 * lg;
+            const h8 ch = ld_h8(Ch + (16 * it + li) * RS + k0);
+            acc2 = mfma_f16(ch, sh[s], acc2);
+            if constexpr (SPLIT) {
+              acc2 = mfma_f16(ch, sl[s], acc2);
+              acc2 = mfma_f16(ld_h8(Cl + (16 * it + li) * RS + k0), sh[s], acc2);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cs[q][it][r] = acc2[r];
+        }
+      }
+    }
+    __syncthreads();  // X^T and the vector are in; the last head's Y is read
+
+    // exp(L_i) C S0^T, which seeds the accumulators of M X below
+    if (has_cols) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const float4 ev = *reinterpret_cast<const float4*>(eLs + 16 * it + 4 * lg);
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          cs[q][it][0] *= ev.x;
+          cs[q][it][1] *= ev.y;
+          cs[q][it][2] *= ev.z;
+          cs[q][it][3] *= ev.w;
+        }
+      }
+    }
+    // M = (C B^T) masked and weighted by head h's decays; the blocks above
+    // the diagonal are zero
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > wave) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ms[(16 * wave + 4 * lg + r) * MS + 16 * J + li] = 0.0f;
+        continue;
+      }
+      const int j = 16 * J + li;
+      const double Lj = Ls[j];
+      const float dj = dts[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * wave + 4 * lg + r;
+        const float mv = cb[J][r] * fast_exp((float)(Ls[i] - Lj)) * dj;
+        Ms[i * MS + j] = (J < wave || j <= i) ? mv : 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // Y[16 it + .., 16 pt + ..] = (M X) + exp(L_i) (C S0^T), pt = the wave's
+    // tiles, accumulated over the second term.  With 16-bit activations M
+    // enters as its f16 hi part alone: Y only feeds the 16-bit outputs
+    if (has_cols) {
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const int pt = wave + 4 * q;
+        h8 xh[2], xl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          xh[s] = ld_h8(XTh + (16 * pt + li) * kTS + 32 * s + 8 * lg);
+          if constexpr (SPLIT) xl[s] = ld_h8(XTl + (16 * pt + li) * kTS + 32 * s + 8 * lg);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          f32x4 acc = {cs[q][it][0], cs[q][it][1], cs[q][it][2], cs[q][it][3]};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if (32 * s > 16 * it + 15) break;
+            float m[8];
+#pragma unroll
+            for (int e4 = 0; e4 < 2; ++e4) {
+              const float4 v = *reinterpret_cast<const float4*>(Ms + (16 * it + li) * MS + 32 * s + 8 * lg + 4 * e4);
+              m[4 * e4] = v.x; m[4 * e4 + 1] = v.y; m[4 * e4 + 2] = v.z; m[4 * e4 + 3] = v.w;
+            }
+            h8 mh, ml;
+            if constexpr (SPLIT) {
+              split8(m, mh, ml);
+              acc = mfma_f16(mh, xh[s], acc);
+              acc = mfma_f16(ml, xh[s], acc);
+              acc = mfma_f16(mh, xl[s], acc);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) mh[e] = (_Float16)m[e];
+              acc = mfma_f16(mh, xh[s], acc);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cs[q][it][r] = acc[r];
+        }
+      }
+    }
+    __syncthreads();  // M and X^T are done with; Y goes over M
+    if (has_cols) {
+#pragma unroll
+      for (int q = 0; q < NPT; ++q)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ys[(16 * it + 4 * lg + r) * YS + 16 * (wave + 4 * q) + li] = cs[q][it][r];
+    }
+    __syncthreads();
+
+    // epilogue, 8 consecutive p of one token per item: + D x, * silu(z)
+#pragma unroll
+    for (int u = 0; u < EPI; ++u) {
+      const int v = tid + 256 * u;
+      const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
+      if (v >= kSsdChunk * (P / 8) || i >= n) continue;
+      const int64_t off = ((t0 + i) * p.H + h) * P + p0;
+      const float4 y0 = *reinterpret_cast<const float4*>(Ys + i * YS + p0);
+      const float4 y1 = *reinterpret_cast<const float4*>(Ys + i * YS + p0 + 4);
+      float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      if (p.D) {
+        float xv[8];
+#pragma unroll
+        for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(R.xr[u][w], xv + w * Elem<ActT>::kVec);
+        const float4 d0 = *reinterpret_cast<const float4*>(Ds + p0);
+        const float4 d1 = *reinterpret_cast<const float4*>(Ds + p0 + 4);
+        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] += dv[e] * xv[e];
+      }
+      if (zg) {
+        float zv[8];
+#pragma unroll
+        for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(R.zr[u][w], zv + w * Elem<ActT>::kVec);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= silu_f(zv[e]);
+      }
+      store_n<ActT, 8>(og + off, y);
+    }
+  };
+
+  if constexpr (kSsdOutWaves<ActT, P, N> > 1) {
+    // the heads in turn, two per trip, each trip's second head loaded while
+    // its first is formed and the next trip's first while its second is
+#pragma unroll 1
+    for (int k = 0; k < hpg; k += 2) {
+      if (k + 1 < hpg) load_head(RB, h_first + k + 1);
+      process(RA, h_first + k);
+      if (k + 1 >= hpg) break;
+      if (k + 2 < hpg) load_head(RA, h_first + k + 2);
+      process(RB, h_first + k + 1);
+    }
+  } else {
+    // wider shapes: one register set, each head loaded where it starts
+#pragma unroll 1
+    for (int k = 0; k < hpg; ++k) {
+      if (k > 0) load_head(RA, h_first + k);
+      process(RA, h_first + k);
+    }
   }
 }
 
@@ -919,7 +1001,7 @@ hipError_t launch_chunked_pn(const Mamba2Params& p, const SsdWs& ws, hipStream_t
       case GDN_BF16: ssd_pass_kernel<bf16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
       default: ssd_pass_kernel<f16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
     }
-    ssd_out_kernel<ActT, P, N><<<grid, 256, 0, stream>>>(p, ws);
+    ssd_out_kernel<ActT, P, N><<<dim3((unsigned)p.num_chunks, p.G), 256, 0, stream>>>(p, ws);
   }
   return hipGetLastError();
 }
