@@ -401,8 +401,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
     float dec_dt;
     double dec_lc;
     const double dec_L = chunk_log_decay<ActT>(p, tk, nk, h, lane, dec_dt, dec_lc);
-    ws_[half][lane] = dec_dt * (float)exp(dec_lc - dec_L);
-    const float elc = (float)exp(dec_lc);
+    // exponentials in f32 of the f64 log-decays and their differences
+    ws_[half][lane] = dec_dt * expf((float)(dec_lc - dec_L));
+    const float elc = expf((float)dec_lc);
     if (lane == 0) {
       lc_s[half] = dec_lc;
       elc_s[half] = elc;
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
     char* vec = (half ? blk2 : blk) + ssd_blk_vec(P, N);
     if (lane == 0) reinterpret_cast<float*>(vec)[0] = elc;
     reinterpret_cast<float*>(vec + kVecDt)[lane] = dec_dt;
-    reinterpret_cast<float*>(vec + kVecEL)[lane] = (float)exp(dec_L);
+    reinterpret_cast<float*>(vec + kVecEL)[lane] = expf((float)dec_L);
     reinterpret_cast<double*>(vec + kVecL)[lane] = dec_L;
   }
   if (half == 0) {
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
   __syncthreads();
 
   if (tid == 0)
-    reinterpret_cast<float*>(blk + ssd_blk_vec(P, N))[1] = (float)exp(lc_s[0] + (two ? lc_s[1] : 0.0));
+    reinterpret_cast<float*>(blk + ssd_blk_vec(P, N))[1] = expf((float)(lc_s[0] + (two ? lc_s[1] : 0.0)));
   // tiles in pt-major order, TPW consecutive tiles to a wave
   const float e2 = two ? elc_s[1] : 1.0f;  // exp(L_C') scales the first chunk's St
   float* Stg = reinterpret_cast<float*>(blk);
