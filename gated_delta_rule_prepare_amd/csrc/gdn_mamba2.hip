@@ -581,17 +581,18 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(Mamba2Params p, SsdWs ws)
 // first chunk of a pair, exp(L_C) S0 + St of the first chunk for the second.
 // C B^T does not depend on the head: the workgroup stages C and B once,
 // keeps C B^T in registers and C in LDS, and walks the group's heads; each
-// head's loads are issued while the head before it is formed.  C and B are
-// staged row-major (the k index of both products is n), X transposed
-// (k = token).
+// head's loads are issued while the head before it is formed.  C, B and X
+// are staged row-major (the k index of C B^T and C S0^T is n); M X takes X's
+// columns as its B operand through transposing LDS reads.
 // ---------------------------------------------------------------------------
 template <int P, int N, bool SPLIT>
 struct SsdOutLds {
   static constexpr int RS = N + 8;            // halves per C/B row
   static constexpr int MS = kSsdChunk + 4;    // floats per M row
   static constexpr int YS = P + 4;            // floats per Y row
+  static constexpr int XS = P + 8;            // halves per X row
   static constexpr int kRowHalves = kSsdChunk * RS;
-  static constexpr int kXHalves = P * kTS;
+  static constexpr int kXHalves = kSsdChunk * XS;
   static constexpr int kParts = SPLIT ? 2 : 1;
   static constexpr int kRowsBytes = kRowHalves * kParts * 2;
   static constexpr int kMBytes = kSsdChunk * MS * 4;
@@ -601,7 +602,7 @@ struct SsdOutLds {
   static constexpr int kU = kRowsBytes;
   static constexpr int kUBytes = kRowsBytes > kMBytes ? (kRowsBytes > kYBytes ? kRowsBytes : kYBytes)
                                                       : (kMBytes > kYBytes ? kMBytes : kYBytes);
-  static constexpr int kX = kU + kUBytes;                    // X^T (hi, lo) of the current head
+  static constexpr int kX = kU + kUBytes;                    // X rows (hi, lo) of the current head
   static constexpr int kL = kX + kXHalves * kParts * 2;      // double L[64]
   static constexpr int kDt = kL + kSsdChunk * 8;
   static constexpr int kE = kDt + kSsdChunk * 4;
@@ -620,7 +621,7 @@ template <typename ActT, int P, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWaves<ActT, P, N>))) void ssd_out_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
   using Lay = SsdOutLds<P, N, SPLIT>;
-  constexpr int RS = Lay::RS, MS = Lay::MS, YS = Lay::YS;
+  constexpr int RS = Lay::RS, MS = Lay::MS, YS = Lay::YS, XS = Lay::XS;
   constexpr int NK = N / 32;
   constexpr int NPT = P / 64 > 0 ? P / 64 : 1;  // column tiles of 16 per wave
   __shared__ __attribute__((aligned(16))) char smem[Lay::kBytes];
@@ -630,8 +631,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   _Float16* Bl = Bh + Lay::kRowHalves;
   float* Ms = reinterpret_cast<float*>(smem + Lay::kU);  // over B
   float* Ys = reinterpret_cast<float*>(smem + Lay::kU);  // over M
-  _Float16* XTh = reinterpret_cast<_Float16*>(smem + Lay::kX);
-  _Float16* XTl = XTh + Lay::kXHalves;
+  _Float16* Xh = reinterpret_cast<_Float16*>(smem + Lay::kX);
+  _Float16* Xl = Xh + Lay::kXHalves;
   double* Ls = reinterpret_cast<double*>(smem + Lay::kL);
   float* dts = reinterpret_cast<float*>(smem + Lay::kDt);
   float* eLs = reinterpret_cast<float*>(smem + Lay::kE);
@@ -655,39 +656,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
   // used in turn): the wave's S0 rows as the B operand S0^T[n][p] (f32
   // activations: f32, with a pair's second chunk's exp(L_C) S0 + St formed
   // as they arrive, split where used; else the f16 copy, and for a pair's
-  // second chunk the first chunk's St); the chunk's x rows (item (token,
-  // 8 consecutive p), token fastest; rows past n zero); the epilogue's x and
-  // z (8 consecutive p of one token per item, kept packed); the decay
-  // vector the state kernel wrote (wave 0), the head's D (thread p holds
-  // column p's) and for a second chunk the first chunk's exp(L_C)
-  constexpr int XIT = kSsdChunk * (P / 8) / 256;
-  static_assert(XIT >= 1 && kSsdChunk * (P / 8) % 256 == 0, "x staging items");
-  constexpr int XNV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
-  constexpr int EPI = (kSsdChunk * (P / 8) + 255) / 256;
+  // second chunk the first chunk's St); the chunk's x and z (8 consecutive
+  // p of one token per item, kept packed; x is staged as rows and feeds the
+  // epilogue's D x); the decay vector the state kernel wrote (wave 0), the
+  // head's D (thread p holds column p's) and for a second chunk the first
+  // chunk's exp(L_C)
+  constexpr int EPI = kSsdChunk * (P / 8) / 256;
+  static_assert(EPI >= 1 && kSsdChunk * (P / 8) % 256 == 0, "x items");
   constexpr int NV = 8 / Elem<ActT>::kVec;  // 16-byte vectors per item
   struct HeadRegs {
     float sv[SPLIT ? NPT : 1][SPLIT ? NK : 1][8];
     h8 svh[SPLIT ? 1 : NPT][SPLIT ? 1 : NK], sth[SPLIT ? 1 : NPT][SPLIT ? 1 : NK];
-    uint4 xs[XIT][XNV];
     uint4 xr[EPI][NV], zr[EPI][NV];
     double dec_L;
     float dec_dt, dec_eL, e1, d;
   };
   const ActT* xg = static_cast<const ActT*>(p.x);
   const ActT* zg = static_cast<const ActT*>(p.z);
-  // per-thread element offsets of head 0 (a head adds h * P): the x rows
-  // staged as X^T and the epilogue's items; rows past n re-read row n - 1
-  // (their X^T columns meet zero rows of M, their outputs are not stored)
-  int64_t xs_off[XIT], epi_off[EPI];
-#pragma unroll
-  for (int u = 0; u < XIT; ++u) {
-    const int v = tid + 256 * u;
-    const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
-    xs_off[u] = (t0 + min(t, n - 1)) * p.H * P + c0;
-  }
+  // per-thread element offsets of head 0 (a head adds h * P) of the x and z
+  // items; rows past n re-read row n - 1 (their X rows meet zero columns of
+  // M, their outputs are not stored)
+  int64_t epi_off[EPI];
 #pragma unroll
   for (int u = 0; u < EPI; ++u) {
-    const int v = min(tid + 256 * u, kSsdChunk * (P / 8) - 1);
+    const int v = tid + 256 * u;
     const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
     epi_off[u] = (t0 + min(i, n - 1)) * p.H * P + p0;
   }
@@ -722,10 +714,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
           }
         }
     }
-#pragma unroll
-    for (int u = 0; u < XIT; ++u)
-#pragma unroll
-      for (int w = 0; w < XNV; ++w) R.xs[u][w] = ld16(xg + xs_off[u] + h * P + w * Elem<ActT>::kVec);
     if (wave == 0) {
       const char* vec = blk0 + ssd_blk_vec(P, N);
       R.dec_L = reinterpret_cast<const double*>(vec + kVecL)[lane];
@@ -737,7 +725,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
     for (int u = 0; u < EPI; ++u)
 #pragma unroll
       for (int w = 0; w < NV; ++w) {
-        if (p.D) R.xr[u][w] = ld16(xg + epi_off[u] + h * P + w * Elem<ActT>::kVec);
+        R.xr[u][w] = ld16(xg + epi_off[u] + h * P + w * Elem<ActT>::kVec);
         if (zg) R.zr[u][w] = ld16(zg + epi_off[u] + h * P + w * Elem<ActT>::kVec);
       }
   };
@@ -776,21 +764,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
 
   ActT* og = static_cast<ActT*>(p.out);
   auto process = [&](const HeadRegs& R, int h) __attribute__((always_inline)) {
-    // X^T and the decay vector of head h into LDS (columns past n hold row
+    // X rows and the decay vector of head h into LDS (rows past n hold row
     // n - 1 again; M is zero there, as B is)
 #pragma unroll
-    for (int u = 0; u < XIT; ++u) {
+    for (int u = 0; u < EPI; ++u) {
       const int v = tid + 256 * u;
-      const int t = v % kSsdChunk, c0 = 8 * (v / kSsdChunk);
+      const int i = v / (P / 8), p0 = 8 * (v % (P / 8));
       float xv[8];
 #pragma unroll
-      for (int w = 0; w < XNV; ++w) Elem<ActT>::unpack(R.xs[u][w], xv + w * Elem<ActT>::kVec);
+      for (int w = 0; w < NV; ++w) Elem<ActT>::unpack(R.xr[u][w], xv + w * Elem<ActT>::kVec);
+      h8 xh8, xl8;
+      if constexpr (SPLIT) {
+        split8(xv, xh8, xl8);
+        *reinterpret_cast<h8*>(Xl + i * XS + p0) = xl8;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const _Float16 hx = (_Float16)xv[i];
-        XTh[(c0 + i) * kTS + t] = hx;
-        if constexpr (SPLIT) XTl[(c0 + i) * kTS + t] = (_Float16)(xv[i] - (float)hx);
+        for (int e = 0; e < 8; ++e) xh8[e] = (_Float16)xv[e];
       }
+      *reinterpret_cast<h8*>(Xh + i * XS + p0) = xh8;
     }
     if (wave == 0) {
       Ls[lane] = R.dec_L;
@@ -833,7 +824,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
         }
       }
     }
-    __syncthreads();  // X^T and the vector are in; the last head's Y is read
+    __syncthreads();  // X and the vector are in; the last head's Y is read
 
     // exp(L_i) C S0^T, which seeds the accumulators of M X below
     if (has_cols) {
@@ -877,11 +868,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
 #pragma unroll
       for (int q = 0; q < NPT; ++q) {
         const int pt = wave + 4 * q;
+        // X[32 s + 8 lg .. +7][16 pt + li] from the X rows: in each 16-lane
+        // group a transposing read hands lane 4a + c element c of the
+        // 8-byte reads of lanes a, a+4, a+8, a+12, so lane li reads token
+        // 32 s + 8 lg + 4 e + li / 4 at columns 16 pt + 4 (li % 4) .. +3
         h8 xh[2], xl[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          xh[s] = ld_h8(XTh + (16 * pt + li) * kTS + 32 * s + 8 * lg);
-          if constexpr (SPLIT) xl[s] = ld_h8(XTl + (16 * pt + li) * kTS + 32 * s + 8 * lg);
+          const int r0 = 32 * s + 8 * lg + (li >> 2), c = 16 * pt + 4 * (li & 3);
+          const uint2 a0 = lds_read_tr16(Xh + r0 * XS + c), a1 = lds_read_tr16(Xh + (r0 + 4) * XS + c);
+          xh[s] = __builtin_bit_cast(h8, u32x4{a0.x, a0.y, a1.x, a1.y});
+          if constexpr (SPLIT) {
+            const uint2 b0 = lds_read_tr16(Xl + r0 * XS + c), b1 = lds_read_tr16(Xl + (r0 + 4) * XS + c);
+            xl[s] = __builtin_bit_cast(h8, u32x4{b0.x, b0.y, b1.x, b1.y});
+          }
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
         }
       }
     }
-    __syncthreads();  // M and X^T are done with; Y goes over M
+    __syncthreads();  // M and X are done with; Y goes over M
     if (has_cols) {
 #pragma unroll
       for (int q = 0; q < NPT; ++q)
