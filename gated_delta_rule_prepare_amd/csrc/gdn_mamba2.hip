@@ -351,7 +351,8 @@ __device__ __forceinline__ double chunk_log_decay(const Mamba2Params& p, int64_t
 // leaves in the second chunk's block.  Pairs start at even chunk offsets
 // within a sequence; the last chunk of a sequence with an odd chunk count
 // is a pair of one.  Each half of the workgroup loads one chunk; the first
-// is staged, its tiles formed, then the second staged over it.  The
+// is staged (B and x rows, row-major), its tiles formed, then the second
+// staged over it.  The
 // workgroup of a pair's second chunk has nothing to do.  The grid is one
 // dimensional, head fastest: workgroups are dealt to the XCDs in turn, so
 // with the chunk fastest every busy workgroup would land on every other XCD.
@@ -367,8 +368,11 @@ template <typename ActT, int P, int N>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWaves<ActT, P, N>))) void ssd_state_kernel(Mamba2Params p, SsdWs ws) {
   constexpr bool SPLIT = std::is_same<ActT, float>::value;
   constexpr int PT = P / 16, NT = N / 16, TILES = PT * NT, TPW = (TILES + 7) / 8;
-  __shared__ __attribute__((aligned(16))) _Float16 BTh[N * kTS], XTh[P * kTS];
-  __shared__ __attribute__((aligned(16))) _Float16 BTl[SPLIT ? N * kTS : 8], XTl[SPLIT ? P * kTS : 8];
+  // B and x rows, row-major: the products take their columns through
+  // transposing LDS reads
+  constexpr int BS = N + 8, XS = P + 8;  // halves per row
+  __shared__ __attribute__((aligned(16))) _Float16 Brh[kSsdChunk * BS], Xrh[kSsdChunk * XS];
+  __shared__ __attribute__((aligned(16))) _Float16 Brl[SPLIT ? kSsdChunk * BS : 8], Xrl[SPLIT ? kSsdChunk * XS : 8];
   __shared__ __attribute__((aligned(16))) float ws_[2][kSsdChunk];
   __shared__ double lc_s[2];
   __shared__ float elc_s[2];
@@ -393,8 +397,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
 
   // both chunks' loads first; the second chunk is staged once the first is
   // done with
-  Staged<ActT, N, false> bt;
-  Staged<ActT, P, false> xt;
+  Staged<ActT, N, true> bt;
+  Staged<ActT, P, true> xt;
   bt.load(static_cast<const ActT*>(p.B) + (tk * p.G + g) * N, (int64_t)p.G * N, nk, ht);
   xt.load(static_cast<const ActT*>(p.x) + (tk * p.H + h) * P, (int64_t)p.H * P, nk, ht);
   if ((wave & 3) == 0 && nk > 0) {  // the first wave of each half with a chunk
@@ -418,8 +422,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
     reinterpret_cast<double*>(vec + kVecL)[lane] = dec_L;
   }
   if (half == 0) {
-    bt.store(BTh, BTl, ht);
-    xt.store(XTh, XTl, ht);
+    bt.store(Brh, Brl, ht);
+    xt.store(Xrh, Xrl, ht);
   }
   __syncthreads();
 
@@ -429,14 +433,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
   const float e2 = two ? elc_s[1] : 1.0f;  // exp(L_C') scales the first chunk's St
   float* Stg = reinterpret_cast<float*>(blk);
   h8 bh[2], bl[2];
+  // column c0 + li of rows 32 s + 8 lg .. +7 of a row-major tile: in each
+  // 16-lane group a transposing read hands lane 4a + c element c of the
+  // 8-byte reads of lanes a, a+4, a+8, a+12, so lane li reads row
+  // 32 s + 8 lg + 4 e + li / 4 at columns c0 + 4 (li % 4) .. +3
+  auto column8 = [&](const _Float16* rows, int stride, int s, int c0) {
+    const int r0 = 32 * s + 8 * lg + (li >> 2), c = c0 + 4 * (li & 3);
+    const uint2 a0 = lds_read_tr16(rows + r0 * stride + c), a1 = lds_read_tr16(rows + (r0 + 4) * stride + c);
+    return __builtin_bit_cast(h8, u32x4{a0.x, a0.y, a1.x, a1.y});
+  };
   // B operand (w X)[j][p] of chunk k: column p = 16 pt + li, rows j = 32 s + 8 lg ..
   auto operand = [&](int k, int pt) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int j0 = 32 * s + 8 * lg;
-      const h8 xh = ld_h8(XTh + (16 * pt + li) * kTS + j0);
+      const h8 xh = column8(Xrh, XS, s, 16 * pt);
       h8 xl;
-      if constexpr (SPLIT) xl = ld_h8(XTl + (16 * pt + li) * kTS + j0);
+      if constexpr (SPLIT) xl = column8(Xrl, XS, s, 16 * pt);
       const float4 w0 = *reinterpret_cast<const float4*>(&ws_[k][j0]);
       const float4 w1 = *reinterpret_cast<const float4*>(&ws_[k][j0 + 4]);
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -454,11 +467,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
   auto product = [&](int nt, f32x4 acc) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      // A operand B^T[n][j]: row n = 16 nt + li
-      const h8 ah = ld_h8(BTh + (16 * nt + li) * kTS + 32 * s + 8 * lg);
+      // A operand B^T[n][j]: row n = 16 nt + li, a column of the B rows
+      const h8 ah = column8(Brh, BS, s, 16 * nt);
       acc = mfma_f16(ah, bh[s], acc);
       acc = mfma_f16(ah, bl[s], acc);
-      if constexpr (SPLIT) acc = mfma_f16(ld_h8(BTl + (16 * nt + li) * kTS + 32 * s + 8 * lg), bh[s], acc);
+      if constexpr (SPLIT) acc = mfma_f16(column8(Brl, BS, s, 16 * nt), bh[s], acc);
     }
     return acc;
   };
@@ -498,8 +511,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
   if (two) {
     __syncthreads();  // the first chunk's tiles are done with
     if (half == 1) {
-      bt.store(BTh, BTl, ht);
-      xt.store(XTh, XTl, ht);
+      bt.store(Brh, Brl, ht);
+      xt.store(Xrh, Xrl, ht);
     }
     __syncthreads();
     cur_pt = -1;
