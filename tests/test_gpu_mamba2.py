@@ -75,6 +75,10 @@ SCAN_CASES = [
     ("bf16_f32_h2_p32_n128", 2, 32, 1, 128, (90, 64), "bf16", "f32", {}),
     # more sequences than the chunk-table wave has lanes
     ("bf16_f32_h2_p64_n64_70seqs", 2, 64, 1, 64, tuple(1 + (i * 37) % 150 for i in range(70)), "bf16", "f32", {}),
+    # three heads per group (the output kernel's heads taken two at a time,
+    # with a last one alone) and one head per group; chunk counts 1 to 5
+    ("bf16_f32_h6_p64_n64_3pergroup", 6, 64, 2, 64, (300, 65, 129, 1, 192), "bf16", "f32", dict(has_init=(1, 1, 0, 1, 0))),
+    ("bf16_f16_h2_p32_n128_1pergroup", 2, 32, 2, 128, (257, 64), "bf16", "f16", {}),
 ]
 
 
