@@ -455,9 +455,20 @@ __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _
 template <typename QkvT>
 constexpr int kPrepWaves = std::is_same<QkvT, float>::value ? 1 : 3;
 
+// Value heads per prep workgroup: with bf16 q/k/v (the T form) one
+// workgroup takes every value head of a key head, up to kMaxVpw of them,
+// and forms K K^T and Q K^T once for all; otherwise one value head each.
+// Two keep the LDS at 40 KB, four workgroups to a CU.
+constexpr int kMaxVpw = 2;
+__host__ __device__ inline int prep_vpw(const PrefillParams& p) {
+  const int r = p.Hv / p.Hk;
+  return (p.qkv != GDN_F32 && r <= kMaxVpw && p.h0 % r == 0 && p.hg % r == 0) ? r : 1;
+}
+
 template <typename QkvT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<QkvT>))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
+  constexpr bool STAGE_VPW = !SPLIT;
   constexpr int NKS = D / 32;      // 32-wide k steps over the head dim
   constexpr int NCT = D / 16;      // 16-column tiles of W (and of U)
   constexpr int TS = kChunk + 4;   // f32 row stride of A and T
@@ -469,25 +480,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
   __shared__ __attribute__((aligned(16))) float As[kChunk * TS];
   __shared__ __attribute__((aligned(16))) float Ts[kChunk * TS];
   __shared__ float Ms[4 * 16 * 17];
-  __shared__ double Gs[kChunk];
-  __shared__ float bs[kChunk], bg[kChunk], kn[kChunk];
+  __shared__ double Gs[kMaxVpw][kChunk];
+  __shared__ float bs[kMaxVpw][kChunk], bg[kChunk], kn[kChunk];
 
-  const int cid = blockIdx.x, h = p.h0 + (int)blockIdx.y;
+  // value heads hv0 .. hv0 + vpw - 1 of one key head (vpw > 1 only with bf16
+  // q/k/v, where nothing below depends on V)
+  const int vpw = STAGE_VPW ? prep_vpw(p) : 1;
+  const int cid = blockIdx.x, hv0 = p.h0 + (int)blockIdx.y * vpw;
+  const int h = hv0;
   const int kh = h / (p.Hv / p.Hk);
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
   const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  char* blk = ws.blocks + ((int64_t)cid * p.hg + blockIdx.y) * blk_bytes(D);
+  // the block of value head hv0 + v
+  auto block_of = [&](int v) { return ws.blocks + ((int64_t)cid * p.hg + (hv0 - p.h0 + v)) * blk_bytes(D); };
+  char* blk = block_of(0);
   _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
   _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
-  _Float16* Ph = reinterpret_cast<_Float16*>(blk + blk_p_hi(D));
-  _Float16* Pl = reinterpret_cast<_Float16*>(blk + blk_p_lo(D));
   float* UTg = reinterpret_cast<float*>(blk + blk_ut(D));
-  float* gam_g = reinterpret_cast<float*>(blk + blk_vec(D));
-  float* dc_g = gam_g + kChunk;
-  float* kn_g = dc_g + kChunk;
-  float* qn_g = kn_g + kChunk;
 
   const int64_t qk_stride = (int64_t)p.Hk * D, v_stride = (int64_t)p.Hv * D;
   const QkvT* kp = static_cast<const QkvT*>(p.k) + (t0 * p.Hk + kh) * D;
@@ -536,10 +547,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
   }
   const int gt = min(lane, n - 1);
-  // a decay factor exp(g) below e^-200 is exactly zero in f32; the clamp
-  // keeps the running sums finite when g = -inf
-  const float graw = fmaxf(p.g[(t0 + gt) * p.Hv + h], -200.0f);
-  const float braw = p.beta[(t0 + gt) * p.Hv + h];
+  // the gates of the value head whose scan this wave runs (wave v: head
+  // hv0 + v); a decay factor exp(g) below e^-200 is exactly zero in f32; the
+  // clamp keeps the running sums finite when g = -inf
+  const int gv = wave < vpw ? wave : 0;
+  const float graw = fmaxf(p.g[(t0 + gt) * p.Hv + hv0 + gv], -200.0f);
+  const float braw = p.beta[(t0 + gt) * p.Hv + hv0 + gv];
   if constexpr (STAGE) {
     __syncthreads();
     // this wave's own K rows (rows past the end hold the last row again, their
@@ -581,11 +594,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     qsc = valid ? (p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.0f;
     if (lg == 0) {
       kn[row] = ksc;
-      kn_g[row] = ksc;
-      qn_g[row] = qsc;
+      for (int v = 0; v < vpw; ++v) {
+        float* kn_g = reinterpret_cast<float*>(block_of(v) + blk_vec(D)) + 2 * kChunk;
+        kn_g[row] = ksc;
+        kn_g[kChunk + row] = qsc;
+      }
     }
   }
-  if (wave == 0) {
+  if (wave < vpw) {  // the gates of value head hv0 + wave
     const bool valid = lane < n;
     double G = valid ? (double)graw : 0.0;
 #pragma unroll
@@ -593,14 +609,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
       const double o = __shfl_up(G, off, 64);
       if (lane >= off) G += o;
     }
-    Gs[lane] = G;
+    Gs[wave][lane] = G;
     const double Glast = __shfl(G, 63, 64);
     const float gam = expf((float)G);
     const float bt = valid ? braw : 0.0f;
-    bs[lane] = bt;
-    bg[lane] = bt * gam;
+    bs[wave][lane] = bt;
+    if (wave == 0) bg[lane] = bt * gam;  // W form only (one value head)
+    float* gam_g = reinterpret_cast<float*>(block_of(wave) + blk_vec(D));
     gam_g[lane] = gam;
-    dc_g[lane] = expf((float)(Glast - G));
+    gam_g[kChunk + lane] = expf((float)(Glast - G));
   }
   __syncthreads();
   if constexpr (!STAGE) {
@@ -608,21 +625,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     vtile.store(VTh, VTl, nullptr, n);
   }
 
-  // (K_J K_w^T) and (K_J Q_w^T): lane holds row i = 16w + li, columns j = 16J + 4lg + r
+  // (K_J K_w^T) and (K_J Q_w^T): lane holds row i = 16w + li, columns j =
+  // 16J + 4lg + r; they depend on the key head only and are kept for every
+  // value head's A and P
+  f32x4 akks[4], aqks[4];
   {
-    const int i = row;
-    const double Gi = Gs[i];
-    const float bi = bs[i];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-      if (J > wave) {
-        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (SPLIT)
-          store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), z);
-        else
-          store_h4(Ph + p_frag(wave, li, J, lg), z);
-        continue;
-      }
+      akks[J] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      aqks[J] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (J > wave) continue;
       const float sj = kn[16 * J + li];  // scale of the K row this lane feeds as operand A
       f32x4 akk = {0.0f, 0.0f, 0.0f, 0.0f}, aqk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -672,26 +684,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
           aqk[r] *= qsc * sk;
         }
       }
+      akks[J] = akk;
+      aqks[J] = aqk;
+    }
+  }
+  // A and P of value head hv0 + v: A into LDS for the inverse, P to the block
+  auto form_a_p = [&](int v) {
+    const int i = row;
+    const double Gi = Gs[v][i];
+    const float bi = bs[v][i];
+    char* bv = block_of(v);
+    _Float16* Ph = reinterpret_cast<_Float16*>(bv + blk_p_hi(D));
+    _Float16* Pl = reinterpret_cast<_Float16*>(bv + blk_p_lo(D));
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
       float av[4], pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * J + 4 * lg + r;
-        const float dec = j <= i ? expf((float)(Gi - Gs[j])) : 0.0f;
-        av[r] = j < i ? bi * dec * akk[r] : 0.0f;
-        pv[r] = j <= i ? p.scale * dec * aqk[r] : 0.0f;
+        const float dec = (J <= wave && j <= i) ? expf((float)(Gi - Gs[v][j])) : 0.0f;
+        av[r] = (J <= wave && j < i) ? bi * dec * akks[J][r] : 0.0f;
+        pv[r] = (J <= wave && j <= i) ? p.scale * dec * aqks[J][r] : 0.0f;
       }
-      *reinterpret_cast<float4*>(As + i * TS + 16 * J + 4 * lg) = make_float4(av[0], av[1], av[2], av[3]);
+      if (J <= wave) *reinterpret_cast<float4*>(As + i * TS + 16 * J + 4 * lg) = make_float4(av[0], av[1], av[2], av[3]);
       if constexpr (SPLIT)
         store_h4_split(Ph + p_frag(wave, li, J, lg), Pl + p_frag(wave, li, J, lg), pv);
       else
         store_h4(Ph + p_frag(wave, li, J, lg), pv);
     }
-  }
+  };
+  if constexpr (SPLIT) form_a_p(0);
   __syncthreads();
   // K^T and the K rows depend on the key head only: the first value head of
   // the key head in this launch writes them, and the scan reads them from
   // that head's block
-  if (STAGE && h == kv_first(p, h)) {
+  if (STAGE && (vpw > 1 || h == kv_first(p, h))) {
     // T form: the K rows for the scan, each group of 32 columns in the
     // contraction order (position 8b + 4a + c holds column 16a + 4b + c), in
     // the K^T lo slot (unused with bf16 q/k/v).  f16 holds bf16 rows
@@ -743,12 +770,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
           *reinterpret_cast<const uint4*>(KTl + r * KTS + 8 * c8);
   }
 
-  unit_lower_inverse<TS>(As, Ts, Ms);
-
-  if constexpr (SPLIT)
-    w_u_products<SPLIT, SPLIT, TS, D>(Ts, bg, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
-  else
-    store_t_beta<TS>(Ts, bs, reinterpret_cast<_Float16*>(blk + blk_tb_hi()), reinterpret_cast<_Float16*>(blk + blk_tb_lo()));
+  if constexpr (SPLIT) {
+    unit_lower_inverse<TS>(As, Ts, Ms);
+    w_u_products<SPLIT, SPLIT, TS, D>(Ts, bg, bs[0], KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+  } else {
+    // per value head: A and P, T = (I + A)^-1, T diag(beta).  The barrier
+    // after A also orders the last head's reads of T before this head's
+    // inverse writes it.
+    for (int v = 0; v < vpw; ++v) {
+      form_a_p(v);
+      __syncthreads();
+      unit_lower_inverse<TS>(As, Ts, Ms);
+      char* bv = block_of(v);
+      store_t_beta<TS>(Ts, bs[v], reinterpret_cast<_Float16*>(bv + blk_tb_hi()), reinterpret_cast<_Float16*>(bv + blk_tb_lo()));
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1935,7 +1971,7 @@ hipError_t launch_seq(const PrefillParams& p, hipStream_t stream) {
 
 template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
-  chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.hg), 256, 0, stream>>>(p, ws);
+  chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.hg / prep_vpw(p)), 256, 0, stream>>>(p, ws);
   const int nwg = (D / 16) * p.hg * p.N;
   chunk_scan_kernel<QkvT, StT, D, false><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
   return hipGetLastError();
