@@ -899,37 +899,51 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
       qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
     }
   }
-  if (tid < kChunk) bs[tid] = tid < n ? p.beta[(t0 + tid) * p.Hv + h] : 0.0f;
+  // every load of this phase is issued before any is waited on: the beta
+  // of thread t's token, the K and Q rows (staged below), the raw log-decays
+  // (4 channels each) and, last, the channels' dt bias (a thread's channels
+  // are the same for each of its items)
+  const float braw = tid < kChunk ? p.beta[(t0 + min(tid, n - 1)) * p.Hv + h] : 0.0f;
+  constexpr int VPR = D / 8, NV = STAGE ? (kChunk * VPR + 64 * NW - 1) / (64 * NW) : 1;
+  u32x4 krow[NV], qrow[NV];
   if constexpr (STAGE) {
-    constexpr int VPR = D / 8, NV = (kChunk * VPR + 64 * NW - 1) / (64 * NW);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int v = tid + 64 * NW * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      const int v = min(tid + 64 * NW * j, kChunk * VPR - 1), r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      krow[j] = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
+      qrow[j] = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+    }
+  }
+  constexpr int NG = (kChunk * (D / 4) + 64 * NW - 1) / (64 * NW);
+  static_assert((64 * NW) % (D / 4) == 0, "a thread's channels are the same for each item");
+  float4 raw[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int v = min(tid + 64 * NW * j, kChunk * (D / 4) - 1), t = v / (D / 4), c = 4 * (v % (D / 4));
+    raw[j] = *reinterpret_cast<const float4*>(p.g + ((t0 + min(t, n - 1)) * p.Hv + h) * D + c);
+  }
+  const float4 bias = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + 4 * (tid % (D / 4)))
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (tid < kChunk) bs[tid] = tid < n ? braw : 0.0f;
+  if constexpr (STAGE) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + 64 * NW * j, r = v / VPR, c = v % VPR;
       if (v < kChunk * VPR) {
-        *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
-        *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+        *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = krow[j];
+        *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = qrow[j];
       }
     }
   }
-  // the chunk's log-decays, gate applied, all threads, 4 channels each: every
-  // load is issued before any is used
+  // the chunk's log-decays, gate applied, all threads, 4 channels each
   {
-    constexpr int NG = (kChunk * (D / 4) + 64 * NW - 1) / (64 * NW);
     const float a = p.A_log ? -expf(p.A_log[h]) : 0.0f;
-    float4 raw[NG], bias[NG];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const int v = min(tid + 64 * NW * j, kChunk * (D / 4) - 1), t = v / (D / 4), c = 4 * (v % (D / 4));
-      raw[j] = *reinterpret_cast<const float4*>(p.g + ((t0 + min(t, n - 1)) * p.Hv + h) * D + c);
-      bias[j] = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + c)
-                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int v = tid + 64 * NW * j, t = v / (D / 4), c = 4 * (v % (D / 4));
       if (v >= kChunk * (D / 4)) break;
       float x[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-      const float bb[4] = {bias[j].x, bias[j].y, bias[j].z, bias[j].w};
+      const float bb[4] = {bias.x, bias.y, bias.z, bias.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // gate: a softplus(x + bias), softplus(z) = ln(1 + u), u = e^z, by the

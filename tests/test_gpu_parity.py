@@ -32,18 +32,27 @@ def _say(*a):
     sys.stdout.flush()
 
 
+def _where(err, lim):
+    """Where a mismatch lies: the index of the worst element and how many
+    elements exceed the bound (for the failure message)."""
+    over = err > lim
+    worst = np.unravel_index(int(np.argmax(err)), err.shape) if err.size else ()
+    return f"worst at index {tuple(int(i) for i in worst)} of shape {err.shape}, {int(over.sum())} elements over"
+
+
 def assert_close(got, want, dtype, what):
     got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
     err = np.abs(got - want)
     mx = float(err.max()) if err.size else 0.0
     if dtype == "f32":
-        ok = np.all(err <= 1e-4 + 1e-4 * np.abs(want))
+        lim = 1e-4 + 1e-4 * np.abs(want)
+        ok = np.all(err <= lim)
         bad = float((err - 1e-4 * np.abs(want)).max()) if err.size else 0.0
-        assert ok, f"{what}: f32 mismatch, max abs err {mx:.3e}, worst excess {bad:.3e}"
+        assert ok, f"{what}: f32 mismatch, max abs err {mx:.3e}, worst excess {bad:.3e}; {_where(err - lim + 1e-4, 1e-4)}"
     else:
         lim = 2e-2 if dtype == "bf16" else 2e-3
-        assert mx <= lim, f"{what}: {dtype} max abs err {mx:.3e} > {lim}"
+        assert mx <= lim, f"{what}: {dtype} max abs err {mx:.3e} > {lim}; {_where(err, lim)}"
     return mx
 
 
