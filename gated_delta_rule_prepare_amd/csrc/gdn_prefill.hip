@@ -465,10 +465,10 @@ __host__ __device__ inline int prep_vpw(const PrefillParams& p) {
   return (p.qkv != GDN_F32 && r <= kMaxVpw && p.h0 % r == 0 && p.hg % r == 0) ? r : 1;
 }
 
-template <typename QkvT, int D>
+template <typename QkvT, int D, int VPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<QkvT>))) void chunk_prep_kernel(PrefillParams p, ChunkWs ws) {
   constexpr bool SPLIT = std::is_same<QkvT, float>::value;
-  constexpr bool STAGE_VPW = !SPLIT;
+  static_assert(VPW >= 1 && VPW <= kMaxVpw && (VPW == 1 || !SPLIT), "several value heads per workgroup only in the T form");
   constexpr int NKS = D / 32;      // 32-wide k steps over the head dim
   constexpr int NCT = D / 16;      // 16-column tiles of W (and of U)
   constexpr int TS = kChunk + 4;   // f32 row stride of A and T
@@ -480,12 +480,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
   __shared__ __attribute__((aligned(16))) float As[kChunk * TS];
   __shared__ __attribute__((aligned(16))) float Ts[kChunk * TS];
   __shared__ float Ms[4 * 16 * 17];
-  __shared__ double Gs[kMaxVpw][kChunk];
-  __shared__ float bs[kMaxVpw][kChunk], bg[kChunk], kn[kChunk];
+  __shared__ double Gs[VPW][kChunk];
+  __shared__ float bs[VPW][kChunk], bg[kChunk], kn[kChunk];
 
-  // value heads hv0 .. hv0 + vpw - 1 of one key head (vpw > 1 only with bf16
-  // q/k/v, where nothing below depends on V)
-  const int vpw = STAGE_VPW ? prep_vpw(p) : 1;
+  // value heads hv0 .. hv0 + VPW - 1 of one key head (VPW > 1 only with bf16
+  // q/k/v, where nothing below depends on V); a trip count fixed at compile
+  // time keeps the per-head pointers out of long-lived scalar registers
+  constexpr int vpw = VPW;
   const int cid = blockIdx.x, hv0 = p.h0 + (int)blockIdx.y * vpw;
   const int h = hv0;
   const int kh = h / (p.Hv / p.Hk);
@@ -594,6 +595,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     qsc = valid ? (p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.0f;
     if (lg == 0) {
       kn[row] = ksc;
+#pragma unroll
       for (int v = 0; v < vpw; ++v) {
         float* kn_g = reinterpret_cast<float*>(block_of(v) + blk_vec(D)) + 2 * kChunk;
         kn_g[row] = ksc;
@@ -777,6 +779,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     // per value head: A and P, T = (I + A)^-1, T diag(beta).  The barrier
     // after A also orders the last head's reads of T before this head's
     // inverse writes it.
+#pragma unroll
     for (int v = 0; v < vpw; ++v) {
       form_a_p(v);
       __syncthreads();
@@ -1985,7 +1988,10 @@ hipError_t launch_seq(const PrefillParams& p, hipStream_t stream) {
 
 template <typename QkvT, typename StT, int D>
 hipError_t launch_chunked_d(const PrefillParams& p, const ChunkWs& ws, hipStream_t stream) {
-  chunk_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.hg / prep_vpw(p)), 256, 0, stream>>>(p, ws);
+  if (!std::is_same<QkvT, float>::value && prep_vpw(p) == 2)
+    chunk_prep_kernel<QkvT, D, std::is_same<QkvT, float>::value ? 1 : 2><<<dim3((unsigned)p.num_chunks, p.hg / 2), 256, 0, stream>>>(p, ws);
+  else
+    chunk_prep_kernel<QkvT, D, 1><<<dim3((unsigned)p.num_chunks, p.hg), 256, 0, stream>>>(p, ws);
   const int nwg = (D / 16) * p.hg * p.N;
   chunk_scan_kernel<QkvT, StT, D, false><<<(unsigned)((nwg + 7) / 8 * 8), 512, 0, stream>>>(p, ws);
   return hipGetLastError();
