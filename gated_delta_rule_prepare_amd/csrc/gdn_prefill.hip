@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
   const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
   const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;  // wave index in a scalar register
   // the block of value head hv0 + v
   auto block_of = [&](int v) { return ws.blocks + ((int64_t)cid * p.hg + (hv0 - p.h0 + v)) * blk_bytes(D); };
   char* blk = block_of(0);
@@ -506,21 +506,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
   const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
   const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
 
-  // All loads first: the K and V tiles, this wave's Q row fragments, the
-  // gates.  With bf16 inputs the K and V rows are read whole (contiguous
-  // 16-byte vectors) into row-major LDS tiles that borrow the T and A
-  // buffers (not yet in use), and the K row fragments and the transposed
-  // tiles are formed from there; with f32 inputs the tiles are read in the
-  // transposed pattern and the fragments straight from memory.
+  // All loads first.  With bf16 inputs the chunk's K and Q rows are read
+  // whole (contiguous 16-byte vectors) into row-major LDS tiles that borrow
+  // the T and A buffers (not yet in use); the K and Q row fragments, and the
+  // K rows and q fragments the scan reads, are formed from there.  With f32
+  // inputs the K and V tiles are read in the transposed pattern and the
+  // fragments straight from memory.  Then the gates.
   constexpr bool STAGE = !SPLIT;
   constexpr int RS = D + 8;  // row stride (elements) of the staged rows
   static_assert(!STAGE || kChunk * RS * 2 <= kChunk * TS * 4, "staged rows fit the A / T buffers");
   QkvT* Ks = reinterpret_cast<QkvT*>(Ts);
+  QkvT* Qs = reinterpret_cast<QkvT*>(As);  // the Q rows, read before A is formed
   TransposedTile<QkvT, D> ktile, vtile;
   Raw8<QkvT> kf[4][NKS], qf[NKS];
   if constexpr (STAGE) {
     constexpr int VPR = D / 8, NV = kChunk * VPR / 256;
-    u32x4 kr[NV];
+    u32x4 kr[NV], qr[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
@@ -528,8 +529,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
+      const int v = tid + 256 * j, r = v / VPR, c = v % VPR, rr = min(r, n - 1);
+      qr[j] = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
       const int v = tid + 256 * j, r = v / VPR, c = v % VPR;
       *reinterpret_cast<u32x4*>(Ks + r * RS + 8 * c) = kr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = tid + 256 * j, r = v / VPR, c = v % VPR;
+      *reinterpret_cast<u32x4*>(Qs + r * RS + 8 * c) = qr[j];
     }
   } else {
     ktile.load(kp, qk_stride, n);
@@ -542,7 +553,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
       for (int s = 0; s < NKS; ++s) kf[J][s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
     }
   }
-  {
+  if constexpr (!STAGE) {
     const int rr = min(16 * wave + li, n - 1);
 #pragma unroll
     for (int s = 0; s < NKS; ++s) qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
@@ -559,7 +570,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
     // this wave's own K rows (rows past the end hold the last row again, their
     // scale is 0); the other blocks' rows are read from LDS where they are used
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) kf[0][s].load(Ks + (16 * wave + li) * RS + 32 * s + 8 * lg);
+    for (int s = 0; s < NKS; ++s) {
+      kf[0][s].load(Ks + (16 * wave + li) * RS + 32 * s + 8 * lg);
+      qf[s].load(Qs + (16 * wave + li) * RS + 32 * s + 8 * lg);
+    }
   }
 
   // row scales of this wave's block: 1/sqrt(|row|^2 + 1e-6) with the L2 norm, else 1; zero past the end
@@ -704,7 +718,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * J + 4 * lg + r;
-        const float dec = (J <= wave && j <= i) ? expf((float)(Gi - Gs[v][j])) : 0.0f;
+        // the hardware exponential: its relative error (about 1e-7 times
+        // the exponent's magnitude) is that of rounding the f64 difference
+        const float dec = (J <= wave && j <= i) ? fast_exp((float)(Gi - Gs[v][j])) : 0.0f;
         av[r] = (J <= wave && j < i) ? bi * dec * akks[J][r] : 0.0f;
         pv[r] = (J <= wave && j <= i) ? p.scale * dec * aqks[J][r] : 0.0f;
       }
@@ -747,10 +763,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int f = tid + 256 * j, I = f / (NKS * 64), s = (f / 64) % NKS, ln = f % 64;
-      const int rq = min(16 * I + (ln & 15), n - 1), c0 = 32 * s + 4 * (ln >> 4);
+      const int rq = 16 * I + (ln & 15), c0 = 32 * s + 4 * (ln >> 4);
       float a[4], b[4];
-      load4(qp + rq * qk_stride + c0, a);
-      load4(qp + rq * qk_stride + c0 + 16, b);
+      load4(Qs + rq * RS + c0, a);
+      load4(Qs + rq * RS + c0 + 16, b);
       h8 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
