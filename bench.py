@@ -234,6 +234,31 @@ def extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot
     return copy_gbs, cold_l
 
 
+def prepare_copy_ref(torch, prep_b, dec_call, prep_call, stream, reps=10):
+    """The prepare against a device copy of the same bytes (half read, half
+    written) in the same cache state: each timed call follows a decode call,
+    as in the step, whose state stream leaves the Infinity Cache cold and
+    dirty.  HIP events on the kernels' stream, medians."""
+    n = prep_b // 2 // 4
+    csrc = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    res = {"copy": [], "prepare": []}
+    for i in range(reps + 2):
+        for name, fn in (("copy", lambda: cdst.copy_(csrc)), ("prepare", prep_call)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            dec_call(i)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                res[name].append(e0.elapsed_time(e1))
+    del csrc, cdst
+    cu, pu = (float(np.median(res[k])) * 1e3 for k in ("copy", "prepare"))
+    return {"note": "each call after a decode call; copy of the prepare's bytes, half read and half written",
+            "copy_us": cu, "copy_GBps": prep_b / (cu * 1e-6) / 1e9, "prepare_us": pu, "frac_of_copy": cu / pu}
+
+
 def gated_decode_bytes(B, Hk, Hv, Dk, Dv, K, act_bytes=2):
     """gdn_decode bytes plus the gate (B*Hv*Dv) and the norm weight (Dv)."""
     return decode_bytes(B, Hk, Hv, Dk, Dv, K) + B * Hv * Dv * act_bytes + Dv * act_bytes
@@ -284,6 +309,15 @@ def epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, sl
     dp = [e[0].elapsed_time(e[1]) for e in ev]
     dg = [e[2].elapsed_time(e[3]) for e in ev]
     nm = [e[4].elapsed_time(e[5]) for e in ev]
+    # the norm again, back to back with itself: its operands stay in the
+    # Infinity Cache and no other kernel's dirty lines are written back
+    nev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 2)]
+    for e in nev:
+        e[0].record(stream)
+        gdn.gdn_gated_rmsnorm(xp, zp, wn, outp, 1e-6, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    nm_loop = [e[0].elapsed_time(e[1]) for e in nev[2:]]
     db_ = gated_decode_bytes(B, gd.Hk, gd.Hv, gd.Dk, gd.Dv, gd.K)
     nb = gated_norm_bytes(T, gd.Hv, gd.Dv)
     gbs = lambda b, l: b / (float(np.median(l)) * 1e-3) / 1e9
@@ -293,6 +327,8 @@ def epilogue(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, sl
                          "roofline": {"bound": "hbm", "achieved": gbs(db_, dg), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": gbs(db_, dg) / HBM_PEAK_GBS}},
         "gated_rmsnorm_T4096": {**stats_us(nm), "bytes_per_launch": nb,
+                                "note": "each call after the two decode calls; back_to_back: the norm alone in a loop",
+                                "back_to_back": {**stats_us(nm_loop), "GBps": gbs(nb, nm_loop)},
                                 "roofline": {"bound": "hbm", "achieved": gbs(nb, nm), "peak": HBM_PEAK_GBS,
                                              "unit": "GB/s", "frac": gbs(nb, nm) / HBM_PEAK_GBS}},
     }
@@ -852,7 +888,7 @@ def main():
     pre_l = [e[2].elapsed_time(e[3]) for e in ev]
     dec_ms, prep_ms, pre_ms = (float(np.mean(x)) for x in (dec_l, prep_l, pre_l))
 
-    copy_gbs, cold_l, epi, spec, kda_r, m2, pcfgs = None, None, None, None, None, None, None
+    copy_gbs, cold_l, epi, spec, kda_r, m2, pcfgs, prep_ref = None, None, None, None, None, None, None, None
     if not args.no_extras:
         pcfgs = prefill_configs(torch, gdn)
         spec = speculative(torch, gdn)
@@ -862,6 +898,13 @@ def main():
                        stream, T)
         copy_gbs, cold_l = extras(torch, gdn, gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets, slot_sets_h, dout,
                                   dcfg.scale, stream, nsets)
+        prep_ref = prepare_copy_ref(
+            torch, prepare_bytes(T, d.Hk, d.Hv, d.Dk, d.Dv, d.K),
+            lambda i: gdn.gdn_decode(gd, dx, da, db, dw, dA, ddt, dconv, dssm, slot_sets[i % nsets], dout, dcfg.scale,
+                                     slot_idx_host=slot_sets_h[i % nsets], stream=stream),
+            lambda: gdn.gdn_prepare(gd, cu, px, pa, pb, pw, pA, pdt, pconv, q, k, v, g, beta, slot_idx=sl,
+                                    has_initial_state=hi, cu_seqlens_host=cu_h, slot_idx_host=sl_h, stream=stream),
+            stream)
 
 
     dec_b = decode_bytes(B, d.Hk, d.Hv, d.Dk, d.Dv, d.K)
@@ -880,6 +923,7 @@ def main():
                                 "frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_launch": dec_b,
                                 "traffic": measured_traffic("decode_kernel", ["gdn_decode.hip", "gdn_device.h"])}},
         "prepare": {"avg_ms": prep_ms, "tokens_per_s": T / (prep_ms * 1e-3), **stats_us(prep_l),
+                    "same_state_copy": prep_ref,
                     "roofline": {"bound": "hbm", "achieved": prep_b / (prep_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": prep_b / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                  "bytes_per_launch": prep_b}},
