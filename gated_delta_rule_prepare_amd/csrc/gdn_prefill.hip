@@ -1418,7 +1418,10 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
   __shared__ __attribute__((aligned(16))) uint32_t Yx[TF ? 4 * 64 * 4 : 4];
   // exp(G_C - G_j), then gamma (T form: both times the k row scale, then gamma_C)
   __shared__ __attribute__((aligned(16))) float Vs[2][2 * kChunk + (TF ? 4 : 0)];
-  __shared__ __attribute__((aligned(16))) float Gm[2][KDA ? D : 4];       // KDA: exp(G_C) per state column
+  // KDA: exp(G_C) per state column, three buffers by chunk: the output waves
+  // stage chunk c+1's before the barrier of chunk c, while the state waves
+  // may still read chunk c-1's in their update after the barrier of c-1
+  __shared__ __attribute__((aligned(16))) float Gm[3][KDA ? D : 4];
   constexpr int QEV = 16 / (int)sizeof(QT);     // q elements per 16-byte vector
   constexpr int QVPR = D / QEV;                  // vectors per q row
   constexpr int NQV = 16 * QVPR / 64;            // vectors per lane for a wave's 16 rows
@@ -1592,7 +1595,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     if constexpr (KDA)
       Gr = __builtin_bit_cast(float4, buf_ld16(rb, (uint32_t)(blk_kda_gam<QT>(D) + 4 * (4 * (ot % (D / 4))))));
   };
-  auto stage_uv = [&](int bb) {
+  auto stage_uv = [&](int bb, int b3) {
     if constexpr (TF) {
       const int tk = ot >> 2, e = 4 * (ot & 3);
       Vb[bb][e * 68 + tk] = (uint16_t)(Vt.x & 0xffffu);
@@ -1612,7 +1615,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
       if (ot < 32) *reinterpret_cast<float4*>(Vs[bb] + 4 * ot) = Vr;
     }
     if constexpr (KDA)
-      if (ot < D / 4) *reinterpret_cast<float4*>(Gm[bb] + 4 * ot) = Gr;
+      if (ot < D / 4) *reinterpret_cast<float4*>(Gm[b3] + 4 * ot) = Gr;
   };
   auto stage_kr = [&](int bb) {
     if constexpr (TF) {
@@ -1644,7 +1647,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     if constexpr (!TF) load_kt(c_begin);
     if constexpr (!TF) load_q(c_begin);
     stage_kr(0);
-    stage_uv(0);
+    stage_uv(0, 0);
     if constexpr (!TF) stage_kt(0);
     if constexpr (!TF) stage_q();
     // the loads in flight at the loop's head, issued in the order one pass of
@@ -1781,7 +1784,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         f32x4 a2;
         if constexpr (KDA) {
           // this lane's four columns 16 ct + 4 lg .. +3 decay by exp(G_C) of each
-          const float4 gv = *reinterpret_cast<const float4*>(Gm[b] + 16 * ct + 4 * lg);
+          const float4 gv = *reinterpret_cast<const float4*>(Gm[(cid - c_begin) % 3] + 16 * ct + 4 * lg);
           a2 = f32x4{gv.x * sc[0], gv.y * sc[1], gv.z * sc[2], gv.w * sc[3]};
         } else {
           a2 = f32x4{gc * sc[0], gc * sc[1], gc * sc[2], gc * sc[3]};
@@ -1813,7 +1816,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     } else {
       // next chunk's V^T (W form: U^T) and decay factors into the other
       // buffer, then start loading the one after
-      stage_uv(b ^ 1);
+      stage_uv(b ^ 1, (cid - c_begin + 1) % 3);
       load_uv(min(cid + 2, c_end - 1));
       // T form: this is the barrier behind which the state waves publish Y
       // (and, before it, this chunk's split state), so Q S0^T runs while

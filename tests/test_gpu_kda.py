@@ -100,6 +100,25 @@ def test_kda_prefill_parity(name, d, lens, qkv, sdt, opts):
     assert_close(sp, s_ref, sdt, f"{name} state pool")
 
 
+def test_kda_prefill_repeated_runs():
+    """The ragged KDA case run eight times, every run against the oracle.
+    Regression test: the scan's state waves once read the per-column chunk
+    decays exp(G_C) from a buffer the output waves could already be filling
+    with a later chunk's, so a run now and then gave a wrong final state."""
+    R = _runner()
+    name, d, lens, qkv, sdt, opts = next(c for c in CHUNK_CASES if c[0] == "bf16_f32_ragged_d128")
+    opts = dict(opts)
+    l2 = opts.pop("l2")
+    inp = kda_inputs(d, lens, len(lens) + 2, qkv, sdt, 777, **opts)
+    scale = 1.0 / np.sqrt(d.Dk)
+    o_ref, s_ref = _oracle(d, inp, scale, l2, qkv, sdt)
+    for run in range(8):
+        _say(f"[kda prefill repeated] run {run}")
+        out, sp = R.kda_prefill(d, inp, qkv, sdt, scale, l2)
+        assert_close(out, o_ref, qkv, f"run {run} out")
+        assert_close(sp, s_ref, sdt, f"run {run} state pool")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("which", ["prefill", "decode"])
 def test_kda_full_size(which):
