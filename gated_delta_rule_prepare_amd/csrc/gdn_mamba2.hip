@@ -801,7 +801,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       dts[lane] = R.dec_dt;
       eLs[lane] = R.dec_eL;
     }
-    if (p.D && tid < P) Ds[tid] = R.d;
     // C S0^T for the wave's column tiles (C stays staged for every head)
     float cs[NPT][4][4];
     if (has_cols) {
@@ -838,6 +837,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSsdOutWave
       }
     }
     __syncthreads();  // X and the vector are in; the last head's Y is read
+    // the head's D, read only by the epilogue: written past the barrier that
+    // every thread reaches after the last head's epilogue
+    if (p.D && tid < P) Ds[tid] = R.d;
 
     // exp(L_i) C S0^T, which seeds the accumulators of M X below
     if (has_cols) {
