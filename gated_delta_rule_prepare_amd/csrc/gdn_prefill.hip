@@ -57,6 +57,7 @@
 // 256) run a token-sequential kernel: one wave per sequence, value head and
 // 16 value rows, with the state rows in registers.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -204,6 +205,16 @@ __device__ __forceinline__ void load4(const bf16* p, float* o) {
 // Transposed staging of a [64 tokens][D] tile into LDS as [D][KTS] f16 (hi
 // and, for f32 inputs, lo).  Lane l of a wave takes tokens 2(l%32), 2(l%32)+1
 // of one 8-column segment, so each 32-lane half writes 32 consecutive words.
+// threadIdx.x behind an empty asm statement: a value the compiler cannot
+// hoist out of a loop, so that the per-lane offsets the helpers below derive
+// from it are formed where they are used instead of being held in registers
+// across a persistent kernel's loop
+__device__ __forceinline__ int thread_index() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <typename T, int D, int NW = 4>
 struct TransposedTile {
   static constexpr bool kSplit = std::is_same<T, float>::value;
@@ -214,7 +225,7 @@ struct TransposedTile {
   // segments past D re-read segment 0) so that no load sits under a branch;
   // store() zeroes what lies outside the tile.
   __device__ __forceinline__ void load(const T* src, int64_t stride, int n) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tix = thread_index(), lane = tix & 63, wave = tix >> 6;
     const int t = 2 * (lane & 31), seg0 = wave * 2 + (lane >> 5);
     const int ta = min(t, n - 1), tb = min(t + 1, n - 1);
 #pragma unroll
@@ -226,12 +237,12 @@ struct TransposedTile {
   }
   // row scales (l2 norm) are per token; null means 1
   __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, const float* rowscale, int n) const {
-    const int t = 2 * (threadIdx.x & 31);
+    const int t = 2 * (thread_index() & 31);
     store(hi, lo, rowscale ? rowscale[t] : 1.0f, rowscale ? rowscale[t + 1] : 1.0f, n);
   }
   // s0, s1: scales of this lane's two tokens 2(l%32), 2(l%32)+1
   __device__ __forceinline__ void store(_Float16* hi, _Float16* lo, float s0, float s1, int n) const {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tix = thread_index(), lane = tix & 63, wave = tix >> 6;
     const int t = 2 * (lane & 31), seg0 = wave * 2 + (lane >> 5);
     if (t >= n) s0 = 0.0f;
     if (t + 1 >= n) s1 = 0.0f;
@@ -303,7 +314,7 @@ __device__ __forceinline__ int p_frag(int I, int li, int J, int q) {
 // wave of the workgroup takes the barriers).  Ends with a barrier.
 template <int TS>
 __device__ __forceinline__ void unit_lower_inverse(const float* As, float* Ts, float* Ms) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   if (wave < 4) {
     const int B0 = 16 * wave, j = li;
     float tc[16];
@@ -361,7 +372,7 @@ __device__ __forceinline__ void w_u_products(const float* Ts, const float* bw, c
                                              const _Float16* KTl, const _Float16* VTh, const _Float16* VTl,
                                              _Float16* Wh, _Float16* Wl, float* UTg) {
   constexpr int NCT = D / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   constexpr int NT = (2 * NCT + NW - 1) / NW;  // tiles per wave
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
@@ -877,12 +888,70 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   float* As = GA;
   float* Ts = GA + kChunk * TS;
 
-  const int cid = blockIdx.x, h = blockIdx.y;
-  const int kh = h / (p.Hv / p.Hk);
-  const int seq = ws.single ? 0 : ws.chunk_seq[cid];
-  const int64_t t0 = ws.single ? (int64_t)kChunk * cid : ws.chunk_start[cid];
-  const int n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int64_t qk_stride = (int64_t)p.Hk * D, v_stride = (int64_t)p.Hv * D;
+  constexpr int VPR = D / 8, NV = STAGE ? (kChunk * VPR + 64 * NW - 1) / (64 * NW) : 1;
+  constexpr int NG = (kChunk * (D / 4) + 64 * NW - 1) / (64 * NW);
+  static_assert((64 * NW) % (D / 4) == 0, "a thread's channels are the same for each item");
+
+  // The workgroups are persistent: each takes the items (chunk, value head)
+  // blockIdx.x, + gridDim.x, ... (chunks of a head consecutive), one
+  // workgroup to a CU (the LDS).  The loads that feed an item's staging are
+  // issued as soon as the item before it is staged, so that they are in
+  // flight during that item's work: the V tile, beta, the raw K and Q rows,
+  // the raw log-decays (4 channels each) and the channels' dt bias.
+  struct Item {
+    int cid, h, kh, n;
+    int64_t t0;
+  };
+  auto item_of = [&](int it) {
+    Item I;
+    I.cid = it % p.num_chunks;
+    I.h = it / p.num_chunks;
+    I.kh = I.h / (p.Hv / p.Hk);
+    const int seq = ws.single ? 0 : ws.chunk_seq[I.cid];
+    I.t0 = ws.single ? (int64_t)kChunk * I.cid : ws.chunk_start[I.cid];
+    I.n = (int)min((int64_t)kChunk, (int64_t)p.cu[seq + 1] - I.t0);
+    return I;
+  };
+  TransposedTile<QkvT, D, NW> vtile;
+  u32x4 krow[NV], qrow[NV];
+  float4 raw[NG], bias;
+  float braw;
+  auto issue = [&](const Item& I, int tid) {
+    const QkvT* kq = static_cast<const QkvT*>(p.k) + (I.t0 * p.Hk + I.kh) * D;
+    const QkvT* qq = static_cast<const QkvT*>(p.q) + (I.t0 * p.Hk + I.kh) * D;
+    vtile.load(static_cast<const QkvT*>(p.v) + (I.t0 * p.Hv + I.h) * D, v_stride, I.n);
+    braw = tid < kChunk ? p.beta[(I.t0 + min(tid, I.n - 1)) * p.Hv + I.h] : 0.0f;
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int v = min(tid + 64 * NW * j, kChunk * VPR - 1), r = v / VPR, c = v % VPR, rr = min(r, I.n - 1);
+        krow[j] = *reinterpret_cast<const u32x4*>(kq + rr * qk_stride + 8 * c);
+        qrow[j] = *reinterpret_cast<const u32x4*>(qq + rr * qk_stride + 8 * c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int v = min(tid + 64 * NW * j, kChunk * (D / 4) - 1), t = v / (D / 4), c = 4 * (v % (D / 4));
+      raw[j] = *reinterpret_cast<const float4*>(p.g + ((I.t0 + min(t, I.n - 1)) * p.Hv + I.h) * D + c);
+    }
+    bias = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)I.h * D + 4 * (tid % (D / 4)))
+                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
+  const int nitems = p.num_chunks * p.Hv;
+  Item nxt = item_of(blockIdx.x);
+  issue(nxt, tid);
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  // the thread index made opaque to the compiler in each pass, so that the
+  // many per-lane LDS offsets below are formed where they are used rather
+  // than hoisted out of the loop and held in registers through it
+  int tid_pass = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_pass));
+  const int tid = tid_pass, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const Item cur = nxt;
+  const int cid = cur.cid, h = cur.h, kh = cur.kh, n = cur.n;
+  const int64_t t0 = cur.t0;
   char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_kda_bytes<QT>(D);
   _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
   _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
@@ -895,10 +964,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   QT* Qg = reinterpret_cast<QT*>(blk + blk_kda_q<QT>(D));
   float* gam_g = reinterpret_cast<float*>(blk + blk_kda_gam<QT>(D));
 
-  const int64_t qk_stride = (int64_t)p.Hk * D, v_stride = (int64_t)p.Hv * D;
   const QkvT* kp = static_cast<const QkvT*>(p.k) + (t0 * p.Hk + kh) * D;
   const QkvT* qp = static_cast<const QkvT*>(p.q) + (t0 * p.Hk + kh) * D;
-  const QkvT* vp = static_cast<const QkvT*>(p.v) + (t0 * p.Hv + h) * D;
 
   // Waves 0-3 (row waves) each own token block I = wave: its row scales,
   // its diagonal block of A and P.  Waves 4-7 (helpers) form the element-wise
@@ -906,43 +973,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   // on all eight.
   const bool roww = wave < 4;
   const int ht = tid - 256;             // helper thread index
-  // ---- loads: V tile, the K / Q fragments of a row wave's own block
-  TransposedTile<QkvT, D, NW> vtile;
-  vtile.load(vp, v_stride, n);
-  Raw8<QkvT> kfo[NKS], qf[NKS];
-  {
-    const int rr = min(16 * (wave & 3) + li, n - 1);
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      kfo[s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
-      qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
-    }
-  }
-  // every load of this phase is issued before any is waited on: the beta
-  // of thread t's token, the K and Q rows (staged below), the raw log-decays
-  // (4 channels each) and, last, the channels' dt bias (a thread's channels
-  // are the same for each of its items)
-  const float braw = tid < kChunk ? p.beta[(t0 + min(tid, n - 1)) * p.Hv + h] : 0.0f;
-  constexpr int VPR = D / 8, NV = STAGE ? (kChunk * VPR + 64 * NW - 1) / (64 * NW) : 1;
-  u32x4 krow[NV], qrow[NV];
-  if constexpr (STAGE) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = min(tid + 64 * NW * j, kChunk * VPR - 1), r = v / VPR, c = v % VPR, rr = min(r, n - 1);
-      krow[j] = *reinterpret_cast<const u32x4*>(kp + rr * qk_stride + 8 * c);
-      qrow[j] = *reinterpret_cast<const u32x4*>(qp + rr * qk_stride + 8 * c);
-    }
-  }
-  constexpr int NG = (kChunk * (D / 4) + 64 * NW - 1) / (64 * NW);
-  static_assert((64 * NW) % (D / 4) == 0, "a thread's channels are the same for each item");
-  float4 raw[NG];
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const int v = min(tid + 64 * NW * j, kChunk * (D / 4) - 1), t = v / (D / 4), c = 4 * (v % (D / 4));
-    raw[j] = *reinterpret_cast<const float4*>(p.g + ((t0 + min(t, n - 1)) * p.Hv + h) * D + c);
-  }
-  const float4 bias = p.dt_bias ? *reinterpret_cast<const float4*>(p.dt_bias + (int64_t)h * D + 4 * (tid % (D / 4)))
-                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  // ---- staging (the item before this one is done with the LDS)
+  if (item != (int)blockIdx.x) __syncthreads();
   if (tid < kChunk) bs[tid] = tid < n ? braw : 0.0f;
   if constexpr (STAGE) {
 #pragma unroll
@@ -954,6 +986,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
       }
     }
   }
+  vtile.store(VTh, VTl, nullptr, n);
   // the chunk's log-decays, gate applied, all threads, 4 channels each
   {
     const float a = p.A_log ? -expf(p.A_log[h]) : 0.0f;
@@ -983,6 +1016,22 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
     }
   }
   __syncthreads();
+
+  // the K / Q fragments of a row wave's own block
+  Raw8<QkvT> kfo[NKS], qf[NKS];
+  {
+    const int r = 16 * (wave & 3) + li, rr = min(r, n - 1);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      if constexpr (STAGE) {
+        kfo[s].load(Ks + r * RS + 32 * s + 8 * lg);
+        qf[s].load(Qs + r * RS + 32 * s + 8 * lg);
+      } else {
+        kfo[s].load(kp + rr * qk_stride + 32 * s + 8 * lg);
+        qf[s].load(qp + rr * qk_stride + 32 * s + 8 * lg);
+      }
+    }
+  }
 
   // ---- per-channel running sums (f64), one thread per (channel, token
   // block), in place: the sums within the block, then the block totals
@@ -1049,9 +1098,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   // ---- element-wise tiles: (k exp(G))^T into LDS, (k exp(G_C - G))^T and
   // q exp(G) into the block.  Item (t, 8 channels), t fastest; V^T by all
   // eight waves, the rest by the helpers.
-  vtile.store(VTh, VTl, nullptr, n);
-  for (int item = roww ? kChunk * (D / 8) : ht; item < kChunk * (D / 8); item += 256) {
-    const int t = item & (kChunk - 1), c0 = 8 * (item / kChunk), I = t >> 4;
+  for (int e_item = roww ? kChunk * (D / 8) : ht; e_item < kChunk * (D / 8); e_item += 256) {
+    const int t = e_item & (kChunk - 1), c0 = 8 * (e_item / kChunk), I = t >> 4;
     const int rr = min(t, n - 1);
     Raw8<QkvT> kr, qr;
     if constexpr (STAGE) {
@@ -1298,9 +1346,16 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
           make_float4(avh[u][0], avh[u][1], avh[u][2], avh[u][3]);
     }
   }
+  // the next item's loads, in flight during the inverse and the W / U
+  // products (they hold no registers through the block products above)
+  if (item + (int)gridDim.x < nitems) {
+    nxt = item_of(item + (int)gridDim.x);
+    issue(nxt, tid);
+  }
   __syncthreads();
   unit_lower_inverse<TS>(As, Ts, Ms);
   w_u_products<true, SPLIT, TS, D, NW>(Ts, bs, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2037,10 +2092,26 @@ hipError_t launch_state(const PrefillParams& p, hipStream_t stream, bool build_t
   }
 }
 
+// compute units of the current device, queried once per device (the size of
+// a persistent grid)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // ---- KDA
 template <typename QkvT, typename StT, int D>
 hipError_t launch_kda_chunked_d(const KdaParams& p, const ChunkWs& ws, hipStream_t stream) {
-  if (p.num_chunks > 0) kda_prep_kernel<QkvT, D><<<dim3((unsigned)p.num_chunks, p.Hv), 512, 0, stream>>>(p, ws);
+  // persistent prep workgroups, one per CU (each holds 146 KB of LDS)
+  const int64_t items = (int64_t)p.num_chunks * p.Hv;
+  if (items > 0)
+    kda_prep_kernel<QkvT, D><<<(unsigned)std::min<int64_t>(items, device_cus()), 512, 0, stream>>>(p, ws);
   // the scan reads what it needs of the layer through the GDN parameter block
   PrefillParams pp{};
   pp.Hk = p.Hk; pp.Hv = p.Hv; pp.Dk = p.Dk; pp.Dv = p.Dv; pp.N = p.N; pp.T = p.T; pp.cu = p.cu;
