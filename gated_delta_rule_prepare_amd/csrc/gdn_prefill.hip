@@ -952,6 +952,9 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   const Item cur = nxt;
   const int cid = cur.cid, h = cur.h, kh = cur.kh, n = cur.n;
   const int64_t t0 = cur.t0;
+  // the next item's chunk bounds (dependent loads), read while this one is staged
+  const bool more = item + (int)gridDim.x < nitems;
+  if (more) nxt = item_of(item + (int)gridDim.x);
   char* blk = ws.blocks + ((int64_t)cid * p.Hv + h) * blk_kda_bytes<QT>(D);
   _Float16* Wh = reinterpret_cast<_Float16*>(blk + blk_w_hi(D));
   _Float16* Wl = reinterpret_cast<_Float16*>(blk + blk_w_lo(D));
@@ -1248,8 +1251,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * s + 8 * lg + e;
+          // exp2(min(x, 0)) and exp2(min(-x, 0)): one of the two is 1, the
+          // other exp2(-|x|), so one exponential gives both
           const float x = gb_row[d] - sig[d];
-          const float fl = exp2_f(fminf(x, 0.0f)), fr = exp2_f(fminf(-x, 0.0f));
+          const float ex = exp2_f(-fabsf(x));
+          const float fl = x <= 0.0f ? ex : 1.0f, fr = x >= 0.0f ? ex : 1.0f;
           r8[e] = rmask ? xk[e] * ksc * fr : 0.0f;
           l8[e] = lmask ? xk[e] * ksc * fl : 0.0f;
           m8[e] = lmask ? xq[e] * qsc * fl : 0.0f;
@@ -1348,10 +1354,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, ChunkWs ws) 
   }
   // the next item's loads, in flight during the inverse and the W / U
   // products (they hold no registers through the block products above)
-  if (item + (int)gridDim.x < nitems) {
-    nxt = item_of(item + (int)gridDim.x);
-    issue(nxt, tid);
-  }
+  if (more) issue(nxt, tid);
   __syncthreads();
   unit_lower_inverse<TS>(As, Ts, Ms);
   w_u_products<true, SPLIT, TS, D, NW>(Ts, bs, bs, KTh, KTl, VTh, VTl, Wh, Wl, UTg);
