@@ -1685,6 +1685,44 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     }
   };
 
+  // k step w4 of the split state, published for the output waves' Q S0^T
+  auto publish_split = [&](const h8* Sh, const h8* Sl, int bb) {
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+      if (s == w4) {
+        *reinterpret_cast<h8*>(SSh[bb] + li * WS + 32 * s + 8 * lg) = Sh[s];
+        if constexpr (SPLIT) *reinterpret_cast<h8*>(SSh[bb] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
+      }
+  };
+  // T form: Y_J = V_J - diag(gamma) K_J S0^T for this wave's token block J =
+  // w4, published (f16 hi/lo) for every state wave; then Delta = T diag(beta)
+  // Y over the lower-triangular row block.  Lane (li, lg) holds tokens
+  // 16 J + 4 lg + r of row li, and in the contraction order of T diag(beta)'s
+  // columns the B operand of step s2 is the Y of blocks 2 s2 and 2 s2 + 1 at
+  // this same lane.  Blocks past w4 meet zero columns of T diag(beta).
+  // K S0^T, k step s (K rows from buffer bb against the state hi and lo)
+  auto ks_step = [&](const h8& sh, const h8& sl, int bb, int s, f32x4& xh, f32x4& xl) {
+    const h8 kf = ld_h8(Krow[bb] + krow_at(16 * w4 + li, 4 * s + lg));
+    xh = mfma_f16(kf, sh, xh);
+    xl = mfma_f16(kf, sl, xl);
+  };
+  // Y from K S0^T and V, gamma of buffer bb, split and published
+  auto finish_y = [&](const f32x4& xh, const f32x4& xl, int bb) {
+    const uint2 vv = *reinterpret_cast<const uint2*>(Vb[bb] + li * 68 + 16 * w4 + 4 * lg);
+    const float vt[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+    const float4 gm = *reinterpret_cast<const float4*>(Vs[bb] + kChunk + 16 * w4 + 4 * lg);
+    const float g4[4] = {gm.x, gm.y, gm.z, gm.w};
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+      const float y0 = vt[2 * r2] - g4[2 * r2] * (xh[2 * r2] + xl[2 * r2]);
+      const float y1 = vt[2 * r2 + 1] - g4[2 * r2 + 1] * (xh[2 * r2 + 1] + xl[2 * r2 + 1]);
+      split2(y0, y1, hw[r2], lw[r2]);
+    }
+    *reinterpret_cast<u32x4*>(Yx + (w4 * 64 + lane) * 4) = u32x4{hw[0], hw[1], lw[0], lw[1]};
+  };
+
   // ---- prologue
   if (state_wave) {
 #pragma unroll
@@ -1723,53 +1761,34 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
     if constexpr (!TF) load_kt(n1);
   }
   __syncthreads();
+  if (TF && state_wave) {
+    // the first chunk's Y and split state
+    h8 Sh[NKS], Sl[NKS];
+    f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      split8(Sf + 8 * s, Sh[s], Sl[s]);
+      ks_step(Sh[s], Sl[s], 0, s, xh, xl);
+    }
+    publish_split(Sh, Sl, 0);
+    finish_y(xh, xl, 0);
+  }
 
   for (int cid = c_begin; cid < c_end; ++cid) {
     const int b = (cid - c_begin) & 1;
     const int cn = min(cid + 1, c_end - 1);
     if (state_wave) {
       h8 Sh[NKS], Sl[NKS];
+      if constexpr (!TF) {
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) split8(Sf + 8 * s, Sh[s], Sl[s]);
-      // publish k step w4 of the split state for the output waves
-#pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        if (s == w4) {
-          *reinterpret_cast<h8*>(SSh[b] + li * WS + 32 * s + 8 * lg) = Sh[s];
-          if constexpr (SPLIT) *reinterpret_cast<h8*>(SSh[b] + (16 + li) * WS + 32 * s + 8 * lg) = Sl[s];
-        }
+        for (int s = 0; s < NKS; ++s) split8(Sf + 8 * s, Sh[s], Sl[s]);
+        publish_split(Sh, Sl, b);
+      }
       // Delta rows of this wave's 16 tokens
       float dl[4];
       if constexpr (TF) {
-        // Y_J = V_J - diag(gamma) K_J S0^T for this wave's token block J = w4,
-        // published (f16 hi/lo) for every state wave; then Delta =
-        // T diag(beta) Y over the lower-triangular row block.  Lane (li, lg)
-        // holds tokens 16 J + 4 lg + r of row li, and in the contraction order
-        // of T diag(beta)'s columns the B operand of step s2 is the Y of
-        // blocks 2 s2 and 2 s2 + 1 at this same lane.  Blocks past w4 meet
-        // zero columns of T diag(beta).
-        {
-          f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            const h8 kf = ld_h8(Krow[b] + krow_at(16 * w4 + li, 4 * s + lg));
-            xh = mfma_f16(kf, Sh[s], xh);
-            xl = mfma_f16(kf, Sl[s], xl);
-          }
-          const uint2 vv = *reinterpret_cast<const uint2*>(Vb[b] + li * 68 + 16 * w4 + 4 * lg);
-          const float vt[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
-                               __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
-          const float4 gm = *reinterpret_cast<const float4*>(Vs[b] + kChunk + 16 * w4 + 4 * lg);
-          const float g4[4] = {gm.x, gm.y, gm.z, gm.w};
-          uint32_t hw[2], lw[2];
-#pragma unroll
-          for (int r2 = 0; r2 < 2; ++r2) {
-            const float y0 = vt[2 * r2] - g4[2 * r2] * (xh[2 * r2] + xl[2 * r2]);
-            const float y1 = vt[2 * r2 + 1] - g4[2 * r2 + 1] * (xh[2 * r2 + 1] + xl[2 * r2 + 1]);
-            split2(y0, y1, hw[r2], lw[r2]);
-          }
-          *reinterpret_cast<u32x4*>(Yx + (w4 * 64 + lane) * 4) = u32x4{hw[0], hw[1], lw[0], lw[1]};
-        }
+        // Y of this chunk, and its split state for the output waves, were
+        // published at the end of the previous chunk (or in the prologue)
         __syncthreads();  // every state wave's Y is published
         f32x4 dhh = {0.0f, 0.0f, 0.0f, 0.0f}, dhl = dhh, dlh = dhh;
 #pragma unroll
@@ -1836,6 +1855,11 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         eh[s] = ld_h8(ETh[b] + li * KTS + 32 * s + 8 * lg);
         el[s] = ld_h8(ETl[b] + li * KTS + 32 * s + 8 * lg);
       }
+      // T form: the next chunk's Y follows the update k step by k step: k
+      // step s of the state is tiles 2s and 2s+1, split and multiplied into
+      // K S^T as soon as both are updated, so the two chains overlap
+      const bool next_y = TF && cid + 1 < c_end;
+      f32x4 xh = {0.0f, 0.0f, 0.0f, 0.0f}, xl = xh;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         float* sc = Sf + 8 * (ct >> 1) + 4 * (ct & 1);
@@ -1870,6 +1894,15 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillParams p, ChunkW
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = a2[r];
+        if (next_y && (ct & 1)) {
+          const int s = ct >> 1;
+          split8(Sf + 8 * s, Sh[s], Sl[s]);
+          ks_step(Sh[s], Sl[s], b ^ 1, s, xh, xl);
+        }
+      }
+      if (next_y) {
+        publish_split(Sh, Sl, b ^ 1);
+        finish_y(xh, xl, b ^ 1);
       }
     } else {
       // next chunk's V^T (W form: U^T) and decay factors into the other
