@@ -78,6 +78,10 @@ CHUNK_CASES = [
      dict(gate=True, dt_bias=True, l2=True, A_log_range=(-4.0, -1.0))),
     ("fallback_dk64_dv32", Dims(2, 2, 64, 32, 4), (70, 0), "bf16", "f32", dict(gate=True, dt_bias=True, l2=True)),
     ("all_empty", Dims(1, 2, 64, 64, 4), (0, 0), "bf16", "f32", dict(gate=True, has_init=(0, 1), l2=True)),
+    # more (chunk, value head) items than the prep has persistent workgroups
+    # (one per CU), over several sequences: each workgroup walks several items
+    ("many_items_varlen", Dims(2, 8, 128, 128, 4), (2000, 1500, 700), "bf16", "f32",
+     dict(gate=True, dt_bias=True, l2=True, has_init=(1, 0, 1))),
     # more sequences than the chunk-table wave has lanes, empty ones among them
     ("over_64_seqs", Dims(1, 2, 64, 64, 4), tuple((i * 37) % 150 for i in range(70)), "bf16", "f32",
      dict(gate=True, dt_bias=True, l2=True)),
