@@ -441,11 +441,16 @@ template <int TS>
 __device__ __forceinline__ void store_t_beta(const float* Ts, const float* bs, _Float16* hi, _Float16* lo) {
   const int i = threadIdx.x >> 2, q = threadIdx.x & 3;
   float v[16];
+  // positions 16 q + 4 g .. +3 are four consecutive columns j0 .. j0 + 3
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int pos = 16 * q + m, w = pos & 31;
-    const int j = (pos & ~31) + 16 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
-    v[m] = j <= i ? Ts[i * TS + j] * bs[j] : 0.0f;
+  for (int g = 0; g < 4; ++g) {
+    const int pos = 16 * q + 4 * g;
+    const int j0 = (pos & ~31) + 16 * (g & 1) + 8 * (q & 1) + 4 * (g >> 1);
+    const float4 t4 = *reinterpret_cast<const float4*>(Ts + i * TS + j0);
+    const float4 b4 = *reinterpret_cast<const float4*>(bs + j0);
+    const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * g + e] = j0 + e <= i ? tv[e] * bv[e] : 0.0f;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -492,7 +497,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrepWaves<
   __shared__ __attribute__((aligned(16))) float Ts[kChunk * TS];
   __shared__ float Ms[4 * 16 * 17];
   __shared__ double Gs[VPW][kChunk];
-  __shared__ float bs[VPW][kChunk], bg[kChunk], kn[kChunk];
+  __shared__ __attribute__((aligned(16))) float bs[VPW][kChunk];
+  __shared__ float bg[kChunk], kn[kChunk];
 
   // value heads hv0 .. hv0 + VPW - 1 of one key head (VPW > 1 only with bf16
   // q/k/v, where nothing below depends on V); a trip count fixed at compile
