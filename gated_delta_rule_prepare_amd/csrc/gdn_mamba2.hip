@@ -352,9 +352,9 @@ __device__ __forceinline__ double chunk_log_decay(const Mamba2Params& p, int64_t
 // within a sequence; the last chunk of a sequence with an odd chunk count
 // is a pair of one.  Each half of the workgroup loads one chunk; the first
 // is staged (B and x rows, row-major), its tiles formed, then the second
-// staged over it.  The
-// workgroup of a pair's second chunk has nothing to do.  The grid is one
-// dimensional, head fastest: workgroups are dealt to the XCDs in turn, so
+// staged over it.  With one sequence the grid holds one workgroup per pair;
+// otherwise one per chunk, and the workgroup of a pair's second chunk has
+// nothing to do.  The grid is one dimensional, head fastest: workgroups are dealt to the XCDs in turn, so
 // with the chunk fastest every busy workgroup would land on every other XCD.
 // With H a multiple of 8 the heads are permuted so that one XCD takes whole
 // groups of heads, which share B.
@@ -377,11 +377,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSsdStateWa
   __shared__ double lc_s[2];
   __shared__ float elc_s[2];
 
-  const int hx = (int)(blockIdx.x % (unsigned)p.H), cid = (int)(blockIdx.x / (unsigned)p.H);
+  const int hx = (int)(blockIdx.x % (unsigned)p.H), bx = (int)(blockIdx.x / (unsigned)p.H);
+  const int cid = ws.single ? 2 * bx : bx;
   const int h = p.H % 8 == 0 ? (hx % 8) * (p.H / 8) + hx / 8 : hx;
   const int seq = ws.single ? 0 : ws.chunk_seq[cid];
   const int c_first = ws.single ? 0 : ws.seq_chunk_off[seq];
-  if ((cid - c_first) & 1) return;  // the second chunk of a pair: its first chunk's workgroup does it
+  if ((cid - c_first) & 1) return;
   const int c_end = ws.single ? (int)p.num_chunks : ws.seq_chunk_off[seq + 1];
   const bool two = cid + 1 < c_end;
   const int g = h / (p.H / p.G);
@@ -1011,7 +1012,8 @@ template <typename ActT, int P, int N>
 hipError_t launch_chunked_pn(const Mamba2Params& p, const SsdWs& ws, hipStream_t stream) {
   if (p.num_chunks > 0) {
     const dim3 grid((unsigned)p.num_chunks, p.H);
-    ssd_state_kernel<ActT, P, N><<<dim3((unsigned)(p.num_chunks * p.H)), 512, 0, stream>>>(p, ws);
+    const int64_t units = ws.single ? (p.num_chunks + 1) / 2 : p.num_chunks;
+    ssd_state_kernel<ActT, P, N><<<dim3((unsigned)(units * p.H)), 512, 0, stream>>>(p, ws);
     switch (p.state) {
       case GDN_F32: ssd_pass_kernel<float><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
       case GDN_BF16: ssd_pass_kernel<bf16><<<dim3(P * N / 1024, p.H, p.Nseq), 256, 0, stream>>>(p, ws); break;
